@@ -1,0 +1,405 @@
+// C ABI of libspechead: argument validation (host only, before any HIP call), workspace
+// carving and the kernel sequence of each call.  Declarations and contracts: spechead.h.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/spechead.h"
+#include "device_common.h"
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* where) {
+  return fail(SH_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+constexpr int64_t kMaxV = (int64_t{1} << 31) - 64;
+constexpr int64_t kMaxRowBytes = 16 * 1024;     // d * esize for the row-dot and gather kernels
+constexpr int64_t kMaxK = 16384;
+constexpr int64_t kMaxGamma = 64;
+constexpr int kValuMaxRows = 8;                 // skinny path up to this many rows
+constexpr int kMfmaMaxRows = 256;               // rows per MFMA pass (8 column blocks)
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+size_t esize(int dtype) { return dtype == SH_BF16 ? 2 : 4; }
+
+int check_dtype_mode(int dtype, int mode) {
+  if (dtype != SH_F32 && dtype != SH_BF16) return fail(SH_ERR_DTYPE, "unknown dtype %d", dtype);
+  if (mode != SH_GREEDY && mode != SH_SAMPLE) return fail(SH_ERR_DTYPE, "unknown mode %d", mode);
+  return SH_OK;
+}
+
+int check_temperature(float T) {
+  if (!(T > 0.f) || !std::isfinite(T)) return fail(SH_ERR_PARAM, "temperature must be > 0 and finite");
+  return SH_OK;
+}
+
+int check_rowlen(const char* name, int64_t n, int dtype) {
+  if (n < 1) return fail(SH_ERR_SHAPE, "%s must be >= 1", name);
+  if ((n * static_cast<int64_t>(esize(dtype))) % 16 != 0)
+    return fail(SH_ERR_SHAPE, "%s * element size must be a multiple of 16 bytes (got %lld)", name,
+                static_cast<long long>(n));
+  return SH_OK;
+}
+
+int check_ptr(const void* p, const char* name) {
+  if (p == nullptr) return fail(SH_ERR_NULL, "%s is NULL", name);
+  if (!aligned(p, 16)) return fail(SH_ERR_ALIGN, "%s is not 16-byte aligned", name);
+  return SH_OK;
+}
+int check_out(const void* p, const char* name) {
+  if (p == nullptr) return fail(SH_ERR_NULL, "%s is NULL", name);
+  if (!aligned(p, 4)) return fail(SH_ERR_ALIGN, "%s is not 4-byte aligned", name);
+  return SH_OK;
+}
+int check_opt_out(const void* p, const char* name) {
+  if (p != nullptr && !aligned(p, 4)) return fail(SH_ERR_ALIGN, "%s is not 4-byte aligned", name);
+  return SH_OK;
+}
+
+struct HeadLayout {
+  size_t hr_off, hr_bytes;
+  size_t part_off, part_bytes;
+  size_t score_off, score_bytes;
+  size_t z_off, z_bytes;
+  size_t total;
+};
+
+HeadLayout head_layout(int op, int64_t M, int64_t r, int64_t V, int64_t k, int dtype) {
+  HeadLayout L{};
+  size_t off = 0;
+  L.hr_off = off;
+  L.hr_bytes = (op == SH_OP_DENSE) ? 0 : align_up(static_cast<size_t>(M * r) * esize(dtype), 256);
+  off += L.hr_bytes;
+  L.part_off = off;
+  L.part_bytes = (op == SH_OP_SPECVOCAB) ? 0 : align_up(static_cast<size_t>(M) * sh::kMaxPartials * sizeof(sh::Partial), 256);
+  off += L.part_bytes;
+  L.score_off = off;
+  L.score_bytes = (op == SH_OP_SPECVOCAB) ? align_up(static_cast<size_t>(M * V) * 4, 256) : 0;
+  off += L.score_bytes;
+  L.z_off = off;
+  L.z_bytes = (op == SH_OP_SPECVOCAB) ? align_up(static_cast<size_t>(M * k) * 4, 256) : 0;
+  off += L.z_bytes;
+  L.total = off;
+  return L;
+}
+
+int check_workspace(void* ws, size_t have, size_t need) {
+  if (need == 0) return SH_OK;
+  if (ws == nullptr) return fail(SH_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+  if (!aligned(ws, 256)) return fail(SH_ERR_ALIGN, "workspace is not 256-byte aligned");
+  if (have < need) return fail(SH_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", have, need);
+  return SH_OK;
+}
+
+#define SH_TRY(expr)              \
+  do {                            \
+    const int _rc = (expr);       \
+    if (_rc != SH_OK) return _rc; \
+  } while (0)
+
+#define SH_HIP(expr, where)                      \
+  do {                                           \
+    const hipError_t _e = (expr);                \
+    if (_e != hipSuccess) return hip_fail(_e, where); \
+  } while (0)
+
+// Stream z = W x over V rows for M rows of x, then finalize selection.  Shared by the dense
+// and low-rank heads.
+int run_head(const void* x, int64_t M, int64_t K, const void* W, int64_t V, int dtype, int mode,
+             float temperature, uint64_t seed, uint64_t offset, int32_t* token, float* lse,
+             float* logprob, float* logits, sh::Partial* partials, hipStream_t st) {
+  const bool bf16 = dtype == SH_BF16;
+  const float invT = 1.0f / temperature;
+  int stats = mode == SH_SAMPLE ? sh::kStatsSample
+                                : ((lse != nullptr || logprob != nullptr) ? sh::kStatsLse : sh::kStatsArgmax);
+  const bool mfma = bf16 && M > kValuMaxRows;
+  const int64_t chunk = mfma ? kMfmaMaxRows : kValuMaxRows;
+  int producers = 0;
+  for (int64_t m0 = 0; m0 < M; m0 += chunk) {
+    const int64_t mc = (M - m0) < chunk ? (M - m0) : chunk;
+    sh::StreamArgs a{};
+    a.W = W;
+    a.x = static_cast<const char*>(x) + static_cast<size_t>(m0 * K) * esize(dtype);
+    a.V = V;
+    a.K = K;
+    a.M = static_cast<int>(mc);
+    a.bf16 = bf16;
+    a.stats = stats;
+    a.invT = invT;
+    a.seed = seed;
+    a.offset = offset;
+    a.row0 = m0;
+    a.zout = logits ? logits + m0 * V : nullptr;
+    a.zout_ld = V;
+    a.partials = partials + m0 * sh::kMaxPartials;
+    a.partials_ld = sh::kMaxPartials;
+    int p = 0;
+    SH_HIP(sh::launch_stream(a, mfma, &p, st), "head stream kernel");
+    producers = p;
+  }
+  sh::FinalizeArgs f{};
+  f.partials = partials;
+  f.partials_ld = sh::kMaxPartials;
+  f.P = producers;
+  f.W = W;
+  f.x = x;
+  f.V = V;
+  f.K = K;
+  f.M = static_cast<int>(M);
+  f.bf16 = bf16;
+  f.mode = mode == SH_SAMPLE ? 1 : 0;
+  f.invT = invT;
+  f.seed = seed;
+  f.offset = offset;
+  f.row0 = 0;
+  f.token = token;
+  f.lse = lse;
+  f.logprob = logprob;
+  SH_HIP(sh::launch_head_finalize(f, st), "head finalize kernel");
+  return SH_OK;
+}
+
+int check_common_head(const void* h, int64_t M, int64_t d, int64_t V, int dtype, int mode,
+                      float temperature, int32_t* token, float* lse, float* logprob) {
+  SH_TRY(check_dtype_mode(dtype, mode));
+  SH_TRY(check_temperature(temperature));
+  SH_TRY(check_ptr(h, "h"));
+  if (M < 1 || M > (int64_t{1} << 20)) return fail(SH_ERR_SHAPE, "M must be in [1, 2^20]");
+  SH_TRY(check_rowlen("d", d, dtype));
+  if (d * static_cast<int64_t>(esize(dtype)) > kMaxRowBytes)
+    return fail(SH_ERR_UNSUPPORTED, "d * element size above %lld bytes", static_cast<long long>(kMaxRowBytes));
+  if (V < 1 || V > kMaxV) return fail(SH_ERR_SHAPE, "V must be in [1, 2^31 - 64]");
+  SH_TRY(check_out(token, "token"));
+  SH_TRY(check_opt_out(lse, "lse"));
+  SH_TRY(check_opt_out(logprob, "logprob"));
+  return SH_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sh_status_str(int status) {
+  switch (status) {
+    case SH_OK: return "ok";
+    case SH_ERR_NULL: return "null pointer";
+    case SH_ERR_SHAPE: return "bad shape";
+    case SH_ERR_DTYPE: return "bad dtype or mode";
+    case SH_ERR_ALIGN: return "misaligned pointer";
+    case SH_ERR_WORKSPACE: return "workspace missing or too small";
+    case SH_ERR_PARAM: return "bad parameter";
+    case SH_ERR_UNSUPPORTED: return "unsupported";
+    case SH_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char* sh_last_error(void) { return g_last_error.c_str(); }
+
+size_t sh_head_workspace_bytes(int op, int64_t M, int64_t d, int64_t r, int64_t V, int64_t k) {
+  if (M < 1 || d < 1 || V < 1) return 0;
+  if (op == SH_OP_DENSE) r = 0;
+  else if (r < 1) return 0;
+  if (op == SH_OP_SPECVOCAB && (k < 1 || k > V)) return 0;
+  if (op != SH_OP_DENSE && op != SH_OP_LOWRANK && op != SH_OP_SPECVOCAB) return 0;
+  // sized for f32 intermediates so one workspace serves both dtypes
+  return head_layout(op, M, r, V, k, SH_F32).total;
+}
+
+size_t sh_verify_workspace_bytes(int mode, int64_t B, int64_t gamma, int64_t V) {
+  if ((mode != SH_GREEDY && mode != SH_SAMPLE) || B < 1 || gamma < 1 || V < 1) return 0;
+  const int64_t R = mode == SH_GREEDY ? gamma + 1 : 2 * gamma + 1;
+  const int S = sh::verify_segments(B, gamma, V, mode);
+  return align_up(static_cast<size_t>(B * R * S) * sizeof(sh::Partial), 256);
+}
+
+size_t sh_topk_workspace_bytes(int64_t M, int64_t V, int64_t k) {
+  (void)M;
+  (void)V;
+  (void)k;
+  return 0;
+}
+
+int draft_head_dense(const void* h, int64_t M, int64_t d, const void* W, int64_t V, int dtype,
+                     int mode, float temperature, uint64_t seed, uint64_t offset, int32_t* token,
+                     float* lse, float* logprob, float* logits, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  SH_TRY(check_common_head(h, M, d, V, dtype, mode, temperature, token, lse, logprob));
+  SH_TRY(check_ptr(W, "W"));
+  SH_TRY(check_opt_out(logits, "logits"));
+  const HeadLayout L = head_layout(SH_OP_DENSE, M, 0, V, 0, SH_F32);
+  SH_TRY(check_workspace(workspace, workspace_bytes, L.total));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  auto* parts = reinterpret_cast<sh::Partial*>(static_cast<char*>(workspace) + L.part_off);
+  return run_head(h, M, d, W, V, dtype, mode, temperature, seed, offset, token, lse, logprob,
+                  logits, parts, st);
+}
+
+int draft_head_lowrank(const void* h, int64_t M, int64_t d, const void* W_down, int64_t r,
+                       const void* W_up, int64_t V, int dtype, int mode, float temperature,
+                       uint64_t seed, uint64_t offset, int32_t* token, float* lse, float* logprob,
+                       float* logits, void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  SH_TRY(check_common_head(h, M, d, V, dtype, mode, temperature, token, lse, logprob));
+  SH_TRY(check_ptr(W_down, "W_down"));
+  SH_TRY(check_ptr(W_up, "W_up"));
+  SH_TRY(check_rowlen("r", r, dtype));
+  if (r * static_cast<int64_t>(esize(dtype)) > kMaxRowBytes)
+    return fail(SH_ERR_UNSUPPORTED, "r * element size above %lld bytes", static_cast<long long>(kMaxRowBytes));
+  SH_TRY(check_opt_out(logits, "logits"));
+  const HeadLayout L = head_layout(SH_OP_LOWRANK, M, r, V, 0, SH_F32);
+  SH_TRY(check_workspace(workspace, workspace_bytes, L.total));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  void* hr = ws + L.hr_off;
+  auto* parts = reinterpret_cast<sh::Partial*>(ws + L.part_off);
+  SH_HIP(sh::launch_rowdot(W_down, h, r, d, M, dtype == SH_BF16, hr, st), "down-projection kernel");
+  return run_head(hr, M, r, W_up, V, dtype, mode, temperature, seed, offset, token, lse, logprob,
+                  logits, parts, st);
+}
+
+int draft_head_specvocab(const void* h, int64_t M, int64_t d, const void* W_down, int64_t dprime,
+                         const void* W_vocab, const void* U, int64_t V, int64_t k, int dtype,
+                         int mode, float temperature, uint64_t seed, uint64_t offset,
+                         int32_t* topk_idx, float* topk_logit, float* topk_prob, int32_t* token,
+                         float* lse, float* logprob, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  g_last_error.clear();
+  SH_TRY(check_common_head(h, M, d, V, dtype, mode, temperature, token, lse, logprob));
+  SH_TRY(check_ptr(W_down, "W_down"));
+  SH_TRY(check_ptr(W_vocab, "W_vocab"));
+  SH_TRY(check_ptr(U, "U"));
+  SH_TRY(check_rowlen("dprime", dprime, dtype));
+  if (dprime * static_cast<int64_t>(esize(dtype)) > kMaxRowBytes)
+    return fail(SH_ERR_UNSUPPORTED, "dprime * element size above %lld bytes", static_cast<long long>(kMaxRowBytes));
+  if (k < 1 || k > V) return fail(SH_ERR_PARAM, "k must be in [1, V]");
+  if (k > kMaxK) return fail(SH_ERR_UNSUPPORTED, "k above %lld", static_cast<long long>(kMaxK));
+  SH_TRY(check_out(topk_idx, "topk_idx"));
+  SH_TRY(check_opt_out(topk_logit, "topk_logit"));
+  SH_TRY(check_opt_out(topk_prob, "topk_prob"));
+  const HeadLayout L = head_layout(SH_OP_SPECVOCAB, M, dprime, V, k, SH_F32);
+  SH_TRY(check_workspace(workspace, workspace_bytes, L.total));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  void* hp = ws + L.hr_off;
+  float* scores = reinterpret_cast<float*>(ws + L.score_off);
+  float* zbuf = reinterpret_cast<float*>(ws + L.z_off);
+  const bool bf16 = dtype == SH_BF16;
+  SH_HIP(sh::launch_rowdot(W_down, h, dprime, d, M, bf16, hp, st), "reduced-state kernel");
+  const bool mfma = bf16 && M > kValuMaxRows;
+  const int64_t chunk = mfma ? kMfmaMaxRows : kValuMaxRows;
+  for (int64_t m0 = 0; m0 < M; m0 += chunk) {
+    const int64_t mc = (M - m0) < chunk ? (M - m0) : chunk;
+    sh::StreamArgs a{};
+    a.W = W_vocab;
+    a.x = static_cast<const char*>(hp) + static_cast<size_t>(m0 * dprime) * esize(dtype);
+    a.V = V;
+    a.K = dprime;
+    a.M = static_cast<int>(mc);
+    a.bf16 = bf16;
+    a.stats = sh::kStatsNone;
+    a.invT = 1.f;
+    a.row0 = m0;
+    a.zout = scores + m0 * V;
+    a.zout_ld = V;
+    a.partials = nullptr;
+    a.partials_ld = 0;
+    int p = 0;
+    SH_HIP(sh::launch_stream(a, mfma, &p, st), "approximate scorer kernel");
+  }
+  SH_HIP(sh::launch_topk(scores, M, V, k, topk_idx, st), "top-k kernel");
+  SH_HIP(sh::launch_gather_exact(U, h, topk_idx, M, d, V, k, bf16, zbuf, st), "gather kernel");
+  SH_HIP(sh::launch_gather_finalize(zbuf, topk_idx, M, k, mode == SH_SAMPLE ? 1 : 0, 1.0f / temperature,
+                                    seed, offset, topk_logit, topk_prob, token, lse, logprob, st),
+         "candidate softmax kernel");
+  return SH_OK;
+}
+
+int spec_verify(int mode, int64_t B, int64_t gamma, int64_t V, int dtype, const void* target_logits,
+                const void* draft_logits, const int32_t* draft_tokens, const float* u_accept,
+                float temperature, uint64_t seed, uint64_t offset, int32_t* accept_len,
+                int32_t* out_tokens, void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  SH_TRY(check_dtype_mode(dtype, mode));
+  SH_TRY(check_temperature(temperature));
+  if (B < 1 || B > (int64_t{1} << 20)) return fail(SH_ERR_SHAPE, "B must be in [1, 2^20]");
+  if (gamma < 1 || gamma > kMaxGamma) return fail(SH_ERR_SHAPE, "gamma must be in [1, %lld]", static_cast<long long>(kMaxGamma));
+  SH_TRY(check_rowlen("V", V, dtype));
+  if (V > kMaxV) return fail(SH_ERR_SHAPE, "V above 2^31 - 64");
+  if (B * (gamma + 1) > 65535) return fail(SH_ERR_UNSUPPORTED, "B * (gamma + 1) above 65535");
+  SH_TRY(check_ptr(target_logits, "target_logits"));
+  if (draft_tokens == nullptr) return fail(SH_ERR_NULL, "draft_tokens is NULL");
+  if (!aligned(draft_tokens, 4)) return fail(SH_ERR_ALIGN, "draft_tokens is not 4-byte aligned");
+  if (mode == SH_SAMPLE) {
+    SH_TRY(check_ptr(draft_logits, "draft_logits"));
+    if (u_accept == nullptr) return fail(SH_ERR_NULL, "u_accept is NULL");
+    if (!aligned(u_accept, 4)) return fail(SH_ERR_ALIGN, "u_accept is not 4-byte aligned");
+  }
+  SH_TRY(check_out(accept_len, "accept_len"));
+  SH_TRY(check_out(out_tokens, "out_tokens"));
+  const size_t need = sh_verify_workspace_bytes(mode, B, gamma, V);
+  SH_TRY(check_workspace(workspace, workspace_bytes, need));
+  sh::VerifyArgs a{};
+  a.mode = mode == SH_SAMPLE ? 1 : 0;
+  a.B = B;
+  a.gamma = gamma;
+  a.V = V;
+  a.bf16 = dtype == SH_BF16;
+  a.target = target_logits;
+  a.draft = draft_logits;
+  a.tokens = draft_tokens;
+  a.u = u_accept;
+  a.invT = 1.0f / temperature;
+  a.seed = seed;
+  a.offset = offset;
+  a.accept_len = accept_len;
+  a.out_tokens = out_tokens;
+  a.partials = static_cast<sh::Partial*>(workspace);
+  a.S = sh::verify_segments(B, gamma, V, mode);
+  SH_HIP(sh::launch_verify(a, static_cast<hipStream_t>(stream)), "verify kernels");
+  return SH_OK;
+}
+
+int sh_topk(const float* scores, int64_t M, int64_t V, int64_t k, int32_t* topk_idx, void* workspace,
+            size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  SH_TRY(check_ptr(scores, "scores"));
+  SH_TRY(check_out(topk_idx, "topk_idx"));
+  if (M < 1 || M > 65535) return fail(SH_ERR_SHAPE, "M must be in [1, 65535]");
+  if (V < 1 || V > kMaxV) return fail(SH_ERR_SHAPE, "V must be in [1, 2^31 - 64]");
+  if (k < 1 || k > V) return fail(SH_ERR_PARAM, "k must be in [1, V]");
+  SH_TRY(check_workspace(workspace, workspace_bytes, sh_topk_workspace_bytes(M, V, k)));
+  SH_HIP(sh::launch_topk(scores, M, V, k, topk_idx, static_cast<hipStream_t>(stream)), "top-k kernel");
+  return SH_OK;
+}
+
+int sh_philox_uniform(uint64_t seed, uint64_t offset, uint32_t purpose, int64_t rows, int64_t n,
+                      float* out, void* stream) {
+  g_last_error.clear();
+  if (out == nullptr) return fail(SH_ERR_NULL, "out is NULL");
+  if (!aligned(out, 4)) return fail(SH_ERR_ALIGN, "out is not 4-byte aligned");
+  if (rows < 1 || n < 1 || rows * n > (int64_t{1} << 31))
+    return fail(SH_ERR_SHAPE, "rows * n must be in [1, 2^31]");
+  SH_HIP(sh::launch_philox(seed, offset, purpose, rows, n, out, static_cast<hipStream_t>(stream)),
+         "philox kernel");
+  return SH_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,194 @@
+// Device-side helpers shared by the head, top-k and verification kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sh {
+
+constexpr int kWave = 64;
+constexpr int kGroup = 64;           // sampling group: 64 consecutive candidates
+constexpr int kMaxPartials = 2048;   // upper bound on producer workgroups per row
+
+// ---------------------------------------------------------------------------------------
+// Per-row partial result of a streaming pass over part of the vocabulary.
+//   (m, s):      online log-sum-exp of y = z / T over the rows seen: lse = m + log s
+//   (gscore, g): best group score L_g + Gumbel(u_g) and its group id (sampling)
+//   (zmax, zid): largest raw logit and its id, lowest id on ties (greedy)
+// ---------------------------------------------------------------------------------------
+struct alignas(16) Partial {
+  float m, s, gscore;
+  int32_t g;
+  float zmax;
+  int32_t zid;
+  float pad0, pad1;
+};
+
+__device__ __forceinline__ Partial partial_empty() {
+  Partial p;
+  p.m = -INFINITY;
+  p.s = 0.f;
+  p.gscore = -INFINITY;
+  p.g = 0x7fffffff;
+  p.zmax = -INFINITY;
+  p.zid = 0x7fffffff;
+  p.pad0 = p.pad1 = 0.f;
+  return p;
+}
+
+__device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
+  const float mn = fmaxf(m, m2);
+  if (mn == -INFINITY) {
+    m = mn;
+    s = 0.f;
+    return;
+  }
+  s = s * __expf(m - mn) + s2 * __expf(m2 - mn);
+  m = mn;
+}
+
+// larger value wins, lower index on ties
+__device__ __forceinline__ void argmax_merge(float& v, int32_t& i, float v2, int32_t i2) {
+  if (v2 > v || (v2 == v && i2 < i)) {
+    v = v2;
+    i = i2;
+  }
+}
+
+__device__ __forceinline__ void partial_merge(Partial& a, const Partial& b) {
+  lse_merge(a.m, a.s, b.m, b.s);
+  argmax_merge(a.gscore, a.g, b.gscore, b.g);
+  argmax_merge(a.zmax, a.zid, b.zmax, b.zid);
+}
+
+// ---------------------------------------------------------------------------------------
+// bf16
+// ---------------------------------------------------------------------------------------
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t v) {
+  return __uint_as_float(static_cast<uint32_t>(v) << 16);
+}
+
+// a.lo*b.lo + a.hi*b.hi + acc (bf16 pairs, float accumulate)
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), acc, false);
+}
+
+// 16-byte chunk dot products: 8 bf16 or 4 f32 elements
+__device__ __forceinline__ float chunk_dot_bf16(const uint4& w, const uint4& x, float acc) {
+  acc = dot2_bf16(w.x, x.x, acc);
+  acc = dot2_bf16(w.y, x.y, acc);
+  acc = dot2_bf16(w.z, x.z, acc);
+  acc = dot2_bf16(w.w, x.w, acc);
+  return acc;
+}
+__device__ __forceinline__ float chunk_dot_f32(const uint4& w, const uint4& x, float acc) {
+  acc = fmaf(__uint_as_float(w.x), __uint_as_float(x.x), acc);
+  acc = fmaf(__uint_as_float(w.y), __uint_as_float(x.y), acc);
+  acc = fmaf(__uint_as_float(w.z), __uint_as_float(x.z), acc);
+  acc = fmaf(__uint_as_float(w.w), __uint_as_float(x.w), acc);
+  return acc;
+}
+template <bool BF16>
+__device__ __forceinline__ float chunk_dot(const uint4& w, const uint4& x, float acc) {
+  if constexpr (BF16)
+    return chunk_dot_bf16(w, x, acc);
+  else
+    return chunk_dot_f32(w, x, acc);
+}
+
+// float -> bf16 bits, round to nearest even (finite inputs; NaN stays NaN)
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  const uint32_t r = u + 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(r >> 16);
+}
+
+// ---------------------------------------------------------------------------------------
+// Philox4x64-10 (Salmon, Moraes, Dror, Shaw, SC'11): key (seed, 0),
+// counter (index / 4, row, purpose, offset); the draw is word index % 4 mapped to
+// ((w >> 41) + 0.5) * 2^-23, exact in float32 and strictly inside (0, 1).
+// ---------------------------------------------------------------------------------------
+enum Purpose : uint32_t {
+  kDraftGroup = 0,
+  kDraftElem = 1,
+  kAccept = 2,
+  kResidGroup = 3,
+  kResidElem = 4,
+  kBonusGroup = 5,
+  kBonusElem = 6
+};
+
+__device__ __forceinline__ uint64_t philox_word(uint64_t seed, uint64_t offset, uint32_t purpose,
+                                                uint64_t row, uint64_t index) {
+  const uint64_t kM0 = 0xD2E7470EE14C6C93ull, kM1 = 0xCA5A826395121157ull;
+  const uint64_t kW0 = 0x9E3779B97F4A7C15ull, kW1 = 0xBB67AE8584CAA73Bull;
+  uint64_t c0 = index >> 2, c1 = row, c2 = purpose, c3 = offset;
+  uint64_t k0 = seed, k1 = 0;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) {
+      k0 += kW0;
+      k1 += kW1;
+    }
+    const uint64_t hi0 = __umul64hi(kM0, c0), lo0 = kM0 * c0;
+    const uint64_t hi1 = __umul64hi(kM1, c2), lo1 = kM1 * c2;
+    const uint64_t n0 = hi1 ^ c1 ^ k0;
+    const uint64_t n2 = hi0 ^ c3 ^ k1;
+    c0 = n0;
+    c1 = lo1;
+    c2 = n2;
+    c3 = lo0;
+  }
+  const uint32_t sel = static_cast<uint32_t>(index & 3);
+  return sel == 0 ? c0 : sel == 1 ? c1 : sel == 2 ? c2 : c3;
+}
+
+__device__ __forceinline__ float philox_uniform(uint64_t seed, uint64_t offset, uint32_t purpose,
+                                                uint64_t row, uint64_t index) {
+  const uint64_t w = philox_word(seed, offset, purpose, row, index);
+  return (static_cast<float>(static_cast<uint32_t>(w >> 41)) + 0.5f) * 0x1p-23f;
+}
+
+// standard Gumbel variate from a uniform in (0,1)
+__device__ __forceinline__ float gumbel(float u) { return -logf(-logf(u)); }
+
+// ---------------------------------------------------------------------------------------
+// wave helpers
+// ---------------------------------------------------------------------------------------
+__device__ __forceinline__ int lane_id() { return static_cast<int>(threadIdx.x) & (kWave - 1); }
+__device__ __forceinline__ int wave_id() { return static_cast<int>(threadIdx.x) / kWave; }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) v += __shfl_xor(v, s);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) v = fmaxf(v, __shfl_xor(v, s));
+  return v;
+}
+// wave-wide argmax, lowest index on ties; every lane gets the result
+__device__ __forceinline__ void wave_argmax(float& v, int32_t& i) {
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) {
+    const float v2 = __shfl_xor(v, s);
+    const int32_t i2 = __shfl_xor(i, s);
+    argmax_merge(v, i, v2, i2);
+  }
+}
+
+__device__ __forceinline__ uint4 load16(const void* p) {
+  return *reinterpret_cast<const uint4*>(p);
+}
+__device__ __forceinline__ uint4 zero16() { return make_uint4(0u, 0u, 0u, 0u); }
+
+}  // namespace sh

@@ -1,0 +1,99 @@
+// Internal launch interface between the C-ABI layer (api.hip) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sh {
+
+struct Partial;
+
+enum Stats : int {
+  kStatsNone = 0,    // only write z (scores)
+  kStatsArgmax = 1,  // greedy token, no lse
+  kStatsLse = 2,     // greedy token + lse / logprob
+  kStatsSample = 3   // lse + group-Gumbel scores for sampling
+};
+
+// One streaming pass z[m, v] = W[v, :] . x[m, :] for v < V, m < M (M rows of this chunk).
+struct StreamArgs {
+  const void* W;      // [V, K] dtype
+  const void* x;      // [M, K] dtype
+  int64_t V, K;
+  int M;
+  bool bf16;
+  int stats;
+  float invT;
+  uint64_t seed, offset;
+  int64_t row0;          // global row index of x[0] (Philox row)
+  float* zout;           // nullable [M, zout_ld]
+  int64_t zout_ld;
+  Partial* partials;     // [M, partials_ld], one per producer workgroup
+  int64_t partials_ld;
+};
+
+struct FinalizeArgs {
+  const Partial* partials;  // [M, ld]
+  int64_t partials_ld;
+  int P;                    // producers per row
+  const void* W;            // [V, K] (sampling: recompute the winning group)
+  const void* x;            // [M, K]
+  int64_t V, K;
+  int M;
+  bool bf16;
+  int mode;                 // 0 greedy, 1 sample
+  float invT;
+  uint64_t seed, offset;
+  int64_t row0;
+  int32_t* token;
+  float* lse;
+  float* logprob;
+};
+
+struct DeviceInfo {
+  int cus;
+  int max_lds;   // bytes of dynamic LDS a workgroup may use
+};
+hipError_t device_info(DeviceInfo* out);
+
+// h_out[m, j] = round_dtype(sum_k Wd[j, k] x[m, k]), j < R
+hipError_t launch_rowdot(const void* Wd, const void* x, int64_t R, int64_t K, int64_t M, bool bf16,
+                         void* out, hipStream_t st);
+// Chooses the VALU (skinny) or MFMA path; returns the number of producer workgroups.
+hipError_t launch_stream(const StreamArgs& a, bool use_mfma, int* producers, hipStream_t st);
+hipError_t launch_head_finalize(const FinalizeArgs& f, hipStream_t st);
+
+// SpecVocab pieces
+hipError_t launch_topk(const float* scores, int64_t M, int64_t V, int64_t k, int32_t* idx,
+                       hipStream_t st);
+hipError_t launch_gather_exact(const void* U, const void* h, const int32_t* idx, int64_t M,
+                               int64_t d, int64_t V, int64_t k, bool bf16, float* zbuf,
+                               hipStream_t st);
+hipError_t launch_gather_finalize(const float* zbuf, const int32_t* idx, int64_t M, int64_t k,
+                                  int mode, float invT, uint64_t seed, uint64_t offset,
+                                  float* topk_logit, float* topk_prob, int32_t* token, float* lse,
+                                  float* logprob, hipStream_t st);
+
+// verification
+struct VerifyArgs {
+  int mode;
+  int64_t B, gamma, V;
+  bool bf16;
+  const void* target;
+  const void* draft;
+  const int32_t* tokens;
+  const float* u;
+  float invT;
+  uint64_t seed, offset;
+  int32_t* accept_len;
+  int32_t* out_tokens;
+  Partial* partials;   // [B, rows, S]
+  int S;
+};
+int verify_segments(int64_t B, int64_t gamma, int64_t V, int mode);
+hipError_t launch_verify(const VerifyArgs& a, hipStream_t st);
+
+hipError_t launch_philox(uint64_t seed, uint64_t offset, uint32_t purpose, int64_t rows, int64_t n,
+                         float* out, hipStream_t st);
+
+}  // namespace sh

@@ -1,0 +1,228 @@
+"""Thin ctypes binding of libspechead.so (C ABI in include/spechead.h).
+
+Argument marshalling only: every step of the head and verification path runs in the HIP
+kernels behind the C ABI.  PyTorch provides device memory and the current stream.  If the
+library has not been built, ``load()`` raises; there is no fallback.
+"""
+import ctypes
+import os
+import threading
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspechead.so")
+
+SH_OK, SH_ERR_NULL, SH_ERR_SHAPE, SH_ERR_DTYPE, SH_ERR_ALIGN = 0, 1, 2, 3, 4
+SH_ERR_WORKSPACE, SH_ERR_PARAM, SH_ERR_UNSUPPORTED, SH_ERR_HIP = 5, 6, 7, 8
+SH_F32, SH_BF16 = 0, 1
+GREEDY, SAMPLE = 0, 1
+OP_DENSE, OP_LOWRANK, OP_SPECVOCAB = 0, 1, 2
+
+_lib = None
+_lock = threading.Lock()
+
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_u64 = ctypes.c_uint64
+_f = ctypes.c_float
+_i = ctypes.c_int
+_sz = ctypes.c_size_t
+
+_SIGS = {
+    "sh_head_workspace_bytes": (_sz, [_i, _i64, _i64, _i64, _i64, _i64]),
+    "sh_verify_workspace_bytes": (_sz, [_i, _i64, _i64, _i64]),
+    "sh_topk_workspace_bytes": (_sz, [_i64, _i64, _i64]),
+    "draft_head_dense": (_i, [_vp, _i64, _i64, _vp, _i64, _i, _i, _f, _u64, _u64, _vp, _vp, _vp, _vp,
+                              _vp, _sz, _vp]),
+    "draft_head_lowrank": (_i, [_vp, _i64, _i64, _vp, _i64, _vp, _i64, _i, _i, _f, _u64, _u64, _vp,
+                                _vp, _vp, _vp, _vp, _sz, _vp]),
+    "draft_head_specvocab": (_i, [_vp, _i64, _i64, _vp, _i64, _vp, _vp, _i64, _i64, _i, _i, _f, _u64,
+                                  _u64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "spec_verify": (_i, [_i, _i64, _i64, _i64, _i, _vp, _vp, _vp, _vp, _f, _u64, _u64, _vp, _vp, _vp,
+                         _sz, _vp]),
+    "sh_topk": (_i, [_vp, _i64, _i64, _i64, _vp, _vp, _sz, _vp]),
+    "sh_philox_uniform": (_i, [_u64, _u64, ctypes.c_uint32, _i64, _i64, _vp, _vp]),
+    "sh_status_str": (ctypes.c_char_p, [_i]),
+    "sh_last_error": (ctypes.c_char_p, []),
+}
+
+
+class SpecHeadError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"spechead status {status}: {msg}")
+        self.status = status
+
+
+def load(path=None):
+    """Load libspechead.so (once) and declare its signatures.  Raises if it is missing."""
+    global _lib
+    with _lock:
+        if _lib is not None and path is None:
+            return _lib
+        p = path or LIB_PATH
+        if not os.path.exists(p):
+            raise FileNotFoundError(
+                f"{p} not found: build it with `python -m drafter_lm_head_slimspec_amd.build`")
+        lib = ctypes.CDLL(p)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        if path is None:
+            _lib = lib
+        return lib
+
+
+def _check(rc):
+    if rc != SH_OK:
+        lib = load()
+        raise SpecHeadError(rc, lib.sh_last_error().decode(errors="replace"))
+
+
+def _dt(t):
+    if t.dtype == torch.bfloat16:
+        return SH_BF16
+    if t.dtype == torch.float32:
+        return SH_F32
+    raise TypeError(f"unsupported dtype {t.dtype}: use torch.bfloat16 or torch.float32")
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _mode(mode):
+    if mode in ("greedy", GREEDY):
+        return GREEDY
+    if mode in ("sample", SAMPLE):
+        return SAMPLE
+    raise ValueError(mode)
+
+
+_ws_cache = {}
+
+
+def workspace(nbytes, device):
+    """Zero-filled device workspace of at least nbytes, cached per (device, stream)."""
+    key = (torch.device(device).index, torch.cuda.current_stream(device).cuda_stream)
+    buf = _ws_cache.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+        _ws_cache[key] = buf
+    return buf
+
+
+def _contig(*ts):
+    for t in ts:
+        if t is not None and not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def draft_head_dense(h, W, mode="greedy", temperature=1.0, seed=0, offset=0, want_logits=False,
+                     want_lse=True):
+    lib = load()
+    _contig(h, W)
+    M, d = h.shape
+    V = W.shape[0]
+    dev = h.device
+    token = torch.empty(M, dtype=torch.int32, device=dev)
+    lse = torch.empty(M, dtype=torch.float32, device=dev) if want_lse else None
+    logprob = torch.empty(M, dtype=torch.float32, device=dev) if want_lse else None
+    logits = torch.empty(M, V, dtype=torch.float32, device=dev) if want_logits else None
+    need = lib.sh_head_workspace_bytes(OP_DENSE, M, d, 0, V, 0)
+    ws = workspace(need, dev)
+    _check(lib.draft_head_dense(_p(h), M, d, _p(W), V, _dt(h), _mode(mode), float(temperature),
+                                int(seed), int(offset), _p(token), _p(lse), _p(logprob), _p(logits),
+                                _p(ws), ws.numel(), _stream(dev)))
+    return {"token": token, "lse": lse, "logprob": logprob, "logits": logits}
+
+
+def draft_head_lowrank(h, W_down, W_up, mode="greedy", temperature=1.0, seed=0, offset=0,
+                       want_logits=False, want_lse=True):
+    lib = load()
+    _contig(h, W_down, W_up)
+    M, d = h.shape
+    r = W_down.shape[0]
+    V = W_up.shape[0]
+    dev = h.device
+    token = torch.empty(M, dtype=torch.int32, device=dev)
+    lse = torch.empty(M, dtype=torch.float32, device=dev) if want_lse else None
+    logprob = torch.empty(M, dtype=torch.float32, device=dev) if want_lse else None
+    logits = torch.empty(M, V, dtype=torch.float32, device=dev) if want_logits else None
+    need = lib.sh_head_workspace_bytes(OP_LOWRANK, M, d, r, V, 0)
+    ws = workspace(need, dev)
+    _check(lib.draft_head_lowrank(_p(h), M, d, _p(W_down), r, _p(W_up), V, _dt(h), _mode(mode),
+                                  float(temperature), int(seed), int(offset), _p(token), _p(lse),
+                                  _p(logprob), _p(logits), _p(ws), ws.numel(), _stream(dev)))
+    return {"token": token, "lse": lse, "logprob": logprob, "logits": logits}
+
+
+def draft_head_specvocab(h, W_down, W_vocab, U, k, mode="greedy", temperature=1.0, seed=0, offset=0,
+                         want_lse=True):
+    lib = load()
+    _contig(h, W_down, W_vocab, U)
+    M, d = h.shape
+    dprime = W_down.shape[0]
+    V = W_vocab.shape[0]
+    dev = h.device
+    idx = torch.empty(M, k, dtype=torch.int32, device=dev)
+    zl = torch.empty(M, k, dtype=torch.float32, device=dev)
+    q = torch.empty(M, k, dtype=torch.float32, device=dev)
+    token = torch.empty(M, dtype=torch.int32, device=dev)
+    lse = torch.empty(M, dtype=torch.float32, device=dev) if want_lse else None
+    logprob = torch.empty(M, dtype=torch.float32, device=dev) if want_lse else None
+    need = lib.sh_head_workspace_bytes(OP_SPECVOCAB, M, d, dprime, V, k)
+    ws = workspace(need, dev)
+    _check(lib.draft_head_specvocab(_p(h), M, d, _p(W_down), dprime, _p(W_vocab), _p(U), V, int(k),
+                                    _dt(h), _mode(mode), float(temperature), int(seed), int(offset),
+                                    _p(idx), _p(zl), _p(q), _p(token), _p(lse), _p(logprob), _p(ws),
+                                    ws.numel(), _stream(dev)))
+    return {"topk_idx": idx, "topk_logit": zl, "topk_prob": q, "token": token, "lse": lse,
+            "logprob": logprob}
+
+
+def spec_verify(target, draft, tokens, u=None, mode="sample", temperature=1.0, seed=0, offset=0):
+    lib = load()
+    m = _mode(mode)
+    _contig(target, draft, tokens, u)
+    B, g1, V = target.shape
+    gamma = g1 - 1
+    dev = target.device
+    if tokens.dtype != torch.int32:
+        raise TypeError("draft tokens must be int32")
+    if u is not None and u.dtype != torch.float32:
+        raise TypeError("u must be float32")
+    acc = torch.empty(B, dtype=torch.int32, device=dev)
+    out = torch.empty(B, gamma + 1, dtype=torch.int32, device=dev)
+    need = lib.sh_verify_workspace_bytes(m, B, gamma, V)
+    ws = workspace(need, dev)
+    _check(lib.spec_verify(m, B, gamma, V, _dt(target), _p(target), _p(draft) if m == SAMPLE else None,
+                           _p(tokens), _p(u) if m == SAMPLE else None, float(temperature), int(seed),
+                           int(offset), _p(acc), _p(out), _p(ws), ws.numel(), _stream(dev)))
+    return acc, out
+
+
+def topk(scores, k):
+    lib = load()
+    _contig(scores)
+    if scores.dtype != torch.float32:
+        raise TypeError("scores must be float32")
+    M, V = scores.shape
+    dev = scores.device
+    idx = torch.empty(M, k, dtype=torch.int32, device=dev)
+    need = lib.sh_topk_workspace_bytes(M, V, k)
+    ws = workspace(need, dev)
+    _check(lib.sh_topk(_p(scores), M, V, int(k), _p(idx), _p(ws), ws.numel(), _stream(dev)))
+    return idx
+
+
+def philox_uniform(seed, offset, purpose, rows, n, device):
+    lib = load()
+    out = torch.empty(rows, n, dtype=torch.float32, device=device)
+    _check(lib.sh_philox_uniform(int(seed), int(offset), int(purpose), rows, n, _p(out),
+                                 _stream(device)))
+    return out

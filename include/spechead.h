@@ -1,0 +1,179 @@
+/*
+ * spechead.h -- C ABI of the MI355X (gfx950) drafter LM-head and speculative-verification
+ * library (libspechead.so).
+ *
+ * What the calls compute (sources: the pages this library is built from):
+ *   - draft_head_dense:     z = W h over the whole vocabulary (SlimSpec write-up, mhpn.cn,
+ *                           section 三: a V x d matrix projects the d-dim hidden state).
+ *   - draft_head_lowrank:   SlimSpec, same section and Q&A Q1: h_r = W_down h (d -> r),
+ *                           z = W_up h_r (r -> V), all V scores kept.
+ *   - draft_head_specvocab: SpecVocab write-up (2kiu.com), sections 2.2.1-2.2.3:
+ *                           h' = W_down h (d' = d/16), s = W_vocab h', K = top-k(s),
+ *                           z' = U[K,:] h, q = softmax(z') over the k candidates.
+ *   - spec_verify:          speculative-decoding explainer (liuchunshan.com), sections
+ *                           "小模型起草，大模型批改" and "为什么答案不会变": greedy
+ *                           longest-prefix match, or rejection sampling accepting with
+ *                           min(1, p/q), residual draw from norm(max(0, p - q)) at the first
+ *                           rejection, bonus draw from the target when all drafts pass.
+ *   Each head is fused with selection: greedy argmax (ties -> lowest id) or sampling from
+ *   softmax(z / T), and returns the row's log-sum-exp and the chosen token's log-probability.
+ *
+ * Conventions (all calls):
+ *   - Buffers are DEVICE pointers owned by the caller, packed row-major, 16-byte aligned
+ *     (the workspace 256-byte aligned).  `stream` is a hipStream_t (NULL = null stream).
+ *   - dtype: SH_F32 (float32) or SH_BF16 (bfloat16 stored as 16-bit patterns) for hidden
+ *     states, weights and logits inputs.  Row lengths must be a multiple of 16 bytes
+ *     (bf16: multiple of 8 elements; f32: multiple of 4).  Outputs are int32 / float32.
+ *   - Return value: SH_OK (0) means all work was enqueued on `stream`; the call never
+ *     synchronises.  Any other value below SH_ERR_HIP means validation failed BEFORE any
+ *     HIP call: nothing was enqueued and no output was touched.  SH_ERR_HIP means a HIP
+ *     runtime call or launch failed; sh_last_error() holds a thread-local message.
+ *   - No allocation: the caller passes a workspace of at least sh_*_workspace_bytes(...)
+ *     bytes.  It must be zero-filled before its first use (e.g. allocated with a zeroing
+ *     allocator); every call leaves its counter area zero again.  Calls that may overlap
+ *     in time must use distinct workspaces.
+ *   - Determinism: identical inputs, seed and offset give bit-identical outputs.
+ *   - Sampling randomness: Philox4x64-10 (Salmon et al., SC'11) with key (seed, 0) and
+ *     counter (index / 4, row, purpose, offset); the draw is output word index % 4 mapped to
+ *     u = ((word >> 41) + 0.5) * 2^-23 in (0,1).  Purposes: 0 draft group, 1 draft element,
+ *     2 verify accept (caller-side), 3 residual group, 4 residual element, 5 bonus group,
+ *     6 bonus element.  A draw from softmax(l) is a two-level Gumbel-max: groups of 64
+ *     consecutive candidates compete with log-sum-exp + Gumbel(u_group) (ties -> lowest
+ *     group), then the members of the winning group with l_i + Gumbel(u_i) (ties -> lowest
+ *     index), which is an exact draw from softmax(l).  Callers advance `offset` per call.
+ */
+#ifndef SPECHEAD_H
+#define SPECHEAD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum sh_status {
+  SH_OK = 0,
+  SH_ERR_NULL = 1,        /* a required pointer is NULL                               */
+  SH_ERR_SHAPE = 2,       /* a size is out of range or inconsistent                   */
+  SH_ERR_DTYPE = 3,       /* unknown dtype or mode                                    */
+  SH_ERR_ALIGN = 4,       /* a pointer is not 16-byte (workspace: 256-byte) aligned    */
+  SH_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required                  */
+  SH_ERR_PARAM = 6,       /* temperature <= 0 or not finite, k outside [1, V], ...    */
+  SH_ERR_UNSUPPORTED = 7, /* valid request this build does not implement              */
+  SH_ERR_HIP = 8          /* a HIP call or kernel launch failed                       */
+};
+
+enum sh_dtype { SH_F32 = 0, SH_BF16 = 1 };
+enum sh_mode { SH_GREEDY = 0, SH_SAMPLE = 1 };
+enum sh_op { SH_OP_DENSE = 0, SH_OP_LOWRANK = 1, SH_OP_SPECVOCAB = 2 };
+
+/* Workspace size for a head call.  op = SH_OP_*; r is the low-rank width (lowrank) or the
+ * reduced width d' (specvocab) and is ignored for dense; k is ignored except for specvocab.
+ * Pure host arithmetic, no HIP call.  Returns 0 for invalid arguments. */
+size_t sh_head_workspace_bytes(int op, int64_t M, int64_t d, int64_t r, int64_t V, int64_t k);
+
+/* Workspace size for spec_verify.  Pure host arithmetic, no HIP call. */
+size_t sh_verify_workspace_bytes(int mode, int64_t B, int64_t gamma, int64_t V);
+
+/*
+ * Dense head (SlimSpec write-up, section 三).
+ *   h       [M, d]   hidden states, dtype
+ *   W       [V, d]   head matrix, dtype
+ *   mode, temperature: SH_GREEDY picks argmax_i z_i (ties -> lowest i); SH_SAMPLE draws from
+ *           softmax(z / T).  temperature must be > 0 and finite in both modes: lse and
+ *           logprob are those of y = z / T.
+ *   seed, offset: Philox key / counter word (sampling; ignored when greedy).  Row index of
+ *           the draw = row of h.
+ *   token   [M] int32 (required)   chosen vocabulary id
+ *   lse     [M] float (nullable)   log sum_i exp(y_i)
+ *   logprob [M] float (nullable)   y_token - lse
+ *   logits  [M, V] float (nullable) raw z, written only when non-NULL (extra M*V*4 bytes)
+ */
+int draft_head_dense(const void* h, int64_t M, int64_t d, const void* W, int64_t V, int dtype,
+                     int mode, float temperature, uint64_t seed, uint64_t offset,
+                     int32_t* token, float* lse, float* logprob, float* logits,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * SlimSpec low-rank head (SlimSpec write-up, section 三 and Q&A Q1).
+ *   W_down  [r, d]   (the d -> r map stored row per output), dtype
+ *   W_up    [V, r]   dtype
+ *   h_r = W_down h is accumulated in float32 and rounded once (nearest-even) to dtype, then
+ *   z = W_up h_r.  Other arguments and outputs as draft_head_dense.
+ */
+int draft_head_lowrank(const void* h, int64_t M, int64_t d, const void* W_down, int64_t r,
+                       const void* W_up, int64_t V, int dtype, int mode, float temperature,
+                       uint64_t seed, uint64_t offset, int32_t* token, float* lse,
+                       float* logprob, float* logits, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/*
+ * SpecVocab dynamic-vocabulary head (SpecVocab write-up, sections 2.2.1-2.2.3 and 5.1).
+ *   W_down  [d', d]  reduced-state map, dtype;  h' = W_down h rounded once to dtype
+ *   W_vocab [V, d']  approximate scorer, dtype;  s = W_vocab h' (float32)
+ *   U       [V, d]   exact head, dtype; only the k gathered rows are read
+ *   k       1 <= k <= min(V, 16384): K = the k largest s (ties -> lowest id), ascending ids
+ *   topk_idx   [M, k] int32 (required)  K
+ *   topk_logit [M, k] float (nullable)  z'_j = U[K_j,:] . h   (full-precision h)
+ *   topk_prob  [M, k] float (nullable)  softmax(z' / T) over the k candidates
+ *   token      [M] int32 (required)     chosen vocabulary id (an element of K); sampling
+ *              groups are formed over candidate positions 0..k-1 (ascending ids)
+ *   lse, logprob [M] (nullable)          over the k candidates
+ */
+int draft_head_specvocab(const void* h, int64_t M, int64_t d, const void* W_down, int64_t dprime,
+                         const void* W_vocab, const void* U, int64_t V, int64_t k, int dtype,
+                         int mode, float temperature, uint64_t seed, uint64_t offset,
+                         int32_t* topk_idx, float* topk_logit, float* topk_prob, int32_t* token,
+                         float* lse, float* logprob, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/*
+ * Batched verification (explainer sections "小模型起草，大模型批改", "为什么答案不会变";
+ * SpecTr-GBV write-up: the first rejection ends the block, residual next token, bonus token).
+ *   target_logits [B, gamma+1, V] dtype: target scores at the gamma+1 positions
+ *   draft_logits  [B, gamma,   V] dtype: draft scores (SH_SAMPLE only; NULL for greedy)
+ *   draft_tokens  [B, gamma] int32: proposed ids; an id outside [0, V) is never accepted
+ *   u_accept      [B, gamma] float in (0,1): accept uniforms (SH_SAMPLE only; else NULL)
+ *   temperature > 0: p = softmax(target / T), q = softmax(draft / T) (sampling)
+ *   SH_GREEDY: a = first t with draft_tokens[t] != argmax target[t] (ties -> lowest id),
+ *              else gamma; emitted = drafts[0..a-1], argmax target[a].
+ *   SH_SAMPLE: accept t iff u_t < p_t(x_t) / q_t(x_t); a = leading accepts; if a < gamma the
+ *              last token is drawn from norm(max(0, p_a - q_a)) (purposes 3/4, row b; if that
+ *              mass is 0, from p_a), else from p_gamma (purposes 5/6, row b).
+ *   accept_len [B] int32: a
+ *   out_tokens [B, gamma+1] int32: emitted tokens, -1 after the last one
+ */
+int spec_verify(int mode, int64_t B, int64_t gamma, int64_t V, int dtype,
+                const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
+                const float* u_accept, float temperature, uint64_t seed, uint64_t offset,
+                int32_t* accept_len, int32_t* out_tokens, void* workspace,
+                size_t workspace_bytes, void* stream);
+
+/*
+ * Top-k building block of draft_head_specvocab (SpecVocab write-up, section 2.2.2), exposed
+ * so it can be checked on given scores: for each of M rows of float32 scores [M, V], the k
+ * largest (ties -> lowest index), written as ascending ids to topk_idx [M, k].  Scores must
+ * be finite.  Workspace: sh_topk_workspace_bytes(M, V, k).
+ */
+size_t sh_topk_workspace_bytes(int64_t M, int64_t V, int64_t k);
+int sh_topk(const float* scores, int64_t M, int64_t V, int64_t k, int32_t* topk_idx,
+            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The library's in-kernel uniform stream, exported for checking: out[row, i] = the uniform
+ * for (seed, offset, purpose, row, index i), rows x n floats.
+ */
+int sh_philox_uniform(uint64_t seed, uint64_t offset, uint32_t purpose, int64_t rows, int64_t n,
+                      float* out, void* stream);
+
+/* Static description of a status code. */
+const char* sh_status_str(int status);
+/* Message of the last failed call on this host thread ("" if none). */
+const char* sh_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECHEAD_H */

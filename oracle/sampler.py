@@ -66,8 +66,20 @@ def two_level_sample(ell, group_uniforms, elem_uniforms, group=GROUP):
         "group": g_star,
         "group_margin": g_gap,
         "group_score": float(gs[g_star]),
+        "group_scores": gs,
         "elem_margin": e_gap,
         "elem_score": float(es[i_star]),
+        "elem_scores": es,
         "group_lse": L,
     }
     return lo + i_star, diag
+
+
+def pick_in_group(ell, g, elem_uniforms, group=GROUP):
+    """The element step of the rule applied to group g: (position, scores of its members)."""
+    ell = np.asarray(ell, dtype=np.float64)
+    lo, hi = g * group, min(ell.size, (g + 1) * group)
+    pos = np.arange(lo, hi)
+    es = ell[lo:hi] + gumbel(elem_uniforms(pos))
+    i_star, _ = _argmax_lowest(es)
+    return lo + i_star, es

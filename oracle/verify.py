@@ -12,7 +12,7 @@ Sampling (explainer, "‰∏∫‰ªÄ‰πàÁ≠îÊ°à‰∏ç‰ºöÂèò"; SpecTr-GBV page, "‰∏∫‰ªÄ‰πàÈáçÊ
   p_gamma.  Both p and q are softmax(z / T) over the full vocabulary (SpecVocab page 3.3:
   verification keeps the full vocabulary).
 
-Readings: u_t are given inputs in (0,1); the residual and bonus draws use the two-level
+Readings: u_t are given inputs in (0,1); a draft id outside [0, V) is never accepted; the residual and bonus draws use the two-level
 Gumbel rule with Philox purposes 3/4 (residual group/element) and 5/6 (bonus), row = b;
 if the residual mass is exactly zero the draw falls back to p_a (unreachable for finite,
 distinct logits).  Output rows are padded with -1 after the last emitted token.
@@ -66,6 +66,9 @@ def verify_sample(target_logits, draft_logits, draft_tokens, u_accept, dtype, te
     for b in range(B):
         a = gamma
         for t in range(gamma):
+            if not (0 <= x[b, t] < tl.shape[2]):
+                a = t
+                break
             lp = tl[b, t, x[b, t]] - logsumexp(tl[b, t])
             lq = dl[b, t, x[b, t]] - logsumexp(dl[b, t])
             ratio = np.exp(lp - lq)

@@ -1,0 +1,166 @@
+"""GPU parity of the dense and SlimSpec low-rank heads against the oracle (via the C ABI)."""
+import numpy as np
+import pytest
+import torch
+
+from drafter_lm_head_slimspec_amd import configs, spechead as sh, synth
+from oracle import fp, heads
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    sh.load()
+
+
+def _check_outputs(out, o, dtype, mode, T, seed, offset, bound=None, name=""):
+    M = o["logits"].shape[0]
+    tok = out["token"].cpu().numpy()
+    if out.get("logits") is not None:
+        r = P.assert_logits_close(out["logits"].cpu().numpy(), o["logits"], dtype, name + " logits")
+        P.log(f"  {name} logits ok (max err / tol = {r:.3g})")
+    lse = out["lse"].cpu().numpy().astype(np.float64)
+    tol = P.RTOL[dtype] * (1 + np.abs(o["lse"]))
+    assert np.all(np.abs(lse - o["lse"]) <= tol), (lse, o["lse"])
+    ex = P.Excusals(name + " tokens")
+    if mode == "greedy":
+        P.check_greedy_tokens(tok, o["logits"], ex, bound)
+    else:
+        P.head_sample_check(tok, o, seed, offset, T, ex, bound)
+    ex.report(M)
+    # logprob of the GPU's own token under the oracle's distribution
+    y_tok = o["logits"][np.arange(M), tok] / T
+    lp = out["logprob"].cpu().numpy().astype(np.float64)
+    want = y_tok - o["lse"]
+    assert np.all(np.abs(lp - want) <= P.RTOL[dtype] * (1 + np.abs(want))), (lp, want)
+
+
+def _lowrank(d, V, r, M, dtype, mode, T, seed=7, offset=3, want_logits=True):
+    P.log(f"lowrank d={d} V={V} r={r} M={M} {dtype} {mode} T={T}")
+    h = synth.hidden(M, d, dtype, seed)
+    Wd, Wu = synth.lowrank_weights(V, d, r, dtype, seed)
+    out = sh.draft_head_lowrank(P.to_device(h, dtype), P.to_device(Wd, dtype), P.to_device(Wu, dtype),
+                                mode=mode, temperature=T, seed=seed, offset=offset, want_logits=want_logits)
+    torch.cuda.synchronize()
+    o = heads.head_lowrank(h, Wd, Wu, dtype, mode, T, seed, offset)
+    terms = np.abs(fp.decode(h, dtype)) @ np.abs(fp.decode(Wd, dtype)).T
+    bound = P.rounding_flip_bound(o["h_r_exact"], terms, dtype, np.abs(fp.decode(Wu, dtype)))
+    _check_outputs(out, o, dtype, mode, T, seed, offset, bound, f"lowrank M={M}")
+    return out
+
+
+def _dense(d, V, M, dtype, mode, T, seed=11, offset=5, want_logits=True):
+    P.log(f"dense d={d} V={V} M={M} {dtype} {mode} T={T}")
+    h = synth.hidden(M, d, dtype, seed)
+    W = synth.dense_weights(V, d, dtype, seed)
+    out = sh.draft_head_dense(P.to_device(h, dtype), P.to_device(W, dtype), mode=mode, temperature=T,
+                              seed=seed, offset=offset, want_logits=want_logits)
+    torch.cuda.synchronize()
+    o = heads.head_dense(h, W, dtype, mode, T, seed, offset)
+    _check_outputs(out, o, dtype, mode, T, seed, offset, None, f"dense M={M}")
+    return out
+
+
+LOWRANK_SMALL = [
+    # d, V, r, M, dtype          path exercised
+    (256, 1024, 32, 4, "f32"),     # the tiny fp32 configuration (VALU, 8 lanes per row)
+    (512, 1000, 64, 1, "bf16"),    # ragged last group, VALU
+    (512, 1000, 64, 3, "bf16"),
+    (512, 1000, 64, 6, "bf16"),
+    (512, 1000, 64, 8, "bf16"),
+    (512, 1000, 120, 5, "bf16"),   # 15 chunks per row, 16-lane rows with one masked lane
+    (360, 777, 360, 2, "bf16"),    # 45 chunks per row, masked lanes
+    (512, 1000, 64, 9, "bf16"),    # MFMA, one column block
+    (512, 1000, 64, 33, "bf16"),   # MFMA, two column blocks, ragged
+    (512, 2000, 360, 70, "bf16"),  # MFMA, k not a multiple of 16
+    (512, 1000, 64, 300, "bf16"),  # MFMA, rows split over two passes
+]
+
+
+@pytest.mark.parametrize("mode,T", [("greedy", 1.0), ("sample", 1.0), ("sample", 0.7)])
+@pytest.mark.parametrize("case", LOWRANK_SMALL, ids=lambda c: "d%d-V%d-r%d-M%d-%s" % c)
+def test_lowrank_small(case, mode, T):
+    _lowrank(*case, mode, T)
+
+
+DENSE_SMALL = [
+    (256, 1024, 4, "f32"),
+    (520, 1000, 3, "bf16"),    # 65 chunks per row: two chunks per lane, masked
+    (1024, 700, 6, "bf16"),
+    (520, 1000, 40, "bf16"),   # MFMA
+    (4096, 600, 40, "bf16"),   # MFMA with the hidden state staged in two LDS chunks
+]
+
+
+@pytest.mark.parametrize("mode,T", [("greedy", 1.0), ("sample", 1.0)])
+@pytest.mark.parametrize("case", DENSE_SMALL, ids=lambda c: "d%d-V%d-M%d-%s" % c)
+def test_dense_small(case, mode, T):
+    _dense(*case, mode, T)
+
+
+def test_lowrank_without_lse_outputs():
+    d, V, r, M = 512, 1000, 64, 6
+    h = synth.hidden(M, d, "bf16", 1)
+    Wd, Wu = synth.lowrank_weights(V, d, r, "bf16", 1)
+    out = sh.draft_head_lowrank(P.to_device(h, "bf16"), P.to_device(Wd, "bf16"), P.to_device(Wu, "bf16"),
+                                want_lse=False)
+    o = heads.head_lowrank(h, Wd, Wu, "bf16")
+    ex = P.Excusals("no-lse greedy")
+    P.check_greedy_tokens(out["token"].cpu().numpy(), o["logits"], ex)
+    ex.report(M)
+
+
+def test_identity_down_projection_equals_dense():
+    # r = d and W_down = I: the low-rank head is the dense head with W = W_up (fp32)
+    d, V, M = 256, 1024, 4
+    h = synth.hidden(M, d, "f32", 2)
+    W = synth.dense_weights(V, d, "f32", 2)
+    eye = np.eye(d, dtype=np.float32)
+    a = sh.draft_head_lowrank(P.to_device(h, "f32"), P.to_device(eye, "f32"), P.to_device(W, "f32"),
+                              mode="sample", seed=4, offset=1, want_logits=True)
+    b = sh.draft_head_dense(P.to_device(h, "f32"), P.to_device(W, "f32"), mode="sample", seed=4, offset=1,
+                            want_logits=True)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(a["logits"].cpu().numpy(), b["logits"].cpu().numpy(), rtol=1e-5, atol=1e-6)
+    assert torch.equal(a["token"], b["token"])
+
+
+# ----- full-size shapes ----------------------------------------------------------------------
+
+@pytest.mark.parametrize("M", configs.LLAMA.Ms)
+@pytest.mark.parametrize("mode", ["greedy", "sample"])
+def test_llama_lowrank_full(M, mode):
+    w = configs.LLAMA
+    _lowrank(w.d, w.V, w.r, M, w.dtype, mode, w.temperature, seed=w.seeds["weights"], offset=1,
+             want_logits=(M == 6))
+
+
+@pytest.mark.parametrize("M", configs.LLAMA.Ms)
+def test_llama_dense_full(M):
+    w = configs.LLAMA
+    _dense(w.d, w.V, M, w.dtype, "sample" if M == 48 else "greedy", 1.0, seed=w.seeds["weights"],
+           want_logits=False)
+
+
+@pytest.mark.parametrize("mode", ["sample", "greedy"])
+def test_gptoss_lowrank_full(mode):
+    w = configs.GPTOSS
+    _lowrank(w.d, w.V, w.r, w.Ms[0], w.dtype, mode, w.temperature, seed=w.seeds["weights"], offset=2,
+             want_logits=False)
+
+
+def test_runs_are_bit_identical():
+    w = configs.LLAMA
+    M = 48
+    h = P.to_device(synth.hidden(M, w.d, "bf16", 3), "bf16")
+    Wd, Wu = synth.lowrank_weights(w.V, w.d, w.r, "bf16", 3)
+    Wd, Wu = P.to_device(Wd, "bf16"), P.to_device(Wu, "bf16")
+    a = sh.draft_head_lowrank(h, Wd, Wu, mode="sample", seed=9, offset=4)
+    b = sh.draft_head_lowrank(h, Wd, Wu, mode="sample", seed=9, offset=4)
+    torch.cuda.synchronize()
+    for k in ("token", "lse", "logprob"):
+        assert torch.equal(a[k], b[k]), k
