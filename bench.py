@@ -1,0 +1,339 @@
+#!/usr/bin/env python3
+"""Throughput of the drafter LM head and speculative verification on one MI355X.
+
+Default workload: the Llama-3.1-8B-shaped drafter head (d = 4096, V = 128256, bf16), one
+call over 8 sequences x 6 draft steps = 48 hidden-state rows.  One step is one call of the
+SlimSpec low-rank head (r = 512) with fused log-softmax and temperature-1 sampling; `value`
+is rows scored per second.  Secondary legs, reported in the same JSON line: the same head at
+1 x 6 rows and greedy, the dense V x d head, the SpecVocab head (d' = 256, k = 2048) at this
+shape, and batched verification (64 sequences, gamma 5, V = 151936).
+
+Weights are copied to several rotated device buffers whose total exceeds the 256 MB
+Infinity Cache, so each timed call streams its weights from HBM.  Per-kernel durations come
+from events the library records around each launch on the launch stream (sh_trace_*).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+HBM_PEAK_GBS = 8000.0
+METRIC = "draft LM-head tokens/s and % HBM roofline (V=128256,d=4096); verify tokens/s"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--legs", default="all",
+                   help="comma list of legs (lowrank48,lowrank48g,lowrank6,dense48,dense6,specvocab1,"
+                        "specvocab16,verify,verifyg) or 'all' or 'headline'")
+    p.add_argument("--rotate", type=int, default=5, help="device copies of each weight set")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-trace", action="store_true", help="skip the per-kernel event pass")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="only run a device-to-device copy of this many MiB (counter calibration)")
+    return p.parse_args()
+
+
+def sha_of(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+KERNEL_SOURCES = ["drafter_lm_head_slimspec_amd/csrc/head_kernels.hip",
+                  "drafter_lm_head_slimspec_amd/csrc/device_common.h"]
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        log(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for {args.gpus}).")
+        sys.exit(2)
+    import torch
+    from drafter_lm_head_slimspec_amd import configs, spechead as sh, synth
+
+    sh.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "launches": 3}))
+        return
+
+    w = configs.LLAMA
+    d, V, r, dp, k = w.d, w.V, w.r, w.dprime, w.k
+    seeds = w.seeds
+    legs_all = ["lowrank48", "lowrank48g", "lowrank6", "dense48", "dense6", "specvocab1", "specvocab16",
+                "verify", "verifyg"]
+    if args.legs == "all":
+        legs = legs_all
+    elif args.legs == "headline":
+        legs = ["lowrank48"]
+    else:
+        legs = [x for x in args.legs.split(",") if x]
+    R = max(1, args.rotate)
+
+    def bf(arr):
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    t0 = time.time()
+    log("generating inputs ...")
+    h48_np = synth.hidden(48, d, "bf16", seeds["hidden"])
+    h6_np = h48_np[:6].copy()
+    Wd_np, Wu_np = synth.lowrank_weights(V, d, r, "bf16", seeds["weights"])
+    Wd = [bf(Wd_np)] + []
+    Wu = [bf(Wu_np)]
+    for _ in range(R - 1):
+        Wd.append(Wd[0].clone())
+        Wu.append(Wu[0].clone())
+    h48 = bf(h48_np)
+    h6 = bf(h6_np)
+    need_dense = any(x.startswith("dense") or x.startswith("specvocab") for x in legs)
+    W = bf(synth.dense_weights(V, d, "bf16", seeds["weights"])) if need_dense else None
+    log(f"  inputs ready in {time.time() - t0:.1f}s")
+
+    results = {}
+    kernel_trace = {}
+
+    def timed(calls, steps, warmup):
+        n = len(calls)
+        for i in range(warmup):
+            calls[i % n]()
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for i in range(steps):
+            calls[i % n]()
+        e.record()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / steps
+
+    def traced(calls, steps):
+        n = len(calls)
+        sh.trace_enable(8 * steps + 64)
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for i in range(steps):
+            calls[i % n]()
+        e.record()
+        torch.cuda.synchronize()
+        tr = sh.trace_read()
+        sh.trace_enable(0)
+        return s.elapsed_time(e) / steps, tr
+
+    def run_leg(name, calls, rows, alg_bytes, unit_rows="rows"):
+        ms = timed(calls, args.steps, args.warmup)
+        out = {"ms_per_call": ms, "us_per_call": 1000 * ms, "tokens_per_s": rows / (ms / 1000.0),
+               "alg_bytes": alg_bytes, "hbm_frac": alg_bytes / (ms / 1000.0) / (HBM_PEAK_GBS * 1e9),
+               "rows": rows, "unit": unit_rows}
+        if not args.no_trace:
+            ms_t, tr = traced(calls, args.steps)
+            out["ms_per_call_traced"] = ms_t
+            out["kernels"] = {kname: {"count": v["count"], "avg_us": v["total_us"] / v["count"],
+                                      "min_us": v["min_us"], "max_us": v["max_us"]}
+                              for kname, v in tr.items()}
+            kernel_trace[name] = out["kernels"]
+        results[name] = out
+        log(f"  {name:12s} {1000 * ms:9.2f} us/call  {out['tokens_per_s']:12.0f} {unit_rows}/s  "
+            f"{100 * out['hbm_frac']:5.1f}% of HBM roofline")
+        return out
+
+    def lowrank_calls(h, M, mode):
+        calls = []
+        for i in range(R):
+            tok = torch.empty(M, dtype=torch.int32, device=dev)
+            lse = torch.empty(M, dtype=torch.float32, device=dev)
+            lp = torch.empty(M, dtype=torch.float32, device=dev)
+            need = sh.load().sh_head_workspace_bytes(sh.OP_LOWRANK, M, d, r, V, 0)
+            ws = torch.zeros(need, dtype=torch.uint8, device=dev)
+            calls.append(sh.prepared("draft_head_lowrank", h, M, d, Wd[i], r, Wu[i], V, sh.SH_BF16,
+                                     mode, 1.0, seeds["philox"], i, tok, lse, lp, None, ws, need,
+                                     torch.cuda.current_stream().cuda_stream))
+            calls[-1].keep = (tok, lse, lp, ws)
+        return calls
+
+    def dense_calls(h, M, mode):
+        tok = torch.empty(M, dtype=torch.int32, device=dev)
+        lse = torch.empty(M, dtype=torch.float32, device=dev)
+        lp = torch.empty(M, dtype=torch.float32, device=dev)
+        need = sh.load().sh_head_workspace_bytes(sh.OP_DENSE, M, d, 0, V, 0)
+        ws = torch.zeros(need, dtype=torch.uint8, device=dev)
+        c = sh.prepared("draft_head_dense", h, M, d, W, V, sh.SH_BF16, mode, 1.0, seeds["philox"], 0,
+                        tok, lse, lp, None, ws, need, torch.cuda.current_stream().cuda_stream)
+        c.keep = (tok, lse, lp, ws)
+        return [c]
+
+    lowrank_bytes = lambda M: (r * d + V * r + M * d) * 2 + M * 12
+    if "lowrank48" in legs:
+        run_leg("lowrank48", lowrank_calls(h48, 48, sh.SAMPLE), 48, lowrank_bytes(48))
+    if "lowrank48g" in legs:
+        run_leg("lowrank48g", lowrank_calls(h48, 48, sh.GREEDY), 48, lowrank_bytes(48))
+    if "lowrank6" in legs:
+        run_leg("lowrank6", lowrank_calls(h6, 6, sh.SAMPLE), 6, lowrank_bytes(6))
+    dense_bytes = lambda M: (V * d + M * d) * 2 + M * 12
+    if "dense48" in legs:
+        run_leg("dense48", dense_calls(h48, 48, sh.SAMPLE), 48, dense_bytes(48))
+    if "dense6" in legs:
+        run_leg("dense6", dense_calls(h6, 6, sh.SAMPLE), 6, dense_bytes(6))
+
+    if any(x.startswith("specvocab") for x in legs):
+        Wdp_np, Wv_np, _ = synth.specvocab_weights(V, d, dp, "bf16", seeds["weights"], with_U=False)
+        Wdp = [bf(Wdp_np)]
+        Wv = [bf(Wv_np)]
+        for _ in range(R):
+            Wdp.append(Wdp[0].clone())
+            Wv.append(Wv[0].clone())
+        for M in (1, 16):
+            name = f"specvocab{M}"
+            if name not in legs:
+                continue
+            calls, union_rows = [], []
+            for i in range(R + 1):
+                hi = bf(synth.hidden(M, d, "bf16", seeds["hidden"] + 100 + i))
+                idx = torch.empty(M, k, dtype=torch.int32, device=dev)
+                zl = torch.empty(M, k, dtype=torch.float32, device=dev)
+                q = torch.empty(M, k, dtype=torch.float32, device=dev)
+                tok = torch.empty(M, dtype=torch.int32, device=dev)
+                lse = torch.empty(M, dtype=torch.float32, device=dev)
+                lp = torch.empty(M, dtype=torch.float32, device=dev)
+                need = sh.load().sh_head_workspace_bytes(sh.OP_SPECVOCAB, M, d, dp, V, k)
+                ws = torch.zeros(need, dtype=torch.uint8, device=dev)
+                c = sh.prepared("draft_head_specvocab", hi, M, d, Wdp[i], dp, Wv[i], W, V, k, sh.SH_BF16,
+                                sh.SAMPLE, 1.0, seeds["philox"], i, idx, zl, q, tok, lse, lp, ws, need,
+                                torch.cuda.current_stream().cuda_stream)
+                c.keep = (hi, idx, zl, q, tok, lse, lp, ws)
+                c()
+                torch.cuda.synchronize()
+                union_rows.append(len(np.unique(idx.cpu().numpy())))
+                calls.append(c)
+            u = float(np.mean(union_rows))
+            alg = (dp * d + V * dp) * 2 + u * d * 2 + M * d * 2 + M * k * 12
+            out = run_leg(name, calls, M, alg)
+            out["union_rows"] = u
+
+    if "verify" in legs or "verifyg" in legs:
+        vw = configs.VERIFY
+        inp = synth.verify_inputs(vw.B, vw.gamma, vw.V, 1.0, "bf16", vw.seeds)
+        tl = [bf(inp["target"])]
+        dl = [bf(inp["draft"])]
+        for _ in range(2):
+            tl.append(tl[0].clone())
+            dl.append(dl[0].clone())
+        toks = torch.from_numpy(inp["tokens"]).to(dev)
+        u = torch.from_numpy(inp["u"]).to(dev)
+        for name, mode in (("verify", sh.SAMPLE), ("verifyg", sh.GREEDY)):
+            if name not in legs:
+                continue
+            calls = []
+            for i in range(3):
+                acc = torch.empty(vw.B, dtype=torch.int32, device=dev)
+                out = torch.empty(vw.B, vw.gamma + 1, dtype=torch.int32, device=dev)
+                need = sh.load().sh_verify_workspace_bytes(mode, vw.B, vw.gamma, vw.V)
+                ws = torch.zeros(need, dtype=torch.uint8, device=dev)
+                c = sh.prepared("spec_verify", mode, vw.B, vw.gamma, vw.V, sh.SH_BF16, tl[i],
+                                dl[i] if mode == sh.SAMPLE else None, toks, u if mode == sh.SAMPLE else None,
+                                1.0, vw.seeds["philox"], i, acc, out, ws, need,
+                                torch.cuda.current_stream().cuda_stream)
+                c.keep = (acc, out, ws)
+                calls.append(c)
+            rows_bytes = vw.B * (vw.gamma + 1) * vw.V * 2 + (vw.B * vw.gamma * vw.V * 2 if mode == sh.SAMPLE else 0)
+            alg = rows_bytes + vw.B * vw.gamma * 8 + vw.B * (vw.gamma + 2) * 4
+            o = run_leg(name, calls, vw.B * vw.gamma, alg, "draft tokens")
+            o["config"] = {"B": vw.B, "gamma": vw.gamma, "V": vw.V, "sigma": 1.0}
+
+    head = results.get("lowrank48")
+    line = {
+        "metric": METRIC,
+        "value": head["tokens_per_s"] if head else None,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_call"] if head else None,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) hidden states, N(0, 1/fan_in) weights)",
+        "config": {"workload": w.name, "head": "slimspec-lowrank", "d": d, "V": V, "r": r,
+                   "rows": 48, "sequences": 8, "gamma": 6, "mode": "sample", "temperature": 1.0,
+                   "parallelism": "none (one GPU)"},
+    }
+    if head:
+        line["hbm_roofline_frac_call"] = head["hbm_frac"]
+    # roofline of the dominant kernel: the W_up streaming kernel of the headline leg
+    if head and "kernels" in head:
+        kname = "stream_mfma" if "stream_mfma" in head["kernels"] else "stream_valu"
+        kavg = head["kernels"][kname]["avg_us"]
+        kbytes = V * r * 2 + 48 * r * 2
+        achieved = kbytes / (kavg * 1e-6) / 1e9
+        traffic = None
+        tpath = os.path.join(ROOT, "profiles", "traffic_stream_mfma_llama_lowrank_M48.json")
+        if os.path.exists(tpath):
+            t = json.load(open(tpath))
+            if t.get("source_sha256") == sha_of(KERNEL_SOURCES):
+                traffic = t.get("hbm_bytes_per_launch")
+        line["roofline"] = {"bound": "hbm", "kernel": kname, "achieved": achieved, "peak": HBM_PEAK_GBS,
+                            "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                            "alg_bytes_per_launch": kbytes, "avg_launch_us": kavg}
+    if "dense48" in results and head:
+        line["nu_lowrank_vs_dense_M48"] = head["ms_per_call"] / results["dense48"]["ms_per_call"]
+    if "dense6" in results and "lowrank6" in results:
+        line["nu_lowrank_vs_dense_M6"] = results["lowrank6"]["ms_per_call"] / results["dense6"]["ms_per_call"]
+    if "specvocab1" in results and "dense6" in results:
+        line["nu_specvocab1_vs_dense6"] = results["specvocab1"]["ms_per_call"] / results["dense6"]["ms_per_call"]
+    if "verify" in results:
+        line["verify_tokens_per_s"] = results["verify"]["tokens_per_s"]
+    line["legs"] = {kk: {x: v for x, v in vv.items() if x != "kernels"} for kk, vv in results.items()}
+    line["kernels_us"] = {kk: {kn: round(kv["avg_us"], 3) for kn, kv in vv.items()} for kk, vv in kernel_trace.items()}
+
+    if head and not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(h48_np, Wd_np, Wu_np, seeds["philox"])
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(h, Wd, Wu, seed):
+    """The oracle, as it stands, on the headline workload: full low-rank calls (48 rows, all V,
+    sampling), repeated until about 10 s of host time has been spent (at most 5 calls)."""
+    from oracle import heads
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # noqa: BLE001
+        threads = os.cpu_count()
+    n = 0
+    t0 = time.time()
+    while n < 5 and (time.time() - t0) < 10.0:
+        heads.head_lowrank(h, Wd, Wu, "bf16", "sample", 1.0, seed, n)
+        n += 1
+    dt = time.time() - t0
+    return {"value": 48 * n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} full oracle calls of the headline workload (48 rows x V=128256, r=512, "
+                      f"sampling), {dt:.1f} s on the host"}
+
+
+if __name__ == "__main__":
+    main()

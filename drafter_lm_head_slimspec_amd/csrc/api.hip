@@ -32,7 +32,7 @@ constexpr int64_t kMaxRowBytes = 16 * 1024;     // d * esize for the row-dot and
 constexpr int64_t kMaxK = 16384;
 constexpr int64_t kMaxGamma = 64;
 constexpr int kValuMaxRows = 8;                 // skinny path up to this many rows
-constexpr int kMfmaMaxRows = 256;               // rows per MFMA pass (8 column blocks)
+constexpr int kMfmaMaxRows = 192;               // rows per MFMA pass (6 column blocks, no spills)
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }

@@ -166,24 +166,97 @@ __device__ __forceinline__ float gumbel(float u) { return -logf(-logf(u)); }
 __device__ __forceinline__ int lane_id() { return static_cast<int>(threadIdx.x) & (kWave - 1); }
 __device__ __forceinline__ int wave_id() { return static_cast<int>(threadIdx.x) / kWave; }
 
+// Value of lane (l ^ S) without going through LDS: DPP quad permutes for S = 1, 2, DPP row
+// shifts for S = 4, 8, and the gfx950 v_permlane16_swap / v_permlane32_swap for S = 16, 32.
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+template <int S>
+__device__ __forceinline__ uint32_t xor_lane_u32(uint32_t v) {
+  if constexpr (S == 1) {
+    return __builtin_amdgcn_update_dpp(0u, v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+  } else if constexpr (S == 2) {
+    return __builtin_amdgcn_update_dpp(0u, v, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+  } else if constexpr (S == 4 || S == 8) {
+    const uint32_t up = __builtin_amdgcn_update_dpp(0u, v, 0x100 + S, 0xF, 0xF, false);  // row_shl
+    const uint32_t dn = __builtin_amdgcn_update_dpp(0u, v, 0x110 + S, 0xF, 0xF, false);  // row_shr
+    return (lane_id() & S) ? dn : up;
+  } else if constexpr (S == 16) {
+    const u32x2_t r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return ((lane_id() >> 4) & 1) ? r.x : r.y;
+  } else {
+    static_assert(S == 32, "xor distance must be a power of two below 64");
+    const u32x2_t r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return (lane_id() >> 5) ? r.x : r.y;
+  }
+}
+// runtime distance (folds to one case once loops over s are unrolled)
+__device__ __forceinline__ uint32_t xor_lane_u32(uint32_t v, int s) {
+  switch (s) {
+    case 1: return xor_lane_u32<1>(v);
+    case 2: return xor_lane_u32<2>(v);
+    case 4: return xor_lane_u32<4>(v);
+    case 8: return xor_lane_u32<8>(v);
+    case 16: return xor_lane_u32<16>(v);
+    default: return xor_lane_u32<32>(v);
+  }
+}
+__device__ __forceinline__ float xor_lane(float v, int s) {
+  return __uint_as_float(xor_lane_u32(__float_as_uint(v), s));
+}
+__device__ __forceinline__ int32_t xor_lane(int32_t v, int s) {
+  return static_cast<int32_t>(xor_lane_u32(static_cast<uint32_t>(v), s));
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
-  for (int s = 32; s >= 1; s >>= 1) v += __shfl_xor(v, s);
+  for (int s = 32; s >= 1; s >>= 1) v += xor_lane(v, s);
   return v;
 }
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
-  for (int s = 32; s >= 1; s >>= 1) v = fmaxf(v, __shfl_xor(v, s));
+  for (int s = 32; s >= 1; s >>= 1) v = fmaxf(v, xor_lane(v, s));
   return v;
 }
 // wave-wide argmax, lowest index on ties; every lane gets the result
 __device__ __forceinline__ void wave_argmax(float& v, int32_t& i) {
 #pragma unroll
   for (int s = 32; s >= 1; s >>= 1) {
-    const float v2 = __shfl_xor(v, s);
-    const int32_t i2 = __shfl_xor(i, s);
+    const float v2 = xor_lane(v, s);
+    const int32_t i2 = xor_lane(i, s);
     argmax_merge(v, i, v2, i2);
   }
+}
+// merge of Partials across the wave (xor tree); every lane gets the result
+__device__ __forceinline__ void wave_partial_merge(Partial& p) {
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) {
+    Partial q;
+    q.m = xor_lane(p.m, s);
+    q.s = xor_lane(p.s, s);
+    q.gscore = xor_lane(p.gscore, s);
+    q.g = xor_lane(p.g, s);
+    q.zmax = xor_lane(p.zmax, s);
+    q.zid = xor_lane(p.zid, s);
+    partial_merge(p, q);
+  }
+}
+
+// Buffer loads: a resource descriptor (base, byte range) lets the hardware return zero for
+// offsets outside the range, so ragged tails need no branch around the load.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kOutOfRange = 0x80000000u;   // above any range used here
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           static_cast<int>(bytes), 0x00020000);
+}
+__device__ __forceinline__ uint4 buffer_load16(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+// Branch-free 16-byte load: reads the clamped (always valid) address and returns zero when
+// `ok` is false, so that loads stay unconditional and their waits can be counted exactly.
+__device__ __forceinline__ uint4 load16_or_zero(const char* base_valid, const char* p, bool ok) {
+  const uint4 v = *reinterpret_cast<const uint4*>(ok ? p : base_valid);
+  return ok ? v : make_uint4(0u, 0u, 0u, 0u);
 }
 
 __device__ __forceinline__ uint4 load16(const void* p) {

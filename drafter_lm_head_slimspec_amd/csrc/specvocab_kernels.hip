@@ -6,6 +6,7 @@
 //   k_gather_finalize softmax over the k candidates, argmax or two-level Gumbel draw
 #include "device_common.h"
 #include "launch.h"
+#include "trace.h"
 
 namespace sh {
 
@@ -103,6 +104,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const float* __restrict__
 
 hipError_t launch_topk(const float* scores, int64_t M, int64_t V, int64_t k, int32_t* idx,
                        hipStream_t st) {
+  TraceScope ts("topk", st);
   hipLaunchKernelGGL(k_topk, dim3(static_cast<unsigned>(M)), dim3(kTopkThreads), 0, st, scores,
                      static_cast<int>(V), static_cast<int>(k), idx);
   return hipGetLastError();
@@ -168,6 +170,7 @@ hipError_t launch_gather_exact(const void* U, const void* h, const int32_t* idx,
   const int C = static_cast<int>(d * (bf16 ? 2 : 4) / 16);
   const int per_wg = 4 * kGatherPerWave;
   const dim3 grid(static_cast<unsigned>((k + per_wg - 1) / per_wg), static_cast<unsigned>(M));
+  TraceScope ts("gather_exact", st);
   if (bf16)
     hipLaunchKernelGGL(k_gather_exact<true>, grid, dim3(256), 0, st, U, h, idx, C,
                        static_cast<int>(k), static_cast<int>(V), zbuf);
@@ -270,6 +273,7 @@ hipError_t launch_gather_finalize(const float* zbuf, const int32_t* idx, int64_t
                                   int mode, float invT, uint64_t seed, uint64_t offset,
                                   float* topk_logit, float* topk_prob, int32_t* token, float* lse,
                                   float* logprob, hipStream_t st) {
+  TraceScope ts("gather_finalize", st);
   hipLaunchKernelGGL(k_gather_finalize, dim3(static_cast<unsigned>(M)), dim3(256), 0, st, zbuf, idx,
                      static_cast<int>(k), mode, invT, seed, offset, topk_logit, topk_prob, token,
                      lse, logprob);

@@ -8,6 +8,7 @@
 //                      rejection or the bonus draw, output assembly
 #include "device_common.h"
 #include "launch.h"
+#include "trace.h"
 
 namespace sh {
 
@@ -56,12 +57,12 @@ __device__ __forceinline__ Partial block_merge(Partial p, Partial* red4) {
 #pragma unroll
   for (int s = 32; s >= 1; s >>= 1) {
     Partial q;
-    q.m = __shfl_xor(p.m, s);
-    q.s = __shfl_xor(p.s, s);
-    q.gscore = __shfl_xor(p.gscore, s);
-    q.g = __shfl_xor(p.g, s);
-    q.zmax = __shfl_xor(p.zmax, s);
-    q.zid = __shfl_xor(p.zid, s);
+    q.m = xor_lane(p.m, s);
+    q.s = xor_lane(p.s, s);
+    q.gscore = xor_lane(p.gscore, s);
+    q.g = xor_lane(p.g, s);
+    q.zmax = xor_lane(p.zmax, s);
+    q.zid = xor_lane(p.zid, s);
     partial_merge(p, q);
   }
   const int w = wave_id(), nw = blockDim.x / kWave;
@@ -115,10 +116,10 @@ __global__ __launch_bounds__(256) void k_verify_rows(VerifyArgs a) {
       // group = LPG consecutive lanes; reduce (max, sum) inside the group
       float gm = lmax;
 #pragma unroll
-      for (int o = 1; o < LPG; o <<= 1) gm = fmaxf(gm, __shfl_xor(gm, o));
+      for (int o = 1; o < LPG; o <<= 1) gm = fmaxf(gm, xor_lane(gm, o));
       float gs = (in && gm != -INFINITY) ? lsum * __expf(lmax - gm) : 0.f;
 #pragma unroll
-      for (int o = 1; o < LPG; o <<= 1) gs += __shfl_xor(gs, o);
+      for (int o = 1; o < LPG; o <<= 1) gs += xor_lane(gs, o);
       if (in && (l % LPG) == 0) {
         const int64_t gi = e0 / kGroup;
         const float L = gm + logf(gs);
@@ -235,15 +236,15 @@ __global__ __launch_bounds__(256) void k_verify_finalize(VerifyArgs a) {
         if (!fallback) {
           float gs = lsum;
 #pragma unroll
-          for (int o = 1; o < LPG; o <<= 1) gs += __shfl_xor(gs, o);
+          for (int o = 1; o < LPG; o <<= 1) gs += xor_lane(gs, o);
           L = gs > 0.f ? logf(gs) : -INFINITY;
         } else {
           float gm = lmax;
 #pragma unroll
-          for (int o = 1; o < LPG; o <<= 1) gm = fmaxf(gm, __shfl_xor(gm, o));
+          for (int o = 1; o < LPG; o <<= 1) gm = fmaxf(gm, xor_lane(gm, o));
           float gs = (in && gm != -INFINITY) ? lsum * __expf(lmax - gm) : 0.f;
 #pragma unroll
-          for (int o = 1; o < LPG; o <<= 1) gs += __shfl_xor(gs, o);
+          for (int o = 1; o < LPG; o <<= 1) gs += xor_lane(gs, o);
           L = gm + logf(gs);
         }
         if (in && (l % LPG) == 0 && L != -INFINITY) {
@@ -304,13 +305,17 @@ int verify_segments(int64_t B, int64_t gamma, int64_t V, int mode) {
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t st) {
   const int R = a.mode == 0 ? static_cast<int>(a.gamma + 1) : static_cast<int>(2 * a.gamma + 1);
   const dim3 grid(static_cast<unsigned>(a.S), static_cast<unsigned>(R), static_cast<unsigned>(a.B));
-  if (a.bf16) {
-    hipLaunchKernelGGL(k_verify_rows<true>, grid, dim3(256), 0, st, a);
-  } else {
-    hipLaunchKernelGGL(k_verify_rows<false>, grid, dim3(256), 0, st, a);
+  {
+    TraceScope ts("verify_rows", st);
+    if (a.bf16) {
+      hipLaunchKernelGGL(k_verify_rows<true>, grid, dim3(256), 0, st, a);
+    } else {
+      hipLaunchKernelGGL(k_verify_rows<false>, grid, dim3(256), 0, st, a);
+    }
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  TraceScope ts("verify_finalize", st);
   if (a.bf16)
     hipLaunchKernelGGL(k_verify_finalize<true>, dim3(static_cast<unsigned>(a.B)), dim3(256), 0, st, a);
   else

@@ -42,6 +42,8 @@ _SIGS = {
                          _sz, _vp]),
     "sh_topk": (_i, [_vp, _i64, _i64, _i64, _vp, _vp, _sz, _vp]),
     "sh_philox_uniform": (_i, [_u64, _u64, ctypes.c_uint32, _i64, _i64, _vp, _vp]),
+    "sh_trace_enable": (_i, [_i64]),
+    "sh_trace_read": (_i, [ctypes.c_char_p, _sz]),
     "sh_status_str": (ctypes.c_char_p, [_i]),
     "sh_last_error": (ctypes.c_char_p, []),
 }
@@ -226,3 +228,37 @@ def philox_uniform(seed, offset, purpose, rows, n, device):
     _check(lib.sh_philox_uniform(int(seed), int(offset), int(purpose), rows, n, _p(out),
                                  _stream(device)))
     return out
+
+
+def trace_enable(max_records=65536):
+    """Start per-kernel event timing inside the library (0 disables)."""
+    _check(load().sh_trace_enable(int(max_records)))
+
+
+def trace_read():
+    """Per-kernel timing since the last read: {name: {count, total_us, min_us, max_us}}."""
+    import json
+    buf = ctypes.create_string_buffer(1 << 16)
+    _check(load().sh_trace_read(buf, len(buf)))
+    return json.loads(buf.value.decode())
+
+
+def prepared(fn_name, *args):
+    """A zero-argument callable that invokes the C entry point `fn_name` with arguments
+    converted once up front (tensors become device addresses).  For launch loops whose
+    per-call Python cost must stay small; raises SpecHeadError on a non-zero status."""
+    lib = load()
+    fn = getattr(lib, fn_name)
+    conv = []
+    for a in args:
+        if isinstance(a, torch.Tensor):
+            conv.append(ctypes.c_void_p(a.data_ptr()))
+        else:
+            conv.append(a)
+    conv = tuple(conv)
+
+    def call():
+        rc = fn(*conv)
+        if rc != SH_OK:
+            _check(rc)
+    return call

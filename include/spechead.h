@@ -167,6 +167,17 @@ int sh_topk(const float* scores, int64_t M, int64_t V, int64_t k, int32_t* topk_
 int sh_philox_uniform(uint64_t seed, uint64_t offset, uint32_t purpose, int64_t rows, int64_t n,
                       float* out, void* stream);
 
+/*
+ * Opt-in kernel timing (tracing).  sh_trace_enable(n) creates 2n host-side event objects and,
+ * from then on, brackets every kernel this library launches with two events recorded on the
+ * launch stream (at most n launches until the next read); n = 0 disables and frees them.
+ * sh_trace_read waits for the recorded events and writes a JSON object
+ * {"kernel": {"count", "total_us", "min_us", "max_us"}, ...} into buf (NUL-terminated),
+ * then clears the records.  SH_ERR_PARAM if buf is too small; SH_ERR_HIP on event errors.
+ */
+int sh_trace_enable(int64_t max_records);
+int sh_trace_read(char* buf, size_t bytes);
+
 /* Static description of a status code. */
 const char* sh_status_str(int status);
 /* Message of the last failed call on this host thread ("" if none). */

@@ -77,7 +77,7 @@ LOWRANK_SMALL = [
     (512, 1000, 64, 9, "bf16"),    # MFMA, one column block
     (512, 1000, 64, 33, "bf16"),   # MFMA, two column blocks, ragged
     (512, 2000, 360, 70, "bf16"),  # MFMA, k not a multiple of 16
-    (512, 1000, 64, 300, "bf16"),  # MFMA, rows split over two passes
+    (512, 1000, 64, 300, "bf16"),  # MFMA, rows split over two passes (192 + 108)
 ]
 
 
@@ -92,7 +92,7 @@ DENSE_SMALL = [
     (520, 1000, 3, "bf16"),    # 65 chunks per row: two chunks per lane, masked
     (1024, 700, 6, "bf16"),
     (520, 1000, 40, "bf16"),   # MFMA
-    (4096, 600, 40, "bf16"),   # MFMA with the hidden state staged in two LDS chunks
+    (4096, 600, 40, "bf16"),   # MFMA with B fragments read from global memory (K too large for LDS)
 ]
 
 
