@@ -75,6 +75,7 @@ int check_opt_out(const void* p, const char* name) {
 struct HeadLayout {
   size_t hr_off, hr_bytes;
   size_t part_off, part_bytes;
+  size_t lg_off, lg_bytes;
   size_t score_off, score_bytes;
   size_t z_off, z_bytes;
   size_t total;
@@ -89,6 +90,9 @@ HeadLayout head_layout(int op, int64_t M, int64_t r, int64_t V, int64_t k, int d
   L.part_off = off;
   L.part_bytes = (op == SH_OP_SPECVOCAB) ? 0 : align_up(static_cast<size_t>(M) * sh::kMaxPartials * sizeof(sh::Partial), 256);
   off += L.part_bytes;
+  L.lg_off = off;
+  L.lg_bytes = (op == SH_OP_SPECVOCAB) ? 0 : align_up(static_cast<size_t>(M) * static_cast<size_t>((V + sh::kGroup - 1) / sh::kGroup) * 4, 256);
+  off += L.lg_bytes;
   L.score_off = off;
   L.score_bytes = (op == SH_OP_SPECVOCAB) ? align_up(static_cast<size_t>(M * V) * 4, 256) : 0;
   off += L.score_bytes;
@@ -120,14 +124,14 @@ int check_workspace(void* ws, size_t have, size_t need) {
   } while (0)
 
 // Stream z = W x over V rows for M rows of x, then finalize selection.  Shared by the dense
-// and low-rank heads.
+// and low-rank heads.  lg: [M][ceil(V/64)] group log-sum-exps, partials: [M][kMaxPartials].
 int run_head(const void* x, int64_t M, int64_t K, const void* W, int64_t V, int dtype, int mode,
              float temperature, uint64_t seed, uint64_t offset, int32_t* token, float* lse,
-             float* logprob, float* logits, sh::Partial* partials, hipStream_t st) {
+             float* logprob, float* logits, sh::Partial* partials, float* lg, hipStream_t st) {
   const bool bf16 = dtype == SH_BF16;
   const float invT = 1.0f / temperature;
-  int stats = mode == SH_SAMPLE ? sh::kStatsSample
-                                : ((lse != nullptr || logprob != nullptr) ? sh::kStatsLse : sh::kStatsArgmax);
+  const bool want_lg = mode == SH_SAMPLE || lse != nullptr || logprob != nullptr;
+  const int64_t NG = (V + sh::kGroup - 1) / sh::kGroup;
   const bool mfma = bf16 && M > kValuMaxRows;
   const int64_t chunk = mfma ? kMfmaMaxRows : kValuMaxRows;
   int producers = 0;
@@ -140,13 +144,12 @@ int run_head(const void* x, int64_t M, int64_t K, const void* W, int64_t V, int 
     a.K = K;
     a.M = static_cast<int>(mc);
     a.bf16 = bf16;
-    a.stats = stats;
+    a.want_argmax = mode == SH_GREEDY;
     a.invT = invT;
-    a.seed = seed;
-    a.offset = offset;
-    a.row0 = m0;
     a.zout = logits ? logits + m0 * V : nullptr;
     a.zout_ld = V;
+    a.lg = want_lg ? lg + m0 * NG : nullptr;
+    a.lg_ld = NG;
     a.partials = partials + m0 * sh::kMaxPartials;
     a.partials_ld = sh::kMaxPartials;
     int p = 0;
@@ -157,6 +160,8 @@ int run_head(const void* x, int64_t M, int64_t K, const void* W, int64_t V, int 
   f.partials = partials;
   f.partials_ld = sh::kMaxPartials;
   f.P = producers;
+  f.lg = lg;
+  f.lg_ld = NG;
   f.W = W;
   f.x = x;
   f.V = V;
@@ -167,7 +172,6 @@ int run_head(const void* x, int64_t M, int64_t K, const void* W, int64_t V, int 
   f.invT = invT;
   f.seed = seed;
   f.offset = offset;
-  f.row0 = 0;
   f.token = token;
   f.lse = lse;
   f.logprob = logprob;
@@ -248,8 +252,9 @@ int draft_head_dense(const void* h, int64_t M, int64_t d, const void* W, int64_t
   SH_TRY(check_workspace(workspace, workspace_bytes, L.total));
   hipStream_t st = static_cast<hipStream_t>(stream);
   auto* parts = reinterpret_cast<sh::Partial*>(static_cast<char*>(workspace) + L.part_off);
+  auto* lg = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.lg_off);
   return run_head(h, M, d, W, V, dtype, mode, temperature, seed, offset, token, lse, logprob,
-                  logits, parts, st);
+                  logits, parts, lg, st);
 }
 
 int draft_head_lowrank(const void* h, int64_t M, int64_t d, const void* W_down, int64_t r,
@@ -270,9 +275,10 @@ int draft_head_lowrank(const void* h, int64_t M, int64_t d, const void* W_down, 
   char* ws = static_cast<char*>(workspace);
   void* hr = ws + L.hr_off;
   auto* parts = reinterpret_cast<sh::Partial*>(ws + L.part_off);
+  auto* lg = reinterpret_cast<float*>(ws + L.lg_off);
   SH_HIP(sh::launch_rowdot(W_down, h, r, d, M, dtype == SH_BF16, hr, st), "down-projection kernel");
   return run_head(hr, M, r, W_up, V, dtype, mode, temperature, seed, offset, token, lse, logprob,
-                  logits, parts, st);
+                  logits, parts, lg, st);
 }
 
 int draft_head_specvocab(const void* h, int64_t M, int64_t d, const void* W_down, int64_t dprime,
@@ -314,11 +320,12 @@ int draft_head_specvocab(const void* h, int64_t M, int64_t d, const void* W_down
     a.K = dprime;
     a.M = static_cast<int>(mc);
     a.bf16 = bf16;
-    a.stats = sh::kStatsNone;
+    a.want_argmax = false;
     a.invT = 1.f;
-    a.row0 = m0;
     a.zout = scores + m0 * V;
     a.zout_ld = V;
+    a.lg = nullptr;
+    a.lg_ld = 0;
     a.partials = nullptr;
     a.partials_ld = 0;
     int p = 0;

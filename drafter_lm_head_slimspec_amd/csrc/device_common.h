@@ -4,7 +4,18 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace sh {
+
+// f(std::integral_constant<int, I>{}) for I = B .. E-1, fully unrolled
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
 
 constexpr int kWave = 64;
 constexpr int kGroup = 64;           // sampling group: 64 consecutive candidates
@@ -149,6 +160,37 @@ __device__ __forceinline__ uint64_t philox_word(uint64_t seed, uint64_t offset, 
   }
   const uint32_t sel = static_cast<uint32_t>(index & 3);
   return sel == 0 ? c0 : sel == 1 ? c1 : sel == 2 ? c2 : c3;
+}
+
+// all four words of the block holding `index4` (a multiple of 4)
+__device__ __forceinline__ void philox_block(uint64_t seed, uint64_t offset, uint32_t purpose, uint64_t row,
+                                             uint64_t index4, uint64_t (&out)[4]) {
+  const uint64_t kM0 = 0xD2E7470EE14C6C93ull, kM1 = 0xCA5A826395121157ull;
+  const uint64_t kW0 = 0x9E3779B97F4A7C15ull, kW1 = 0xBB67AE8584CAA73Bull;
+  uint64_t c0 = index4 >> 2, c1 = row, c2 = purpose, c3 = offset;
+  uint64_t k0 = seed, k1 = 0;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) {
+      k0 += kW0;
+      k1 += kW1;
+    }
+    const uint64_t hi0 = __umul64hi(kM0, c0), lo0 = kM0 * c0;
+    const uint64_t hi1 = __umul64hi(kM1, c2), lo1 = kM1 * c2;
+    const uint64_t n0 = hi1 ^ c1 ^ k0;
+    const uint64_t n2 = hi0 ^ c3 ^ k1;
+    c0 = n0;
+    c1 = lo1;
+    c2 = n2;
+    c3 = lo0;
+  }
+  out[0] = c0;
+  out[1] = c1;
+  out[2] = c2;
+  out[3] = c3;
+}
+__device__ __forceinline__ float word_to_uniform(uint64_t w) {
+  return (static_cast<float>(static_cast<uint32_t>(w >> 41)) + 0.5f) * 0x1p-23f;
 }
 
 __device__ __forceinline__ float philox_uniform(uint64_t seed, uint64_t offset, uint32_t purpose,

@@ -3,24 +3,30 @@
 //   k_rowdot        h_r = round(W_down h): the SlimSpec d -> r map (SlimSpec write-up,
 //                   section 三) and the SpecVocab d -> d' map (SpecVocab write-up, 2.2.1).
 //   k_stream_valu   skinny head product (M <= 8 rows): coalesced 16-byte weight streaming,
-//                   one 64-row vocabulary group per wave, fused softmax / argmax /
-//                   group-Gumbel statistics.
+//                   one 64-row vocabulary group per wave at a time.
 //   k_stream_mfma   the same contract once the rows make the product dense (M > 8):
 //                   v_mfma_f32_32x32x16_bf16, weights HBM -> VGPR, activations in LDS.
-//   k_head_finalize fixed-order combine of the per-workgroup partials, row lse, token
-//                   (argmax, or the winning group's element draw when sampling).
+//   k_head_finalize per row: argmax from the per-workgroup partials (greedy), or the row
+//                   lse and the two-level draw from the per-group log-sum-exps (sampling).
 //
-// Memory-level parallelism is explicit everywhere: global loads of a batch are issued into
-// registers before any of them is consumed (and, in the streaming loops, one batch ahead of
-// the compute), because a load followed by an LDS store, a lane shuffle or an atomic in the
-// same loop iteration is otherwise waited for before the next iteration's load is issued.
+// The streaming kernels fold each 64-row group into one log-sum-exp per row, L_g, written
+// to the workspace; everything that needs random numbers (the group scores L_g + Gumbel(u_g)
+// and the element draw inside the winning group) runs once per row in the finalize kernel.
+//
+// Loads use buffer descriptors whose byte range makes out-of-range lanes read zero, so no
+// load sits behind a branch; the streaming loops keep one batch of loads in flight while
+// the previous batch is consumed (ping-pong buffers, no register copies between them).
 #include "device_common.h"
 #include "launch.h"
 #include "trace.h"
 
 namespace sh {
 
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
 // Copy `items` 16-byte words fetch(i) -> lds[i] with BATCH loads in flight per thread.
+// fetch(-1) must return a harmless (zero) value.
 template <int BATCH, typename F>
 __device__ __forceinline__ void stage16(uint4* lds, int items, F fetch) {
   for (int base = threadIdx.x; base < items; base += blockDim.x * BATCH) {
@@ -28,7 +34,7 @@ __device__ __forceinline__ void stage16(uint4* lds, int items, F fetch) {
 #pragma unroll
     for (int b = 0; b < BATCH; ++b) {
       const int i = base + b * static_cast<int>(blockDim.x);
-      v[b] = i < items ? fetch(i) : zero16();
+      v[b] = fetch(i < items ? i : -1);
     }
 #pragma unroll
     for (int b = 0; b < BATCH; ++b) {
@@ -55,28 +61,28 @@ __global__ __launch_bounds__(256) void k_rowdot(const void* __restrict__ Wd,
   const int l = lane_id(), w = wave_id();
   const int j0 = blockIdx.x * kRowdotRows + w * 2;
   const int CPL = (C + kWave - 1) / kWave;
-  // weight rows first (their loads overlap the staging below)
+  const uint32_t rowbytes = static_cast<uint32_t>(C) * 16;
+  // the two weight rows of this wave (zero past R), issued before the staging below
+  const int wrows = j0 + 2 <= R ? 2 : (j0 < R ? 1 : 0);
+  const rsrc_t wrs = make_rsrc(static_cast<const char*>(Wd) + static_cast<size_t>(j0 < R ? j0 : 0) * rowbytes,
+                               static_cast<uint32_t>(wrows) * rowbytes);
   uint4 wr0[kRowdotMaxCPL], wr1[kRowdotMaxCPL];
 #pragma unroll
   for (int q = 0; q < kRowdotMaxCPL; ++q) {
     const int c = q * kWave + l;
     const bool ok = q < CPL && c < C;
-    wr0[q] = (ok && j0 < R) ? load16(static_cast<const char*>(Wd) + (static_cast<size_t>(j0) * C + c) * 16)
-                            : zero16();
-    wr1[q] = (ok && j0 + 1 < R)
-                 ? load16(static_cast<const char*>(Wd) + (static_cast<size_t>(j0 + 1) * C + c) * 16)
-                 : zero16();
+    wr0[q] = buffer_load16(wrs, ok ? static_cast<uint32_t>(c) * 16 : kOutOfRange);
+    wr1[q] = buffer_load16(wrs, ok ? rowbytes + static_cast<uint32_t>(c) * 16 : kOutOfRange);
   }
-  const char* xb = static_cast<const char*>(x);
+  const int mrows = M - m0 < kRowdotM ? M - m0 : kRowdotM;
+  const rsrc_t xrs = make_rsrc(static_cast<const char*>(x) + static_cast<size_t>(m0) * rowbytes,
+                               static_cast<uint32_t>(mrows) * rowbytes);
   stage16<8>(xs, kRowdotM * C, [&](int i) {
-    const int mm = i / C, c = i - mm * C;
-    const int m = m0 + mm;
-    return (m < M) ? load16(xb + (static_cast<size_t>(m) * C + c) * 16) : zero16();
+    return buffer_load16(xrs, i >= 0 ? static_cast<uint32_t>(i) * 16 : kOutOfRange);
   });
   __syncthreads();
-  for (int mm = 0; mm < kRowdotM; ++mm) {
+  for (int mm = 0; mm < mrows; ++mm) {
     const int m = m0 + mm;
-    if (m >= M) break;
     float a0 = 0.f, a1 = 0.f;
 #pragma unroll
     for (int q = 0; q < kRowdotMaxCPL; ++q) {
@@ -104,19 +110,50 @@ __global__ __launch_bounds__(256) void k_rowdot(const void* __restrict__ Wd,
 }
 
 // ----------------------------------------------------------------------------------------
-// Workgroup-level combine of per-wave running states into one Partial per row.
-// rec: LDS scratch of nwaves * M Partials.  Every wave calls with its lane-m state.
+// Workgroup-level combine of per-wave argmax states into one Partial per row.
 // ----------------------------------------------------------------------------------------
-__device__ __forceinline__ void wg_combine_store(Partial* rec, const Partial& mine, bool holds,
-                                                 int m_of_lane, int M, Partial* partials,
-                                                 int64_t ld) {
+__device__ __forceinline__ void wg_argmax_store(Partial* rec, float z, int32_t id, bool holds,
+                                                int m_of_lane, int M, Partial* partials, int64_t ld) {
   const int w = wave_id(), nw = blockDim.x / kWave;
-  if (holds) rec[w * M + m_of_lane] = mine;
+  if (holds) {
+    Partial p = partial_empty();
+    p.zmax = z;
+    p.zid = id;
+    rec[w * M + m_of_lane] = p;
+  }
   __syncthreads();
   for (int m = threadIdx.x; m < M; m += blockDim.x) {
     Partial p = rec[m];
-    for (int i = 1; i < nw; ++i) partial_merge(p, rec[i * M + m]);
+    for (int i = 1; i < nw; ++i) argmax_merge(p.zmax, p.zid, rec[i * M + m].zmax, rec[i * M + m].zid);
     partials[static_cast<int64_t>(m) * ld + blockIdx.x] = p;
+  }
+}
+
+// Halving step of the transposed reduction: lanes with bit s clear end with lo + lo[l ^ s],
+// lanes with bit s set with hi + hi[l ^ s].  One permlane swap plus one add for s = 32, 16.
+template <int S>
+__device__ __forceinline__ float pair_fold(float lo, float hi) {
+  if constexpr (S == 32) {
+    const u32x2_t r = __builtin_amdgcn_permlane32_swap(__float_as_uint(lo), __float_as_uint(hi), false, false);
+    return __uint_as_float(r.x) + __uint_as_float(r.y);
+  } else if constexpr (S == 16) {
+    const u32x2_t r = __builtin_amdgcn_permlane16_swap(__float_as_uint(lo), __float_as_uint(hi), false, false);
+    return __uint_as_float(r.x) + __uint_as_float(r.y);
+  } else {
+    const float a = lo + xor_lane(lo, S);
+    const float b = hi + xor_lane(hi, S);
+    return (lane_id() & S) ? b : a;
+  }
+}
+
+__device__ __forceinline__ float pair_fold_rt(float lo, float hi, int s) {
+  switch (s) {
+    case 32: return pair_fold<32>(lo, hi);
+    case 16: return pair_fold<16>(lo, hi);
+    case 8: return pair_fold<8>(lo, hi);
+    case 4: return pair_fold<4>(lo, hi);
+    case 2: return pair_fold<2>(lo, hi);
+    default: return pair_fold<1>(lo, hi);
   }
 }
 
@@ -125,8 +162,8 @@ __device__ __forceinline__ void wg_combine_store(Partial* rec, const Partial& mi
 //   A row of the weight matrix is C = K*esize/16 chunks of 16 bytes.  LPR lanes share a row
 //   (LPR = 64 when C >= 64, else the next power of two >= C), so one load instruction reads
 //   RPI = 64/LPR rows.  A row-block is 8 load-instructions deep; its per-lane partial sums
-//   acc[8][MB] are reduced with a halving butterfly so that afterwards each lane holds one
-//   finished row (the row-slot given by its top 3 lane bits inside the LPR segment).
+//   acc[8][MB] are reduced with a halving (transposed) butterfly so that afterwards each lane
+//   holds one finished row: the row-slot given by its top 3 lane bits inside the segment.
 //   ONE (each lane owns one chunk of every row, C <= LPR): the next row-block's weights are
 //   loaded before the current one is reduced, across group boundaries.
 // ----------------------------------------------------------------------------------------
@@ -140,12 +177,13 @@ __global__ __launch_bounds__(256) void k_stream_valu(StreamArgs a) {
   extern __shared__ uint4 xs[];  // [MB][C] then (after the loop) Partial records
   const int C = static_cast<int>(a.K * (BF16 ? 2 : 4) / 16);
   const int CPL = (C + LPR - 1) / LPR;
-  const char* xg = static_cast<const char*>(a.x);
-  const int Mx = a.M;
-  stage16<4>(xs, MB * C, [&](int i) {
-    const int m = i / C, c = i - m * C;
-    return (m < Mx) ? load16(xg + (static_cast<size_t>(m) * C + c) * 16) : zero16();
-  });
+  const uint32_t rowbytes = static_cast<uint32_t>(C) * 16;
+  {
+    const rsrc_t xrs = make_rsrc(a.x, static_cast<uint32_t>(a.M) * rowbytes);
+    stage16<4>(xs, MB * C, [&](int i) {
+      return buffer_load16(xrs, i >= 0 ? static_cast<uint32_t>(i) * 16 : kOutOfRange);
+    });
+  }
   __syncthreads();
 
   const int l = lane_id(), w = wave_id();
@@ -153,161 +191,162 @@ __global__ __launch_bounds__(256) void k_stream_valu(StreamArgs a) {
   const int ri = l / LPR;
   const int jslot = lr / DUP;
   const bool leader = (lr % DUP) == 0;
-  const int64_t NG = (a.V + kGroup - 1) / kGroup;
-  const int64_t nwt = static_cast<int64_t>(gridDim.x) * (blockDim.x / kWave);
-  const size_t rowbytes = static_cast<size_t>(C) * 16;
+  const int V32 = static_cast<int>(a.V);
+  const int NG = (V32 + kGroup - 1) / kGroup;
+  const int nwt = static_cast<int>(gridDim.x) * (blockDim.x / kWave);
   const char* Wb = static_cast<const char*>(a.W);
+  const float c2 = a.invT * kLog2e;   // exp(y - ym) = exp2((z - zm) * c2)
 
   uint4 xr[MB];
 #pragma unroll
   for (int m = 0; m < MB; ++m) xr[m] = (ONE && lr < C) ? xs[m * C + lr] : zero16();
 
-  Partial run = partial_empty();  // lane m holds row m's running state
-  float gm[MB], gs[MB], gz[MB];
+  float run_z = -INFINITY;     // lane m: running argmax of row m
+  int32_t run_i = 0x7fffffff;
+  float vals[NRB][MB];         // the lane's finished z of each row-block of the group
+  float gz[MB];
   int32_t gi[MB];
 
-  auto group_reset = [&]() {
-#pragma unroll
-    for (int m = 0; m < MB; ++m) {
-      gm[m] = -INFINITY;
-      gs[m] = 0.f;
-      gz[m] = -INFINITY;
-      gi[m] = 0x7fffffff;
-    }
-  };
-
-  // reduce acc over the row's lanes, then fold the finished row into the group state
-  auto finish_rb = [&](float (&acc)[RB][MB], int64_t rbase) {
+  // reduce acc over the row's lanes, then record the finished row
+  auto finish_rb = [&](float (&acc)[RB][MB], int g, auto rbc) {
+    constexpr int rb = decltype(rbc)::value;
 #pragma unroll
     for (int step = 0; step < 3; ++step) {
-      const int n = RB >> step;
+      const int half = RB >> (step + 1);
       const int s = LPR >> (step + 1);
-      const bool upper = (lr & s) != 0;
 #pragma unroll
-      for (int i = 0; i < (RB >> (step + 1)); ++i) {
+      for (int i = 0; i < half; ++i)
 #pragma unroll
-        for (int m = 0; m < MB; ++m) {
-          const float lo = acc[i][m], hi = acc[i + n / 2][m];
-          const float send = upper ? lo : hi;
-          const float keep = upper ? hi : lo;
-          acc[i][m] = keep + xor_lane(send, s);
-        }
-      }
+        for (int m = 0; m < MB; ++m) acc[i][m] = pair_fold_rt(acc[i][m], acc[i + half][m], s);
     }
 #pragma unroll
     for (int s = LPR >> 4; s >= 1; s >>= 1)
 #pragma unroll
       for (int m = 0; m < MB; ++m) acc[0][m] += xor_lane(acc[0][m], s);
-    const int64_t row = rbase + jslot * RPI + ri;
-    const bool valid = row < a.V;
+    const int row = g * kGroup + rb * ROWS_RB + jslot * RPI + ri;
+    const bool valid = row < V32;
     if (a.zout != nullptr && leader && valid) {
 #pragma unroll
       for (int m = 0; m < MB; ++m)
         if (m < a.M) a.zout[static_cast<int64_t>(m) * a.zout_ld + row] = acc[0][m];
     }
-    if (a.stats != kStatsNone && valid) {
 #pragma unroll
-      for (int m = 0; m < MB; ++m) {
-        const float z = acc[0][m];
-        argmax_merge(gz[m], gi[m], z, static_cast<int32_t>(row));
-        if (a.stats >= kStatsLse) lse_merge(gm[m], gs[m], z * a.invT, 1.f);
+    for (int m = 0; m < MB; ++m) {
+      const float z = valid ? acc[0][m] : -INFINITY;
+      vals[rb][m] = z;
+      if (z > gz[m]) {   // rows of a lane increase with rb: strict > keeps the lowest on ties
+        gz[m] = z;
+        gi[m] = row;
       }
     }
   };
 
-  auto group_end = [&](int64_t g) {
-    if (a.stats == kStatsNone) return;
-#pragma unroll
-    for (int s = DUP; s < kWave; s <<= 1) {
+  auto group_end = [&](int g) {
+    if (a.lg != nullptr) {
 #pragma unroll
       for (int m = 0; m < MB; ++m) {
-        const float m2 = xor_lane(gm[m], s), s2 = xor_lane(gs[m], s);
-        const float z2 = xor_lane(gz[m], s);
-        const int32_t i2 = xor_lane(gi[m], s);
-        lse_merge(gm[m], gs[m], m2, s2);
-        argmax_merge(gz[m], gi[m], z2, i2);
+        float mx = vals[0][m];
+#pragma unroll
+        for (int rb = 1; rb < NRB; ++rb) mx = fmaxf(mx, vals[rb][m]);
+#pragma unroll
+        for (int s = DUP; s < kWave; s <<= 1) mx = fmaxf(mx, xor_lane(mx, s));
+        float sm = 0.f;
+        if (mx != -INFINITY) {
+#pragma unroll
+          for (int rb = 0; rb < NRB; ++rb) sm += exp2f((vals[rb][m] - mx) * c2);
+        }
+#pragma unroll
+        for (int s = DUP; s < kWave; s <<= 1) sm += xor_lane(sm, s);
+        if (l == m && m < a.M) a.lg[static_cast<int64_t>(m) * a.lg_ld + g] = mx * a.invT + log2f(sm) * kLn2;
       }
     }
-    float my_m = -INFINITY, my_s = 0.f, my_z = -INFINITY;
-    int32_t my_i = 0x7fffffff;
+    if (a.want_argmax) {
 #pragma unroll
-    for (int m = 0; m < MB; ++m)
-      if (l == m) {
-        my_m = gm[m];
-        my_s = gs[m];
-        my_z = gz[m];
-        my_i = gi[m];
+      for (int m = 0; m < MB; ++m) {
+#pragma unroll
+        for (int s = DUP; s < kWave; s <<= 1) {
+          const float z2 = xor_lane(gz[m], s);
+          const int32_t i2 = xor_lane(gi[m], s);
+          argmax_merge(gz[m], gi[m], z2, i2);
+        }
+        if (l == m) argmax_merge(run_z, run_i, gz[m], gi[m]);
       }
-    if (l < a.M) {
-      if (a.stats == kStatsSample) {
-        const float L = my_m + logf(my_s);
-        const float u = philox_uniform(a.seed, a.offset, kDraftGroup, a.row0 + l, g);
-        argmax_merge(run.gscore, run.g, L + gumbel(u), static_cast<int32_t>(g));
-      }
-      lse_merge(run.m, run.s, my_m, my_s);
-      argmax_merge(run.zmax, run.zid, my_z, my_i);
     }
   };
 
-  const int64_t gw = static_cast<int64_t>(blockIdx.x) * (blockDim.x / kWave) + w;
+  auto group_reset = [&]() {
+#pragma unroll
+    for (int m = 0; m < MB; ++m) {
+      gz[m] = -INFINITY;
+      gi[m] = 0x7fffffff;
+    }
+  };
+
+  // descriptor over one group's rows: rows past V read as zero
+  auto group_rsrc = [&](int g) {
+    const int g0 = g * kGroup;
+    const int rows = V32 - g0 < kGroup ? V32 - g0 : kGroup;
+    return make_rsrc(Wb + static_cast<size_t>(g0) * rowbytes, static_cast<uint32_t>(rows) * rowbytes);
+  };
+
+  const int gw = static_cast<int>(blockIdx.x) * (blockDim.x / kWave) + w;
   if constexpr (ONE) {
-    auto load_rb = [&](int64_t g, int rb, uint4 (&wv)[RB]) {
-      // descriptor over this group's rows: rows past V read as zero
-      const int64_t g0 = g * kGroup;
-      const int64_t rows = a.V - g0 < kGroup ? a.V - g0 : kGroup;
-      const rsrc_t rs = make_rsrc(Wb + static_cast<size_t>(g0) * rowbytes, static_cast<uint32_t>(rows * rowbytes));
+    auto load_rb = [&](int g, int rb, uint4 (&wv)[RB]) {
+      const rsrc_t rs = group_rsrc(g);
 #pragma unroll
       for (int j = 0; j < RB; ++j) {
         const int rin = rb * ROWS_RB + j * RPI + ri;
-        const uint32_t off = lr < C ? static_cast<uint32_t>(rin * rowbytes + lr * 16) : kOutOfRange;
-        wv[j] = buffer_load16(rs, off);
+        wv[j] = buffer_load16(rs, lr < C ? static_cast<uint32_t>(rin) * rowbytes + static_cast<uint32_t>(lr) * 16 : kOutOfRange);
       }
     };
-    // one pipeline step: prefetch the next row-block into `fill`, consume `use`
-    int64_t g = gw;
-    int rb = 0;
-    auto step = [&](uint4 (&use)[RB], uint4 (&fill)[RB]) -> bool {
-      int64_t g2 = g;
-      int rb2 = rb + 1;
-      if (rb2 == NRB) {
-        rb2 = 0;
-        g2 += nwt;
-      }
-      // unconditional prefetch (at the end of the wave's work it re-reads the current,
-      // cache-resident block) so the wait below can leave exactly these loads in flight
-      if (g2 < NG)
-        load_rb(g2, rb2, fill);
-      else
-        load_rb(g, rb, fill);
-      if (rb == 0) group_reset();
+    // Row-blocks are unrolled so that every index is static.  Each step prefetches the next
+    // row-block into the other buffer before consuming its own; the prefetch is
+    // unconditional (after the wave's last block it re-reads the current, cache-resident
+    // block) so the wait before the consumption leaves exactly those loads in flight.
+    uint4 bufA[RB], bufB[RB];
+    auto consume = [&](uint4 (&use)[RB], int g, int rb_for_row, auto rbc) {
+      constexpr int rb = decltype(rbc)::value;
+      (void)rb_for_row;
       float acc[RB][MB];
 #pragma unroll
       for (int j = 0; j < RB; ++j)
 #pragma unroll
         for (int m = 0; m < MB; ++m) acc[j][m] = chunk_dot<BF16>(use[j], xr[m], 0.f);
-      finish_rb(acc, g * kGroup + rb * ROWS_RB);
-      if (rb == NRB - 1) group_end(g);
-      g = g2;
-      rb = rb2;
-      return g < NG;
+      finish_rb(acc, g, rbc);
     };
-    uint4 bufA[RB], bufB[RB];
-    if (g < NG) {
-      load_rb(g, 0, bufA);
-      for (;;) {
-        if (!step(bufA, bufB)) break;
-        if (!step(bufB, bufA)) break;
+    int g = gw;
+    if (g < NG) load_rb(g, 0, bufA);
+    while (g < NG) {
+      group_reset();
+      const int gnext = g + nwt;
+      static_for<0, NRB>([&](auto rbc) {
+        constexpr int rb = decltype(rbc)::value;
+        if constexpr (rb % 2 == 0) {
+          if (rb + 1 < NRB) load_rb(g, rb + 1, bufB);
+          else if (gnext < NG) load_rb(gnext, 0, bufB);
+          else load_rb(g, rb, bufB);
+          consume(bufA, g, rb, rbc);
+        } else {
+          if (rb + 1 < NRB) load_rb(g, rb + 1, bufA);
+          else if (gnext < NG) load_rb(gnext, 0, bufA);
+          else load_rb(g, rb, bufA);
+          consume(bufB, g, rb, rbc);
+        }
+      });
+      group_end(g);
+      if constexpr (NRB % 2 == 1) {
+        // the next group's first block landed in bufB
+#pragma unroll
+        for (int j = 0; j < RB; ++j) bufA[j] = bufB[j];
       }
+      g = gnext;
     }
   } else {
-    for (int64_t g = gw; g < NG; g += nwt) {
+    for (int g = gw; g < NG; g += nwt) {
       group_reset();
-      const int64_t g0 = g * kGroup;
-      const int64_t grows = a.V - g0 < kGroup ? a.V - g0 : kGroup;
-      const rsrc_t rs = make_rsrc(Wb + static_cast<size_t>(g0) * rowbytes, static_cast<uint32_t>(grows * rowbytes));
-#pragma unroll 1
-      for (int rb = 0; rb < NRB; ++rb) {
-        const int64_t rbase = g * kGroup + rb * ROWS_RB;
+      const rsrc_t rs = group_rsrc(g);
+      static_for<0, NRB>([&](auto rbc) {
+        constexpr int rb = decltype(rbc)::value;
         float acc[RB][MB];
 #pragma unroll
         for (int j = 0; j < RB; ++j)
@@ -320,7 +359,7 @@ __global__ __launch_bounds__(256) void k_stream_valu(StreamArgs a) {
 #pragma unroll
           for (int j = 0; j < RB; ++j) {
             const int rin = rb * ROWS_RB + j * RPI + ri;
-            wv[j] = buffer_load16(rs, cok ? static_cast<uint32_t>(rin * rowbytes + c * 16) : kOutOfRange);
+            wv[j] = buffer_load16(rs, cok ? static_cast<uint32_t>(rin) * rowbytes + static_cast<uint32_t>(c) * 16 : kOutOfRange);
           }
           uint4 xq[MB];
 #pragma unroll
@@ -330,33 +369,32 @@ __global__ __launch_bounds__(256) void k_stream_valu(StreamArgs a) {
 #pragma unroll
             for (int m = 0; m < MB; ++m) acc[j][m] = chunk_dot<BF16>(wv[j], xq[m], acc[j][m]);
         }
-        finish_rb(acc, rbase);
-      }
+        finish_rb(acc, g, rbc);
+      });
       group_end(g);
     }
   }
-  if (a.stats == kStatsNone) return;
+  if (!a.want_argmax) return;
   __syncthreads();
-  Partial* rec = reinterpret_cast<Partial*>(xs);
-  wg_combine_store(rec, run, l < a.M, l, a.M, a.partials, a.partials_ld);
+  wg_argmax_store(reinterpret_cast<Partial*>(xs), run_z, run_i, l < a.M, l, a.M, a.partials, a.partials_ld);
 }
 
 // ----------------------------------------------------------------------------------------
-// k_stream_mfma: bf16, M <= 32*NCB rows.  Each wave walks its 64-row vocabulary groups as
-// 32-row tiles computed with v_mfma_f32_32x32x16_bf16: A = weight tile from HBM straight
-// into registers, B = activations.  The weight fragments are loaded KB k-steps at a time,
-// one batch ahead, the prefetch running across tile and group boundaries so the next loads
-// are in flight while a tile's statistics are folded.
+// k_stream_mfma2: bf16, M <= 32*NCB rows, NCB <= 2.  Each wave walks its 64-row vocabulary
+// groups with v_mfma_f32_32x32x16_bf16, both 32-row tiles of a group at once so that each activation
+// (B) fragment is read once per k-step for 64 vocabulary rows.  A = weight fragments from HBM
+// straight into registers, KB k-steps per batch, one batch ahead; the prefetch runs across
+// group boundaries, and the first batch is issued before the activations are staged.
 //   BG = false: B comes from LDS, staged once per workgroup and pre-swizzled into fragment
 //               order [k-step][column block][lane] (one conflict-free 16-byte read per lane).
 //   BG = true:  the activations do not fit in LDS (large K): each lane loads its B fragment
 //               directly from the (L2-resident) activation rows.
-// Output layout of the 32x32 tile: lane l holds column l%32 and rows
-// 8*(v/4) + 4*(l/32) + v%4 for its 16 accumulators v.
+// Output layout of a 32x32 tile: lane l holds column l%32 and rows
+// 8*(v/4) + 4*(l/32) + v%4 for its 16 accumulators v (increasing in v).
 // ----------------------------------------------------------------------------------------
 template <int NCB, bool BG>
-__global__ __launch_bounds__(256) void k_stream_mfma(StreamArgs a) {
-  constexpr int KB = BG ? 4 : 8;
+__global__ __launch_bounds__(256, 2) void k_stream_mfma2(StreamArgs a) {
+  constexpr int KB = 4;
   extern __shared__ uint4 bs[];  // [KS][NCB][64] 16-byte B fragments, later Partial records
   const int l = lane_id(), w = wave_id();
   const int NW = blockDim.x / kWave;
@@ -364,113 +402,339 @@ __global__ __launch_bounds__(256) void k_stream_mfma(StreamArgs a) {
   const int K = static_cast<int>(a.K);
   const int KS = (K + 15) / 16;
   const int nb = (KS + KB - 1) / KB;
-  const size_t rowbytes = static_cast<size_t>(K) * 2;
-  const int64_t NG = (a.V + kGroup - 1) / kGroup;
-  const int64_t nwt = static_cast<int64_t>(gridDim.x) * NW;
-  const char* xb = static_cast<const char*>(a.x);
+  const uint32_t rowbytes = static_cast<uint32_t>(K) * 2;
+  const int V32 = static_cast<int>(a.V);
+  const int NG = (V32 + kGroup - 1) / kGroup;
+  const int nwt = static_cast<int>(gridDim.x) * NW;
   const char* Wb = static_cast<const char*>(a.W);
   const int Mx = a.M;
+  const float c2 = a.invT * kLog2e;
+  const rsrc_t xrs = make_rsrc(a.x, static_cast<uint32_t>(Mx) * rowbytes);
 
-  if constexpr (!BG) {
-    stage16<8>(bs, KS * NCB * kWave, [&](int it) {
-      const int ks = it / (NCB * kWave);
-      const int cb = (it / kWave) % NCB;
-      const int ll = it & (kWave - 1);
-      const int m = cb * 32 + (ll & 31);
-      const int k = ks * 16 + (ll >> 5) * 8;
-      return (m < Mx && k < K) ? load16(xb + (static_cast<size_t>(m) * K + k) * 2) : zero16();
-    });
-    __syncthreads();
+  float run_z[NCB];             // running argmax of column m = cb*32 + n
+  int32_t run_i[NCB];
+  f32x16_t acc0[NCB], acc1[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) {
+    run_z[cb] = -INFINITY;
+    run_i[cb] = 0x7fffffff;
   }
 
-  Partial run[NCB];
-  float hm[NCB], hs[NCB], hz[NCB];
-  int32_t hi[NCB];
-  f32x16_t acc[NCB];
-#pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) run[cb] = partial_empty();
-
-  // B fragment addresses of this lane (BG): column m = cb*32 + n, k-half hf
-  const rsrc_t xrs = make_rsrc(xb, static_cast<uint32_t>(static_cast<size_t>(Mx) * K * 2));
-  auto load_batch = [&](int64_t g, int t, int b, uint4 (&X)[KB], uint4 (&Y)[KB][NCB]) {
-    // descriptor over this group's rows: rows past V read as zero
-    const int64_t g0 = g * kGroup;
-    const int64_t rows = a.V - g0 < kGroup ? a.V - g0 : kGroup;
-    const rsrc_t rs = make_rsrc(Wb + static_cast<size_t>(g0) * rowbytes, static_cast<uint32_t>(rows * rowbytes));
-    const uint32_t rbase = static_cast<uint32_t>((t * 32 + n) * rowbytes);
+  // batch b of group g: KB k-steps of both tiles (X0: rows 0..31, X1: rows 32..63)
+  auto load_batch = [&](int g, int b, uint4 (&X0)[KB], uint4 (&X1)[KB], uint4 (&Y)[KB][NCB]) {
+    const int g0 = g * kGroup;
+    const int rows = V32 - g0 < kGroup ? V32 - g0 : kGroup;
+    const rsrc_t rs = make_rsrc(Wb + static_cast<size_t>(g0) * rowbytes, static_cast<uint32_t>(rows) * rowbytes);
+    const uint32_t rb0 = static_cast<uint32_t>(n) * rowbytes;
+    const uint32_t rb1 = static_cast<uint32_t>(32 + n) * rowbytes;
 #pragma unroll
     for (int j = 0; j < KB; ++j) {
       const int ks = b * KB + j;
       const int k = ks * 16 + hf * 8;
       const bool kok = ks < KS && k < K;
-      X[j] = buffer_load16(rs, kok ? rbase + static_cast<uint32_t>(k * 2) : kOutOfRange);
+      X0[j] = buffer_load16(rs, kok ? rb0 + static_cast<uint32_t>(k) * 2 : kOutOfRange);
+      X1[j] = buffer_load16(rs, kok ? rb1 + static_cast<uint32_t>(k) * 2 : kOutOfRange);
       if constexpr (BG) {
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
           const int m = cb * 32 + n;
-          Y[j][cb] = buffer_load16(xrs, (kok && m < Mx) ? static_cast<uint32_t>((m * K + k) * 2) : kOutOfRange);
+          Y[j][cb] = buffer_load16(xrs, (kok && m < Mx) ? static_cast<uint32_t>(m) * rowbytes + static_cast<uint32_t>(k) * 2
+                                                        : kOutOfRange);
         }
       }
     }
   };
 
-  auto epilogue_tile = [&](int64_t g, int t) {
-    const int64_t tbase = g * kGroup + t * 32;
+  // fold the group's 64 rows (two tiles) into the statistics of each column
+  auto epilogue = [&](int g) {
+    const int gbase = g * kGroup;
+    const bool full = gbase + kGroup <= V32;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
       const int m = cb * 32 + n;
-      float zb = -INFINITY, ym = -INFINITY, ss = 0.f;
-      int32_t ib = 0x7fffffff;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t row = tbase + 8 * (v >> 2) + 4 * hf + (v & 3);
-        if (row < a.V) {
-          const float z = acc[cb][v];
-          argmax_merge(zb, ib, z, static_cast<int32_t>(row));
-          ym = fmaxf(ym, z * a.invT);
-          if (a.zout != nullptr && m < a.M) a.zout[static_cast<int64_t>(m) * a.zout_ld + row] = z;
-        }
-      }
-      if (a.stats == kStatsNone) continue;
-      if (a.stats >= kStatsLse && ym != -INFINITY) {
+      if (!full) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int64_t row = tbase + 8 * (v >> 2) + 4 * hf + (v & 3);
-          if (row < a.V) ss += __expf(acc[cb][v] * a.invT - ym);
+          const int r = 8 * (v >> 2) + 4 * hf + (v & 3);
+          if (gbase + r >= V32) acc0[cb][v] = -INFINITY;
+          if (gbase + 32 + r >= V32) acc1[cb][v] = -INFINITY;
         }
       }
-      const float zb2 = xor_lane(zb, 32);
-      const int32_t ib2 = xor_lane(ib, 32);
-      const float ym2 = xor_lane(ym, 32), ss2 = xor_lane(ss, 32);
-      argmax_merge(zb, ib, zb2, ib2);
-      lse_merge(ym, ss, ym2, ss2);
-      if (t == 0) {
-        hm[cb] = ym;
-        hs[cb] = ss;
-        hz[cb] = zb;
-        hi[cb] = ib;
-        continue;
+      if (a.zout != nullptr && m < a.M) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int r = gbase + 8 * (v >> 2) + 4 * hf + (v & 3);
+          if (r < V32) a.zout[static_cast<int64_t>(m) * a.zout_ld + r] = acc0[cb][v];
+          if (r + 32 < V32) a.zout[static_cast<int64_t>(m) * a.zout_ld + r + 32] = acc1[cb][v];
+        }
       }
-      lse_merge(ym, ss, hm[cb], hs[cb]);
-      argmax_merge(zb, ib, hz[cb], hi[cb]);
+      float zm = acc0[cb][0];
+#pragma unroll
+      for (int v = 1; v < 16; ++v) zm = fmaxf(zm, acc0[cb][v]);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) zm = fmaxf(zm, acc1[cb][v]);
+      int32_t zi = 0x7fffffff;
+      if (a.want_argmax) {
+        // lowest row holding zm: tile 0 rows come first, and rows grow with v in a tile
+        int bv = 32;
+#pragma unroll
+        for (int v = 15; v >= 0; --v)
+          if (acc1[cb][v] == zm) bv = 16 + v;
+#pragma unroll
+        for (int v = 15; v >= 0; --v)
+          if (acc0[cb][v] == zm) bv = v;
+        const int vv = bv & 15;
+        zi = (zm == -INFINITY) ? 0x7fffffff : gbase + (bv >> 4) * 32 + 8 * (vv >> 2) + 4 * hf + (vv & 3);
+      }
+      float ss = 0.f;
+      if (a.lg != nullptr && zm != -INFINITY) {
+        const float off = zm * c2;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) ss += exp2f(fmaf(acc0[cb][v], c2, -off)) + exp2f(fmaf(acc1[cb][v], c2, -off));
+      }
+      // merge with the other 32 rows of the column (lane l ^ 32)
+      const float zm2 = xor_lane(zm, 32), ss2 = xor_lane(ss, 32);
+      const int32_t zi2 = xor_lane(zi, 32);
+      const float gmx = fmaxf(zm, zm2);
+      float gsm = 0.f;
+      if (gmx != -INFINITY) gsm = ss * exp2f((zm - gmx) * c2) + ss2 * exp2f((zm2 - gmx) * c2);
+      argmax_merge(zm, zi, zm2, zi2);
       if (m < a.M) {
-        if (a.stats == kStatsSample) {
-          const float L = ym + logf(ss);
-          const float u = philox_uniform(a.seed, a.offset, kDraftGroup, a.row0 + m, g);
-          argmax_merge(run[cb].gscore, run[cb].g, L + gumbel(u), static_cast<int32_t>(g));
-        }
-        lse_merge(run[cb].m, run[cb].s, ym, ss);
-        argmax_merge(run[cb].zmax, run[cb].zid, zb, ib);
+        if (a.lg != nullptr && hf == 0) a.lg[static_cast<int64_t>(m) * a.lg_ld + g] = gmx * a.invT + log2f(gsm) * kLn2;
+        if (a.want_argmax) argmax_merge(run_z[cb], run_i[cb], zm, zi);
       }
     }
   };
 
-  int64_t g = static_cast<int64_t>(blockIdx.x) * NW + w;
+  int g = static_cast<int>(blockIdx.x) * NW + w;
+  int b = 0;
+  uint4 XA0[KB], XA1[KB], XB0[KB], XB1[KB];
+  uint4 YA[KB][NCB], YB[KB][NCB];
+  if (g < NG) load_batch(g, 0, XA0, XA1, YA);   // in flight while the activations are staged
+
+  if constexpr (!BG) {
+    stage16<8>(bs, KS * NCB * kWave, [&](int it) {
+      if (it < 0) return buffer_load16(xrs, kOutOfRange);
+      const int ks = it / (NCB * kWave);
+      const int cb = (it / kWave) % NCB;
+      const int ll = it & (kWave - 1);
+      const int m = cb * 32 + (ll & 31);
+      const int k = ks * 16 + (ll >> 5) * 8;
+      return buffer_load16(xrs, (m < Mx && k < K) ? static_cast<uint32_t>(m) * rowbytes + static_cast<uint32_t>(k) * 2
+                                                  : kOutOfRange);
+    });
+    __syncthreads();
+  }
+
+  // one pipeline step: prefetch the next batch into F*, consume U*.  The prefetch is
+  // unconditional (re-reads the current, cache-resident batch at the very end).
+  auto step = [&](uint4 (&U0)[KB], uint4 (&U1)[KB], uint4 (&UY)[KB][NCB], uint4 (&F0)[KB], uint4 (&F1)[KB],
+                  uint4 (&FY)[KB][NCB]) -> bool {
+    int g2 = g, b2 = b + 1;
+    if (b2 == nb) {
+      b2 = 0;
+      g2 = g + nwt;
+    }
+    if (g2 < NG)
+      load_batch(g2, b2, F0, F1, FY);
+    else
+      load_batch(g, b, F0, F1, FY);
+    if (b == 0) {
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          acc0[cb][v] = 0.f;
+          acc1[cb][v] = 0.f;
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < KB; ++j) {
+      const int ks = b * KB + j;
+      if (ks < KS) {
+        const bf16x8_t a0f = __builtin_bit_cast(bf16x8_t, U0[j]);
+        const bf16x8_t a1f = __builtin_bit_cast(bf16x8_t, U1[j]);
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+          const uint4 bv = BG ? UY[j][cb] : bs[(ks * NCB + cb) * kWave + l];
+          const bf16x8_t bf = __builtin_bit_cast(bf16x8_t, bv);
+          acc0[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0f, bf, acc0[cb], 0, 0, 0);
+          acc1[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1f, bf, acc1[cb], 0, 0, 0);
+        }
+      }
+    }
+    if (b == nb - 1) epilogue(g);
+    g = g2;
+    b = b2;
+    return g < NG;
+  };
+  if (g < NG) {
+    for (;;) {
+      if (!step(XA0, XA1, YA, XB0, XB1, YB)) break;
+      if (!step(XB0, XB1, YB, XA0, XA1, YA)) break;
+    }
+  }
+  if (!a.want_argmax) return;
+  __syncthreads();
+  Partial* rec = reinterpret_cast<Partial*>(bs);
+  if (hf == 0) {
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      const int m = cb * 32 + n;
+      if (m < a.M) {
+        Partial p = partial_empty();
+        p.zmax = run_z[cb];
+        p.zid = run_i[cb];
+        rec[w * a.M + m] = p;
+      }
+    }
+  }
+  __syncthreads();
+  for (int m = threadIdx.x; m < a.M; m += blockDim.x) {
+    Partial p = rec[m];
+    for (int i = 1; i < NW; ++i) argmax_merge(p.zmax, p.zid, rec[i * a.M + m].zmax, rec[i * a.M + m].zid);
+    a.partials[static_cast<int64_t>(m) * a.partials_ld + blockIdx.x] = p;
+  }
+}
+
+// ----------------------------------------------------------------------------------------
+// k_stream_mfma: the same contract for 3..6 column blocks, where two tiles of accumulators do
+// not fit next to the prefetch buffers: the group's two 32-row tiles are computed one after
+// the other (the prefetch still runs one batch ahead across tile and group boundaries).
+// ----------------------------------------------------------------------------------------
+template <int NCB, bool BG>
+__global__ __launch_bounds__(256) void k_stream_mfma(StreamArgs a) {
+  constexpr int KB = BG ? (NCB >= 5 ? 2 : 4) : 8;
+  extern __shared__ uint4 bs[];
+  const int l = lane_id(), w = wave_id();
+  const int NW = blockDim.x / kWave;
+  const int n = l & 31, hf = l >> 5;
+  const int K = static_cast<int>(a.K);
+  const int KS = (K + 15) / 16;
+  const int nb = (KS + KB - 1) / KB;
+  const uint32_t rowbytes = static_cast<uint32_t>(K) * 2;
+  const int V32 = static_cast<int>(a.V);
+  const int NG = (V32 + kGroup - 1) / kGroup;
+  const int nwt = static_cast<int>(gridDim.x) * NW;
+  const char* Wb = static_cast<const char*>(a.W);
+  const int Mx = a.M;
+  const float c2 = a.invT * kLog2e;
+  const rsrc_t xrs = make_rsrc(a.x, static_cast<uint32_t>(Mx) * rowbytes);
+
+  float run_z[NCB];
+  int32_t run_i[NCB];
+  float hm[NCB], hs[NCB], hz[NCB];
+  int32_t hi[NCB];
+  f32x16_t acc[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) {
+    run_z[cb] = -INFINITY;
+    run_i[cb] = 0x7fffffff;
+  }
+
+  auto load_batch = [&](int g, int t, int b, uint4 (&X)[KB], uint4 (&Y)[KB][NCB]) {
+    const int g0 = g * kGroup;
+    const int rows = V32 - g0 < kGroup ? V32 - g0 : kGroup;
+    const rsrc_t rs = make_rsrc(Wb + static_cast<size_t>(g0) * rowbytes, static_cast<uint32_t>(rows) * rowbytes);
+    const uint32_t rbase = static_cast<uint32_t>(t * 32 + n) * rowbytes;
+#pragma unroll
+    for (int j = 0; j < KB; ++j) {
+      const int ks = b * KB + j;
+      const int k = ks * 16 + hf * 8;
+      const bool kok = ks < KS && k < K;
+      X[j] = buffer_load16(rs, kok ? rbase + static_cast<uint32_t>(k) * 2 : kOutOfRange);
+      if constexpr (BG) {
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+          const int m = cb * 32 + n;
+          Y[j][cb] = buffer_load16(xrs, (kok && m < Mx) ? static_cast<uint32_t>(m) * rowbytes + static_cast<uint32_t>(k) * 2
+                                                        : kOutOfRange);
+        }
+      }
+    }
+  };
+
+  auto epilogue_tile = [&](int g, int t) {
+    const int tbase = g * kGroup + t * 32;
+    const bool full = tbase + 32 <= V32;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      const int m = cb * 32 + n;
+      if (!full) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          if (tbase + 8 * (v >> 2) + 4 * hf + (v & 3) >= V32) acc[cb][v] = -INFINITY;
+      }
+      if (a.zout != nullptr && m < a.M) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = tbase + 8 * (v >> 2) + 4 * hf + (v & 3);
+          if (row < V32) a.zout[static_cast<int64_t>(m) * a.zout_ld + row] = acc[cb][v];
+        }
+      }
+      float zm = acc[cb][0];
+#pragma unroll
+      for (int v = 1; v < 16; ++v) zm = fmaxf(zm, acc[cb][v]);
+      int32_t zi = 0x7fffffff;
+      if (a.want_argmax) {
+        int bv = 0;
+#pragma unroll
+        for (int v = 15; v >= 0; --v)
+          if (acc[cb][v] == zm) bv = v;
+        zi = zm == -INFINITY ? 0x7fffffff : tbase + 8 * (bv >> 2) + 4 * hf + (bv & 3);
+      }
+      float ss = 0.f;
+      if (a.lg != nullptr && zm != -INFINITY) {
+        const float off = zm * c2;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) ss += exp2f(fmaf(acc[cb][v], c2, -off));
+      }
+      const float zm2 = xor_lane(zm, 32), ss2 = xor_lane(ss, 32);
+      const int32_t zi2 = xor_lane(zi, 32);
+      const float gmx = fmaxf(zm, zm2);
+      float gsm = 0.f;
+      if (gmx != -INFINITY) gsm = ss * exp2f((zm - gmx) * c2) + ss2 * exp2f((zm2 - gmx) * c2);
+      argmax_merge(zm, zi, zm2, zi2);
+      if (t == 0) {
+        hm[cb] = gmx;
+        hs[cb] = gsm;
+        hz[cb] = zm;
+        hi[cb] = zi;
+        continue;
+      }
+      const float tm = fmaxf(gmx, hm[cb]);
+      float ts = 0.f;
+      if (tm != -INFINITY) ts = gsm * exp2f((gmx - tm) * c2) + hs[cb] * exp2f((hm[cb] - tm) * c2);
+      argmax_merge(zm, zi, hz[cb], hi[cb]);
+      if (m < a.M) {
+        if (a.lg != nullptr && hf == 0) a.lg[static_cast<int64_t>(m) * a.lg_ld + g] = tm * a.invT + log2f(ts) * kLn2;
+        if (a.want_argmax) argmax_merge(run_z[cb], run_i[cb], zm, zi);
+      }
+    }
+  };
+
+  int g = static_cast<int>(blockIdx.x) * NW + w;
   int t = 0, b = 0;
-  // one pipeline step: prefetch the next batch into (FX, FY), consume (UX, UY)
+  uint4 XA[KB], XB[KB];
+  uint4 YA[KB][NCB], YB[KB][NCB];
+  if (g < NG) load_batch(g, 0, 0, XA, YA);
+
+  if constexpr (!BG) {
+    stage16<8>(bs, KS * NCB * kWave, [&](int it) {
+      if (it < 0) return buffer_load16(xrs, kOutOfRange);
+      const int ks = it / (NCB * kWave);
+      const int cb = (it / kWave) % NCB;
+      const int ll = it & (kWave - 1);
+      const int m = cb * 32 + (ll & 31);
+      const int k = ks * 16 + (ll >> 5) * 8;
+      return buffer_load16(xrs, (m < Mx && k < K) ? static_cast<uint32_t>(m) * rowbytes + static_cast<uint32_t>(k) * 2
+                                                  : kOutOfRange);
+    });
+    __syncthreads();
+  }
+
   auto step = [&](uint4 (&UX)[KB], uint4 (&UY)[KB][NCB], uint4 (&FX)[KB], uint4 (&FY)[KB][NCB]) -> bool {
-    int64_t g2 = g;
-    int t2 = t, b2 = b + 1;
+    int g2 = g, t2 = t, b2 = b + 1;
     if (b2 == nb) {
       b2 = 0;
       t2 = t + 1;
@@ -479,7 +743,6 @@ __global__ __launch_bounds__(256) void k_stream_mfma(StreamArgs a) {
         g2 = g + nwt;
       }
     }
-    // unconditional prefetch (re-reads the current, cache-resident batch at the very end)
     if (g2 < NG)
       load_batch(g2, t2, b2, FX, FY);
     else
@@ -508,85 +771,145 @@ __global__ __launch_bounds__(256) void k_stream_mfma(StreamArgs a) {
     b = b2;
     return g < NG;
   };
-  uint4 XA[KB], XB[KB];
-  uint4 YA[KB][NCB], YB[KB][NCB];
   if (g < NG) {
-    load_batch(g, 0, 0, XA, YA);
     for (;;) {
       if (!step(XA, YA, XB, YB)) break;
       if (!step(XB, YB, XA, YA)) break;
     }
   }
-  if (a.stats == kStatsNone) return;
+  if (!a.want_argmax) return;
   __syncthreads();
   Partial* rec = reinterpret_cast<Partial*>(bs);
   if (hf == 0) {
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
       const int m = cb * 32 + n;
-      if (m < a.M) rec[w * a.M + m] = run[cb];
+      if (m < a.M) {
+        Partial p = partial_empty();
+        p.zmax = run_z[cb];
+        p.zid = run_i[cb];
+        rec[w * a.M + m] = p;
+      }
     }
   }
   __syncthreads();
   for (int m = threadIdx.x; m < a.M; m += blockDim.x) {
     Partial p = rec[m];
-    for (int i = 1; i < NW; ++i) partial_merge(p, rec[i * a.M + m]);
+    for (int i = 1; i < NW; ++i) argmax_merge(p.zmax, p.zid, rec[i * a.M + m].zmax, rec[i * a.M + m].zid);
     a.partials[static_cast<int64_t>(m) * a.partials_ld + blockIdx.x] = p;
   }
 }
 
 // ----------------------------------------------------------------------------------------
 // k_head_finalize: one workgroup (16 waves) per row.
+//   greedy:  token = argmax over the producers' partials; lse (if wanted) over the L_g.
+//   sample:  lse over the L_g; group g* = argmax_g L_g + Gumbel(u_g) with one Philox block
+//            per four groups; then the 64 logits of g* are recomputed and the element draw
+//            argmax_i y_i + Gumbel(u_i) picks the token.
 // ----------------------------------------------------------------------------------------
 constexpr int kFinThreads = 1024;
+constexpr int kFinWaves = kFinThreads / kWave;
 constexpr int kFinPerThread = (kMaxPartials + kFinThreads - 1) / kFinThreads;
-constexpr int kFinRowsPerWave = kGroup / (kFinThreads / kWave);   // 4
-constexpr int kFinMaxCPL = 16;
+constexpr int kFinRowsPerWave = kGroup / kFinWaves;   // 4
 
 template <bool BF16>
 __global__ __launch_bounds__(kFinThreads) void k_head_finalize(FinalizeArgs f) {
-  __shared__ Partial red[kFinThreads / kWave];
+  __shared__ float redf[kFinWaves];
+  __shared__ float redf2[kFinWaves];
+  __shared__ int32_t redi[kFinWaves];
   __shared__ float zs[kGroup];
   const int m = blockIdx.x;
   const int l = lane_id(), w = wave_id();
-  const Partial* pp = f.partials + static_cast<int64_t>(m) * f.partials_ld;
-  Partial loaded[kFinPerThread];
+  const int NG = static_cast<int>((f.V + kGroup - 1) / kGroup);
+  const bool want_lse = f.lse != nullptr || f.logprob != nullptr || f.mode == 1;
+  const float* lgr = f.lg + static_cast<int64_t>(m) * f.lg_ld;
+
+  // ---- row lse and (sampling) the group scores, four groups per thread per pass
+  float lmx = -INFINITY, lsm = 0.f;
+  float best = -INFINITY;
+  int32_t bg = 0x7fffffff;
+  if (want_lse) {
+    for (int q = threadIdx.x; q * 4 < NG; q += kFinThreads) {
+      float L[4];
 #pragma unroll
-  for (int i = 0; i < kFinPerThread; ++i) {
-    const int idx = threadIdx.x + i * kFinThreads;
-    loaded[i] = idx < f.P ? pp[idx] : partial_empty();
+      for (int j = 0; j < 4; ++j) L[j] = (q * 4 + j < NG) ? lgr[q * 4 + j] : -INFINITY;
+      const float qm = fmaxf(fmaxf(L[0], L[1]), fmaxf(L[2], L[3]));
+      float qs = 0.f;
+      if (qm != -INFINITY) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) qs += __expf(L[j] - qm);
+      }
+      lse_merge(lmx, lsm, qm, qs);
+      if (f.mode == 1) {
+        uint64_t words[4];
+        philox_block(f.seed, f.offset, kDraftGroup, static_cast<uint64_t>(m), static_cast<uint64_t>(q) * 4, words);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (q * 4 + j < NG && L[j] != -INFINITY)
+            argmax_merge(best, bg, L[j] + gumbel(word_to_uniform(words[j])), q * 4 + j);
+      }
+    }
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) {
+      const float m2 = xor_lane(lmx, s), s2 = xor_lane(lsm, s);
+      lse_merge(lmx, lsm, m2, s2);
+      const float b2 = xor_lane(best, s);
+      const int32_t i2 = xor_lane(bg, s);
+      argmax_merge(best, bg, b2, i2);
+    }
+    if (l == 0) {
+      redf[w] = lmx;
+      redf2[w] = lsm;
+    }
+    __syncthreads();
+    lmx = redf[0];
+    lsm = redf2[0];
+    for (int i = 1; i < kFinWaves; ++i) lse_merge(lmx, lsm, redf[i], redf2[i]);
+    __syncthreads();
   }
-  Partial p = loaded[0];
-#pragma unroll
-  for (int i = 1; i < kFinPerThread; ++i) partial_merge(p, loaded[i]);
-#pragma unroll
-  for (int s = 32; s >= 1; s >>= 1) {
-    Partial q;
-    q.m = xor_lane(p.m, s);
-    q.s = xor_lane(p.s, s);
-    q.gscore = xor_lane(p.gscore, s);
-    q.g = xor_lane(p.g, s);
-    q.zmax = xor_lane(p.zmax, s);
-    q.zid = xor_lane(p.zid, s);
-    partial_merge(p, q);
-  }
-  if (l == 0) red[w] = p;
-  __syncthreads();
-  p = red[0];
-  for (int i = 1; i < kFinThreads / kWave; ++i) partial_merge(p, red[i]);
-  const float lse = p.m + logf(p.s);
+  const float lse = lmx + logf(lsm);
+
   int32_t tok;
   float ytok;
   if (f.mode == 0) {
-    tok = p.zid;
-    ytok = p.zmax * f.invT;
+    const Partial* pp = f.partials + static_cast<int64_t>(m) * f.partials_ld;
+    float z = -INFINITY;
+    int32_t zi = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < kFinPerThread; ++i) {
+      const int idx = threadIdx.x + i * kFinThreads;
+      if (idx < f.P) argmax_merge(z, zi, pp[idx].zmax, pp[idx].zid);
+    }
+    wave_argmax(z, zi);
+    if (l == 0) {
+      redf[w] = z;
+      redi[w] = zi;
+    }
+    __syncthreads();
+    z = redf[0];
+    zi = redi[0];
+    for (int i = 1; i < kFinWaves; ++i) argmax_merge(z, zi, redf[i], redi[i]);
+    tok = zi;
+    ytok = z * f.invT;
   } else {
+    if (l == 0) {
+      redf[w] = best;
+      redi[w] = bg;
+    }
+    __syncthreads();
+    best = redf[0];
+    bg = redi[0];
+    for (int i = 1; i < kFinWaves; ++i) argmax_merge(best, bg, redf[i], redi[i]);
     // recompute the 64 logits of the winning group (4 rows per wave, loads issued together)
     const int C = static_cast<int>(f.K * (BF16 ? 2 : 4) / 16);
     const int CPL = (C + kWave - 1) / kWave;
-    const size_t rowbytes = static_cast<size_t>(C) * 16;
-    const char* xr = static_cast<const char*>(f.x) + static_cast<size_t>(m) * rowbytes;
-    const int64_t gbase = static_cast<int64_t>(p.g) * kGroup;
+    const uint32_t rowbytes = static_cast<uint32_t>(C) * 16;
+    const int64_t gbase = static_cast<int64_t>(bg == 0x7fffffff ? 0 : bg) * kGroup;
+    const int64_t r0 = gbase + w * kFinRowsPerWave;
+    const int nrows = f.V - r0 >= kFinRowsPerWave ? kFinRowsPerWave : (f.V - r0 > 0 ? static_cast<int>(f.V - r0) : 0);
+    const rsrc_t wrs = make_rsrc(static_cast<const char*>(f.W) + static_cast<size_t>(nrows > 0 ? r0 : 0) * rowbytes,
+                                 static_cast<uint32_t>(nrows) * rowbytes);
+    const rsrc_t xrs = make_rsrc(static_cast<const char*>(f.x) + static_cast<size_t>(m) * rowbytes, rowbytes);
     float z[kFinRowsPerWave];
 #pragma unroll
     for (int j = 0; j < kFinRowsPerWave; ++j) z[j] = 0.f;
@@ -596,14 +919,10 @@ __global__ __launch_bounds__(kFinThreads) void k_head_finalize(FinalizeArgs f) {
       for (int qq = 0; qq < 4; ++qq) {
         const int c = (q0 + qq) * kWave + l;
         const bool cok = q0 + qq < CPL && c < C;
-        xv[qq] = cok ? load16(xr + static_cast<size_t>(c) * 16) : zero16();
+        xv[qq] = buffer_load16(xrs, cok ? static_cast<uint32_t>(c) * 16 : kOutOfRange);
 #pragma unroll
-        for (int j = 0; j < kFinRowsPerWave; ++j) {
-          const int64_t row = gbase + w * kFinRowsPerWave + j;
-          wv[qq][j] = (cok && row < f.V)
-                          ? load16(static_cast<const char*>(f.W) + static_cast<size_t>(row) * rowbytes + static_cast<size_t>(c) * 16)
-                          : zero16();
-        }
+        for (int j = 0; j < kFinRowsPerWave; ++j)
+          wv[qq][j] = buffer_load16(wrs, cok ? static_cast<uint32_t>(j) * rowbytes + static_cast<uint32_t>(c) * 16 : kOutOfRange);
       }
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq)
@@ -619,11 +938,12 @@ __global__ __launch_bounds__(kFinThreads) void k_head_finalize(FinalizeArgs f) {
     const int64_t row = gbase + l;
     const bool valid = row < f.V;
     const float y = zs[l] * f.invT;
-    float e = valid ? y + gumbel(philox_uniform(f.seed, f.offset, kDraftElem, f.row0 + m, row)) : -INFINITY;
+    float e = valid ? y + gumbel(philox_uniform(f.seed, f.offset, kDraftElem, static_cast<uint64_t>(m), row)) : -INFINITY;
     int32_t ei = valid ? l : 0x7fffffff;
     wave_argmax(e, ei);
-    tok = static_cast<int32_t>(gbase + ei);
-    ytok = __shfl(y, ei);
+    const int el = ei == 0x7fffffff ? 0 : ei;
+    tok = static_cast<int32_t>(gbase + el);
+    ytok = __shfl(y, el);
   }
   if (threadIdx.x == 0) {
     f.token[m] = tok;
@@ -727,13 +1047,29 @@ static hipError_t run_mfma(const StreamArgs& a, int grid, bool bg, hipStream_t s
   const int KS = static_cast<int>((a.K + 15) / 16);
   const int frag = bg ? 0 : KS * NCB * 1024;
   const int bytes = frag > rec ? frag : rec;
-  hipError_t e = bg ? allow_lds(k_stream_mfma<NCB, true>, bytes) : allow_lds(k_stream_mfma<NCB, false>, bytes);
-  if (e != hipSuccess) return e;
+  hipError_t e;
   TraceScope ts("stream_mfma", st);
-  if (bg)
-    hipLaunchKernelGGL((k_stream_mfma<NCB, true>), dim3(grid), dim3(nw * kWave), bytes, st, a);
-  else
-    hipLaunchKernelGGL((k_stream_mfma<NCB, false>), dim3(grid), dim3(nw * kWave), bytes, st, a);
+  // Weights and fragments both from global memory: computing the group's two tiles together
+  // halves the fragment loads per weight byte.  With fragments in LDS the sequential form is
+  // faster (fewer live registers, deeper weight batches).
+  if constexpr (NCB <= 2) {
+    if (bg) {
+      e = allow_lds(k_stream_mfma2<NCB, true>, bytes);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL((k_stream_mfma2<NCB, true>), dim3(grid), dim3(nw * kWave), bytes, st, a);
+    } else {
+      e = allow_lds(k_stream_mfma<NCB, false>, bytes);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL((k_stream_mfma<NCB, false>), dim3(grid), dim3(nw * kWave), bytes, st, a);
+    }
+  } else {
+    e = bg ? allow_lds(k_stream_mfma<NCB, true>, bytes) : allow_lds(k_stream_mfma<NCB, false>, bytes);
+    if (e != hipSuccess) return e;
+    if (bg)
+      hipLaunchKernelGGL((k_stream_mfma<NCB, true>), dim3(grid), dim3(nw * kWave), bytes, st, a);
+    else
+      hipLaunchKernelGGL((k_stream_mfma<NCB, false>), dim3(grid), dim3(nw * kWave), bytes, st, a);
+  }
   return hipGetLastError();
 }
 

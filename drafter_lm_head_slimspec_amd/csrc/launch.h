@@ -8,34 +8,32 @@ namespace sh {
 
 struct Partial;
 
-enum Stats : int {
-  kStatsNone = 0,    // only write z (scores)
-  kStatsArgmax = 1,  // greedy token, no lse
-  kStatsLse = 2,     // greedy token + lse / logprob
-  kStatsSample = 3   // lse + group-Gumbel scores for sampling
-};
-
 // One streaming pass z[m, v] = W[v, :] . x[m, :] for v < V, m < M (M rows of this chunk).
+// Outputs, each optional: the raw logits (zout), the per-group log-sum-exp of y = z * invT
+// (lg, one value per row and 64-row vocabulary group, consumed by the finalize for the row
+// lse and the group draw), and per-workgroup argmax partials (greedy).
 struct StreamArgs {
   const void* W;      // [V, K] dtype
   const void* x;      // [M, K] dtype
   int64_t V, K;
   int M;
   bool bf16;
-  int stats;
+  bool want_argmax;
   float invT;
-  uint64_t seed, offset;
-  int64_t row0;          // global row index of x[0] (Philox row)
   float* zout;           // nullable [M, zout_ld]
   int64_t zout_ld;
-  Partial* partials;     // [M, partials_ld], one per producer workgroup
+  float* lg;             // nullable [M, lg_ld], lg_ld >= ceil(V / 64)
+  int64_t lg_ld;
+  Partial* partials;     // [M, partials_ld] when want_argmax, one per producer workgroup
   int64_t partials_ld;
 };
 
 struct FinalizeArgs {
-  const Partial* partials;  // [M, ld]
+  const Partial* partials;  // [M, ld] argmax partials (greedy)
   int64_t partials_ld;
   int P;                    // producers per row
+  const float* lg;          // [M, lg_ld] group log-sum-exp (lse and sampling)
+  int64_t lg_ld;
   const void* W;            // [V, K] (sampling: recompute the winning group)
   const void* x;            // [M, K]
   int64_t V, K;
@@ -44,7 +42,6 @@ struct FinalizeArgs {
   int mode;                 // 0 greedy, 1 sample
   float invT;
   uint64_t seed, offset;
-  int64_t row0;
   int32_t* token;
   float* lse;
   float* logprob;
