@@ -317,7 +317,7 @@ def main():
 
 def cpu_baseline(h, Wd, Wu, seed):
     """The oracle, as it stands, on the headline workload: full low-rank calls (48 rows, all V,
-    sampling), repeated until about 10 s of host time has been spent (at most 5 calls)."""
+    sampling), repeated until about 12 s of host time has been spent (at most 100 calls)."""
     from oracle import heads
     try:
         from threadpoolctl import threadpool_info
@@ -326,7 +326,7 @@ def cpu_baseline(h, Wd, Wu, seed):
         threads = os.cpu_count()
     n = 0
     t0 = time.time()
-    while n < 5 and (time.time() - t0) < 10.0:
+    while n < 100 and (time.time() - t0) < 12.0:
         heads.head_lowrank(h, Wd, Wu, "bf16", "sample", 1.0, seed, n)
         n += 1
     dt = time.time() - t0
