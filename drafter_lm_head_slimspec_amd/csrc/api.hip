@@ -72,7 +72,46 @@ int check_opt_out(const void* p, const char* name) {
   return SH_OK;
 }
 
+// Top-k scratch: the counter block (cleared at the start of each call) first, then the
+// candidates and the bitmask.
+struct TopkLayout {
+  size_t hist_off, count_off, cand_off, mask_off, total;
+};
+
+TopkLayout topk_layout(int64_t M, int64_t V) {
+  TopkLayout L{};
+  size_t off = 0;
+  L.hist_off = off;
+  off += static_cast<size_t>(M) * 4096 * 4;
+  L.count_off = off;
+  off = align_up(off + static_cast<size_t>(M) * sh::kTkCounterStride * 4, 256);
+  L.cand_off = off;
+  off = align_up(off + static_cast<size_t>(M * V) * 8, 256);
+  L.mask_off = off;
+  off = align_up(off + static_cast<size_t>(M) * static_cast<size_t>((V + 63) / 64) * 8, 256);
+  L.total = off;
+  return L;
+}
+
+sh::TopkArgs topk_args(void* ws, const TopkLayout& L, const float* scores, int64_t M, int64_t V,
+                       int64_t k, int32_t* out) {
+  char* b = static_cast<char*>(ws);
+  sh::TopkArgs a{};
+  a.scores = scores;
+  a.V = V;
+  a.k = static_cast<int>(k);
+  a.M = static_cast<int>(M);
+  a.chunks = sh::topk_chunks(V);
+  a.hist = reinterpret_cast<uint32_t*>(b + L.hist_off);
+  a.count = reinterpret_cast<uint32_t*>(b + L.count_off);
+  a.cand = reinterpret_cast<uint2*>(b + L.cand_off);
+  a.mask = reinterpret_cast<uint64_t*>(b + L.mask_off);
+  a.out = out;
+  return a;
+}
+
 struct HeadLayout {
+  size_t tk_off, tk_bytes;   // SpecVocab: the top-k block, at offset 0
   size_t hr_off, hr_bytes;
   size_t part_off, part_bytes;
   size_t lg_off, lg_bytes;
@@ -84,6 +123,9 @@ struct HeadLayout {
 HeadLayout head_layout(int op, int64_t M, int64_t r, int64_t V, int64_t k, int dtype) {
   HeadLayout L{};
   size_t off = 0;
+  L.tk_off = off;
+  L.tk_bytes = (op == SH_OP_SPECVOCAB) ? topk_layout(M, V).total : 0;
+  off += L.tk_bytes;
   L.hr_off = off;
   L.hr_bytes = (op == SH_OP_DENSE) ? 0 : align_up(static_cast<size_t>(M * r) * esize(dtype), 256);
   off += L.hr_bytes;
@@ -99,6 +141,26 @@ HeadLayout head_layout(int op, int64_t M, int64_t r, int64_t V, int64_t k, int d
   L.z_off = off;
   L.z_bytes = (op == SH_OP_SPECVOCAB) ? align_up(static_cast<size_t>(M * k) * 4, 256) : 0;
   off += L.z_bytes;
+  L.total = off;
+  return L;
+}
+
+// Verification scratch: row-segment partials, then residual-segment partials.
+struct VerifyLayout {
+  size_t part_off, part2_off, total;
+  int S, S2;
+};
+
+VerifyLayout verify_layout(int mode, int64_t B, int64_t gamma, int64_t V) {
+  VerifyLayout L{};
+  const int64_t R = mode == SH_GREEDY ? gamma + 1 : 2 * gamma + 1;
+  L.S = sh::verify_segments(B, gamma, V, mode);
+  L.S2 = sh::verify_resid_segments(B, V, mode);
+  size_t off = 0;
+  L.part_off = off;
+  off = align_up(off + static_cast<size_t>(B * R * L.S) * sizeof(sh::Partial), 256);
+  L.part2_off = off;
+  off = align_up(off + static_cast<size_t>(B * L.S2) * sizeof(sh::Partial), 256);
   L.total = off;
   return L;
 }
@@ -228,16 +290,12 @@ size_t sh_head_workspace_bytes(int op, int64_t M, int64_t d, int64_t r, int64_t 
 
 size_t sh_verify_workspace_bytes(int mode, int64_t B, int64_t gamma, int64_t V) {
   if ((mode != SH_GREEDY && mode != SH_SAMPLE) || B < 1 || gamma < 1 || V < 1) return 0;
-  const int64_t R = mode == SH_GREEDY ? gamma + 1 : 2 * gamma + 1;
-  const int S = sh::verify_segments(B, gamma, V, mode);
-  return align_up(static_cast<size_t>(B * R * S) * sizeof(sh::Partial), 256);
+  return verify_layout(mode, B, gamma, V).total;
 }
 
 size_t sh_topk_workspace_bytes(int64_t M, int64_t V, int64_t k) {
-  (void)M;
-  (void)V;
-  (void)k;
-  return 0;
+  if (M < 1 || V < 1 || k < 1 || k > V) return 0;
+  return topk_layout(M, V).total;
 }
 
 int draft_head_dense(const void* h, int64_t M, int64_t d, const void* W, int64_t V, int dtype,
@@ -297,6 +355,8 @@ int draft_head_specvocab(const void* h, int64_t M, int64_t d, const void* W_down
     return fail(SH_ERR_UNSUPPORTED, "dprime * element size above %lld bytes", static_cast<long long>(kMaxRowBytes));
   if (k < 1 || k > V) return fail(SH_ERR_PARAM, "k must be in [1, V]");
   if (k > kMaxK) return fail(SH_ERR_UNSUPPORTED, "k above %lld", static_cast<long long>(kMaxK));
+  if (V > sh::kTopkMaxV) return fail(SH_ERR_UNSUPPORTED, "V above %lld", static_cast<long long>(sh::kTopkMaxV));
+  if (M > 65535) return fail(SH_ERR_UNSUPPORTED, "M above 65535");
   SH_TRY(check_out(topk_idx, "topk_idx"));
   SH_TRY(check_opt_out(topk_logit, "topk_logit"));
   SH_TRY(check_opt_out(topk_prob, "topk_prob"));
@@ -308,7 +368,10 @@ int draft_head_specvocab(const void* h, int64_t M, int64_t d, const void* W_down
   float* scores = reinterpret_cast<float*>(ws + L.score_off);
   float* zbuf = reinterpret_cast<float*>(ws + L.z_off);
   const bool bf16 = dtype == SH_BF16;
-  SH_HIP(sh::launch_rowdot(W_down, h, dprime, d, M, bf16, hp, st), "reduced-state kernel");
+  const TopkLayout TL = topk_layout(M, V);
+  SH_HIP(sh::launch_rowdot(W_down, h, dprime, d, M, bf16, hp, st,
+                           reinterpret_cast<uint32_t*>(ws + L.tk_off + TL.hist_off), sh::topk_counter_words(M)),
+         "reduced-state kernel");
   const bool mfma = bf16 && M > kValuMaxRows;
   const int64_t chunk = mfma ? kMfmaMaxRows : kValuMaxRows;
   for (int64_t m0 = 0; m0 < M; m0 += chunk) {
@@ -331,7 +394,7 @@ int draft_head_specvocab(const void* h, int64_t M, int64_t d, const void* W_down
     int p = 0;
     SH_HIP(sh::launch_stream(a, mfma, &p, st), "approximate scorer kernel");
   }
-  SH_HIP(sh::launch_topk(scores, M, V, k, topk_idx, st), "top-k kernel");
+  SH_HIP(sh::launch_topk(topk_args(ws + L.tk_off, TL, scores, M, V, k, topk_idx), st), "top-k kernels");
   SH_HIP(sh::launch_gather_exact(U, h, topk_idx, M, d, V, k, bf16, zbuf, st), "gather kernel");
   SH_HIP(sh::launch_gather_finalize(zbuf, topk_idx, M, k, mode == SH_SAMPLE ? 1 : 0, 1.0f / temperature,
                                     seed, offset, topk_logit, topk_prob, token, lse, logprob, st),
@@ -349,8 +412,8 @@ int spec_verify(int mode, int64_t B, int64_t gamma, int64_t V, int dtype, const 
   if (B < 1 || B > (int64_t{1} << 20)) return fail(SH_ERR_SHAPE, "B must be in [1, 2^20]");
   if (gamma < 1 || gamma > kMaxGamma) return fail(SH_ERR_SHAPE, "gamma must be in [1, %lld]", static_cast<long long>(kMaxGamma));
   SH_TRY(check_rowlen("V", V, dtype));
-  if (V > kMaxV) return fail(SH_ERR_SHAPE, "V above 2^31 - 64");
-  if (B * (gamma + 1) > 65535) return fail(SH_ERR_UNSUPPORTED, "B * (gamma + 1) above 65535");
+  if (V > (int64_t{1} << 28)) return fail(SH_ERR_SHAPE, "V above 2^28");
+  if (B > 65535) return fail(SH_ERR_UNSUPPORTED, "B above 65535");
   SH_TRY(check_ptr(target_logits, "target_logits"));
   if (draft_tokens == nullptr) return fail(SH_ERR_NULL, "draft_tokens is NULL");
   if (!aligned(draft_tokens, 4)) return fail(SH_ERR_ALIGN, "draft_tokens is not 4-byte aligned");
@@ -378,8 +441,12 @@ int spec_verify(int mode, int64_t B, int64_t gamma, int64_t V, int dtype, const 
   a.offset = offset;
   a.accept_len = accept_len;
   a.out_tokens = out_tokens;
-  a.partials = static_cast<sh::Partial*>(workspace);
-  a.S = sh::verify_segments(B, gamma, V, mode);
+  const VerifyLayout L = verify_layout(mode, B, gamma, V);
+  char* ws = static_cast<char*>(workspace);
+  a.partials = reinterpret_cast<sh::Partial*>(ws + L.part_off);
+  a.S = L.S;
+  a.partials2 = reinterpret_cast<sh::Partial*>(ws + L.part2_off);
+  a.S2 = L.S2;
   SH_HIP(sh::launch_verify(a, static_cast<hipStream_t>(stream)), "verify kernels");
   return SH_OK;
 }
@@ -390,10 +457,15 @@ int sh_topk(const float* scores, int64_t M, int64_t V, int64_t k, int32_t* topk_
   SH_TRY(check_ptr(scores, "scores"));
   SH_TRY(check_out(topk_idx, "topk_idx"));
   if (M < 1 || M > 65535) return fail(SH_ERR_SHAPE, "M must be in [1, 65535]");
-  if (V < 1 || V > kMaxV) return fail(SH_ERR_SHAPE, "V must be in [1, 2^31 - 64]");
+  if (V < 1 || V > sh::kTopkMaxV) return fail(SH_ERR_SHAPE, "V must be in [1, 2^19]");
   if (k < 1 || k > V) return fail(SH_ERR_PARAM, "k must be in [1, V]");
   SH_TRY(check_workspace(workspace, workspace_bytes, sh_topk_workspace_bytes(M, V, k)));
-  SH_HIP(sh::launch_topk(scores, M, V, k, topk_idx, static_cast<hipStream_t>(stream)), "top-k kernel");
+  const TopkLayout TL = topk_layout(M, V);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  SH_HIP(sh::launch_zero(reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + TL.hist_off),
+                         sh::topk_counter_words(M), st),
+         "top-k counter clear");
+  SH_HIP(sh::launch_topk(topk_args(workspace, TL, scores, M, V, k, topk_idx), st), "top-k kernels");
   return SH_OK;
 }
 

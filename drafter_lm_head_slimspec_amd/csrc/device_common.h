@@ -206,7 +206,11 @@ __device__ __forceinline__ float gumbel(float u) { return -logf(-logf(u)); }
 // wave helpers
 // ---------------------------------------------------------------------------------------
 __device__ __forceinline__ int lane_id() { return static_cast<int>(threadIdx.x) & (kWave - 1); }
-__device__ __forceinline__ int wave_id() { return static_cast<int>(threadIdx.x) / kWave; }
+// uniform across the wave; read from one lane so the compiler keeps what derives from it
+// (group indices, descriptors, loop bounds) in scalar registers
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+}
 
 // Value of lane (l ^ S) without going through LDS: DPP quad permutes for S = 1, 2, DPP row
 // shifts for S = 4, 8, and the gfx950 v_permlane16_swap / v_permlane32_swap for S = 16, 32.
@@ -286,12 +290,23 @@ __device__ __forceinline__ void wave_partial_merge(Partial& p) {
 // offsets outside the range, so ragged tails need no branch around the load.
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr uint32_t kOutOfRange = 0x80000000u;   // above any range used here
+// base and bytes must be the same in every active lane of the wave (all descriptors here are
+// per wave, per workgroup or per call).  They are moved to scalar registers explicitly so the
+// compiler never wraps a load in a loop over distinct descriptors.
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
-                                           static_cast<int>(bytes), 0x00020000);
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
+  const uint64_t ua = (static_cast<uint64_t>(hi) << 32) | lo;
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(ua), static_cast<short>(0),
+                                           static_cast<int>(__builtin_amdgcn_readfirstlane(bytes)),
+                                           0x00020000);
 }
 __device__ __forceinline__ uint4 buffer_load16(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ uint32_t buffer_load4(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
 }
 
 // Branch-free 16-byte load: reads the clamped (always valid) address and returns zero when

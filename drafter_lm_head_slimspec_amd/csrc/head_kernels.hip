@@ -55,8 +55,17 @@ constexpr int kRowdotMaxCPL = 16;   // row bytes <= 16 KB
 template <bool BF16>
 __global__ __launch_bounds__(256) void k_rowdot(const void* __restrict__ Wd,
                                                 const void* __restrict__ x, int R, int C, int M,
-                                                void* __restrict__ out) {
+                                                void* __restrict__ out, uint32_t* __restrict__ zero,
+                                                int64_t zero_words) {
   extern __shared__ uint4 xs[];  // [kRowdotM][C]
+  if (zero != nullptr) {
+    // side job: clear a scratch block a later kernel of the same call accumulates into
+    const int64_t nwg = static_cast<int64_t>(gridDim.x) * gridDim.y;
+    const int64_t per = (zero_words + nwg - 1) / nwg;
+    const int64_t z0 = (static_cast<int64_t>(blockIdx.y) * gridDim.x + blockIdx.x) * per;
+    const int64_t z1 = z0 + per < zero_words ? z0 + per : zero_words;
+    for (int64_t i = z0 + threadIdx.x; i < z1; i += blockDim.x) zero[i] = 0u;
+  }
   const int m0 = blockIdx.y * kRowdotM;
   const int l = lane_id(), w = wave_id();
   const int j0 = blockIdx.x * kRowdotRows + w * 2;
@@ -321,15 +330,15 @@ __global__ __launch_bounds__(256) void k_stream_valu(StreamArgs a) {
       const int gnext = g + nwt;
       static_for<0, NRB>([&](auto rbc) {
         constexpr int rb = decltype(rbc)::value;
+        // one descriptor per prefetch, built from the already-selected group
+        const bool more = gnext < NG;
+        const int pg = rb + 1 < NRB ? g : (more ? gnext : g);
+        const int prb = rb + 1 < NRB ? rb + 1 : (more ? 0 : rb);
         if constexpr (rb % 2 == 0) {
-          if (rb + 1 < NRB) load_rb(g, rb + 1, bufB);
-          else if (gnext < NG) load_rb(gnext, 0, bufB);
-          else load_rb(g, rb, bufB);
+          load_rb(pg, prb, bufB);
           consume(bufA, g, rb, rbc);
         } else {
-          if (rb + 1 < NRB) load_rb(g, rb + 1, bufA);
-          else if (gnext < NG) load_rb(gnext, 0, bufA);
-          else load_rb(g, rb, bufA);
+          load_rb(pg, prb, bufA);
           consume(bufB, g, rb, rbc);
         }
       });
@@ -988,7 +997,7 @@ static hipError_t allow_lds(F kernel, int bytes) {
 }
 
 hipError_t launch_rowdot(const void* Wd, const void* x, int64_t R, int64_t K, int64_t M, bool bf16,
-                         void* out, hipStream_t st) {
+                         void* out, hipStream_t st, uint32_t* zero, int64_t zero_words) {
   const int C = static_cast<int>(K * (bf16 ? 2 : 4) / 16);
   const dim3 grid(static_cast<unsigned>((R + kRowdotRows - 1) / kRowdotRows),
                   static_cast<unsigned>((M + kRowdotM - 1) / kRowdotM));
@@ -999,12 +1008,12 @@ hipError_t launch_rowdot(const void* Wd, const void* x, int64_t R, int64_t K, in
     e = allow_lds(k_rowdot<true>, lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_rowdot<true>, grid, dim3(256), lds, st, Wd, x, static_cast<int>(R), C,
-                       static_cast<int>(M), out);
+                       static_cast<int>(M), out, zero, zero_words);
   } else {
     e = allow_lds(k_rowdot<false>, lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_rowdot<false>, grid, dim3(256), lds, st, Wd, x, static_cast<int>(R), C,
-                       static_cast<int>(M), out);
+                       static_cast<int>(M), out, zero, zero_words);
   }
   return hipGetLastError();
 }

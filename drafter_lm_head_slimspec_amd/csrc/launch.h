@@ -53,16 +53,35 @@ struct DeviceInfo {
 };
 hipError_t device_info(DeviceInfo* out);
 
-// h_out[m, j] = round_dtype(sum_k Wd[j, k] x[m, k]), j < R
+// h_out[m, j] = round_dtype(sum_k Wd[j, k] x[m, k]), j < R; also clears zero[0, zero_words)
 hipError_t launch_rowdot(const void* Wd, const void* x, int64_t R, int64_t K, int64_t M, bool bf16,
-                         void* out, hipStream_t st);
+                         void* out, hipStream_t st, uint32_t* zero = nullptr, int64_t zero_words = 0);
 // Chooses the VALU (skinny) or MFMA path; returns the number of producer workgroups.
 hipError_t launch_stream(const StreamArgs& a, bool use_mfma, int* producers, hipStream_t st);
 hipError_t launch_head_finalize(const FinalizeArgs& f, hipStream_t st);
 
 // SpecVocab pieces
-hipError_t launch_topk(const float* scores, int64_t M, int64_t V, int64_t k, int32_t* idx,
-                       hipStream_t st);
+// Top-k of [M, V] float scores.  hist and count (contiguous, topk_counter_words(M) words
+// from hist) must be zero when the top-k kernels start; cand and mask are scratch.
+struct TopkArgs {
+  const float* scores;  // [M, V]
+  int64_t V;
+  int k;
+  int M;
+  int chunks;           // topk_chunks(V) workgroups per row
+  uint32_t* hist;       // [M, 4096]
+  uint32_t* count;      // [M, kTkCounterStride] (one 128-byte line per row)
+  uint2* cand;          // [M, V]
+  uint64_t* mask;       // [M, ceil(V / 64)]
+  int32_t* out;         // [M, k] ascending ids
+};
+constexpr int64_t kTopkMaxV = int64_t{1} << 19;  // finishing bitmasks live in LDS
+int topk_chunks(int64_t V);
+constexpr int kTkCounterStride = 32;
+inline int64_t topk_counter_words(int64_t M) { return M * 4096 + M * kTkCounterStride; }
+hipError_t launch_zero(uint32_t* p, int64_t words, hipStream_t st);
+size_t topk_finish_lds(int64_t V);
+hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
 hipError_t launch_gather_exact(const void* U, const void* h, const int32_t* idx, int64_t M,
                                int64_t d, int64_t V, int64_t k, bool bf16, float* zbuf,
                                hipStream_t st);
@@ -84,10 +103,13 @@ struct VerifyArgs {
   uint64_t seed, offset;
   int32_t* accept_len;
   int32_t* out_tokens;
-  Partial* partials;   // [B, rows, S]
+  Partial* partials;   // [B, rows, S] row-segment partials
   int S;
+  Partial* partials2;  // [B, S2] residual-segment partials (sampling)
+  int S2;
 };
 int verify_segments(int64_t B, int64_t gamma, int64_t V, int mode);
+int verify_resid_segments(int64_t B, int64_t V, int mode);
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t st);
 
 hipError_t launch_philox(uint64_t seed, uint64_t offset, uint32_t purpose, int64_t rows, int64_t n,

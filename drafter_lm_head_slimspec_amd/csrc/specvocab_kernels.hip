@@ -1,6 +1,6 @@
 // SpecVocab dynamic-vocabulary pieces (SpecVocab write-up, sections 2.2.2, 2.2.3 and 2.3):
-//   k_topk            per-row exact radix select of the k largest approximate scores,
-//                     ties -> lowest id, compacted in ascending id order
+//   k_topk_*          exact top-k of the approximate scores (ties -> lowest id), as a
+//                     threshold search over order-preserving keys, ascending ids out
 //   k_gather_exact    z'_j = U[K_j, :] . h read straight from the gathered rows (no slice copy),
 //                     the hidden state held in registers
 //   k_gather_finalize softmax over the k candidates, argmax or two-level Gumbel draw
@@ -17,96 +17,322 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-constexpr int kTopkThreads = 1024;
-constexpr int kTopkWaves = kTopkThreads / kWave;
+// ----------------------------------------------------------------------------------------
+// Top-k as a threshold search over the order keys, spread over many workgroups per row:
+//   k_topk_hist    grid (chunks, M): histogram of the top 12 key bits of each 2048-score
+//                  chunk in LDS, added into the row histogram [M, 4096] in the workspace.
+//   k_topk_select  grid (chunks, M): every workgroup finds the threshold bin b* (the bin
+//                  where the count of larger keys reaches k) from the row histogram, marks
+//                  its chunk's keys above b* in the row's selection bitmask (one 64-bit word
+//                  per 64 scores) and appends the keys inside b* to the row's candidate list
+//                  (one counter update per workgroup).
+//   k_topk_finish  one workgroup per row: resolves the candidates on the remaining 20 key
+//                  bits (two 10-bit histogram passes), takes the lowest ids among keys equal
+//                  to the final threshold and compacts the bitmask into ascending ids.
+//   The histogram and the candidate counter are cleared by an earlier kernel of the call.
+//   Kernel boundaries order the phases: an in-kernel hand-off between workgroups would need
+//   a device-scope release per workgroup, which writes back the issuing XCD's L2.
+// ----------------------------------------------------------------------------------------
+constexpr int kTkBins = 4096;
+constexpr int kTkShift = 20;            // key >> 20 = top 12 bits
+constexpr int kTkThreads = 256;
+constexpr int kTkPerThread = 8;
+constexpr int kTkChunk = kTkThreads * kTkPerThread;
+constexpr int kTkWaves = kTkThreads / kWave;
 
-__global__ __launch_bounds__(kTopkThreads) void k_topk(const float* __restrict__ scores, int V, int k,
-                                                       int32_t* __restrict__ out) {
-  __shared__ uint32_t hist[kTopkWaves][256];
-  __shared__ uint32_t total[256];
-  __shared__ uint32_t sh_prefix, sh_mask, sh_rem;
-  __shared__ uint32_t wcnt[kTopkWaves], wcnt2[kTopkWaves];
-  const int m = blockIdx.x;
-  const float* s = scores + static_cast<size_t>(m) * V;
-  const int tid = threadIdx.x, l = lane_id(), w = wave_id();
-  uint32_t prefix = 0u, mask = 0u, rem = static_cast<uint32_t>(k);
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    for (int i = tid; i < kTopkWaves * 256; i += kTopkThreads) (&hist[0][0])[i] = 0u;
-    __syncthreads();
-    for (int i = tid; i < V; i += kTopkThreads) {
-      const uint32_t key = order_key(s[i]);
-      if ((key & mask) == prefix) atomicAdd(&hist[w][(key >> shift) & 255u], 1u);
-    }
-    __syncthreads();
-    if (tid < 256) {
-      uint32_t c = 0;
-      for (int ww = 0; ww < kTopkWaves; ++ww) c += hist[ww][tid];
-      total[tid] = c;
-    }
-    __syncthreads();
-    if (tid == 0) {
-      uint32_t cum = 0;
-      int d = 255;
-      for (; d > 0; --d) {
-        if (cum + total[d] >= rem) break;
-        cum += total[d];
-      }
-      rem -= cum;
-      prefix |= static_cast<uint32_t>(d) << shift;
-      mask |= 255u << shift;
-      sh_prefix = prefix;
-      sh_mask = mask;
-      sh_rem = rem;
-    }
-    __syncthreads();
-    prefix = sh_prefix;
-    mask = sh_mask;
-    rem = sh_rem;
+__global__ __launch_bounds__(kTkThreads) void k_topk_hist(TopkArgs a) {
+  __shared__ uint32_t h[kTkBins];
+  const int m = blockIdx.y;
+  const int64_t c0 = static_cast<int64_t>(blockIdx.x) * kTkChunk;
+  const int tid = threadIdx.x;
+  const rsrc_t rs = make_rsrc(a.scores + static_cast<size_t>(m) * a.V, static_cast<uint32_t>(a.V) * 4u);
+  uint32_t raw[kTkPerThread];
+#pragma unroll
+  for (int j = 0; j < kTkPerThread; ++j) {
+    const int64_t e = c0 + j * kTkThreads + tid;
+    raw[j] = buffer_load4(rs, e < a.V ? static_cast<uint32_t>(e) * 4u : kOutOfRange);
   }
-  // threshold key T = prefix; take every key > T and the first `rem` keys == T (by index)
-  const uint32_t T = prefix, need = rem;
-  const uint64_t lt = (l == 0) ? 0ull : ((~0ull) >> (64 - l));
-  uint32_t base = 0, eq_before = 0;
-  for (int start = 0; start < V; start += kTopkThreads) {
-    const int i = start + tid;
-    const bool in = i < V;
-    const uint32_t key = in ? order_key(s[i]) : 0u;
-    const bool gt = in && key > T;
-    const bool eq = in && key == T;
-    const uint64_t be = __ballot(eq);
-    if (l == 0) wcnt[w] = static_cast<uint32_t>(__popcll(be));
-    __syncthreads();
-    uint32_t eq_wave = 0, eq_total = 0;
-    for (int ww = 0; ww < kTopkWaves; ++ww) {
-      if (ww < w) eq_wave += wcnt[ww];
-      eq_total += wcnt[ww];
-    }
-    const uint32_t eq_rank = eq_before + eq_wave + static_cast<uint32_t>(__popcll(be & lt));
-    const bool sel = gt || (eq && eq_rank < need);
-    const uint64_t bsel = __ballot(sel);
-    if (l == 0) wcnt2[w] = static_cast<uint32_t>(__popcll(bsel));
-    __syncthreads();
-    uint32_t sel_wave = 0, sel_total = 0;
-    for (int ww = 0; ww < kTopkWaves; ++ww) {
-      if (ww < w) sel_wave += wcnt2[ww];
-      sel_total += wcnt2[ww];
-    }
-    if (sel) {
-      const uint32_t pos = base + sel_wave + static_cast<uint32_t>(__popcll(bsel & lt));
-      if (pos < static_cast<uint32_t>(k)) out[static_cast<size_t>(m) * k + pos] = i;
-    }
-    base += sel_total;
-    eq_before += eq_total;
-    __syncthreads();
+  for (int i = tid; i < kTkBins; i += kTkThreads) h[i] = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kTkPerThread; ++j) {
+    const int64_t e = c0 + j * kTkThreads + tid;
+    if (e < a.V) atomicAdd(&h[order_key(__uint_as_float(raw[j])) >> kTkShift], 1u);
+  }
+  __syncthreads();
+  uint32_t* hg = a.hist + static_cast<size_t>(m) * kTkBins;
+  for (int i = tid; i < kTkBins; i += kTkThreads) {
+    const uint32_t c = h[i];
+    if (c != 0u) atomicAdd(&hg[i], c);
   }
 }
 
-hipError_t launch_topk(const float* scores, int64_t M, int64_t V, int64_t k, int32_t* idx,
-                       hipStream_t st) {
-  TraceScope ts("topk", st);
-  hipLaunchKernelGGL(k_topk, dim3(static_cast<unsigned>(M)), dim3(kTopkThreads), 0, st, scores,
-                     static_cast<int>(V), static_cast<int>(k), idx);
+// Exclusive prefix sum over the threads of the workgroup (thread order); also the total.
+__device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wsum, uint32_t* total) {
+  const int l = lane_id(), w = wave_id(), nw = blockDim.x / kWave;
+  uint32_t x = v;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const uint32_t y = __shfl_up(x, d);
+    if (l >= d) x += y;
+  }
+  if (l == kWave - 1) wsum[w] = x;
+  __syncthreads();
+  uint32_t before = 0u, all = 0u;
+  for (int i = 0; i < nw; ++i) {
+    const uint32_t t = wsum[i];
+    if (i < w) before += t;
+    all += t;
+  }
+  __syncthreads();
+  *total = all;
+  return before + x - v;
+}
+
+// Bins [N*tid, N*tid + N) of a histogram are in c[]; find the bin b where the count of
+// larger bins is below `target` and the count including b reaches it.  The thread owning b
+// writes b and the count above it to out[0], out[1].
+template <int N>
+__device__ void find_crossing(const uint32_t (&c)[N], uint32_t target, uint32_t* wsum, uint32_t* out) {
+  uint32_t mine = 0u;
+#pragma unroll
+  for (int i = 0; i < N; ++i) mine += c[i];
+  uint32_t total;
+  const uint32_t before = block_exclusive_scan(mine, wsum, &total);
+  uint32_t cum = total - before - mine;  // count in bins above this thread's range
+#pragma unroll
+  for (int i = N - 1; i >= 0; --i) {
+    if (cum < target && cum + c[i] >= target) {
+      out[0] = static_cast<uint32_t>(N * threadIdx.x + i);
+      out[1] = cum;
+    }
+    cum += c[i];
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(kTkThreads) void k_topk_select(TopkArgs a) {
+  __shared__ uint32_t wsum[kTkWaves];
+  __shared__ uint32_t wcnt[kTkWaves];
+  __shared__ uint32_t res[2];
+  __shared__ uint32_t wbase;
+  const int m = blockIdx.y;
+  const int tid = threadIdx.x, l = lane_id(), w = wave_id();
+  const int64_t V = a.V;
+  const uint32_t k = static_cast<uint32_t>(a.k);
+  const int64_t c0 = static_cast<int64_t>(blockIdx.x) * kTkChunk;
+  const rsrc_t rs = make_rsrc(a.scores + static_cast<size_t>(m) * V, static_cast<uint32_t>(V) * 4u);
+  // the chunk's scores: wave w takes 64-score segments w, w + 4, ... (issued first)
+  uint32_t raw[kTkPerThread];
+#pragma unroll
+  for (int j = 0; j < kTkPerThread; ++j) {
+    const int64_t e = c0 + static_cast<int64_t>(w + kTkWaves * j) * kWave + l;
+    raw[j] = buffer_load4(rs, e < V ? static_cast<uint32_t>(e) * 4u : kOutOfRange);
+  }
+  // 1. threshold bin from the row histogram (16 bins per thread)
+  {
+    const uint4* hg = reinterpret_cast<const uint4*>(a.hist + static_cast<size_t>(m) * kTkBins) + tid * 4;
+    uint32_t c[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint4 t = hg[q];
+      c[4 * q] = t.x;
+      c[4 * q + 1] = t.y;
+      c[4 * q + 2] = t.z;
+      c[4 * q + 3] = t.w;
+    }
+    find_crossing<16>(c, k, wsum, res);
+  }
+  const uint32_t bstar = res[0], above = res[1];
+  // 2. mark keys above b*, collect keys inside b*; one counter update per workgroup
+  const int64_t mw = (V + kWave - 1) / kWave;
+  uint64_t* mask = a.mask + static_cast<size_t>(m) * mw;
+  uint2* cand = a.cand + static_cast<size_t>(m) * V;
+  uint32_t* count = a.count + static_cast<size_t>(m) * kTkCounterStride;
+  uint64_t bcs[kTkPerThread];
+  uint32_t keys[kTkPerThread];
+  uint32_t mine = 0u;
+#pragma unroll
+  for (int j = 0; j < kTkPerThread; ++j) {
+    const int64_t sb = c0 + static_cast<int64_t>(w + kTkWaves * j) * kWave;
+    const int64_t e = sb + l;
+    keys[j] = order_key(__uint_as_float(raw[j]));
+    const uint32_t bin = keys[j] >> kTkShift;
+    const bool in = e < V;
+    const uint64_t bs = __ballot(in && bin > bstar);
+    bcs[j] = __ballot(in && bin == bstar);
+    if (l == 0 && sb < V) mask[sb / kWave] = bs;
+    mine += static_cast<uint32_t>(__popcll(bcs[j]));
+  }
+  if (l == 0) wcnt[w] = mine;
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t tot = 0u;
+    for (int i = 0; i < kTkWaves; ++i) tot += wcnt[i];
+    wbase = tot != 0u ? atomicAdd(count, tot) : 0u;
+  }
+  __syncthreads();
+  uint32_t base = wbase;
+  for (int i = 0; i < w; ++i) base += wcnt[i];
+#pragma unroll
+  for (int j = 0; j < kTkPerThread; ++j) {
+    const uint64_t bc = bcs[j];
+    const int64_t e = c0 + static_cast<int64_t>(w + kTkWaves * j) * kWave + l;
+    const uint32_t rank = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(bc >> 32),
+                                                    __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bc), 0u));
+    // base + rank < V whenever the counter started at zero; the guard keeps a corrupted
+    // counter from writing out of bounds
+    if (((bc >> l) & 1ull) && base + rank < static_cast<uint64_t>(V))
+      cand[base + rank] = make_uint2(keys[j], static_cast<uint32_t>(e));
+    base += static_cast<uint32_t>(__popcll(bc));
+  }
+}
+
+// One workgroup per row: resolve the threshold bin's candidates and compact the row.
+__global__ __launch_bounds__(kTkThreads) void k_topk_finish(TopkArgs a) {
+  extern __shared__ uint32_t fin[];  // sel[nw], tie[nw], hist[1024]
+  __shared__ uint32_t wsum[kTkWaves];
+  __shared__ uint32_t res[2];
+  const int m = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int64_t V = a.V;
+  const uint32_t k = static_cast<uint32_t>(a.k);
+  {
+    const uint4* hg = reinterpret_cast<const uint4*>(a.hist + static_cast<size_t>(m) * kTkBins) + tid * 4;
+    uint32_t c[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint4 t = hg[q];
+      c[4 * q] = t.x;
+      c[4 * q + 1] = t.y;
+      c[4 * q + 2] = t.z;
+      c[4 * q + 3] = t.w;
+    }
+    find_crossing<16>(c, k, wsum, res);
+  }
+  const uint32_t bstar = res[0], above = res[1];
+  const int64_t mw = (V + kWave - 1) / kWave;
+  const uint64_t* mask = a.mask + static_cast<size_t>(m) * mw;
+  const uint2* cand = a.cand + static_cast<size_t>(m) * V;
+  uint32_t C = a.count[static_cast<size_t>(m) * kTkCounterStride];
+  if (C > static_cast<uint64_t>(V)) C = static_cast<uint32_t>(V);
+  const int nw = static_cast<int>(2 * mw);  // 32-bit words of the bitmask
+  uint32_t* sel = fin;
+  uint32_t* tie = fin + nw;
+  uint32_t* h1 = fin + 2 * nw;
+  // 3a. two 10-bit passes over the candidates: key bits 19..10, then 9..0
+  uint32_t need = k - above;
+  uint32_t thr = bstar << kTkShift;
+  for (int pass = 0; pass < 2; ++pass) {
+    const int shift = pass == 0 ? 10 : 0;
+    for (int i = tid; i < 1024; i += kTkThreads) h1[i] = 0u;
+    __syncthreads();
+    for (uint32_t i = tid; i < C; i += kTkThreads) {
+      const uint32_t key = cand[i].x;
+      if (pass == 0 || ((key >> 10) & 1023u) == ((thr >> 10) & 1023u)) atomicAdd(&h1[(key >> shift) & 1023u], 1u);
+    }
+    __syncthreads();
+    uint32_t c[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) c[q] = h1[4 * tid + q];
+    find_crossing<4>(c, need, wsum, res);
+    thr |= res[0] << shift;
+    need -= res[1];
+  }
+  // 3b. keys above the threshold are in; keys equal to it compete by id
+  const uint32_t* mw32 = reinterpret_cast<const uint32_t*>(mask);
+  for (int i = tid; i < nw; i += kTkThreads) {
+    sel[i] = mw32[i];
+    tie[i] = 0u;
+  }
+  __syncthreads();
+  for (uint32_t i = tid; i < C; i += kTkThreads) {
+    const uint2 ce = cand[i];
+    if (ce.y >= static_cast<uint64_t>(V)) continue;
+    if (ce.x > thr)
+      atomicOr(&sel[ce.y >> 5], 1u << (ce.y & 31u));
+    else if (ce.x == thr)
+      atomicOr(&tie[ce.y >> 5], 1u << (ce.y & 31u));
+  }
+  __syncthreads();
+  const int per = (nw + kTkThreads - 1) / kTkThreads;
+  const int w0 = tid * per < nw ? tid * per : nw;
+  const int w1 = w0 + per < nw ? w0 + per : nw;
+  {
+    uint32_t cnt = 0u, total;
+    for (int i = w0; i < w1; ++i) cnt += __popc(tie[i]);
+    uint32_t rank = block_exclusive_scan(cnt, wsum, &total);
+    for (int i = w0; i < w1 && rank < need; ++i) {
+      uint32_t bits = tie[i];
+      while (bits != 0u && rank < need) {
+        const uint32_t b = __builtin_ctz(bits);
+        sel[i] |= 1u << b;
+        bits &= bits - 1u;
+        ++rank;
+      }
+    }
+  }
+  __syncthreads();
+  // 3c. ascending ids
+  {
+    uint32_t cnt = 0u, total;
+    for (int i = w0; i < w1; ++i) cnt += __popc(sel[i]);
+    uint32_t pos = block_exclusive_scan(cnt, wsum, &total);
+    int32_t* out = a.out + static_cast<size_t>(m) * k;
+    for (int i = w0; i < w1; ++i) {
+      uint32_t bits = sel[i];
+      while (bits != 0u) {
+        const uint32_t b = __builtin_ctz(bits);
+        if (pos < k) out[pos] = static_cast<int32_t>(32 * i + b);
+        ++pos;
+        bits &= bits - 1u;
+      }
+    }
+  }
+}
+
+__global__ void k_zero(uint32_t* p, int64_t words) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < words;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+    p[i] = 0u;
+}
+
+hipError_t launch_zero(uint32_t* p, int64_t words, hipStream_t st) {
+  int64_t blocks = (words + 255) / 256;
+  if (blocks > 1024) blocks = 1024;
+  if (blocks < 1) blocks = 1;
+  TraceScope ts("zero", st);
+  hipLaunchKernelGGL(k_zero, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, p, words);
+  return hipGetLastError();
+}
+
+int topk_chunks(int64_t V) { return static_cast<int>((V + kTkChunk - 1) / kTkChunk); }
+
+size_t topk_finish_lds(int64_t V) {
+  const int64_t nw = 2 * ((V + kWave - 1) / kWave);
+  return static_cast<size_t>(2 * nw + 1024) * 4;
+}
+
+hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
+  const dim3 grid(static_cast<unsigned>(a.chunks), static_cast<unsigned>(a.M));
+  {
+    TraceScope ts("topk_hist", st);
+    hipLaunchKernelGGL(k_topk_hist, grid, dim3(kTkThreads), 0, st, a);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  {
+    TraceScope ts("topk_select", st);
+    hipLaunchKernelGGL(k_topk_select, grid, dim3(kTkThreads), 0, st, a);
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const size_t lds = topk_finish_lds(a.V);
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_topk_finish),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+  if (e != hipSuccess) return e;
+  TraceScope ts("topk_finish", st);
+  hipLaunchKernelGGL(k_topk_finish, dim3(static_cast<unsigned>(a.M)), dim3(kTkThreads), lds, st, a);
   return hipGetLastError();
 }
 

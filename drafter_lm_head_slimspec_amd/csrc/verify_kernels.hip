@@ -1,11 +1,15 @@
 // Batched speculative verification (explainer sections "小模型起草，大模型批改" and
 // "为什么答案不会变"; SpecTr-GBV write-up, "第三步").
-//   k_verify_rows      one pass over every target / draft logit row, split in S segments:
-//                      online log-sum-exp of y = z/T, argmax of z, and for the bonus row the
-//                      group-Gumbel scores of the two-level draw
-//   k_verify_finalize  one workgroup per sequence: acceptance (u < p/q or x == argmax),
-//                      leading-accept count, residual draw norm(max(0, p - q)) at the first
-//                      rejection or the bonus draw, output assembly
+//   k_verify_rows   one pass over every target / draft logit row, split in S segments:
+//                   online log-sum-exp of y = z/T, argmax of z, and for the bonus row the
+//                   group-Gumbel scores of the two-level draw
+//   k_verify_resid  (sampling) grid (S2 segments, B sequences): every workgroup merges its
+//                   sequence's row partials, decides acceptance (u < p/q) and the
+//                   leading-accept count a; at a rejection its segment of the residual
+//                   norm(max(0, p_a - q_a)) is folded into group scores
+//   k_verify_finish one workgroup per sequence: the same acceptance, then the last token
+//                   (greedy: argmax of p_a; sampling: the element draw inside the winning
+//                   residual group, or inside the bonus group of p_gamma) and the outputs
 #include "device_common.h"
 #include "launch.h"
 #include "trace.h"
@@ -76,226 +80,276 @@ __device__ __forceinline__ Partial block_merge(Partial p, Partial* red4) {
 
 template <bool BF16>
 __global__ __launch_bounds__(256) void k_verify_rows(VerifyArgs a) {
-  constexpr int EPT = BF16 ? 8 : 4;
-  constexpr int LPG = kGroup / EPT;
+  constexpr int EPT = BF16 ? 8 : 4;   // elements per 16-byte load
+  constexpr int LPG = kGroup / EPT;   // lanes per 64-element group
+  constexpr int UNR = 4;              // loads in flight per thread
+  constexpr size_t ES = BF16 ? 2 : 4;
   __shared__ Partial red4[4];
   const int s = blockIdx.x, r = blockIdx.y;
   const int64_t b = blockIdx.z;
   const int R = rows_per_seq(a.mode, a.gamma);
-  const void* row = row_ptr<BF16>(a, b, r);
+  const char* row = static_cast<const char*>(row_ptr<BF16>(a, b, r));
   const int64_t NG = (a.V + kGroup - 1) / kGroup;
   const int64_t GPS = (NG + a.S - 1) / a.S;
   const int64_t g0 = s * GPS;
   const int64_t g1 = min(NG, g0 + GPS);
   const int64_t e_begin = g0 * kGroup;
   const int64_t e_end = min(a.V, g1 * kGroup);
+  const int64_t n = e_end > e_begin ? e_end - e_begin : 0;
+  const rsrc_t rs = make_rsrc(row + static_cast<size_t>(e_begin) * ES, static_cast<uint32_t>(n * ES));
   const bool bonus = (a.mode == 1) && (r == a.gamma);
   const int l = lane_id();
   Partial p = partial_empty();
-  const int64_t span = static_cast<int64_t>(blockDim.x) * EPT;
-  const int64_t iters = e_end > e_begin ? (e_end - e_begin + span - 1) / span : 0;
-  for (int64_t it = 0; it < iters; ++it) {
-    const int64_t e0 = e_begin + it * span + static_cast<int64_t>(threadIdx.x) * EPT;
-    const bool in = e0 < e_end;
-    float v[EPT];
-    if (in) {
-      unpack<BF16>(load16(static_cast<const char*>(row) + static_cast<size_t>(e0) * (BF16 ? 2 : 4)), v);
-    }
-    float lmax = -INFINITY, lsum = 0.f;
-    if (in) {
+  const int64_t step = static_cast<int64_t>(blockDim.x) * EPT;
+  const int64_t span = step * UNR;
+  for (int64_t base = 0; base < n; base += span) {
+    uint4 raw[UNR];
 #pragma unroll
-      for (int i = 0; i < EPT; ++i) {
-        argmax_merge(p.zmax, p.zid, v[i], static_cast<int32_t>(e0 + i));
-        lmax = fmaxf(lmax, v[i] * a.invT);
+    for (int u = 0; u < UNR; ++u) {
+      const int64_t e = base + u * step + static_cast<int64_t>(threadIdx.x) * EPT;
+      raw[u] = buffer_load16(rs, e < n ? static_cast<uint32_t>(e * ES) : kOutOfRange);
+    }
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int64_t e = base + u * step + static_cast<int64_t>(threadIdx.x) * EPT;
+      const bool in = e < n;
+      const int64_t e0 = e_begin + e;
+      float v[EPT];
+      unpack<BF16>(raw[u], v);
+      float lmax = -INFINITY, lsum = 0.f;
+      if (in) {
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) {
+          if (e0 + i < e_end) {
+            argmax_merge(p.zmax, p.zid, v[i], static_cast<int32_t>(e0 + i));
+            lmax = fmaxf(lmax, v[i] * a.invT);
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < EPT; ++i)
+          if (e0 + i < e_end) lsum += __expf(v[i] * a.invT - lmax);
+        lse_merge(p.m, p.s, lmax, lsum);
       }
+      if (bonus) {
+        // one group = LPG consecutive lanes; (max, sum) inside the group
+        float gm = lmax;
 #pragma unroll
-      for (int i = 0; i < EPT; ++i) lsum += __expf(v[i] * a.invT - lmax);
-      lse_merge(p.m, p.s, lmax, lsum);
-    }
-    if (bonus) {
-      // group = LPG consecutive lanes; reduce (max, sum) inside the group
-      float gm = lmax;
+        for (int o = 1; o < LPG; o <<= 1) gm = fmaxf(gm, xor_lane(gm, o));
+        float gs = (in && gm != -INFINITY) ? lsum * __expf(lmax - gm) : 0.f;
 #pragma unroll
-      for (int o = 1; o < LPG; o <<= 1) gm = fmaxf(gm, xor_lane(gm, o));
-      float gs = (in && gm != -INFINITY) ? lsum * __expf(lmax - gm) : 0.f;
-#pragma unroll
-      for (int o = 1; o < LPG; o <<= 1) gs += xor_lane(gs, o);
-      if (in && (l % LPG) == 0) {
-        const int64_t gi = e0 / kGroup;
-        const float L = gm + logf(gs);
-        const float sc = L + gumbel(philox_uniform(a.seed, a.offset, kBonusGroup, b, gi));
-        argmax_merge(p.gscore, p.g, sc, static_cast<int32_t>(gi));
+        for (int o = 1; o < LPG; o <<= 1) gs += xor_lane(gs, o);
+        if (in && (l % LPG) == 0) {
+          const int64_t gi = e0 / kGroup;
+          const float L = gm + logf(gs);
+          const float sc = L + gumbel(philox_uniform(a.seed, a.offset, kBonusGroup, b, gi));
+          argmax_merge(p.gscore, p.g, sc, static_cast<int32_t>(gi));
+        }
       }
     }
   }
   Partial out = block_merge(p, red4);
-  if (threadIdx.x == 0) a.partials[(b * R + r) * a.S + s] = out;
+  if (threadIdx.x == 0) {
+    a.partials[(b * R + r) * a.S + s] = out;
+  }
 }
 
+// Element draw of a two-level Gumbel-max inside 64-element group g (wave 0): returns the
+// winning index, or 0x7fffffff if no element has finite weight.
+template <bool BF16, typename Ell>
+__device__ __forceinline__ int32_t draw_in_group(int32_t g, int64_t V, uint64_t seed, uint64_t offset,
+                                                 uint32_t purpose, int64_t row, Ell ell_of) {
+  const int l = lane_id();
+  const int64_t i = static_cast<int64_t>(g) * kGroup + l;
+  const bool valid = g != 0x7fffffff && i < V;
+  const float ell = valid ? ell_of(i) : -INFINITY;
+  float e = ell != -INFINITY ? ell + gumbel(philox_uniform(seed, offset, purpose, row, i)) : -INFINITY;
+  int32_t ei = ell != -INFINITY ? static_cast<int32_t>(i) : 0x7fffffff;
+  wave_argmax(e, ei);
+  return ei;
+}
+
+// Merges the row partials of sequence b into rowp (lane i of a wave loads segment partial i,
+// S <= 64, merged by a fixed butterfly: every kernel that calls this computes the same
+// values) and returns the leading-accept count (acceptance of all positions at once, lane t).
 template <bool BF16>
-__global__ __launch_bounds__(256) void k_verify_finalize(VerifyArgs a) {
-  constexpr int EPT = BF16 ? 8 : 4;
-  constexpr int LPG = kGroup / EPT;
-  constexpr int kMaxRows = 2 * 64 + 1;
-  __shared__ Partial rowp[kMaxRows];
-  __shared__ Partial red4[4];
-  __shared__ int sh_a;
-  __shared__ int32_t sh_tok;
-  const int64_t b = blockIdx.x;
+__device__ int seq_accept(const VerifyArgs& a, int64_t b, Partial* rowp, int* sh_a) {
   const int l = lane_id(), w = wave_id();
   const int R = rows_per_seq(a.mode, a.gamma);
   const int gamma = static_cast<int>(a.gamma);
-  // 1. per-row totals from the segment partials (fixed order)
   for (int r = w; r < R; r += blockDim.x / kWave) {
-    if (l == 0) {
-      Partial p = a.partials[(b * R + r) * a.S];
-      for (int i = 1; i < a.S; ++i) partial_merge(p, a.partials[(b * R + r) * a.S + i]);
-      rowp[r] = p;
-    }
+    Partial p = l < a.S ? a.partials[(b * R + r) * a.S + l] : partial_empty();
+    wave_partial_merge(p);
+    if (l == 0) rowp[r] = p;
   }
   __syncthreads();
-  // 2. acceptance and leading-accept count
-  if (threadIdx.x == 0) {
-    int acc_len = gamma;
-    for (int t = 0; t < gamma; ++t) {
-      const int32_t x = a.tokens[b * a.gamma + t];
+  if (w == 0) {
+    bool acc = false;
+    if (l < gamma) {
+      const int32_t x = a.tokens[b * a.gamma + l];
       const bool valid = x >= 0 && x < a.V;
-      bool acc;
       if (a.mode == 0) {
-        acc = valid && x == rowp[t].zid;
-      } else if (!valid) {
-        acc = false;
-      } else {
-        const float yp = load_logit<BF16>(row_ptr<BF16>(a, b, t), x) * a.invT;
-        const float yq = load_logit<BF16>(row_ptr<BF16>(a, b, gamma + 1 + t), x) * a.invT;
-        const float lp = yp - (rowp[t].m + logf(rowp[t].s));
-        const float lq = yq - (rowp[gamma + 1 + t].m + logf(rowp[gamma + 1 + t].s));
-        const float ratio = expf(lp - lq);
-        acc = a.u[b * a.gamma + t] < ratio;
-      }
-      if (!acc) {
-        acc_len = t;
-        break;
+        acc = valid && x == rowp[l].zid;
+      } else if (valid) {
+        const float yp = load_logit<BF16>(row_ptr<BF16>(a, b, l), x) * a.invT;
+        const float yq = load_logit<BF16>(row_ptr<BF16>(a, b, gamma + 1 + l), x) * a.invT;
+        const float lp = yp - (rowp[l].m + logf(rowp[l].s));
+        const float lq = yq - (rowp[gamma + 1 + l].m + logf(rowp[gamma + 1 + l].s));
+        acc = a.u[b * a.gamma + l] < expf(lp - lq);
       }
     }
-    sh_a = acc_len;
+    const uint64_t rej = __ballot(!acc);   // lanes >= gamma count as rejections
+    const int first = rej == 0ull ? kWave : static_cast<int>(__builtin_ctzll(rej));
+    if (l == 0) *sh_a = first < gamma ? first : gamma;
   }
   __syncthreads();
-  const int acc_len = sh_a;
-  int32_t tok = 0;
+  return *sh_a;
+}
+
+constexpr int kMaxVerifyRows = 2 * 64 + 1;
+
+// Residual group scores of one vocabulary segment of the rejected position (sampling only).
+template <bool BF16>
+__global__ __launch_bounds__(256) void k_verify_resid(VerifyArgs a) {
+  constexpr int EPT = BF16 ? 8 : 4;
+  constexpr int LPG = kGroup / EPT;
+  constexpr size_t ES = BF16 ? 2 : 4;
+  __shared__ Partial rowp[kMaxVerifyRows];
+  __shared__ Partial red4[4];
+  __shared__ int sh_a;
+  const int s2 = blockIdx.x;
+  const int64_t b = blockIdx.y;
+  const int l = lane_id();
+  const int gamma = static_cast<int>(a.gamma);
+  const int acc_len = seq_accept<BF16>(a, b, rowp, &sh_a);
+  if (acc_len == gamma) return;   // bonus: drawn by the finish kernel from the row pass
+  const char* prow = static_cast<const char*>(row_ptr<BF16>(a, b, acc_len));
+  const char* qrow = static_cast<const char*>(row_ptr<BF16>(a, b, gamma + 1 + acc_len));
+  const float lse_p = rowp[acc_len].m + logf(rowp[acc_len].s);
+  const float lse_q = rowp[gamma + 1 + acc_len].m + logf(rowp[gamma + 1 + acc_len].s);
+  const bool resid = true;
+  // 3. residual group scores over this workgroup's segment: gscore/g for max(0, p - q),
+  //    zmax/zid for p itself (used only if the residual has no mass anywhere)
+  if (resid) {
+    const int64_t NG = (a.V + kGroup - 1) / kGroup;
+    const int64_t GPS = (NG + a.S2 - 1) / a.S2;
+    const int64_t e_begin = s2 * GPS * kGroup;
+    const int64_t e_end = min(a.V, (s2 + 1) * GPS * kGroup);
+    const int64_t n = e_end > e_begin ? e_end - e_begin : 0;
+    const rsrc_t rp = make_rsrc(prow + static_cast<size_t>(e_begin) * ES, static_cast<uint32_t>(n * ES));
+    const rsrc_t rq = make_rsrc(qrow + static_cast<size_t>(e_begin) * ES, static_cast<uint32_t>(n * ES));
+    Partial best = partial_empty();
+    const int64_t step = static_cast<int64_t>(blockDim.x) * EPT;
+    for (int64_t base = 0; base < n; base += 2 * step) {
+      uint4 rawp[2], rawq[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int64_t e = base + u * step + static_cast<int64_t>(threadIdx.x) * EPT;
+        rawp[u] = buffer_load16(rp, e < n ? static_cast<uint32_t>(e * ES) : kOutOfRange);
+        rawq[u] = buffer_load16(rq, e < n ? static_cast<uint32_t>(e * ES) : kOutOfRange);
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int64_t e = base + u * step + static_cast<int64_t>(threadIdx.x) * EPT;
+        const bool in = e < n;
+        const int64_t e0 = e_begin + e;
+        float vp[EPT], vq[EPT];
+        unpack<BF16>(rawp[u], vp);
+        unpack<BF16>(rawq[u], vq);
+        float rsum = 0.f, lmax = -INFINITY, lsum = 0.f;
+        if (in) {
+#pragma unroll
+          for (int i = 0; i < EPT; ++i)
+            if (e0 + i < e_end) {
+              rsum += fmaxf(expf(vp[i] * a.invT - lse_p) - expf(vq[i] * a.invT - lse_q), 0.f);
+              lmax = fmaxf(lmax, vp[i] * a.invT);
+            }
+#pragma unroll
+          for (int i = 0; i < EPT; ++i)
+            if (e0 + i < e_end) lsum += __expf(vp[i] * a.invT - lmax);
+        }
+        float gr = rsum, gm = lmax;
+#pragma unroll
+        for (int o = 1; o < LPG; o <<= 1) {
+          gr += xor_lane(gr, o);
+          gm = fmaxf(gm, xor_lane(gm, o));
+        }
+        float gs = (in && gm != -INFINITY) ? lsum * __expf(lmax - gm) : 0.f;
+#pragma unroll
+        for (int o = 1; o < LPG; o <<= 1) gs += xor_lane(gs, o);
+        if (in && (l % LPG) == 0) {
+          const int64_t gi = e0 / kGroup;
+          const float G = gumbel(philox_uniform(a.seed, a.offset, kResidGroup, b, gi));
+          if (gr > 0.f) argmax_merge(best.gscore, best.g, logf(gr) + G, static_cast<int32_t>(gi));
+          argmax_merge(best.zmax, best.zid, gm + logf(gs) + G, static_cast<int32_t>(gi));
+        }
+      }
+    }
+    best = block_merge(best, red4);
+    if (threadIdx.x == 0) a.partials2[b * a.S2 + s2] = best;
+  }
+}
+
+// One workgroup per sequence: the accepted prefix, the last token, the outputs.
+template <bool BF16>
+__global__ __launch_bounds__(256) void k_verify_finish(VerifyArgs a) {
+  __shared__ Partial rowp[kMaxVerifyRows];
+  __shared__ int sh_a;
+  const int64_t b = blockIdx.x;
+  const int l = lane_id(), w = wave_id();
+  const int gamma = static_cast<int>(a.gamma);
+  const int acc_len = seq_accept<BF16>(a, b, rowp, &sh_a);
+  if (w != 0) return;
+  const bool resid = a.mode == 1 && acc_len < gamma;
+  const char* prow = static_cast<const char*>(row_ptr<BF16>(a, b, acc_len));
+  const char* qrow = resid ? static_cast<const char*>(row_ptr<BF16>(a, b, gamma + 1 + acc_len)) : nullptr;
+  const float lse_p = rowp[acc_len].m + logf(rowp[acc_len].s);
+  const float lse_q = resid ? rowp[gamma + 1 + acc_len].m + logf(rowp[gamma + 1 + acc_len].s) : 0.f;
+  int32_t tok;
   if (a.mode == 0) {
     tok = rowp[acc_len].zid;
-  } else if (acc_len == gamma) {
-    // bonus: draw inside the winning group of p_gamma
-    if (w == 0) {
-      const void* row = row_ptr<BF16>(a, b, gamma);
-      const int64_t i = static_cast<int64_t>(rowp[gamma].g) * kGroup + l;
-      const bool valid = i < a.V;
-      float e = valid ? load_logit<BF16>(row, i) * a.invT +
-                            gumbel(philox_uniform(a.seed, a.offset, kBonusElem, b, i))
-                      : -INFINITY;
-      int32_t ei = valid ? static_cast<int32_t>(i) : 0x7fffffff;
-      wave_argmax(e, ei);
-      if (l == 0) sh_tok = ei;
-    }
-    __syncthreads();
-    tok = sh_tok;
+  } else if (!resid) {
+    tok = draw_in_group<BF16>(rowp[gamma].g, a.V, a.seed, a.offset, kBonusElem, b,
+                              [&](int64_t i) { return load_logit<BF16>(prow, i) * a.invT; });
   } else {
-    // residual norm(max(0, p_a - q_a)) at the rejected position
-    const void* prow = row_ptr<BF16>(a, b, acc_len);
-    const void* qrow = row_ptr<BF16>(a, b, gamma + 1 + acc_len);
-    const float lse_p = rowp[acc_len].m + logf(rowp[acc_len].s);
-    const float lse_q = rowp[gamma + 1 + acc_len].m + logf(rowp[gamma + 1 + acc_len].s);
-    const int64_t span = static_cast<int64_t>(blockDim.x) * EPT;
-    const int64_t iters = (a.V + span - 1) / span;
-    Partial best = partial_empty();
-    bool fallback = false;
-    for (int pass = 0; pass < 2; ++pass) {   // pass 1 only if the residual mass is zero
-      fallback = pass == 1;
-      best = partial_empty();
-      for (int64_t it = 0; it < iters; ++it) {
-        const int64_t e0 = it * span + static_cast<int64_t>(threadIdx.x) * EPT;
-        const bool in = e0 < a.V;
-        float vp[EPT], vq[EPT];
-        float lsum = 0.f, lmax = -INFINITY;
-        if (in) {
-          unpack<BF16>(load16(static_cast<const char*>(prow) + static_cast<size_t>(e0) * (BF16 ? 2 : 4)), vp);
-          if (!fallback) {
-            unpack<BF16>(load16(static_cast<const char*>(qrow) + static_cast<size_t>(e0) * (BF16 ? 2 : 4)), vq);
-#pragma unroll
-            for (int i = 0; i < EPT; ++i)
-              lsum += fmaxf(expf(vp[i] * a.invT - lse_p) - expf(vq[i] * a.invT - lse_q), 0.f);
-          } else {
-#pragma unroll
-            for (int i = 0; i < EPT; ++i) lmax = fmaxf(lmax, vp[i] * a.invT);
-#pragma unroll
-            for (int i = 0; i < EPT; ++i) lsum += __expf(vp[i] * a.invT - lmax);
-          }
-        }
-        float L;
-        if (!fallback) {
-          float gs = lsum;
-#pragma unroll
-          for (int o = 1; o < LPG; o <<= 1) gs += xor_lane(gs, o);
-          L = gs > 0.f ? logf(gs) : -INFINITY;
-        } else {
-          float gm = lmax;
-#pragma unroll
-          for (int o = 1; o < LPG; o <<= 1) gm = fmaxf(gm, xor_lane(gm, o));
-          float gs = (in && gm != -INFINITY) ? lsum * __expf(lmax - gm) : 0.f;
-#pragma unroll
-          for (int o = 1; o < LPG; o <<= 1) gs += xor_lane(gs, o);
-          L = gm + logf(gs);
-        }
-        if (in && (l % LPG) == 0 && L != -INFINITY) {
-          const int64_t gi = e0 / kGroup;
-          const float sc = L + gumbel(philox_uniform(a.seed, a.offset, kResidGroup, b, gi));
-          argmax_merge(best.gscore, best.g, sc, static_cast<int32_t>(gi));
-        }
-      }
-      best = block_merge(best, red4);
-      if (best.gscore != -INFINITY) break;
-    }
-    if (w == 0) {
-      // element draw inside the winning group; same arithmetic as the group pass
-      const int64_t i = static_cast<int64_t>(best.g) * kGroup + l;
-      const bool valid = best.g != 0x7fffffff && i < a.V;
-      float ell = -INFINITY;
-      if (valid) {
-        const float yp = load_logit<BF16>(prow, i) * a.invT;
-        if (fallback) {
-          ell = yp;
-        } else {
-          const float yq = load_logit<BF16>(qrow, i) * a.invT;
-          const float rr = fmaxf(expf(yp - lse_p) - expf(yq - lse_q), 0.f);
-          ell = rr > 0.f ? logf(rr) : -INFINITY;
-        }
-      }
-      float e = ell != -INFINITY ? ell + gumbel(philox_uniform(a.seed, a.offset, kResidElem, b, i)) : -INFINITY;
-      int32_t ei = (valid && ell != -INFINITY) ? static_cast<int32_t>(i) : 0x7fffffff;
-      wave_argmax(e, ei);
-      if (l == 0) sh_tok = ei;
-    }
-    __syncthreads();
-    tok = sh_tok;
-  }
-  if (threadIdx.x == 0) {
-    a.accept_len[b] = acc_len;
-    for (int t = 0; t <= gamma; ++t) {
-      int32_t o = -1;
-      if (t < acc_len)
-        o = a.tokens[b * a.gamma + t];
-      else if (t == acc_len)
-        o = tok;
-      a.out_tokens[b * (a.gamma + 1) + t] = o;
+    Partial best = l < a.S2 ? a.partials2[b * a.S2 + l] : partial_empty();
+    wave_partial_merge(best);   // argmax merges: exact in any order
+    if (best.gscore != -INFINITY) {
+      tok = draw_in_group<BF16>(best.g, a.V, a.seed, a.offset, kResidElem, b, [&](int64_t i) {
+        const float rr = fmaxf(expf(load_logit<BF16>(prow, i) * a.invT - lse_p) -
+                                   expf(load_logit<BF16>(qrow, i) * a.invT - lse_q),
+                               0.f);
+        return rr > 0.f ? logf(rr) : -INFINITY;
+      });
+    } else {
+      tok = draw_in_group<BF16>(best.zid, a.V, a.seed, a.offset, kResidElem, b,
+                                [&](int64_t i) { return load_logit<BF16>(prow, i) * a.invT; });
     }
   }
+  for (int t = l; t <= gamma; t += kWave) {
+    int32_t o = -1;
+    if (t < acc_len)
+      o = a.tokens[b * a.gamma + t];
+    else if (t == acc_len)
+      o = tok;
+    a.out_tokens[b * (a.gamma + 1) + t] = o;
+  }
+  if (l == 0) a.accept_len[b] = acc_len;
 }
 
 int verify_segments(int64_t B, int64_t gamma, int64_t V, int mode) {
   const int64_t R = mode == 0 ? gamma + 1 : 2 * gamma + 1;
   const int64_t NG = (V + kGroup - 1) / kGroup;
   int64_t S = (2048 + B * R - 1) / (B * R);
+  if (S > 64) S = 64;
+  if (S > NG) S = NG;
+  if (S < 1) S = 1;
+  return static_cast<int>(S);
+}
+
+int verify_resid_segments(int64_t B, int64_t V, int mode) {
+  if (mode == 0) return 1;
+  const int64_t NG = (V + kGroup - 1) / kGroup;
+  int64_t S = (1024 + B - 1) / B;
   if (S > 64) S = 64;
   if (S > NG) S = NG;
   if (S < 1) S = 1;
@@ -315,11 +369,21 @@ hipError_t launch_verify(const VerifyArgs& a, hipStream_t st) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  TraceScope ts("verify_finalize", st);
+  if (a.mode == 1) {
+    const dim3 grid2(static_cast<unsigned>(a.S2), static_cast<unsigned>(a.B));
+    TraceScope ts("verify_resid", st);
+    if (a.bf16)
+      hipLaunchKernelGGL(k_verify_resid<true>, grid2, dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL(k_verify_resid<false>, grid2, dim3(256), 0, st, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  TraceScope ts("verify_finish", st);
   if (a.bf16)
-    hipLaunchKernelGGL(k_verify_finalize<true>, dim3(static_cast<unsigned>(a.B)), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(k_verify_finish<true>, dim3(static_cast<unsigned>(a.B)), dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL(k_verify_finalize<false>, dim3(static_cast<unsigned>(a.B)), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(k_verify_finish<false>, dim3(static_cast<unsigned>(a.B)), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -108,9 +108,9 @@ def _mode(mode):
 _ws_cache = {}
 
 
-def workspace(nbytes, device):
-    """Zero-filled device workspace of at least nbytes, cached per (device, stream)."""
-    key = (torch.device(device).index, torch.cuda.current_stream(device).cuda_stream)
+def workspace(nbytes, device, kind="head"):
+    """Device workspace of at least nbytes, cached per (device, stream, kind)."""
+    key = (torch.device(device).index, torch.cuda.current_stream(device).cuda_stream, kind)
     buf = _ws_cache.get(key)
     if buf is None or buf.numel() < nbytes:
         buf = torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
@@ -178,7 +178,7 @@ def draft_head_specvocab(h, W_down, W_vocab, U, k, mode="greedy", temperature=1.
     lse = torch.empty(M, dtype=torch.float32, device=dev) if want_lse else None
     logprob = torch.empty(M, dtype=torch.float32, device=dev) if want_lse else None
     need = lib.sh_head_workspace_bytes(OP_SPECVOCAB, M, d, dprime, V, k)
-    ws = workspace(need, dev)
+    ws = workspace(need, dev, "specvocab")
     _check(lib.draft_head_specvocab(_p(h), M, d, _p(W_down), dprime, _p(W_vocab), _p(U), V, int(k),
                                     _dt(h), _mode(mode), float(temperature), int(seed), int(offset),
                                     _p(idx), _p(zl), _p(q), _p(token), _p(lse), _p(logprob), _p(ws),
@@ -201,7 +201,7 @@ def spec_verify(target, draft, tokens, u=None, mode="sample", temperature=1.0, s
     acc = torch.empty(B, dtype=torch.int32, device=dev)
     out = torch.empty(B, gamma + 1, dtype=torch.int32, device=dev)
     need = lib.sh_verify_workspace_bytes(m, B, gamma, V)
-    ws = workspace(need, dev)
+    ws = workspace(need, dev, "verify")
     _check(lib.spec_verify(m, B, gamma, V, _dt(target), _p(target), _p(draft) if m == SAMPLE else None,
                            _p(tokens), _p(u) if m == SAMPLE else None, float(temperature), int(seed),
                            int(offset), _p(acc), _p(out), _p(ws), ws.numel(), _stream(dev)))
@@ -217,7 +217,7 @@ def topk(scores, k):
     dev = scores.device
     idx = torch.empty(M, k, dtype=torch.int32, device=dev)
     need = lib.sh_topk_workspace_bytes(M, V, k)
-    ws = workspace(need, dev)
+    ws = workspace(need, dev, "topk")
     _check(lib.sh_topk(_p(scores), M, V, int(k), _p(idx), _p(ws), ws.numel(), _stream(dev)))
     return idx
 

@@ -29,9 +29,8 @@
  *     HIP call: nothing was enqueued and no output was touched.  SH_ERR_HIP means a HIP
  *     runtime call or launch failed; sh_last_error() holds a thread-local message.
  *   - No allocation: the caller passes a workspace of at least sh_*_workspace_bytes(...)
- *     bytes.  It must be zero-filled before its first use (e.g. allocated with a zeroing
- *     allocator); every call leaves its counter area zero again.  Calls that may overlap
- *     in time must use distinct workspaces.
+ *     bytes; its contents on entry do not matter (each call clears what it counts into).
+ *     Calls that may overlap in time must use distinct workspaces.
  *   - Determinism: identical inputs, seed and offset give bit-identical outputs.
  *   - Sampling randomness: Philox4x64-10 (Salmon et al., SC'11) with key (seed, 0) and
  *     counter (index / 4, row, purpose, offset); the draw is output word index % 4 mapped to
@@ -113,7 +112,8 @@ int draft_head_lowrank(const void* h, int64_t M, int64_t d, const void* W_down, 
  *   W_down  [d', d]  reduced-state map, dtype;  h' = W_down h rounded once to dtype
  *   W_vocab [V, d']  approximate scorer, dtype;  s = W_vocab h' (float32)
  *   U       [V, d]   exact head, dtype; only the k gathered rows are read
- *   k       1 <= k <= min(V, 16384): K = the k largest s (ties -> lowest id), ascending ids
+ *   k       1 <= k <= min(V, 16384): K = the k largest s (ties -> lowest id), ascending ids;
+ *           V <= 2^19, M <= 65535
  *   topk_idx   [M, k] int32 (required)  K
  *   topk_logit [M, k] float (nullable)  z'_j = U[K_j,:] . h   (full-precision h)
  *   topk_prob  [M, k] float (nullable)  softmax(z' / T) over the k candidates
@@ -133,6 +133,7 @@ int draft_head_specvocab(const void* h, int64_t M, int64_t d, const void* W_down
  * SpecTr-GBV write-up: the first rejection ends the block, residual next token, bonus token).
  *   target_logits [B, gamma+1, V] dtype: target scores at the gamma+1 positions
  *   draft_logits  [B, gamma,   V] dtype: draft scores (SH_SAMPLE only; NULL for greedy)
+ *   B <= 65535, 1 <= gamma <= 64, V <= 2^28
  *   draft_tokens  [B, gamma] int32: proposed ids; an id outside [0, V) is never accepted
  *   u_accept      [B, gamma] float in (0,1): accept uniforms (SH_SAMPLE only; else NULL)
  *   temperature > 0: p = softmax(target / T), q = softmax(draft / T) (sampling)
@@ -143,6 +144,7 @@ int draft_head_specvocab(const void* h, int64_t M, int64_t d, const void* W_down
  *              mass is 0, from p_a), else from p_gamma (purposes 5/6, row b).
  *   accept_len [B] int32: a
  *   out_tokens [B, gamma+1] int32: emitted tokens, -1 after the last one
+ *   Workspace: sh_verify_workspace_bytes(mode, B, gamma, V).
  */
 int spec_verify(int mode, int64_t B, int64_t gamma, int64_t V, int dtype,
                 const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
@@ -154,7 +156,7 @@ int spec_verify(int mode, int64_t B, int64_t gamma, int64_t V, int dtype,
  * Top-k building block of draft_head_specvocab (SpecVocab write-up, section 2.2.2), exposed
  * so it can be checked on given scores: for each of M rows of float32 scores [M, V], the k
  * largest (ties -> lowest index), written as ascending ids to topk_idx [M, k].  Scores must
- * be finite.  Workspace: sh_topk_workspace_bytes(M, V, k).
+ * be finite; V <= 2^19.  Workspace: sh_topk_workspace_bytes(M, V, k).
  */
 size_t sh_topk_workspace_bytes(int64_t M, int64_t V, int64_t k);
 int sh_topk(const float* scores, int64_t M, int64_t V, int64_t k, int32_t* topk_idx,

@@ -97,3 +97,33 @@ def test_small_bf16_specvocab(M):
 def test_qwen_specvocab_full(M, mode):
     w = configs.QWEN
     _specvocab(w.d, w.V, w.dprime, w.k, M, w.dtype, mode, 1.0, seed=w.seeds["weights"])
+
+
+@pytest.mark.parametrize("V,k", [(5, 3), (64, 64), (2049, 100), (4097, 2048), (30000, 1)])
+def test_topk_edge_shapes(V, k):
+    """Shapes at the chunk and 64-score segment boundaries, a single score, k = V."""
+    M = 4
+    rng = np.random.default_rng(7 * V + k)
+    s = rng.standard_normal((M, V)).astype(np.float32)
+    s[1] = -np.abs(s[1]) * 1e30                    # negative only, large magnitudes
+    s[2] = 1.5                                     # every score equal: the lowest k ids
+    s[3, ::3] = s[3, 0]                            # a third of the row tied with one value
+    P.log(f"topk edge M={M} V={V} k={k}")
+    got = sh.topk(torch.from_numpy(s).cuda(), k).cpu().numpy()
+    for m in range(M):
+        np.testing.assert_array_equal(got[m], heads.topk_ascending(s[m].astype(np.float64), k))
+
+
+def test_topk_on_a_dirty_workspace_repeats():
+    """The workspace's contents on entry do not matter: calls on a workspace filled with
+    junk, and repeated calls on one workspace, give the same ids."""
+    M, V, k = 16, 151936, 2048
+    rng = np.random.default_rng(5)
+    s = torch.from_numpy(rng.standard_normal((M, V)).astype(np.float32)).cuda()
+    first = sh.topk(s, k)
+    ws = sh.workspace(sh.load().sh_topk_workspace_bytes(M, V, k), s.device, "topk")
+    ws.fill_(0xA5)
+    for _ in range(3):
+        assert torch.equal(sh.topk(s, k), first)
+    want = heads.topk_ascending(s[0].cpu().numpy().astype(np.float64), k)
+    np.testing.assert_array_equal(first[0].cpu().numpy(), want)

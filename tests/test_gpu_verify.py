@@ -34,11 +34,13 @@ def _greedy(B, gamma, V, sigma, dtype, seeds):
     P.log(f"  mean accepted {oa.mean():.3f}")
 
 
-def _sample(B, gamma, V, sigma, dtype, seeds, T=1.0, seed=99, offset=7, tokens=None):
+def _sample(B, gamma, V, sigma, dtype, seeds, T=1.0, seed=99, offset=7, tokens=None, mutate=None):
     P.log(f"verify sample B={B} gamma={gamma} V={V} sigma={sigma} {dtype} T={T}")
     inp = synth.verify_inputs(B, gamma, V, sigma, dtype, seeds, mode="sample", temperature=T)
     if tokens is not None:
         inp["tokens"] = tokens
+    if mutate is not None:
+        mutate(inp)
     d = _dev(inp, dtype)
     acc, out = sh.spec_verify(d["target"], d["draft"], d["tokens"], d["u"], mode="sample", temperature=T,
                               seed=seed, offset=offset)
@@ -63,6 +65,11 @@ def _sample(B, gamma, V, sigma, dtype, seeds, T=1.0, seed=99, offset=7, tokens=N
         if dg["kind"] == "bonus":
             ell = tl[gamma]
             gp, ep = philox.PURPOSE_BONUS_GROUP, philox.PURPOSE_BONUS_ELEM
+            tol_fn = lambda i, j: 0.0
+        elif not np.any(dg["p"] - dg["q"] > 0):
+            # no residual mass: the draw falls back to p at the rejected position
+            ell = tl[a]
+            gp, ep = philox.PURPOSE_RESID_GROUP, philox.PURPOSE_RESID_ELEM
             tol_fn = lambda i, j: 0.0
         else:
             p, q = dg["p"], dg["q"]
@@ -110,6 +117,34 @@ def test_invalid_draft_ids_are_rejected():
     tok[2, 2] = 1 << 30
     acc = _sample(B, gamma, V, 1.0, "f32", seeds, tokens=tok)
     assert acc[0] == 0 and acc[1] <= 1 and acc[2] <= 2
+
+
+def test_zero_residual_falls_back_to_target():
+    """Draft equal to target makes p - q vanish; a rejected (invalid) draft id then leaves no
+    residual mass and the token is drawn from p at that position."""
+    seeds = {"logits": 51, "tokens": 52, "uniforms": 53}
+    B, gamma, V = 6, 3, 1000
+
+    def same_draft(inp):
+        inp["draft"] = inp["target"][:, :gamma].copy()
+        for b in range(B):
+            inp["tokens"][b, b % gamma] = -5
+
+    acc = _sample(B, gamma, V, 1.0, "bf16", seeds, mutate=same_draft)
+    assert np.all(acc == np.arange(B) % gamma)
+
+
+def test_verify_on_a_dirty_workspace():
+    w = configs.VERIFY
+    B = 32
+    inp = synth.verify_inputs(B, w.gamma, w.V, 1.0, "bf16", w.seeds)
+    d = _dev(inp, "bf16")
+    a1, o1 = sh.spec_verify(d["target"], d["draft"], d["tokens"], d["u"], seed=5, offset=1)
+    need = sh.load().sh_verify_workspace_bytes(sh.SAMPLE, B, w.gamma, w.V)
+    sh.workspace(need, d["target"].device, "verify").fill_(0x5A)
+    a2, o2 = sh.spec_verify(d["target"], d["draft"], d["tokens"], d["u"], seed=5, offset=1)
+    torch.cuda.synchronize()
+    assert torch.equal(a1, a2) and torch.equal(o1, o2)
 
 
 @pytest.mark.parametrize("sigma", configs.VERIFY.sigmas)
