@@ -112,6 +112,7 @@ sh::TopkArgs topk_args(void* ws, const TopkLayout& L, const float* scores, int64
 
 struct HeadLayout {
   size_t tk_off, tk_bytes;   // SpecVocab: the top-k block, at offset 0
+  size_t rd_off, rd_bytes;   // fp32 split-K partials of the down-projection
   size_t hr_off, hr_bytes;
   size_t part_off, part_bytes;
   size_t lg_off, lg_bytes;
@@ -120,12 +121,15 @@ struct HeadLayout {
   size_t total;
 };
 
-HeadLayout head_layout(int op, int64_t M, int64_t r, int64_t V, int64_t k, int dtype) {
+HeadLayout head_layout(int op, int64_t M, int64_t d, int64_t r, int64_t V, int64_t k, int dtype) {
   HeadLayout L{};
   size_t off = 0;
   L.tk_off = off;
   L.tk_bytes = (op == SH_OP_SPECVOCAB) ? topk_layout(M, V).total : 0;
   off += L.tk_bytes;
+  L.rd_off = off;
+  L.rd_bytes = (op == SH_OP_DENSE) ? 0 : align_up(sh::rowdot_scratch_bytes(M, r, d), 256);
+  off += L.rd_bytes;
   L.hr_off = off;
   L.hr_bytes = (op == SH_OP_DENSE) ? 0 : align_up(static_cast<size_t>(M * r) * esize(dtype), 256);
   off += L.hr_bytes;
@@ -285,7 +289,7 @@ size_t sh_head_workspace_bytes(int op, int64_t M, int64_t d, int64_t r, int64_t 
   if (op == SH_OP_SPECVOCAB && (k < 1 || k > V)) return 0;
   if (op != SH_OP_DENSE && op != SH_OP_LOWRANK && op != SH_OP_SPECVOCAB) return 0;
   // sized for f32 intermediates so one workspace serves both dtypes
-  return head_layout(op, M, r, V, k, SH_F32).total;
+  return head_layout(op, M, d, r, V, k, SH_F32).total;
 }
 
 size_t sh_verify_workspace_bytes(int mode, int64_t B, int64_t gamma, int64_t V) {
@@ -306,7 +310,7 @@ int draft_head_dense(const void* h, int64_t M, int64_t d, const void* W, int64_t
   SH_TRY(check_common_head(h, M, d, V, dtype, mode, temperature, token, lse, logprob));
   SH_TRY(check_ptr(W, "W"));
   SH_TRY(check_opt_out(logits, "logits"));
-  const HeadLayout L = head_layout(SH_OP_DENSE, M, 0, V, 0, SH_F32);
+  const HeadLayout L = head_layout(SH_OP_DENSE, M, d, 0, V, 0, SH_F32);
   SH_TRY(check_workspace(workspace, workspace_bytes, L.total));
   hipStream_t st = static_cast<hipStream_t>(stream);
   auto* parts = reinterpret_cast<sh::Partial*>(static_cast<char*>(workspace) + L.part_off);
@@ -327,14 +331,15 @@ int draft_head_lowrank(const void* h, int64_t M, int64_t d, const void* W_down, 
   if (r * static_cast<int64_t>(esize(dtype)) > kMaxRowBytes)
     return fail(SH_ERR_UNSUPPORTED, "r * element size above %lld bytes", static_cast<long long>(kMaxRowBytes));
   SH_TRY(check_opt_out(logits, "logits"));
-  const HeadLayout L = head_layout(SH_OP_LOWRANK, M, r, V, 0, SH_F32);
+  const HeadLayout L = head_layout(SH_OP_LOWRANK, M, d, r, V, 0, SH_F32);
   SH_TRY(check_workspace(workspace, workspace_bytes, L.total));
   hipStream_t st = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   void* hr = ws + L.hr_off;
   auto* parts = reinterpret_cast<sh::Partial*>(ws + L.part_off);
   auto* lg = reinterpret_cast<float*>(ws + L.lg_off);
-  SH_HIP(sh::launch_rowdot(W_down, h, r, d, M, dtype == SH_BF16, hr, st), "down-projection kernel");
+  SH_HIP(sh::launch_rowdot(W_down, h, r, d, M, dtype == SH_BF16, hr, reinterpret_cast<float*>(ws + L.rd_off), st),
+         "down-projection kernels");
   return run_head(hr, M, r, W_up, V, dtype, mode, temperature, seed, offset, token, lse, logprob,
                   logits, parts, lg, st);
 }
@@ -360,7 +365,7 @@ int draft_head_specvocab(const void* h, int64_t M, int64_t d, const void* W_down
   SH_TRY(check_out(topk_idx, "topk_idx"));
   SH_TRY(check_opt_out(topk_logit, "topk_logit"));
   SH_TRY(check_opt_out(topk_prob, "topk_prob"));
-  const HeadLayout L = head_layout(SH_OP_SPECVOCAB, M, dprime, V, k, SH_F32);
+  const HeadLayout L = head_layout(SH_OP_SPECVOCAB, M, d, dprime, V, k, SH_F32);
   SH_TRY(check_workspace(workspace, workspace_bytes, L.total));
   hipStream_t st = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
@@ -369,9 +374,9 @@ int draft_head_specvocab(const void* h, int64_t M, int64_t d, const void* W_down
   float* zbuf = reinterpret_cast<float*>(ws + L.z_off);
   const bool bf16 = dtype == SH_BF16;
   const TopkLayout TL = topk_layout(M, V);
-  SH_HIP(sh::launch_rowdot(W_down, h, dprime, d, M, bf16, hp, st,
+  SH_HIP(sh::launch_rowdot(W_down, h, dprime, d, M, bf16, hp, reinterpret_cast<float*>(ws + L.rd_off), st,
                            reinterpret_cast<uint32_t*>(ws + L.tk_off + TL.hist_off), sh::topk_counter_words(M)),
-         "reduced-state kernel");
+         "reduced-state kernels");
   const bool mfma = bf16 && M > kValuMaxRows;
   const int64_t chunk = mfma ? kMfmaMaxRows : kValuMaxRows;
   for (int64_t m0 = 0; m0 < M; m0 += chunk) {

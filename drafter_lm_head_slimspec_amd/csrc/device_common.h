@@ -18,6 +18,12 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 
 constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// 2^x by the hardware instruction alone (no scaling for denormal results): used for sums of
+// exponentials of non-positive arguments, where a result below 2^-126 is negligible.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 constexpr int kGroup = 64;           // sampling group: 64 consecutive candidates
 constexpr int kMaxPartials = 2048;   // upper bound on producer workgroups per row
 

@@ -22,8 +22,6 @@
 
 namespace sh {
 
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
 
 // Copy `items` 16-byte words fetch(i) -> lds[i] with BATCH loads in flight per thread.
 // fetch(-1) must return a harmless (zero) value.
@@ -115,6 +113,97 @@ __global__ __launch_bounds__(256) void k_rowdot(const void* __restrict__ Wd,
         if (j0 + 1 < R) o[j0 + 1] = a1;
       }
     }
+  }
+}
+
+// ----------------------------------------------------------------------------------------
+// bf16 down-projection on MFMA, split over K:
+//   k_rowdot_mfma    grid (ceil(R/32), ksplit, row chunks): workgroup = 4 waves; each wave
+//                    multiplies a 32-row tile of Wd by up to 32*NCB input rows over
+//                    kRdKSW k-steps of 16 (v_mfma_f32_32x32x16_bf16, fragments straight from
+//                    global memory), the 4 waves' tiles are summed in LDS in a fixed order and
+//                    written as one fp32 partial [ksplit][M][R].
+//   k_rowdot_reduce  sums the ksplit partials of every output in a fixed order and rounds
+//                    once to bf16; also clears a scratch block for a later kernel.
+// ----------------------------------------------------------------------------------------
+constexpr int kRdKSW = 8;                     // k-steps per wave
+constexpr int kRdKWG = 4 * kRdKSW;            // k-steps per workgroup
+
+int rowdot_ksplit(int64_t K) { return static_cast<int>(((K + 15) / 16 + kRdKWG - 1) / kRdKWG); }
+
+template <int NCB>
+__global__ __launch_bounds__(256) void k_rowdot_mfma(const void* __restrict__ Wd, const void* __restrict__ x,
+                                                     int R, int K, int M, float* __restrict__ part) {
+  extern __shared__ float red[];   // [4 waves][NCB][16][64]
+  const int l = lane_id(), w = wave_id();
+  const int n = l & 31, hf = l >> 5;
+  const int j0 = blockIdx.x * 32;
+  const int m0 = blockIdx.z * 32 * NCB;
+  const int ksp = blockIdx.y;
+  const uint32_t rowbytes = static_cast<uint32_t>(K) * 2;
+  const int jrows = R - j0 < 32 ? R - j0 : 32;
+  const int mrows = M - m0 < 32 * NCB ? M - m0 : 32 * NCB;
+  const rsrc_t wrs = make_rsrc(static_cast<const char*>(Wd) + static_cast<size_t>(j0) * rowbytes,
+                               static_cast<uint32_t>(jrows) * rowbytes);
+  const rsrc_t xrs = make_rsrc(static_cast<const char*>(x) + static_cast<size_t>(m0) * rowbytes,
+                               static_cast<uint32_t>(mrows) * rowbytes);
+  const int ks0 = (ksp * 4 + w) * kRdKSW;
+  uint4 A[kRdKSW], B[kRdKSW][NCB];
+#pragma unroll
+  for (int t = 0; t < kRdKSW; ++t) {
+    const int k = (ks0 + t) * 16 + hf * 8;
+    const bool kok = k < K;
+    A[t] = buffer_load16(wrs, kok ? static_cast<uint32_t>(n) * rowbytes + static_cast<uint32_t>(k) * 2 : kOutOfRange);
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+      B[t][cb] = buffer_load16(xrs, kok ? static_cast<uint32_t>(cb * 32 + n) * rowbytes + static_cast<uint32_t>(k) * 2
+                                        : kOutOfRange);
+  }
+  f32x16_t acc[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[cb][v] = 0.f;
+#pragma unroll
+  for (int t = 0; t < kRdKSW; ++t)
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+      acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, A[t]),
+                                                        __builtin_bit_cast(bf16x8_t, B[t][cb]), acc[cb], 0, 0, 0);
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) red[((w * NCB + cb) * 16 + v) * kWave + l] = acc[cb][v];
+  __syncthreads();
+  // thread -> (cb, v, lane): sum the 4 waves in order
+  for (int e = threadIdx.x; e < NCB * 16 * kWave; e += blockDim.x) {
+    const int ll = e & (kWave - 1);
+    const int v = (e / kWave) & 15;
+    const int cb = e / (16 * kWave);
+    float sum = red[e];
+#pragma unroll
+    for (int ww = 1; ww < 4; ++ww) sum += red[ww * NCB * 16 * kWave + e];
+    const int j = j0 + 8 * (v >> 2) + 4 * (ll >> 5) + (v & 3);
+    const int m = m0 + cb * 32 + (ll & 31);
+    if (j < R && m < M) part[(static_cast<int64_t>(ksp) * M + m) * R + j] = sum;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_rowdot_reduce(const float* __restrict__ part, int ksplit, int64_t MR,
+                                                       uint16_t* __restrict__ out, uint32_t* __restrict__ zero,
+                                                       int64_t zero_words) {
+  const int64_t o = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (o < MR) {
+    float sum = part[o];
+    for (int i = 1; i < ksplit; ++i) sum += part[i * MR + o];
+    out[o] = f32_to_bf16_rne(sum);
+  }
+  if (zero != nullptr) {
+    const int64_t nwg = gridDim.x;
+    const int64_t per = (zero_words + nwg - 1) / nwg;
+    const int64_t z0 = static_cast<int64_t>(blockIdx.x) * per;
+    const int64_t z1 = z0 + per < zero_words ? z0 + per : zero_words;
+    for (int64_t i = z0 + threadIdx.x; i < z1; i += blockDim.x) zero[i] = 0u;
   }
 }
 
@@ -262,7 +351,7 @@ __global__ __launch_bounds__(256) void k_stream_valu(StreamArgs a) {
         float sm = 0.f;
         if (mx != -INFINITY) {
 #pragma unroll
-          for (int rb = 0; rb < NRB; ++rb) sm += exp2f((vals[rb][m] - mx) * c2);
+          for (int rb = 0; rb < NRB; ++rb) sm += fast_exp2((vals[rb][m] - mx) * c2);
         }
 #pragma unroll
         for (int s = DUP; s < kWave; s <<= 1) sm += xor_lane(sm, s);
@@ -499,14 +588,14 @@ __global__ __launch_bounds__(256, 2) void k_stream_mfma2(StreamArgs a) {
       if (a.lg != nullptr && zm != -INFINITY) {
         const float off = zm * c2;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) ss += exp2f(fmaf(acc0[cb][v], c2, -off)) + exp2f(fmaf(acc1[cb][v], c2, -off));
+        for (int v = 0; v < 16; ++v) ss += fast_exp2(fmaf(acc0[cb][v], c2, -off)) + fast_exp2(fmaf(acc1[cb][v], c2, -off));
       }
       // merge with the other 32 rows of the column (lane l ^ 32)
       const float zm2 = xor_lane(zm, 32), ss2 = xor_lane(ss, 32);
       const int32_t zi2 = xor_lane(zi, 32);
       const float gmx = fmaxf(zm, zm2);
       float gsm = 0.f;
-      if (gmx != -INFINITY) gsm = ss * exp2f((zm - gmx) * c2) + ss2 * exp2f((zm2 - gmx) * c2);
+      if (gmx != -INFINITY) gsm = ss * fast_exp2((zm - gmx) * c2) + ss2 * fast_exp2((zm2 - gmx) * c2);
       argmax_merge(zm, zi, zm2, zi2);
       if (m < a.M) {
         if (a.lg != nullptr && hf == 0) a.lg[static_cast<int64_t>(m) * a.lg_ld + g] = gmx * a.invT + log2f(gsm) * kLn2;
@@ -696,13 +785,13 @@ __global__ __launch_bounds__(256) void k_stream_mfma(StreamArgs a) {
       if (a.lg != nullptr && zm != -INFINITY) {
         const float off = zm * c2;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) ss += exp2f(fmaf(acc[cb][v], c2, -off));
+        for (int v = 0; v < 16; ++v) ss += fast_exp2(fmaf(acc[cb][v], c2, -off));
       }
       const float zm2 = xor_lane(zm, 32), ss2 = xor_lane(ss, 32);
       const int32_t zi2 = xor_lane(zi, 32);
       const float gmx = fmaxf(zm, zm2);
       float gsm = 0.f;
-      if (gmx != -INFINITY) gsm = ss * exp2f((zm - gmx) * c2) + ss2 * exp2f((zm2 - gmx) * c2);
+      if (gmx != -INFINITY) gsm = ss * fast_exp2((zm - gmx) * c2) + ss2 * fast_exp2((zm2 - gmx) * c2);
       argmax_merge(zm, zi, zm2, zi2);
       if (t == 0) {
         hm[cb] = gmx;
@@ -713,7 +802,7 @@ __global__ __launch_bounds__(256) void k_stream_mfma(StreamArgs a) {
       }
       const float tm = fmaxf(gmx, hm[cb]);
       float ts = 0.f;
-      if (tm != -INFINITY) ts = gsm * exp2f((gmx - tm) * c2) + hs[cb] * exp2f((hm[cb] - tm) * c2);
+      if (tm != -INFINITY) ts = gsm * fast_exp2((gmx - tm) * c2) + hs[cb] * fast_exp2((hm[cb] - tm) * c2);
       argmax_merge(zm, zi, hz[cb], hi[cb]);
       if (m < a.M) {
         if (a.lg != nullptr && hf == 0) a.lg[static_cast<int64_t>(m) * a.lg_ld + g] = tm * a.invT + log2f(ts) * kLn2;
@@ -996,25 +1085,55 @@ static hipError_t allow_lds(F kernel, int bytes) {
                              hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
 }
 
+template <int NCB>
+static hipError_t run_rowdot_mfma(const void* Wd, const void* x, int R, int K, int M, float* part, hipStream_t st) {
+  const dim3 grid(static_cast<unsigned>((R + 31) / 32), static_cast<unsigned>(rowdot_ksplit(K)),
+                  static_cast<unsigned>((M + 32 * NCB - 1) / (32 * NCB)));
+  const int lds = 4 * NCB * 16 * kWave * 4;
+  hipError_t e = allow_lds(k_rowdot_mfma<NCB>, lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_rowdot_mfma<NCB>, grid, dim3(256), lds, st, Wd, x, R, K, M, part);
+  return hipGetLastError();
+}
+
+size_t rowdot_scratch_bytes(int64_t M, int64_t R, int64_t K) {
+  return static_cast<size_t>(rowdot_ksplit(K)) * static_cast<size_t>(M * R) * 4;
+}
+
 hipError_t launch_rowdot(const void* Wd, const void* x, int64_t R, int64_t K, int64_t M, bool bf16,
-                         void* out, hipStream_t st, uint32_t* zero, int64_t zero_words) {
-  const int C = static_cast<int>(K * (bf16 ? 2 : 4) / 16);
+                         void* out, float* scratch, hipStream_t st, uint32_t* zero, int64_t zero_words) {
+  if (bf16) {
+    const int ncb = static_cast<int>((M + 31) / 32) < 6 ? static_cast<int>((M + 31) / 32) : 6;
+    hipError_t e;
+    {
+      TraceScope ts("rowdot", st);
+      switch (ncb) {
+        case 1: e = run_rowdot_mfma<1>(Wd, x, static_cast<int>(R), static_cast<int>(K), static_cast<int>(M), scratch, st); break;
+        case 2: e = run_rowdot_mfma<2>(Wd, x, static_cast<int>(R), static_cast<int>(K), static_cast<int>(M), scratch, st); break;
+        case 3: e = run_rowdot_mfma<3>(Wd, x, static_cast<int>(R), static_cast<int>(K), static_cast<int>(M), scratch, st); break;
+        case 4: e = run_rowdot_mfma<4>(Wd, x, static_cast<int>(R), static_cast<int>(K), static_cast<int>(M), scratch, st); break;
+        case 5: e = run_rowdot_mfma<5>(Wd, x, static_cast<int>(R), static_cast<int>(K), static_cast<int>(M), scratch, st); break;
+        default: e = run_rowdot_mfma<6>(Wd, x, static_cast<int>(R), static_cast<int>(K), static_cast<int>(M), scratch, st); break;
+      }
+    }
+    if (e != hipSuccess) return e;
+    const int64_t MR = M * R;
+    int64_t blocks = (MR + 255) / 256;
+    if (blocks < 1) blocks = 1;
+    TraceScope ts("rowdot_reduce", st);
+    hipLaunchKernelGGL(k_rowdot_reduce, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, scratch,
+                       rowdot_ksplit(K), MR, static_cast<uint16_t*>(out), zero, zero_words);
+    return hipGetLastError();
+  }
+  const int C = static_cast<int>(K * 4 / 16);
   const dim3 grid(static_cast<unsigned>((R + kRowdotRows - 1) / kRowdotRows),
                   static_cast<unsigned>((M + kRowdotM - 1) / kRowdotM));
   const int lds = kRowdotM * C * 16;
-  hipError_t e;
   TraceScope ts("rowdot", st);
-  if (bf16) {
-    e = allow_lds(k_rowdot<true>, lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_rowdot<true>, grid, dim3(256), lds, st, Wd, x, static_cast<int>(R), C,
-                       static_cast<int>(M), out, zero, zero_words);
-  } else {
-    e = allow_lds(k_rowdot<false>, lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_rowdot<false>, grid, dim3(256), lds, st, Wd, x, static_cast<int>(R), C,
-                       static_cast<int>(M), out, zero, zero_words);
-  }
+  hipError_t e = allow_lds(k_rowdot<false>, lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_rowdot<false>, grid, dim3(256), lds, st, Wd, x, static_cast<int>(R), C,
+                     static_cast<int>(M), out, zero, zero_words);
   return hipGetLastError();
 }
 

@@ -53,9 +53,12 @@ struct DeviceInfo {
 };
 hipError_t device_info(DeviceInfo* out);
 
-// h_out[m, j] = round_dtype(sum_k Wd[j, k] x[m, k]), j < R; also clears zero[0, zero_words)
+// h_out[m, j] = round_dtype(sum_k Wd[j, k] x[m, k]), j < R; also clears zero[0, zero_words).
+// bf16 runs split over K on MFMA and needs rowdot_scratch_bytes(M, R, K) of fp32 scratch.
+size_t rowdot_scratch_bytes(int64_t M, int64_t R, int64_t K);
 hipError_t launch_rowdot(const void* Wd, const void* x, int64_t R, int64_t K, int64_t M, bool bf16,
-                         void* out, hipStream_t st, uint32_t* zero = nullptr, int64_t zero_words = 0);
+                         void* out, float* scratch, hipStream_t st, uint32_t* zero = nullptr,
+                         int64_t zero_words = 0);
 // Chooses the VALU (skinny) or MFMA path; returns the number of producer workgroups.
 hipError_t launch_stream(const StreamArgs& a, bool use_mfma, int* producers, hipStream_t st);
 hipError_t launch_head_finalize(const FinalizeArgs& f, hipStream_t st);

@@ -1,12 +1,12 @@
 // Batched speculative verification (explainer sections "小模型起草，大模型批改" and
 // "为什么答案不会变"; SpecTr-GBV write-up, "第三步").
-//   k_verify_rows   one pass over every target / draft logit row, split in S segments:
-//                   online log-sum-exp of y = z/T, argmax of z, and for the bonus row the
-//                   group-Gumbel scores of the two-level draw
+//   k_verify_rows   one pass over the target / draft logit rows, split in S segments:
+//                   greedy: argmax of z; sampling: online log-sum-exp of y = z/T
 //   k_verify_resid  (sampling) grid (S2 segments, B sequences): every workgroup merges its
 //                   sequence's row partials, decides acceptance (u < p/q) and the
-//                   leading-accept count a; at a rejection its segment of the residual
-//                   norm(max(0, p_a - q_a)) is folded into group scores
+//                   leading-accept count a; its segment of the residual
+//                   norm(max(0, p_a - q_a)) (a < gamma) or of p_gamma (a = gamma, the bonus
+//                   draw) is folded into the group scores of the two-level draw
 //   k_verify_finish one workgroup per sequence: the same acceptance, then the last token
 //                   (greedy: argmax of p_a; sampling: the element draw inside the winning
 //                   residual group, or inside the bonus group of p_gamma) and the outputs
@@ -78,16 +78,46 @@ __device__ __forceinline__ Partial block_merge(Partial p, Partial* red4) {
   return r;
 }
 
-template <bool BF16>
+// Software-pipelined walk over [0, n) in spans of UNR chunks: the next span's loads are in
+// flight while the current one is processed (ping-pong buffers; past n the loads are
+// out-of-range, which costs no memory traffic, and proc sees chunks with e >= n).
+template <int UNR, typename Load, typename Proc>
+__device__ __forceinline__ void pipelined(uint32_t n, uint32_t span, Load load, Proc proc) {
+  uint4 A[UNR], B[UNR];
+  load(A, 0u);
+  for (uint32_t base = 0; base < n; base += 2 * span) {
+    load(B, base + span);
+    proc(A, base);
+    load(A, base + 2 * span);
+    proc(B, base + span);
+  }
+}
+
+// Max of the EPT values of one 16-byte chunk.
+template <int EPT>
+__device__ __forceinline__ float chunk_max(const float* v) {
+  float m = v[0];
+#pragma unroll
+  for (int i = 1; i < EPT; ++i) m = fmaxf(m, v[i]);
+  return m;
+}
+
+// Row pass.  The per-element work is kept to what the mode needs (VALU issue, not HBM, bounds
+// a naive version): greedy rows track only the largest chunk maximum and the chunk holding
+// it (the position inside that chunk is found once at the end); sampling rows keep only the
+// running log-sum-exp, in base-2 units.
+template <bool BF16, bool GREEDY>
 __global__ __launch_bounds__(256) void k_verify_rows(VerifyArgs a) {
   constexpr int EPT = BF16 ? 8 : 4;   // elements per 16-byte load
-  constexpr int LPG = kGroup / EPT;   // lanes per 64-element group
   constexpr int UNR = 4;              // loads in flight per thread
-  constexpr size_t ES = BF16 ? 2 : 4;
+  constexpr uint32_t ES = BF16 ? 2 : 4;
   __shared__ Partial red4[4];
   const int s = blockIdx.x, r = blockIdx.y;
   const int64_t b = blockIdx.z;
   const int R = rows_per_seq(a.mode, a.gamma);
+  // sampling never needs the normaliser of p_gamma: its bonus draw (only when every draft
+  // is accepted) is formed by the residual kernel
+  if (!GREEDY && r == a.gamma) return;
   const char* row = static_cast<const char*>(row_ptr<BF16>(a, b, r));
   const int64_t NG = (a.V + kGroup - 1) / kGroup;
   const int64_t GPS = (NG + a.S - 1) / a.S;
@@ -95,62 +125,71 @@ __global__ __launch_bounds__(256) void k_verify_rows(VerifyArgs a) {
   const int64_t g1 = min(NG, g0 + GPS);
   const int64_t e_begin = g0 * kGroup;
   const int64_t e_end = min(a.V, g1 * kGroup);
-  const int64_t n = e_end > e_begin ? e_end - e_begin : 0;
-  const rsrc_t rs = make_rsrc(row + static_cast<size_t>(e_begin) * ES, static_cast<uint32_t>(n * ES));
-  const bool bonus = (a.mode == 1) && (r == a.gamma);
-  const int l = lane_id();
+  const uint32_t n = e_end > e_begin ? static_cast<uint32_t>(e_end - e_begin) : 0u;
+  const rsrc_t rs = make_rsrc(row + static_cast<size_t>(e_begin) * ES, n * ES);
+  const uint32_t tid = threadIdx.x;
+  const uint32_t step = blockDim.x * EPT;
   Partial p = partial_empty();
-  const int64_t step = static_cast<int64_t>(blockDim.x) * EPT;
-  const int64_t span = step * UNR;
-  for (int64_t base = 0; base < n; base += span) {
-    uint4 raw[UNR];
+  auto load = [&](uint4 (&buf)[UNR], uint32_t base) {
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
-      const int64_t e = base + u * step + static_cast<int64_t>(threadIdx.x) * EPT;
-      raw[u] = buffer_load16(rs, e < n ? static_cast<uint32_t>(e * ES) : kOutOfRange);
+      const uint32_t e = base + u * step + tid * EPT;
+      buf[u] = buffer_load16(rs, e < n ? e * ES : kOutOfRange);
     }
+  };
+  if constexpr (GREEDY) {
+    float best = -INFINITY;
+    uint32_t bchunk = 0xffffffffu;
+    pipelined<UNR>(n, step * UNR, load, [&](uint4 (&buf)[UNR], uint32_t base) {
 #pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      const int64_t e = base + u * step + static_cast<int64_t>(threadIdx.x) * EPT;
-      const bool in = e < n;
-      const int64_t e0 = e_begin + e;
+      for (int u = 0; u < UNR; ++u) {
+        const uint32_t e = base + u * step + tid * EPT;
+        float v[EPT];
+        unpack<BF16>(buf[u], v);
+        const float cm = e < n ? chunk_max<EPT>(v) : -INFINITY;
+        if (cm > best) {   // chunks of a thread rise in index: strict > keeps the first
+          best = cm;
+          bchunk = e;
+        }
+      }
+    });
+    int32_t bid = 0x7fffffff;
+    if (bchunk != 0xffffffffu) {
       float v[EPT];
-      unpack<BF16>(raw[u], v);
-      float lmax = -INFINITY, lsum = 0.f;
-      if (in) {
+      unpack<BF16>(buffer_load16(rs, bchunk * ES), v);
+      int j = EPT - 1;
 #pragma unroll
-        for (int i = 0; i < EPT; ++i) {
-          if (e0 + i < e_end) {
-            argmax_merge(p.zmax, p.zid, v[i], static_cast<int32_t>(e0 + i));
-            lmax = fmaxf(lmax, v[i] * a.invT);
-          }
-        }
-#pragma unroll
-        for (int i = 0; i < EPT; ++i)
-          if (e0 + i < e_end) lsum += __expf(v[i] * a.invT - lmax);
-        lse_merge(p.m, p.s, lmax, lsum);
-      }
-      if (bonus) {
-        // one group = LPG consecutive lanes; (max, sum) inside the group
-        float gm = lmax;
-#pragma unroll
-        for (int o = 1; o < LPG; o <<= 1) gm = fmaxf(gm, xor_lane(gm, o));
-        float gs = (in && gm != -INFINITY) ? lsum * __expf(lmax - gm) : 0.f;
-#pragma unroll
-        for (int o = 1; o < LPG; o <<= 1) gs += xor_lane(gs, o);
-        if (in && (l % LPG) == 0) {
-          const int64_t gi = e0 / kGroup;
-          const float L = gm + logf(gs);
-          const float sc = L + gumbel(philox_uniform(a.seed, a.offset, kBonusGroup, b, gi));
-          argmax_merge(p.gscore, p.g, sc, static_cast<int32_t>(gi));
-        }
-      }
+      for (int i = EPT - 1; i >= 0; --i)
+        if (v[i] == best) j = i;
+      bid = static_cast<int32_t>(e_begin + bchunk + j);
     }
+    p.zmax = best;
+    p.zid = bid;
+  } else {
+    const float c = a.invT * kLog2e;   // y * log2(e) = z * c
+    float M = -INFINITY, S = 0.f;      // sum of exp2(z c - M)
+    pipelined<UNR>(n, step * UNR, load, [&](uint4 (&buf)[UNR], uint32_t base) {
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        const uint32_t e = base + u * step + tid * EPT;
+        float v[EPT];
+        unpack<BF16>(buf[u], v);
+        if (e < n) {
+          const float Mn = fmaxf(M, chunk_max<EPT>(v) * c);
+          float cs = 0.f;
+#pragma unroll
+          for (int i = 0; i < EPT; ++i) cs += fast_exp2(fmaf(v[i], c, -Mn));
+          S = S * fast_exp2(M - Mn) + cs;
+          M = Mn;
+        }
+      }
+    });
+    // (m, s) with lse = m + log(s): m = M ln 2, s = S
+    p.m = M == -INFINITY ? -INFINITY : M * kLn2;
+    p.s = S;
   }
   Partial out = block_merge(p, red4);
-  if (threadIdx.x == 0) {
-    a.partials[(b * R + r) * a.S + s] = out;
-  }
+  if (threadIdx.x == 0) a.partials[(b * R + r) * a.S + s] = out;
 }
 
 // Element draw of a two-level Gumbel-max inside 64-element group g (wave 0): returns the
@@ -207,123 +246,154 @@ __device__ int seq_accept(const VerifyArgs& a, int64_t b, Partial* rowp, int* sh
 
 constexpr int kMaxVerifyRows = 2 * 64 + 1;
 
-// Residual group scores of one vocabulary segment of the rejected position (sampling only).
+// Residual group scores of one vocabulary segment of the rejected position (sampling only):
+// per group log2 of sum max(0, p - q), with p = exp2(z_p c - lse_p log2 e) and q likewise.
 template <bool BF16>
 __global__ __launch_bounds__(256) void k_verify_resid(VerifyArgs a) {
   constexpr int EPT = BF16 ? 8 : 4;
   constexpr int LPG = kGroup / EPT;
-  constexpr size_t ES = BF16 ? 2 : 4;
+  constexpr uint32_t ES = BF16 ? 2 : 4;
+  constexpr int UNR = 2;
   __shared__ Partial rowp[kMaxVerifyRows];
   __shared__ Partial red4[4];
   __shared__ int sh_a;
   const int s2 = blockIdx.x;
   const int64_t b = blockIdx.y;
   const int l = lane_id();
+  const uint32_t tid = threadIdx.x;
   const int gamma = static_cast<int>(a.gamma);
   const int acc_len = seq_accept<BF16>(a, b, rowp, &sh_a);
-  if (acc_len == gamma) return;   // bonus: drawn by the finish kernel from the row pass
+  // rejected at a: residual max(0, p_a - q_a); all accepted: the bonus draw from p_gamma
+  const bool bonus = acc_len == gamma;
   const char* prow = static_cast<const char*>(row_ptr<BF16>(a, b, acc_len));
-  const char* qrow = static_cast<const char*>(row_ptr<BF16>(a, b, gamma + 1 + acc_len));
-  const float lse_p = rowp[acc_len].m + logf(rowp[acc_len].s);
-  const float lse_q = rowp[gamma + 1 + acc_len].m + logf(rowp[gamma + 1 + acc_len].s);
-  const bool resid = true;
-  // 3. residual group scores over this workgroup's segment: gscore/g for max(0, p - q),
-  //    zmax/zid for p itself (used only if the residual has no mass anywhere)
-  if (resid) {
-    const int64_t NG = (a.V + kGroup - 1) / kGroup;
-    const int64_t GPS = (NG + a.S2 - 1) / a.S2;
-    const int64_t e_begin = s2 * GPS * kGroup;
-    const int64_t e_end = min(a.V, (s2 + 1) * GPS * kGroup);
-    const int64_t n = e_end > e_begin ? e_end - e_begin : 0;
-    const rsrc_t rp = make_rsrc(prow + static_cast<size_t>(e_begin) * ES, static_cast<uint32_t>(n * ES));
-    const rsrc_t rq = make_rsrc(qrow + static_cast<size_t>(e_begin) * ES, static_cast<uint32_t>(n * ES));
-    Partial best = partial_empty();
-    const int64_t step = static_cast<int64_t>(blockDim.x) * EPT;
-    for (int64_t base = 0; base < n; base += 2 * step) {
-      uint4 rawp[2], rawq[2];
+  const char* qrow = bonus ? prow : static_cast<const char*>(row_ptr<BF16>(a, b, gamma + 1 + acc_len));
+  const float c = a.invT * kLog2e;
+  const float Lp = bonus ? 0.f : (rowp[acc_len].m + logf(rowp[acc_len].s)) * kLog2e;
+  const float Lq = bonus ? 0.f : (rowp[gamma + 1 + acc_len].m + logf(rowp[gamma + 1 + acc_len].s)) * kLog2e;
+  const uint32_t purpose = bonus ? kBonusGroup : kResidGroup;
+  const int64_t NG = (a.V + kGroup - 1) / kGroup;
+  const int64_t GPS = (NG + a.S2 - 1) / a.S2;
+  const int64_t e_begin = s2 * GPS * kGroup;
+  const int64_t e_end = min(a.V, (s2 + 1) * GPS * kGroup);
+  const uint32_t n = e_end > e_begin ? static_cast<uint32_t>(e_end - e_begin) : 0u;
+  const rsrc_t rp = make_rsrc(prow + static_cast<size_t>(e_begin) * ES, n * ES);
+  const rsrc_t rq = make_rsrc(qrow + static_cast<size_t>(e_begin) * ES, n * ES);
+  Partial best = partial_empty();
+  const uint32_t step = blockDim.x * EPT;
+  // p and q chunks interleaved in one buffer: [2u] from p, [2u + 1] from q
+  auto load = [&](uint4 (&buf)[2 * UNR], uint32_t base) {
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int64_t e = base + u * step + static_cast<int64_t>(threadIdx.x) * EPT;
-        rawp[u] = buffer_load16(rp, e < n ? static_cast<uint32_t>(e * ES) : kOutOfRange);
-        rawq[u] = buffer_load16(rq, e < n ? static_cast<uint32_t>(e * ES) : kOutOfRange);
-      }
+    for (int u = 0; u < UNR; ++u) {
+      const uint32_t e = base + u * step + tid * EPT;
+      buf[2 * u] = buffer_load16(rp, e < n ? e * ES : kOutOfRange);
+      buf[2 * u + 1] = buffer_load16(rq, (e < n && !bonus) ? e * ES : kOutOfRange);
+    }
+  };
+  pipelined<2 * UNR>(n, step * UNR, load, [&](uint4 (&buf)[2 * UNR], uint32_t base) {
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int64_t e = base + u * step + static_cast<int64_t>(threadIdx.x) * EPT;
-        const bool in = e < n;
-        const int64_t e0 = e_begin + e;
-        float vp[EPT], vq[EPT];
-        unpack<BF16>(rawp[u], vp);
-        unpack<BF16>(rawq[u], vq);
-        float rsum = 0.f, lmax = -INFINITY, lsum = 0.f;
+    for (int u = 0; u < UNR; ++u) {
+      const uint32_t e = base + u * step + tid * EPT;
+      const bool in = e < n;
+      float vp[EPT], vq[EPT];
+      unpack<BF16>(buf[2 * u], vp);
+      unpack<BF16>(buf[2 * u + 1], vq);
+      float gr = 0.f, gm = 0.f;   // group score log2 sum, relative to gm
+      if (bonus) {
+        // log-sum-exp of the group's y values (base 2), max-shifted over its LPG lanes
+        gm = in ? chunk_max<EPT>(vp) * c : -INFINITY;
+#pragma unroll
+        for (int o = 1; o < LPG; o <<= 1) gm = fmaxf(gm, xor_lane(gm, o));
         if (in) {
 #pragma unroll
-          for (int i = 0; i < EPT; ++i)
-            if (e0 + i < e_end) {
-              rsum += fmaxf(expf(vp[i] * a.invT - lse_p) - expf(vq[i] * a.invT - lse_q), 0.f);
-              lmax = fmaxf(lmax, vp[i] * a.invT);
-            }
-#pragma unroll
-          for (int i = 0; i < EPT; ++i)
-            if (e0 + i < e_end) lsum += __expf(vp[i] * a.invT - lmax);
+          for (int i = 0; i < EPT; ++i) gr += fast_exp2(fmaf(vp[i], c, -gm));
         }
-        float gr = rsum, gm = lmax;
+      } else if (in) {
 #pragma unroll
-        for (int o = 1; o < LPG; o <<= 1) {
-          gr += xor_lane(gr, o);
-          gm = fmaxf(gm, xor_lane(gm, o));
-        }
-        float gs = (in && gm != -INFINITY) ? lsum * __expf(lmax - gm) : 0.f;
+        for (int i = 0; i < EPT; ++i)
+          gr += fmaxf(fast_exp2(fmaf(vp[i], c, -Lp)) - fast_exp2(fmaf(vq[i], c, -Lq)), 0.f);
+      }
 #pragma unroll
-        for (int o = 1; o < LPG; o <<= 1) gs += xor_lane(gs, o);
-        if (in && (l % LPG) == 0) {
-          const int64_t gi = e0 / kGroup;
-          const float G = gumbel(philox_uniform(a.seed, a.offset, kResidGroup, b, gi));
-          if (gr > 0.f) argmax_merge(best.gscore, best.g, logf(gr) + G, static_cast<int32_t>(gi));
-          argmax_merge(best.zmax, best.zid, gm + logf(gs) + G, static_cast<int32_t>(gi));
-        }
+      for (int o = 1; o < LPG; o <<= 1) gr += xor_lane(gr, o);
+      if (in && (l % LPG) == 0 && gr > 0.f) {
+        const int64_t gi = (e_begin + e) / kGroup;
+        const float G = gumbel(philox_uniform(a.seed, a.offset, purpose, b, gi));
+        argmax_merge(best.gscore, best.g, (gm + log2f(gr)) * kLn2 + G, static_cast<int32_t>(gi));
       }
     }
-    best = block_merge(best, red4);
-    if (threadIdx.x == 0) a.partials2[b * a.S2 + s2] = best;
-  }
+  });
+  best = block_merge(best, red4);
+  if (threadIdx.x == 0) a.partials2[b * a.S2 + s2] = best;
 }
 
 // One workgroup per sequence: the accepted prefix, the last token, the outputs.
 template <bool BF16>
 __global__ __launch_bounds__(256) void k_verify_finish(VerifyArgs a) {
+  constexpr int EPT = BF16 ? 8 : 4;
+  constexpr uint32_t ES = BF16 ? 2 : 4;
   __shared__ Partial rowp[kMaxVerifyRows];
+  __shared__ Partial red4[4];
   __shared__ int sh_a;
   const int64_t b = blockIdx.x;
   const int l = lane_id(), w = wave_id();
   const int gamma = static_cast<int>(a.gamma);
   const int acc_len = seq_accept<BF16>(a, b, rowp, &sh_a);
-  if (w != 0) return;
   const bool resid = a.mode == 1 && acc_len < gamma;
   const char* prow = static_cast<const char*>(row_ptr<BF16>(a, b, acc_len));
   const char* qrow = resid ? static_cast<const char*>(row_ptr<BF16>(a, b, gamma + 1 + acc_len)) : nullptr;
-  const float lse_p = rowp[acc_len].m + logf(rowp[acc_len].s);
-  const float lse_q = resid ? rowp[gamma + 1 + acc_len].m + logf(rowp[gamma + 1 + acc_len].s) : 0.f;
+  const float c = a.invT * kLog2e;
+  const float Lp = (rowp[acc_len].m + logf(rowp[acc_len].s)) * kLog2e;
+  const float Lq = resid ? (rowp[gamma + 1 + acc_len].m + logf(rowp[gamma + 1 + acc_len].s)) * kLog2e : 0.f;
+  Partial best = partial_empty();
+  if (a.mode == 1) {   // residual or bonus group winner from the residual kernel's segments
+    best = l < a.S2 ? a.partials2[b * a.S2 + l] : partial_empty();
+    wave_partial_merge(best);   // argmax merges: exact in any order
+  }
+  const bool fallback = resid && best.gscore == -INFINITY;
+  if (fallback) {
+    // no residual mass anywhere (p <= q everywhere): draw from p at this position, scanning
+    // the whole row here (a degenerate case, never on the common path)
+    const int64_t NG = (a.V + kGroup - 1) / kGroup;
+    const rsrc_t rp = make_rsrc(prow, static_cast<uint32_t>(a.V) * ES);
+    Partial f = partial_empty();
+    for (int64_t g = threadIdx.x; g < NG; g += blockDim.x) {
+      float gm = -INFINITY, gs = 0.f;
+      for (int q = 0; q < kGroup / EPT; ++q) {
+        const int64_t e = g * kGroup + q * EPT;
+        if (e >= a.V) break;
+        float v[EPT];
+        unpack<BF16>(buffer_load16(rp, static_cast<uint32_t>(e) * ES), v);
+        const float cm = chunk_max<EPT>(v) * c;
+        const float mn = fmaxf(gm, cm);
+        float cs = 0.f;
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) cs += exp2f(fmaf(v[i], c, -mn));
+        gs = gs * exp2f(gm - mn) + cs;
+        gm = mn;
+      }
+      const float sc = (gm + log2f(gs)) * kLn2 + gumbel(philox_uniform(a.seed, a.offset, kResidGroup, b, g));
+      argmax_merge(f.gscore, f.g, sc, static_cast<int32_t>(g));
+    }
+    f = block_merge(f, red4);
+    best.zmax = f.gscore;
+    best.zid = f.g;
+  }
+  if (w != 0) return;
   int32_t tok;
   if (a.mode == 0) {
     tok = rowp[acc_len].zid;
   } else if (!resid) {
-    tok = draw_in_group<BF16>(rowp[gamma].g, a.V, a.seed, a.offset, kBonusElem, b,
+    tok = draw_in_group<BF16>(best.g, a.V, a.seed, a.offset, kBonusElem, b,
                               [&](int64_t i) { return load_logit<BF16>(prow, i) * a.invT; });
+  } else if (!fallback) {
+    tok = draw_in_group<BF16>(best.g, a.V, a.seed, a.offset, kResidElem, b, [&](int64_t i) {
+      const float rr = fmaxf(fast_exp2(fmaf(load_logit<BF16>(prow, i), c, -Lp)) -
+                                 fast_exp2(fmaf(load_logit<BF16>(qrow, i), c, -Lq)),
+                             0.f);
+      return rr > 0.f ? logf(rr) : -INFINITY;
+    });
   } else {
-    Partial best = l < a.S2 ? a.partials2[b * a.S2 + l] : partial_empty();
-    wave_partial_merge(best);   // argmax merges: exact in any order
-    if (best.gscore != -INFINITY) {
-      tok = draw_in_group<BF16>(best.g, a.V, a.seed, a.offset, kResidElem, b, [&](int64_t i) {
-        const float rr = fmaxf(expf(load_logit<BF16>(prow, i) * a.invT - lse_p) -
-                                   expf(load_logit<BF16>(qrow, i) * a.invT - lse_q),
-                               0.f);
-        return rr > 0.f ? logf(rr) : -INFINITY;
-      });
-    } else {
-      tok = draw_in_group<BF16>(best.zid, a.V, a.seed, a.offset, kResidElem, b,
-                                [&](int64_t i) { return load_logit<BF16>(prow, i) * a.invT; });
-    }
+    tok = draw_in_group<BF16>(best.zid, a.V, a.seed, a.offset, kResidElem, b,
+                              [&](int64_t i) { return load_logit<BF16>(prow, i) * a.invT; });
   }
   for (int t = l; t <= gamma; t += kWave) {
     int32_t o = -1;
@@ -361,10 +431,16 @@ hipError_t launch_verify(const VerifyArgs& a, hipStream_t st) {
   const dim3 grid(static_cast<unsigned>(a.S), static_cast<unsigned>(R), static_cast<unsigned>(a.B));
   {
     TraceScope ts("verify_rows", st);
-    if (a.bf16) {
-      hipLaunchKernelGGL(k_verify_rows<true>, grid, dim3(256), 0, st, a);
+    if (a.mode == 0) {
+      if (a.bf16)
+        hipLaunchKernelGGL((k_verify_rows<true, true>), grid, dim3(256), 0, st, a);
+      else
+        hipLaunchKernelGGL((k_verify_rows<false, true>), grid, dim3(256), 0, st, a);
     } else {
-      hipLaunchKernelGGL(k_verify_rows<false>, grid, dim3(256), 0, st, a);
+      if (a.bf16)
+        hipLaunchKernelGGL((k_verify_rows<true, false>), grid, dim3(256), 0, st, a);
+      else
+        hipLaunchKernelGGL((k_verify_rows<false, false>), grid, dim3(256), 0, st, a);
     }
   }
   hipError_t e = hipGetLastError();
