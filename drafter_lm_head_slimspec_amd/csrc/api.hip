@@ -110,6 +110,9 @@ sh::TopkArgs topk_args(void* ws, const TopkLayout& L, const float* scores, int64
   return a;
 }
 
+// group log-sum-exp rows are padded to a multiple of 4 groups (16-byte aligned quads)
+int64_t lg_stride(int64_t V) { return ((V + sh::kGroup - 1) / sh::kGroup + 3) / 4 * 4; }
+
 struct HeadLayout {
   size_t tk_off, tk_bytes;   // SpecVocab: the top-k block, at offset 0
   size_t rd_off, rd_bytes;   // fp32 split-K partials of the down-projection
@@ -137,7 +140,7 @@ HeadLayout head_layout(int op, int64_t M, int64_t d, int64_t r, int64_t V, int64
   L.part_bytes = (op == SH_OP_SPECVOCAB) ? 0 : align_up(static_cast<size_t>(M) * sh::kMaxPartials * sizeof(sh::Partial), 256);
   off += L.part_bytes;
   L.lg_off = off;
-  L.lg_bytes = (op == SH_OP_SPECVOCAB) ? 0 : align_up(static_cast<size_t>(M) * static_cast<size_t>((V + sh::kGroup - 1) / sh::kGroup) * 4, 256);
+  L.lg_bytes = (op == SH_OP_SPECVOCAB) ? 0 : align_up(static_cast<size_t>(M) * static_cast<size_t>(lg_stride(V)) * 4, 256);
   off += L.lg_bytes;
   L.score_off = off;
   L.score_bytes = (op == SH_OP_SPECVOCAB) ? align_up(static_cast<size_t>(M * V) * 4, 256) : 0;
@@ -214,8 +217,8 @@ int run_head(const void* x, int64_t M, int64_t K, const void* W, int64_t V, int 
     a.invT = invT;
     a.zout = logits ? logits + m0 * V : nullptr;
     a.zout_ld = V;
-    a.lg = want_lg ? lg + m0 * NG : nullptr;
-    a.lg_ld = NG;
+    a.lg = want_lg ? lg + m0 * lg_stride(V) : nullptr;
+    a.lg_ld = lg_stride(V);
     a.partials = partials + m0 * sh::kMaxPartials;
     a.partials_ld = sh::kMaxPartials;
     int p = 0;
@@ -227,7 +230,7 @@ int run_head(const void* x, int64_t M, int64_t K, const void* W, int64_t V, int 
   f.partials_ld = sh::kMaxPartials;
   f.P = producers;
   f.lg = lg;
-  f.lg_ld = NG;
+  f.lg_ld = lg_stride(V);
   f.W = W;
   f.x = x;
   f.V = V;

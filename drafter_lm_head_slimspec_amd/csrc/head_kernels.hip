@@ -928,9 +928,9 @@ __global__ __launch_bounds__(kFinThreads) void k_head_finalize(FinalizeArgs f) {
   int32_t bg = 0x7fffffff;
   if (want_lse) {
     for (int q = threadIdx.x; q * 4 < NG; q += kFinThreads) {
-      float L[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) L[j] = (q * 4 + j < NG) ? lgr[q * 4 + j] : -INFINITY;
+      const float4 L4 = reinterpret_cast<const float4*>(lgr)[q];   // rows padded to 4 groups
+      const float L[4] = {L4.x, q * 4 + 1 < NG ? L4.y : -INFINITY, q * 4 + 2 < NG ? L4.z : -INFINITY,
+                          q * 4 + 3 < NG ? L4.w : -INFINITY};
       const float qm = fmaxf(fmaxf(L[0], L[1]), fmaxf(L[2], L[3]));
       float qs = 0.f;
       if (qm != -INFINITY) {

@@ -189,76 +189,83 @@ __global__ __launch_bounds__(kTkThreads) void k_topk_select(TopkArgs a) {
 }
 
 // One workgroup per row: resolve the threshold bin's candidates and compact the row.
-__global__ __launch_bounds__(kTkThreads) void k_topk_finish(TopkArgs a) {
-  extern __shared__ uint32_t fin[];  // sel[nw], tie[nw], hist[1024]
-  __shared__ uint32_t wsum[kTkWaves];
+// Candidates are staged in LDS when they fit (cand_cap entries), the selection bitmask is
+// loaded into LDS at the start; equal-key ties at the final threshold are resolved by id only
+// when more of them exist than are needed.
+constexpr int kTfThreads = 1024;
+constexpr int kTfWaves = kTfThreads / kWave;
+
+__global__ __launch_bounds__(kTfThreads) void k_topk_finish(TopkArgs a, int cand_cap) {
+  extern __shared__ uint32_t fin[];  // sel[nw], tie[nw], hist[1024], cand[cand_cap] (uint2)
+  __shared__ uint32_t wsum[kTfWaves];
   __shared__ uint32_t res[2];
+  __shared__ uint32_t nties;
   const int m = blockIdx.x;
   const int tid = threadIdx.x;
   const int64_t V = a.V;
   const uint32_t k = static_cast<uint32_t>(a.k);
-  {
-    const uint4* hg = reinterpret_cast<const uint4*>(a.hist + static_cast<size_t>(m) * kTkBins) + tid * 4;
-    uint32_t c[16];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint4 t = hg[q];
-      c[4 * q] = t.x;
-      c[4 * q + 1] = t.y;
-      c[4 * q + 2] = t.z;
-      c[4 * q + 3] = t.w;
-    }
-    find_crossing<16>(c, k, wsum, res);
-  }
-  const uint32_t bstar = res[0], above = res[1];
   const int64_t mw = (V + kWave - 1) / kWave;
-  const uint64_t* mask = a.mask + static_cast<size_t>(m) * mw;
-  const uint2* cand = a.cand + static_cast<size_t>(m) * V;
-  uint32_t C = a.count[static_cast<size_t>(m) * kTkCounterStride];
-  if (C > static_cast<uint64_t>(V)) C = static_cast<uint32_t>(V);
   const int nw = static_cast<int>(2 * mw);  // 32-bit words of the bitmask
   uint32_t* sel = fin;
   uint32_t* tie = fin + nw;
   uint32_t* h1 = fin + 2 * nw;
-  // 3a. two 10-bit passes over the candidates: key bits 19..10, then 9..0
-  uint32_t need = k - above;
+  uint2* cl = reinterpret_cast<uint2*>(fin + 2 * nw + 1024);
+  // loads that depend on nothing: the row histogram, the bitmask, the candidate count
+  const uint4 hq = reinterpret_cast<const uint4*>(a.hist + static_cast<size_t>(m) * kTkBins)[tid];
+  const uint32_t* mw32 = reinterpret_cast<const uint32_t*>(a.mask + static_cast<size_t>(m) * mw);
+  for (int i = tid; i < nw; i += kTfThreads) {
+    sel[i] = mw32[i];
+    tie[i] = 0u;
+  }
+  uint32_t C = a.count[static_cast<size_t>(m) * kTkCounterStride];
+  if (C > static_cast<uint64_t>(V)) C = static_cast<uint32_t>(V);
+  const uint2* cg = a.cand + static_cast<size_t>(m) * V;
+  const bool in_lds = C <= static_cast<uint32_t>(cand_cap);
+  if (in_lds)
+    for (uint32_t i = tid; i < C; i += kTfThreads) cl[i] = cg[i];
+  const uint2* cand = in_lds ? cl : cg;
+  if (tid == 0) nties = 0u;
+  {
+    const uint32_t c[4] = {hq.x, hq.y, hq.z, hq.w};
+    find_crossing<4>(c, k, wsum, res);   // includes a barrier: LDS stores above are visible
+  }
+  const uint32_t bstar = res[0];
+  uint32_t need = k - res[1];
   uint32_t thr = bstar << kTkShift;
+  // two 10-bit passes over the candidates: key bits 19..10, then 9..0
   for (int pass = 0; pass < 2; ++pass) {
     const int shift = pass == 0 ? 10 : 0;
-    for (int i = tid; i < 1024; i += kTkThreads) h1[i] = 0u;
+    h1[tid] = 0u;
     __syncthreads();
-    for (uint32_t i = tid; i < C; i += kTkThreads) {
+    for (uint32_t i = tid; i < C; i += kTfThreads) {
       const uint32_t key = cand[i].x;
       if (pass == 0 || ((key >> 10) & 1023u) == ((thr >> 10) & 1023u)) atomicAdd(&h1[(key >> shift) & 1023u], 1u);
     }
     __syncthreads();
-    uint32_t c[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) c[q] = h1[4 * tid + q];
-    find_crossing<4>(c, need, wsum, res);
+    const uint32_t c[1] = {h1[tid]};
+    find_crossing<1>(c, need, wsum, res);
     thr |= res[0] << shift;
     need -= res[1];
   }
-  // 3b. keys above the threshold are in; keys equal to it compete by id
-  const uint32_t* mw32 = reinterpret_cast<const uint32_t*>(mask);
-  for (int i = tid; i < nw; i += kTkThreads) {
-    sel[i] = mw32[i];
-    tie[i] = 0u;
-  }
-  __syncthreads();
-  for (uint32_t i = tid; i < C; i += kTkThreads) {
+  // keys above the threshold are in; keys equal to it are in if all are needed, else they
+  // compete by id
+  for (uint32_t i = tid; i < C; i += kTfThreads) {
     const uint2 ce = cand[i];
     if (ce.y >= static_cast<uint64_t>(V)) continue;
-    if (ce.x > thr)
+    if (ce.x > thr) {
       atomicOr(&sel[ce.y >> 5], 1u << (ce.y & 31u));
-    else if (ce.x == thr)
+    } else if (ce.x == thr) {
       atomicOr(&tie[ce.y >> 5], 1u << (ce.y & 31u));
+      atomicAdd(&nties, 1u);
+    }
   }
   __syncthreads();
-  const int per = (nw + kTkThreads - 1) / kTkThreads;
+  const int per = (nw + kTfThreads - 1) / kTfThreads;
   const int w0 = tid * per < nw ? tid * per : nw;
   const int w1 = w0 + per < nw ? w0 + per : nw;
-  {
+  if (nties <= need) {
+    for (int i = w0; i < w1; ++i) sel[i] |= tie[i];
+  } else {
     uint32_t cnt = 0u, total;
     for (int i = w0; i < w1; ++i) cnt += __popc(tie[i]);
     uint32_t rank = block_exclusive_scan(cnt, wsum, &total);
@@ -272,21 +279,18 @@ __global__ __launch_bounds__(kTkThreads) void k_topk_finish(TopkArgs a) {
       }
     }
   }
-  __syncthreads();
-  // 3c. ascending ids
-  {
-    uint32_t cnt = 0u, total;
-    for (int i = w0; i < w1; ++i) cnt += __popc(sel[i]);
-    uint32_t pos = block_exclusive_scan(cnt, wsum, &total);
-    int32_t* out = a.out + static_cast<size_t>(m) * k;
-    for (int i = w0; i < w1; ++i) {
-      uint32_t bits = sel[i];
-      while (bits != 0u) {
-        const uint32_t b = __builtin_ctz(bits);
-        if (pos < k) out[pos] = static_cast<int32_t>(32 * i + b);
-        ++pos;
-        bits &= bits - 1u;
-      }
+  // ascending ids (each thread compacts its own words)
+  uint32_t cnt = 0u, total;
+  for (int i = w0; i < w1; ++i) cnt += __popc(sel[i]);
+  uint32_t pos = block_exclusive_scan(cnt, wsum, &total);
+  int32_t* out = a.out + static_cast<size_t>(m) * k;
+  for (int i = w0; i < w1; ++i) {
+    uint32_t bits = sel[i];
+    while (bits != 0u) {
+      const uint32_t b = __builtin_ctz(bits);
+      if (pos < k) out[pos] = static_cast<int32_t>(32 * i + b);
+      ++pos;
+      bits &= bits - 1u;
     }
   }
 }
@@ -327,171 +331,187 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const size_t lds = topk_finish_lds(a.V);
+  // LDS: the two bitmasks and the 1024-bin histogram, then as many candidates as fit
+  const size_t base = topk_finish_lds(a.V);
+  const size_t limit = 160 * 1024 - 1024;   // leave room for the static arrays
+  int cap = base < limit ? static_cast<int>((limit - base) / 8) : 0;
+  if (cap > 8192) cap = 8192;
+  const size_t lds = base + static_cast<size_t>(cap) * 8;
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_topk_finish),
                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
   if (e != hipSuccess) return e;
   TraceScope ts("topk_finish", st);
-  hipLaunchKernelGGL(k_topk_finish, dim3(static_cast<unsigned>(a.M)), dim3(kTkThreads), lds, st, a);
+  hipLaunchKernelGGL(k_topk_finish, dim3(static_cast<unsigned>(a.M)), dim3(kTfThreads), lds, st, a, cap);
   return hipGetLastError();
 }
 
 // ----------------------------------------------------------------------------------------
 // gather + exact logits: grid (ceil(k / 16), M); each wave computes 4 candidates of row m.
 // ----------------------------------------------------------------------------------------
-constexpr int kGatherPerWave = 4;
-constexpr int kGatherMaxCPL = 16;
+constexpr int kGatherRows = 2;   // candidate rows per wave, all loads in flight together
 
-template <bool BF16>
+// z'[m, j] = U[K[m, j], :] . h[m, :].  Each wave takes kGatherRows candidates; a candidate's
+// row is one buffer descriptor (an invalid id gets an empty range, so its loads read zero).
+template <bool BF16, int CPL>
 __global__ __launch_bounds__(256) void k_gather_exact(const void* __restrict__ U,
                                                       const void* __restrict__ h,
                                                       const int32_t* __restrict__ idx, int C,
                                                       int k, int V, float* __restrict__ zbuf) {
   const int m = blockIdx.y;
   const int l = lane_id(), w = wave_id();
-  const int CPL = (C + kWave - 1) / kWave;
-  const size_t rowbytes = static_cast<size_t>(C) * 16;
-  const char* hrow = static_cast<const char*>(h) + static_cast<size_t>(m) * rowbytes;
-  uint4 hr[kGatherMaxCPL];
+  const uint32_t rowbytes = static_cast<uint32_t>(C) * 16;
+  const int j0 = (blockIdx.x * (blockDim.x / kWave) + w) * kGatherRows;
+  uint4 wv[kGatherRows][CPL];
 #pragma unroll
-  for (int q = 0; q < kGatherMaxCPL; ++q) {
-    const int c = q * kWave + l;
-    hr[q] = (q < CPL && c < C) ? load16(hrow + static_cast<size_t>(c) * 16) : zero16();
-  }
-  const int j0 = (blockIdx.x * (blockDim.x / kWave) + w) * kGatherPerWave;
-  int64_t rows[kGatherPerWave];
-#pragma unroll
-  for (int jj = 0; jj < kGatherPerWave; ++jj) {
+  for (int jj = 0; jj < kGatherRows; ++jj) {
     const int j = j0 + jj;
-    const int64_t id = (j < k) ? idx[static_cast<size_t>(m) * k + j] : -1;
-    rows[jj] = (id >= 0 && id < V) ? id : -1;   // ids come from k_topk; guard anyway
-  }
-  float z[kGatherPerWave];
+    const int id = j < k ? idx[static_cast<size_t>(m) * k + j] : -1;
+    const bool ok = id >= 0 && id < V;   // ids come from the top-k; guarded anyway
+    const rsrc_t rs = make_rsrc(static_cast<const char*>(U) + static_cast<size_t>(ok ? id : 0) * rowbytes,
+                                ok ? rowbytes : 0u);
 #pragma unroll
-  for (int jj = 0; jj < kGatherPerWave; ++jj) z[jj] = 0.f;
-#pragma unroll
-  for (int q = 0; q < kGatherMaxCPL; ++q) {
-    const int c = q * kWave + l;
-    if (q < CPL && c < C) {
-      uint4 wv[kGatherPerWave];
-#pragma unroll
-      for (int jj = 0; jj < kGatherPerWave; ++jj)
-        wv[jj] = rows[jj] >= 0 ? load16(static_cast<const char*>(U) + static_cast<size_t>(rows[jj]) * rowbytes +
-                                        static_cast<size_t>(c) * 16)
-                               : zero16();
-#pragma unroll
-      for (int jj = 0; jj < kGatherPerWave; ++jj) z[jj] = chunk_dot<BF16>(wv[jj], hr[q], z[jj]);
+    for (int q = 0; q < CPL; ++q) {
+      const int c = q * kWave + l;
+      wv[jj][q] = buffer_load16(rs, c < C ? static_cast<uint32_t>(c) * 16 : kOutOfRange);
     }
   }
+  const rsrc_t hrs = make_rsrc(static_cast<const char*>(h) + static_cast<size_t>(m) * rowbytes, rowbytes);
+  uint4 hr[CPL];
 #pragma unroll
-  for (int jj = 0; jj < kGatherPerWave; ++jj) {
-    const float t = wave_sum(z[jj]);
-    if (l == 0 && j0 + jj < k) zbuf[static_cast<size_t>(m) * k + j0 + jj] = t;
+  for (int q = 0; q < CPL; ++q) {
+    const int c = q * kWave + l;
+    hr[q] = buffer_load16(hrs, c < C ? static_cast<uint32_t>(c) * 16 : kOutOfRange);
   }
+#pragma unroll
+  for (int jj = 0; jj < kGatherRows; ++jj) {
+    float z = 0.f;
+#pragma unroll
+    for (int q = 0; q < CPL; ++q) z = chunk_dot<BF16>(wv[jj][q], hr[q], z);
+    z = wave_sum(z);
+    if (l == 0 && j0 + jj < k) zbuf[static_cast<size_t>(m) * k + j0 + jj] = z;
+  }
+}
+
+template <bool BF16, int CPL>
+static hipError_t run_gather(const void* U, const void* h, const int32_t* idx, int C, int64_t M,
+                             int64_t V, int64_t k, float* zbuf, hipStream_t st) {
+  const int per_wg = 4 * kGatherRows;
+  const dim3 grid(static_cast<unsigned>((k + per_wg - 1) / per_wg), static_cast<unsigned>(M));
+  hipLaunchKernelGGL((k_gather_exact<BF16, CPL>), grid, dim3(256), 0, st, U, h, idx, C,
+                     static_cast<int>(k), static_cast<int>(V), zbuf);
+  return hipGetLastError();
+}
+
+template <bool BF16>
+static hipError_t gather_dispatch(const void* U, const void* h, const int32_t* idx, int C, int64_t M,
+                                  int64_t V, int64_t k, float* zbuf, hipStream_t st) {
+  const int cpl = (C + kWave - 1) / kWave;
+  if (cpl <= 1) return run_gather<BF16, 1>(U, h, idx, C, M, V, k, zbuf, st);
+  if (cpl <= 2) return run_gather<BF16, 2>(U, h, idx, C, M, V, k, zbuf, st);
+  if (cpl <= 4) return run_gather<BF16, 4>(U, h, idx, C, M, V, k, zbuf, st);
+  if (cpl <= 8) return run_gather<BF16, 8>(U, h, idx, C, M, V, k, zbuf, st);
+  return run_gather<BF16, 16>(U, h, idx, C, M, V, k, zbuf, st);
 }
 
 hipError_t launch_gather_exact(const void* U, const void* h, const int32_t* idx, int64_t M,
                                int64_t d, int64_t V, int64_t k, bool bf16, float* zbuf,
                                hipStream_t st) {
   const int C = static_cast<int>(d * (bf16 ? 2 : 4) / 16);
-  const int per_wg = 4 * kGatherPerWave;
-  const dim3 grid(static_cast<unsigned>((k + per_wg - 1) / per_wg), static_cast<unsigned>(M));
   TraceScope ts("gather_exact", st);
-  if (bf16)
-    hipLaunchKernelGGL(k_gather_exact<true>, grid, dim3(256), 0, st, U, h, idx, C,
-                       static_cast<int>(k), static_cast<int>(V), zbuf);
-  else
-    hipLaunchKernelGGL(k_gather_exact<false>, grid, dim3(256), 0, st, U, h, idx, C,
-                       static_cast<int>(k), static_cast<int>(V), zbuf);
-  return hipGetLastError();
+  return bf16 ? gather_dispatch<true>(U, h, idx, C, M, V, k, zbuf, st)
+              : gather_dispatch<false>(U, h, idx, C, M, V, k, zbuf, st);
 }
 
 // ----------------------------------------------------------------------------------------
-// softmax over the k candidates + selection; one workgroup (4 waves) per row
+// softmax over the k candidates + selection; one workgroup (4 waves) per row.  The row's
+// logits are staged in LDS once; the group draw computes all group uniforms in one pass.
 // ----------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_gather_finalize(const float* __restrict__ zbuf,
-                                                         const int32_t* __restrict__ idx, int k,
-                                                         int mode, float invT, uint64_t seed,
-                                                         uint64_t offset, float* topk_logit,
-                                                         float* topk_prob, int32_t* token,
-                                                         float* lse_out, float* logprob) {
-  __shared__ float red_f[4];
-  __shared__ int32_t red_i[4];
-  __shared__ float sh_lse;
+constexpr int kGfThreads = 256;
+constexpr int kGfWaves = kGfThreads / kWave;
+
+__global__ __launch_bounds__(kGfThreads) void k_gather_finalize(const float* __restrict__ zbuf,
+                                                                const int32_t* __restrict__ idx, int k,
+                                                                int mode, float invT, uint64_t seed,
+                                                                uint64_t offset, float* topk_logit,
+                                                                float* topk_prob, int32_t* token,
+                                                                float* lse_out, float* logprob) {
+  extern __shared__ float zl[];   // [k] logits, then [ceil(k/64)] group log-sum-exps
+  __shared__ float red_f[kGfWaves];
+  __shared__ int32_t red_i[kGfWaves];
   const int m = blockIdx.x;
   const int l = lane_id(), w = wave_id();
   const float* z = zbuf + static_cast<size_t>(m) * k;
-  // max of y
+  const int ng = (k + kGroup - 1) / kGroup;
+  float* Lg = zl + k;
   float mx = -INFINITY;
-  for (int j = threadIdx.x; j < k; j += blockDim.x) mx = fmaxf(mx, z[j] * invT);
+  for (int j = threadIdx.x; j < k; j += blockDim.x) {
+    const float v = z[j];
+    zl[j] = v;
+    mx = fmaxf(mx, v);
+  }
   mx = wave_max(mx);
   if (l == 0) red_f[w] = mx;
   __syncthreads();
-  mx = fmaxf(fmaxf(red_f[0], red_f[1]), fmaxf(red_f[2], red_f[3]));
+  mx = red_f[0];
+  for (int i = 1; i < kGfWaves; ++i) mx = fmaxf(mx, red_f[i]);
+  const float c = invT * kLog2e;
+  const float mxc = mx * c;
+  // group log-sum-exps (base 2, shifted by the row max) and the row sum from them
+  for (int g = w; g < ng; g += kGfWaves) {
+    const int j = g * kGroup + l;
+    const float t = j < k ? fast_exp2(fmaf(zl[j], c, -mxc)) : 0.f;
+    const float gs = wave_sum(t);
+    if (l == 0) Lg[g] = gs;
+  }
   __syncthreads();
   float sm = 0.f;
-  for (int j = threadIdx.x; j < k; j += blockDim.x) sm += __expf(z[j] * invT - mx);
+  for (int g = threadIdx.x; g < ng; g += blockDim.x) sm += Lg[g];
   sm = wave_sum(sm);
+  __syncthreads();
   if (l == 0) red_f[w] = sm;
   __syncthreads();
-  if (threadIdx.x == 0) sh_lse = mx + logf((red_f[0] + red_f[1]) + (red_f[2] + red_f[3]));
-  __syncthreads();
-  const float lse = sh_lse;
+  sm = red_f[0];
+  for (int i = 1; i < kGfWaves; ++i) sm += red_f[i];
+  const float lse = mx * invT + logf(sm);            // natural-log units of y = z / T
+  const float lse2 = mxc + log2f(sm);                // base-2 units of z * c
   for (int j = threadIdx.x; j < k; j += blockDim.x) {
-    const float zj = z[j];
-    if (topk_prob) topk_prob[static_cast<size_t>(m) * k + j] = __expf(zj * invT - lse);
+    const float zj = zl[j];
+    if (topk_prob) topk_prob[static_cast<size_t>(m) * k + j] = fast_exp2(fmaf(zj, c, -lse2));
     if (topk_logit) topk_logit[static_cast<size_t>(m) * k + j] = zj;
   }
-  __syncthreads();
-  int32_t jstar;
-  if (mode == 0) {
-    float v = -INFINITY;
-    int32_t vi = 0x7fffffff;
-    for (int j = threadIdx.x; j < k; j += blockDim.x) argmax_merge(v, vi, z[j], j);
-    wave_argmax(v, vi);
+  int32_t jstar = 0;
+  if (w == 0) {
+    if (mode == 0) {
+      float v = -INFINITY;
+      int32_t vi = 0x7fffffff;
+      for (int j = l; j < k; j += kWave) argmax_merge(v, vi, zl[j], j);
+      wave_argmax(v, vi);
+      jstar = vi;
+    } else {
+      // group scores: log of the group sum (natural units) + Gumbel(u_g), all groups at once
+      float best = -INFINITY;
+      int32_t bg = 0x7fffffff;
+      for (int g = l; g < ng; g += kWave) {
+        const float gs = Lg[g];
+        if (gs > 0.f) {
+          const float L = (mxc + log2f(gs)) * kLn2;
+          argmax_merge(best, bg, L + gumbel(philox_uniform(seed, offset, kDraftGroup, m, g)), g);
+        }
+      }
+      wave_argmax(best, bg);
+      const int j = bg * kGroup + l;
+      const bool valid = bg != 0x7fffffff && j < k;
+      float e = valid ? zl[j] * invT + gumbel(philox_uniform(seed, offset, kDraftElem, m, j)) : -INFINITY;
+      int32_t ei = valid ? j : 0x7fffffff;
+      wave_argmax(e, ei);
+      jstar = ei;
+    }
+    if (jstar < 0 || jstar >= k) jstar = 0;   // only if every candidate score were -inf
     if (l == 0) {
-      red_f[w] = v;
-      red_i[w] = vi;
+      token[m] = idx[static_cast<size_t>(m) * k + jstar];
+      if (lse_out) lse_out[m] = lse;
+      if (logprob) logprob[m] = zl[jstar] * invT - lse;
     }
-    __syncthreads();
-    v = red_f[0];
-    vi = red_i[0];
-    for (int i = 1; i < 4; ++i) argmax_merge(v, vi, red_f[i], red_i[i]);
-    jstar = vi;
-  } else {
-    const int ng = (k + kGroup - 1) / kGroup;
-    float best = -INFINITY;
-    int32_t bg = 0x7fffffff;
-    for (int g = w; g < ng; g += 4) {
-      const int j = g * kGroup + l;
-      const bool valid = j < k;
-      const float y = valid ? z[j] * invT : -INFINITY;
-      const float gm = wave_max(y);
-      const float gs = wave_sum(valid ? __expf(y - gm) : 0.f);
-      const float L = gm + logf(gs);
-      const float sc = L + gumbel(philox_uniform(seed, offset, kDraftGroup, m, g));
-      argmax_merge(best, bg, sc, g);
-    }
-    if (l == 0) {
-      red_f[w] = best;
-      red_i[w] = bg;
-    }
-    __syncthreads();
-    best = red_f[0];
-    bg = red_i[0];
-    for (int i = 1; i < 4; ++i) argmax_merge(best, bg, red_f[i], red_i[i]);
-    const int j = bg * kGroup + l;
-    const bool valid = j < k;
-    float e = valid ? z[j] * invT + gumbel(philox_uniform(seed, offset, kDraftElem, m, j)) : -INFINITY;
-    int32_t ei = valid ? j : 0x7fffffff;
-    wave_argmax(e, ei);
-    jstar = ei;
-  }
-  if (jstar < 0 || jstar >= k) jstar = 0;   // only if every candidate score were -inf
-  if (threadIdx.x == 0) {
-    token[m] = idx[static_cast<size_t>(m) * k + jstar];
-    if (lse_out) lse_out[m] = lse;
-    if (logprob) logprob[m] = z[jstar] * invT - lse;
   }
 }
 
@@ -499,9 +519,13 @@ hipError_t launch_gather_finalize(const float* zbuf, const int32_t* idx, int64_t
                                   int mode, float invT, uint64_t seed, uint64_t offset,
                                   float* topk_logit, float* topk_prob, int32_t* token, float* lse,
                                   float* logprob, hipStream_t st) {
+  const int lds = static_cast<int>((k + (k + kGroup - 1) / kGroup) * 4);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_gather_finalize),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (e != hipSuccess) return e;
   TraceScope ts("gather_finalize", st);
-  hipLaunchKernelGGL(k_gather_finalize, dim3(static_cast<unsigned>(M)), dim3(256), 0, st, zbuf, idx,
-                     static_cast<int>(k), mode, invT, seed, offset, topk_logit, topk_prob, token,
+  hipLaunchKernelGGL(k_gather_finalize, dim3(static_cast<unsigned>(M)), dim3(kGfThreads), lds, st, zbuf,
+                     idx, static_cast<int>(k), mode, invT, seed, offset, topk_logit, topk_prob, token,
                      lse, logprob);
   return hipGetLastError();
 }
