@@ -54,13 +54,11 @@ __device__ __forceinline__ Partial partial_empty() {
 }
 
 __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
+  // branch-free: both exponentials are NaN only when both maxima are -inf, and then the
+  // select discards them
   const float mn = fmaxf(m, m2);
-  if (mn == -INFINITY) {
-    m = mn;
-    s = 0.f;
-    return;
-  }
-  s = s * __expf(m - mn) + s2 * __expf(m2 - mn);
+  const float a = __expf(m - mn), b = __expf(m2 - mn);
+  s = mn == -INFINITY ? 0.f : s * a + s2 * b;
   m = mn;
 }
 

@@ -910,10 +910,39 @@ constexpr int kFinWaves = kFinThreads / kWave;
 constexpr int kFinPerThread = (kMaxPartials + kFinThreads - 1) / kFinThreads;
 constexpr int kFinRowsPerWave = kGroup / kFinWaves;   // 4
 
+// (m, s) log-sum-exp pairs and (value, index) argmax pairs of the kFinWaves waves, written to
+// LDS by lane 0 of each wave, merged by every wave at once: lane i takes pair i, a butterfly
+// over kFinWaves lanes, and lane 0's result (the same in every wave) is returned.
+__device__ __forceinline__ void fin_merge_waves(const float* rm, const float* rs, const float* rb,
+                                                const int32_t* ri, float& m, float& s, float& b,
+                                                int32_t& bi) {
+  const int l = lane_id();
+  m = -INFINITY;
+  s = 0.f;
+  b = -INFINITY;
+  bi = 0x7fffffff;
+  if (l < kFinWaves) {
+    m = rm[l];
+    s = rs[l];
+    b = rb[l];
+    bi = ri[l];
+  }
+#pragma unroll
+  for (int o = 1; o < kFinWaves; o <<= 1) {
+    const float m2 = xor_lane(m, o), s2 = xor_lane(s, o), b2 = xor_lane(b, o);
+    const int32_t i2 = xor_lane(bi, o);
+    lse_merge(m, s, m2, s2);
+    argmax_merge(b, bi, b2, i2);
+  }
+  m = __shfl(m, 0);
+  s = __shfl(s, 0);
+  b = __shfl(b, 0);
+  bi = __shfl(bi, 0);
+}
+
 template <bool BF16>
 __global__ __launch_bounds__(kFinThreads) void k_head_finalize(FinalizeArgs f) {
-  __shared__ float redf[kFinWaves];
-  __shared__ float redf2[kFinWaves];
+  __shared__ float redm[kFinWaves], reds[kFinWaves], redb[kFinWaves];
   __shared__ int32_t redi[kFinWaves];
   __shared__ float zs[kGroup];
   const int m = blockIdx.x;
@@ -922,10 +951,22 @@ __global__ __launch_bounds__(kFinThreads) void k_head_finalize(FinalizeArgs f) {
   const bool want_lse = f.lse != nullptr || f.logprob != nullptr || f.mode == 1;
   const float* lgr = f.lg + static_cast<int64_t>(m) * f.lg_ld;
 
+  // (greedy) this thread's argmax partials, loaded before anything else
+  float bv = -INFINITY;
+  int32_t bi = 0x7fffffff;
+  if (f.mode == 0) {
+    const Partial* pp = f.partials + static_cast<int64_t>(m) * f.partials_ld;
+#pragma unroll
+    for (int i = 0; i < kFinPerThread; ++i) {
+      const int idx = threadIdx.x + i * kFinThreads;
+      if (idx < f.P) {
+        const float2 zz = *reinterpret_cast<const float2*>(&pp[idx].zmax);
+        argmax_merge(bv, bi, zz.x, __float_as_int(zz.y));
+      }
+    }
+  }
   // ---- row lse and (sampling) the group scores, four groups per thread per pass
   float lmx = -INFINITY, lsm = 0.f;
-  float best = -INFINITY;
-  int32_t bg = 0x7fffffff;
   if (want_lse) {
     for (int q = threadIdx.x; q * 4 < NG; q += kFinThreads) {
       const float4 L4 = reinterpret_cast<const float4*>(lgr)[q];   // rows padded to 4 groups
@@ -943,61 +984,36 @@ __global__ __launch_bounds__(kFinThreads) void k_head_finalize(FinalizeArgs f) {
         philox_block(f.seed, f.offset, kDraftGroup, static_cast<uint64_t>(m), static_cast<uint64_t>(q) * 4, words);
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          if (q * 4 + j < NG && L[j] != -INFINITY)
-            argmax_merge(best, bg, L[j] + gumbel(word_to_uniform(words[j])), q * 4 + j);
+          if (L[j] != -INFINITY) argmax_merge(bv, bi, L[j] + gumbel(word_to_uniform(words[j])), q * 4 + j);
       }
     }
-#pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) {
-      const float m2 = xor_lane(lmx, s), s2 = xor_lane(lsm, s);
-      lse_merge(lmx, lsm, m2, s2);
-      const float b2 = xor_lane(best, s);
-      const int32_t i2 = xor_lane(bg, s);
-      argmax_merge(best, bg, b2, i2);
-    }
-    if (l == 0) {
-      redf[w] = lmx;
-      redf2[w] = lsm;
-    }
-    __syncthreads();
-    lmx = redf[0];
-    lsm = redf2[0];
-    for (int i = 1; i < kFinWaves; ++i) lse_merge(lmx, lsm, redf[i], redf2[i]);
-    __syncthreads();
   }
+  // one butterfly per wave, one LDS exchange, one parallel merge of the waves
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) {
+    const float m2 = xor_lane(lmx, s), s2 = xor_lane(lsm, s);
+    lse_merge(lmx, lsm, m2, s2);
+    const float b2 = xor_lane(bv, s);
+    const int32_t i2 = xor_lane(bi, s);
+    argmax_merge(bv, bi, b2, i2);
+  }
+  if (l == 0) {
+    redm[w] = lmx;
+    reds[w] = lsm;
+    redb[w] = bv;
+    redi[w] = bi;
+  }
+  __syncthreads();
+  fin_merge_waves(redm, reds, redb, redi, lmx, lsm, bv, bi);
   const float lse = lmx + logf(lsm);
 
   int32_t tok;
   float ytok;
   if (f.mode == 0) {
-    const Partial* pp = f.partials + static_cast<int64_t>(m) * f.partials_ld;
-    float z = -INFINITY;
-    int32_t zi = 0x7fffffff;
-#pragma unroll
-    for (int i = 0; i < kFinPerThread; ++i) {
-      const int idx = threadIdx.x + i * kFinThreads;
-      if (idx < f.P) argmax_merge(z, zi, pp[idx].zmax, pp[idx].zid);
-    }
-    wave_argmax(z, zi);
-    if (l == 0) {
-      redf[w] = z;
-      redi[w] = zi;
-    }
-    __syncthreads();
-    z = redf[0];
-    zi = redi[0];
-    for (int i = 1; i < kFinWaves; ++i) argmax_merge(z, zi, redf[i], redi[i]);
-    tok = zi;
-    ytok = z * f.invT;
+    tok = bi;
+    ytok = bv * f.invT;
   } else {
-    if (l == 0) {
-      redf[w] = best;
-      redi[w] = bg;
-    }
-    __syncthreads();
-    best = redf[0];
-    bg = redi[0];
-    for (int i = 1; i < kFinWaves; ++i) argmax_merge(best, bg, redf[i], redi[i]);
+    const int32_t bg = bi;
     // recompute the 64 logits of the winning group (4 rows per wave, loads issued together)
     const int C = static_cast<int>(f.K * (BF16 ? 2 : 4) / 16);
     const int CPL = (C + kWave - 1) / kWave;
@@ -1033,6 +1049,7 @@ __global__ __launch_bounds__(kFinThreads) void k_head_finalize(FinalizeArgs f) {
       if (l == 0) zs[w * kFinRowsPerWave + j] = t;
     }
     __syncthreads();
+    if (w != 0) return;   // the element draw is one wave's work
     const int64_t row = gbase + l;
     const bool valid = row < f.V;
     const float y = zs[l] * f.invT;
