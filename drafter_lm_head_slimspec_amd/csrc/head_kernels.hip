@@ -4,8 +4,10 @@
 //                   section 三) and the SpecVocab d -> d' map (SpecVocab write-up, 2.2.1).
 //   k_stream_valu   skinny head product (M <= 8 rows): coalesced 16-byte weight streaming,
 //                   one 64-row vocabulary group per wave at a time.
-//   k_stream_mfma   the same contract once the rows make the product dense (M > 8):
-//                   v_mfma_f32_32x32x16_bf16, weights HBM -> VGPR, activations in LDS.
+//   k_stream_mfma16 the same contract once the rows make the product dense (M > 8):
+//                   v_mfma_f32_16x16x32_bf16, weights HBM -> VGPR, activations in LDS
+//                   (staged whole, or in K chunks for large d).
+//   k_stream_mfma   32x32x16 variant, faster for 17..64 rows with small d.
 //   k_head_finalize per row: argmax from the per-workgroup partials (greedy), or the row
 //                   lse and the two-level draw from the per-group log-sum-exps (sampling).
 //
@@ -478,28 +480,31 @@ __global__ __launch_bounds__(256) void k_stream_valu(StreamArgs a) {
 }
 
 // ----------------------------------------------------------------------------------------
-// k_stream_mfma2: bf16, M <= 32*NCB rows, NCB <= 2.  Each wave walks its 64-row vocabulary
-// groups with v_mfma_f32_32x32x16_bf16, both 32-row tiles of a group at once so that each activation
-// (B) fragment is read once per k-step for 64 vocabulary rows.  A = weight fragments from HBM
-// straight into registers, KB k-steps per batch, one batch ahead; the prefetch runs across
-// group boundaries, and the first batch is issued before the activations are staged.
-//   BG = false: B comes from LDS, staged once per workgroup and pre-swizzled into fragment
-//               order [k-step][column block][lane] (one conflict-free 16-byte read per lane).
-//   BG = true:  the activations do not fit in LDS (large K): each lane loads its B fragment
-//               directly from the (L2-resident) activation rows.
-// Output layout of a 32x32 tile: lane l holds column l%32 and rows
-// 8*(v/4) + 4*(l/32) + v%4 for its 16 accumulators v (increasing in v).
+// k_stream_mfma16: bf16, M <= 16*NCB rows.  Built on v_mfma_f32_16x16x32_bf16: per 32-wide
+// k-step a wave multiplies the four 16-row weight tiles of its 64-row vocabulary group (A,
+// straight from HBM: one 16-byte load per lane per tile covers 16 rows x 64 contiguous
+// bytes) by NCB 16-row activation tiles (B, pre-swizzled in LDS as [k-step][tile][lane], one
+// conflict-free 16-byte read per lane).  Output tile layout: lane l holds column l % 16
+// (an activation row m) for the 4 weight rows 4*(l/16) + v of each tile.
+//   CHUNKED = false: all K fits in LDS; fragments are staged once, waves walk their groups
+//                    independently with the weight loads one batch ahead across groups.
+//   CHUNKED = true:  K is staged in chunks of kch k-steps; the workgroup restages per chunk
+//                    (uniform trip counts, every wave takes part in every barrier).
+// The epilogue folds each group into the row's group log-sum-exp L_g and argmax, as in the
+// VALU kernel.
 // ----------------------------------------------------------------------------------------
-template <int NCB, bool BG>
-__global__ __launch_bounds__(256, 2) void k_stream_mfma2(StreamArgs a) {
-  constexpr int KB = 4;
-  extern __shared__ uint4 bs[];  // [KS][NCB][64] 16-byte B fragments, later Partial records
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+template <int NCB, bool CHUNKED>
+__global__ __launch_bounds__(256, NCB <= 3 ? 3 : 1) void k_stream_mfma16(StreamArgs a, int kch) {
+  // k-steps per load batch: 8 loads per lane in flight, 4 when the accumulators are large
+  constexpr int kM16KB = NCB <= 8 ? 2 : 1;
+  extern __shared__ uint4 bs[];   // [kch][NCB][64] fragments; Partial records at the end
   const int l = lane_id(), w = wave_id();
   const int NW = blockDim.x / kWave;
-  const int n = l & 31, hf = l >> 5;
+  const int col = l & 15, qd = l >> 4;
   const int K = static_cast<int>(a.K);
-  const int KS = (K + 15) / 16;
-  const int nb = (KS + KB - 1) / KB;
+  const int KS = (K + 31) / 32;
   const uint32_t rowbytes = static_cast<uint32_t>(K) * 2;
   const int V32 = static_cast<int>(a.V);
   const int NG = (V32 + kGroup - 1) / kGroup;
@@ -509,196 +514,213 @@ __global__ __launch_bounds__(256, 2) void k_stream_mfma2(StreamArgs a) {
   const float c2 = a.invT * kLog2e;
   const rsrc_t xrs = make_rsrc(a.x, static_cast<uint32_t>(Mx) * rowbytes);
 
-  float run_z[NCB];             // running argmax of column m = cb*32 + n
+  float run_z[NCB];
   int32_t run_i[NCB];
-  f32x16_t acc0[NCB], acc1[NCB];
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) {
     run_z[cb] = -INFINITY;
     run_i[cb] = 0x7fffffff;
   }
+  f32x4_t acc[4][NCB];
 
-  // batch b of group g: KB k-steps of both tiles (X0: rows 0..31, X1: rows 32..63)
-  auto load_batch = [&](int g, int b, uint4 (&X0)[KB], uint4 (&X1)[KB], uint4 (&Y)[KB][NCB]) {
+  auto group_rsrc = [&](int g) {
     const int g0 = g * kGroup;
     const int rows = V32 - g0 < kGroup ? V32 - g0 : kGroup;
-    const rsrc_t rs = make_rsrc(Wb + static_cast<size_t>(g0) * rowbytes, static_cast<uint32_t>(rows) * rowbytes);
-    const uint32_t rb0 = static_cast<uint32_t>(n) * rowbytes;
-    const uint32_t rb1 = static_cast<uint32_t>(32 + n) * rowbytes;
+    return make_rsrc(Wb + static_cast<size_t>(g0) * rowbytes, static_cast<uint32_t>(rows) * rowbytes);
+  };
+  auto load_batch = [&](const rsrc_t& rs, int ks0, uint4 (&X)[kM16KB][4]) {
 #pragma unroll
-    for (int j = 0; j < KB; ++j) {
-      const int ks = b * KB + j;
-      const int k = ks * 16 + hf * 8;
-      const bool kok = ks < KS && k < K;
-      X0[j] = buffer_load16(rs, kok ? rb0 + static_cast<uint32_t>(k) * 2 : kOutOfRange);
-      X1[j] = buffer_load16(rs, kok ? rb1 + static_cast<uint32_t>(k) * 2 : kOutOfRange);
-      if constexpr (BG) {
+    for (int j = 0; j < kM16KB; ++j) {
+      const int k = (ks0 + j) * 32 + qd * 8;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        X[j][t] = buffer_load16(rs, k < K ? static_cast<uint32_t>(t * 16 + col) * rowbytes + static_cast<uint32_t>(k) * 2
+                                          : kOutOfRange);
+    }
+  };
+  // B fragments of k-steps [ks0, ks0 + nks): item (kk, cb, lane) -> bs[(kk * NCB + cb) * 64 + lane]
+  auto stage = [&](int ks0, int nks) {
+    stage16<8>(bs, nks * NCB * kWave, [&](int it) {
+      if (it < 0) return buffer_load16(xrs, kOutOfRange);
+      const int kk = it / (NCB * kWave);
+      const int cb = (it / kWave) % NCB;
+      const int ll = it & (kWave - 1);
+      const int m = cb * 16 + (ll & 15);
+      const int k = (ks0 + kk) * 32 + (ll >> 4) * 8;
+      return buffer_load16(xrs, (m < Mx && k < K) ? static_cast<uint32_t>(m) * rowbytes + static_cast<uint32_t>(k) * 2
+                                                  : kOutOfRange);
+    });
+  };
+  auto zero_acc = [&]() {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) acc[t][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  };
+  // k-steps [ks0, ks0 + kM16KB) of a batch; kk0 = index of ks0 inside the staged chunk
+  auto mma_batch = [&](const uint4 (&X)[kM16KB][4], int ks0, int kk0, int ks_end) {
+#pragma unroll
+    for (int j = 0; j < kM16KB; ++j) {
+      if (ks0 + j < ks_end) {
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
-          const int m = cb * 32 + n;
-          Y[j][cb] = buffer_load16(xrs, (kok && m < Mx) ? static_cast<uint32_t>(m) * rowbytes + static_cast<uint32_t>(k) * 2
-                                                        : kOutOfRange);
+          const bf16x8_t bf = __builtin_bit_cast(bf16x8_t, bs[((kk0 + j) * NCB + cb) * kWave + l]);
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            acc[t][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, X[j][t]), bf,
+                                                                 acc[t][cb], 0, 0, 0);
         }
       }
     }
   };
-
-  // fold the group's 64 rows (two tiles) into the statistics of each column
   auto epilogue = [&](int g) {
     const int gbase = g * kGroup;
     const bool full = gbase + kGroup <= V32;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
-      const int m = cb * 32 + n;
+      const int m = cb * 16 + col;
+      float vals[16];
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) vals[t * 4 + v] = acc[t][cb][v];
       if (!full) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int r = 8 * (v >> 2) + 4 * hf + (v & 3);
-          if (gbase + r >= V32) acc0[cb][v] = -INFINITY;
-          if (gbase + 32 + r >= V32) acc1[cb][v] = -INFINITY;
+        for (int i = 0; i < 16; ++i)
+          if (gbase + (i >> 2) * 16 + qd * 4 + (i & 3) >= V32) vals[i] = -INFINITY;
+      }
+      if (a.zout != nullptr && m < Mx) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int row = gbase + (i >> 2) * 16 + qd * 4 + (i & 3);
+          if (row < V32) a.zout[static_cast<int64_t>(m) * a.zout_ld + row] = vals[i];
         }
       }
-      if (a.zout != nullptr && m < a.M) {
+      float zm = vals[0];
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int r = gbase + 8 * (v >> 2) + 4 * hf + (v & 3);
-          if (r < V32) a.zout[static_cast<int64_t>(m) * a.zout_ld + r] = acc0[cb][v];
-          if (r + 32 < V32) a.zout[static_cast<int64_t>(m) * a.zout_ld + r + 32] = acc1[cb][v];
-        }
-      }
-      float zm = acc0[cb][0];
-#pragma unroll
-      for (int v = 1; v < 16; ++v) zm = fmaxf(zm, acc0[cb][v]);
-#pragma unroll
-      for (int v = 0; v < 16; ++v) zm = fmaxf(zm, acc1[cb][v]);
-      int32_t zi = 0x7fffffff;
-      if (a.want_argmax) {
-        // lowest row holding zm: tile 0 rows come first, and rows grow with v in a tile
-        int bv = 32;
-#pragma unroll
-        for (int v = 15; v >= 0; --v)
-          if (acc1[cb][v] == zm) bv = 16 + v;
-#pragma unroll
-        for (int v = 15; v >= 0; --v)
-          if (acc0[cb][v] == zm) bv = v;
-        const int vv = bv & 15;
-        zi = (zm == -INFINITY) ? 0x7fffffff : gbase + (bv >> 4) * 32 + 8 * (vv >> 2) + 4 * hf + (vv & 3);
-      }
+      for (int i = 1; i < 16; ++i) zm = fmaxf(zm, vals[i]);
       float ss = 0.f;
       if (a.lg != nullptr && zm != -INFINITY) {
         const float off = zm * c2;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) ss += fast_exp2(fmaf(acc0[cb][v], c2, -off)) + fast_exp2(fmaf(acc1[cb][v], c2, -off));
+        for (int i = 0; i < 16; ++i) ss += fast_exp2(fmaf(vals[i], c2, -off));
       }
-      // merge with the other 32 rows of the column (lane l ^ 32)
-      const float zm2 = xor_lane(zm, 32), ss2 = xor_lane(ss, 32);
-      const int32_t zi2 = xor_lane(zi, 32);
-      const float gmx = fmaxf(zm, zm2);
-      float gsm = 0.f;
-      if (gmx != -INFINITY) gsm = ss * fast_exp2((zm - gmx) * c2) + ss2 * fast_exp2((zm2 - gmx) * c2);
-      argmax_merge(zm, zi, zm2, zi2);
-      if (m < a.M) {
-        if (a.lg != nullptr && hf == 0) a.lg[static_cast<int64_t>(m) * a.lg_ld + g] = gmx * a.invT + log2f(gsm) * kLn2;
+      int32_t zi = 0x7fffffff;
+      if (a.want_argmax) {
+        int bi = 15;
+#pragma unroll
+        for (int i = 15; i >= 0; --i)   // the lane's rows rise with i: keep the lowest
+          if (vals[i] == zm) bi = i;
+        zi = zm == -INFINITY ? 0x7fffffff : gbase + (bi >> 2) * 16 + qd * 4 + (bi & 3);
+      }
+      // the four lanes col, col + 16, col + 32, col + 48 hold the group's 64 rows of column m
+#pragma unroll
+      for (int o = 16; o <= 32; o <<= 1) {
+        const float zm2 = xor_lane(zm, o), ss2 = xor_lane(ss, o);
+        const float mx = fmaxf(zm, zm2);
+        if (a.lg != nullptr)
+          ss = mx == -INFINITY ? 0.f : ss * fast_exp2((zm - mx) * c2) + ss2 * fast_exp2((zm2 - mx) * c2);
+        if (a.want_argmax) {
+          const int32_t zi2 = xor_lane(zi, o);
+          argmax_merge(zm, zi, zm2, zi2);
+        }
+        zm = mx;
+      }
+      if (m < Mx) {
+        if (a.lg != nullptr && qd == 0) a.lg[static_cast<int64_t>(m) * a.lg_ld + g] = zm * a.invT + log2f(ss) * kLn2;
         if (a.want_argmax) argmax_merge(run_z[cb], run_i[cb], zm, zi);
       }
     }
   };
 
-  int g = static_cast<int>(blockIdx.x) * NW + w;
-  int b = 0;
-  uint4 XA0[KB], XA1[KB], XB0[KB], XB1[KB];
-  uint4 YA[KB][NCB], YB[KB][NCB];
-  if (g < NG) load_batch(g, 0, XA0, XA1, YA);   // in flight while the activations are staged
-
-  if constexpr (!BG) {
-    stage16<8>(bs, KS * NCB * kWave, [&](int it) {
-      if (it < 0) return buffer_load16(xrs, kOutOfRange);
-      const int ks = it / (NCB * kWave);
-      const int cb = (it / kWave) % NCB;
-      const int ll = it & (kWave - 1);
-      const int m = cb * 32 + (ll & 31);
-      const int k = ks * 16 + (ll >> 5) * 8;
-      return buffer_load16(xrs, (m < Mx && k < K) ? static_cast<uint32_t>(m) * rowbytes + static_cast<uint32_t>(k) * 2
-                                                  : kOutOfRange);
-    });
+  const int gw = static_cast<int>(blockIdx.x) * NW + w;
+  if constexpr (!CHUNKED) {
+    const int nb = (KS + kM16KB - 1) / kM16KB;
+    uint4 XA[kM16KB][4], XB[kM16KB][4];
+    int g = gw, b = 0;
+    rsrc_t rs = group_rsrc(g < NG ? g : 0);
+    if (g < NG) load_batch(rs, 0, XA);
+    stage(0, KS);
     __syncthreads();
-  }
-
-  // one pipeline step: prefetch the next batch into F*, consume U*.  The prefetch is
-  // unconditional (re-reads the current, cache-resident batch at the very end).
-  auto step = [&](uint4 (&U0)[KB], uint4 (&U1)[KB], uint4 (&UY)[KB][NCB], uint4 (&F0)[KB], uint4 (&F1)[KB],
-                  uint4 (&FY)[KB][NCB]) -> bool {
-    int g2 = g, b2 = b + 1;
-    if (b2 == nb) {
-      b2 = 0;
-      g2 = g + nwt;
-    }
-    if (g2 < NG)
-      load_batch(g2, b2, F0, F1, FY);
-    else
-      load_batch(g, b, F0, F1, FY);
-    if (b == 0) {
-#pragma unroll
-      for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          acc0[cb][v] = 0.f;
-          acc1[cb][v] = 0.f;
-        }
-    }
-#pragma unroll
-    for (int j = 0; j < KB; ++j) {
-      const int ks = b * KB + j;
-      if (ks < KS) {
-        const bf16x8_t a0f = __builtin_bit_cast(bf16x8_t, U0[j]);
-        const bf16x8_t a1f = __builtin_bit_cast(bf16x8_t, U1[j]);
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) {
-          const uint4 bv = BG ? UY[j][cb] : bs[(ks * NCB + cb) * kWave + l];
-          const bf16x8_t bf = __builtin_bit_cast(bf16x8_t, bv);
-          acc0[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0f, bf, acc0[cb], 0, 0, 0);
-          acc1[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1f, bf, acc1[cb], 0, 0, 0);
-        }
+    // one step consumes batch b of group g from U while batch b+1 (or the next group's
+    // first) lands in F; past the wave's last group the current batch is re-read
+    auto step = [&](uint4 (&U)[kM16KB][4], uint4 (&F)[kM16KB][4]) -> bool {
+      int g2 = g, b2 = b + 1;
+      if (b2 == nb) {
+        b2 = 0;
+        g2 = g + nwt;
+      }
+      const rsrc_t rs2 = g2 < NG ? group_rsrc(g2) : rs;
+      load_batch(rs2, g2 < NG ? b2 * kM16KB : b * kM16KB, F);
+      if (b == 0) zero_acc();
+      mma_batch(U, b * kM16KB, b * kM16KB, KS);
+      if (b == nb - 1) epilogue(g);
+      g = g2;
+      b = b2;
+      rs = rs2;
+      return g < NG;
+    };
+    if (g < NG) {
+      for (;;) {
+        if (!step(XA, XB)) break;
+        if (!step(XB, XA)) break;
       }
     }
-    if (b == nb - 1) epilogue(g);
-    g = g2;
-    b = b2;
-    return g < NG;
-  };
-  if (g < NG) {
-    for (;;) {
-      if (!step(XA0, XA1, YA, XB0, XB1, YB)) break;
-      if (!step(XB0, XB1, YB, XA0, XA1, YA)) break;
+  } else {
+    const int iters = (NG + nwt - 1) / nwt;
+    for (int it = 0; it < iters; ++it) {
+      const int g = gw + it * nwt;
+      const bool valid = g < NG;
+      const rsrc_t rs = group_rsrc(valid ? g : 0);
+      zero_acc();
+      for (int c0 = 0; c0 < KS; c0 += kch) {
+        const int nks = KS - c0 < kch ? KS - c0 : kch;
+        uint4 XA[kM16KB][4], XB[kM16KB][4];
+        if (valid) load_batch(rs, c0, XA);
+        __syncthreads();   // the previous chunk's fragments are no longer read
+        stage(c0, nks);
+        __syncthreads();
+        if (valid) {
+          for (int kk = 0; kk < nks; kk += 2 * kM16KB) {
+            load_batch(rs, c0 + kk + kM16KB, XB);
+            mma_batch(XA, c0 + kk, kk, c0 + nks);
+            load_batch(rs, c0 + kk + 2 * kM16KB, XA);
+            mma_batch(XB, c0 + kk + kM16KB, kk + kM16KB, c0 + nks);
+          }
+        }
+      }
+      if (valid) epilogue(g);
     }
   }
   if (!a.want_argmax) return;
   __syncthreads();
   Partial* rec = reinterpret_cast<Partial*>(bs);
-  if (hf == 0) {
+  if (qd == 0) {
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
-      const int m = cb * 32 + n;
-      if (m < a.M) {
+      const int m = cb * 16 + col;
+      if (m < Mx) {
         Partial p = partial_empty();
         p.zmax = run_z[cb];
         p.zid = run_i[cb];
-        rec[w * a.M + m] = p;
+        rec[w * Mx + m] = p;
       }
     }
   }
   __syncthreads();
-  for (int m = threadIdx.x; m < a.M; m += blockDim.x) {
+  for (int m = threadIdx.x; m < Mx; m += blockDim.x) {
     Partial p = rec[m];
-    for (int i = 1; i < NW; ++i) argmax_merge(p.zmax, p.zid, rec[i * a.M + m].zmax, rec[i * a.M + m].zid);
+    for (int i = 1; i < NW; ++i) argmax_merge(p.zmax, p.zid, rec[i * Mx + m].zmax, rec[i * Mx + m].zid);
     a.partials[static_cast<int64_t>(m) * a.partials_ld + blockIdx.x] = p;
   }
 }
 
 // ----------------------------------------------------------------------------------------
-// k_stream_mfma: the same contract for 3..6 column blocks, where two tiles of accumulators do
-// not fit next to the prefetch buffers: the group's two 32-row tiles are computed one after
-// the other (the prefetch still runs one batch ahead across tile and group boundaries).
+// k_stream_mfma: the same contract on v_mfma_f32_32x32x16_bf16 for 17..64 rows (NCB column
+// blocks of 32) whose fragments fit in LDS.  Each load reads 32 rows x 32 bytes; the eight
+// k-steps of a batch complete every 128-byte line they touch.  The group's two 32-row tiles
+// are computed one after the other, with the weight loads one batch ahead across tile and
+// group boundaries.
 // ----------------------------------------------------------------------------------------
 template <int NCB, bool BG>
 __global__ __launch_bounds__(256) void k_stream_mfma(StreamArgs a) {
@@ -1186,34 +1208,45 @@ static hipError_t dispatch_mb(const StreamArgs& a, int lpr, bool one, int grid, 
 }
 
 template <int NCB>
-static hipError_t run_mfma(const StreamArgs& a, int grid, bool bg, hipStream_t st) {
+static hipError_t run_mfma(const StreamArgs& a, int grid, hipStream_t st) {
   const int nw = 4;
   const int rec = nw * a.M * static_cast<int>(sizeof(Partial));
   const int KS = static_cast<int>((a.K + 15) / 16);
-  const int frag = bg ? 0 : KS * NCB * 1024;
+  const int frag = KS * NCB * 1024;
   const int bytes = frag > rec ? frag : rec;
-  hipError_t e;
   TraceScope ts("stream_mfma", st);
-  // Weights and fragments both from global memory: computing the group's two tiles together
-  // halves the fragment loads per weight byte.  With fragments in LDS the sequential form is
-  // faster (fewer live registers, deeper weight batches).
-  if constexpr (NCB <= 2) {
-    if (bg) {
-      e = allow_lds(k_stream_mfma2<NCB, true>, bytes);
-      if (e != hipSuccess) return e;
-      hipLaunchKernelGGL((k_stream_mfma2<NCB, true>), dim3(grid), dim3(nw * kWave), bytes, st, a);
-    } else {
-      e = allow_lds(k_stream_mfma<NCB, false>, bytes);
-      if (e != hipSuccess) return e;
-      hipLaunchKernelGGL((k_stream_mfma<NCB, false>), dim3(grid), dim3(nw * kWave), bytes, st, a);
-    }
-  } else {
-    e = bg ? allow_lds(k_stream_mfma<NCB, true>, bytes) : allow_lds(k_stream_mfma<NCB, false>, bytes);
+  hipError_t e = allow_lds(k_stream_mfma<NCB, false>, bytes);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((k_stream_mfma<NCB, false>), dim3(grid), dim3(nw * kWave), bytes, st, a);
+  return hipGetLastError();
+}
+
+// Fragments of the whole K are staged once when they take at most kM16Resident bytes (two
+// workgroups per CU); larger K is staged in chunks of at most kM16Chunk bytes.
+constexpr int kM16Resident = 80 * 1024;
+constexpr int kM16Chunk = 64 * 1024;
+
+template <int NCB>
+static hipError_t run_mfma16(const StreamArgs& a, int grid, hipStream_t st) {
+  const int nw = 4;
+  const int KS = static_cast<int>((a.K + 31) / 32);
+  const int rec = nw * a.M * static_cast<int>(sizeof(Partial));
+  const int per_ks = NCB * kWave * 16;
+  const bool chunked = KS * per_ks > kM16Resident;
+  int kch = chunked ? kM16Chunk / per_ks : KS;
+  if (kch < 1) kch = 1;
+  const int frag = kch * per_ks;
+  const int bytes = frag > rec ? frag : rec;
+  TraceScope ts("stream_mfma", st);
+  hipError_t e;
+  if (chunked) {
+    e = allow_lds(k_stream_mfma16<NCB, true>, bytes);
     if (e != hipSuccess) return e;
-    if (bg)
-      hipLaunchKernelGGL((k_stream_mfma<NCB, true>), dim3(grid), dim3(nw * kWave), bytes, st, a);
-    else
-      hipLaunchKernelGGL((k_stream_mfma<NCB, false>), dim3(grid), dim3(nw * kWave), bytes, st, a);
+    hipLaunchKernelGGL((k_stream_mfma16<NCB, true>), dim3(grid), dim3(nw * kWave), bytes, st, a, kch);
+  } else {
+    e = allow_lds(k_stream_mfma16<NCB, false>, bytes);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((k_stream_mfma16<NCB, false>), dim3(grid), dim3(nw * kWave), bytes, st, a, kch);
   }
   return hipGetLastError();
 }
@@ -1240,16 +1273,26 @@ hipError_t launch_stream(const StreamArgs& a, bool use_mfma, int* producers, hip
     return a.bf16 ? dispatch_mb<true>(a, lpr, one, static_cast<int>(grid), lds, st)
                   : dispatch_mb<false>(a, lpr, one, static_cast<int>(grid), lds, st);
   }
-  const int ncb = (a.M + 31) / 32;
-  const int KS = static_cast<int>((a.K + 15) / 16);
-  const bool bg = static_cast<int64_t>(KS) * ncb * 1024 > di.max_lds;
+  // Measured on MI355X: for 17..64 rows whose 32x32 fragments fit in LDS the 32x32x16 kernel
+  // (32 rows x 32 bytes per load, four loads completing each 128-byte line in one batch) is
+  // the faster one; otherwise the 16x16x32 kernel.
+  const int KS16 = static_cast<int>((a.K + 15) / 16);
+  if (a.M > 16 && a.M <= 64 && static_cast<int64_t>(KS16) * ((a.M + 31) / 32) * 1024 <= di.max_lds)
+    return a.M <= 32 ? run_mfma<1>(a, static_cast<int>(grid), st) : run_mfma<2>(a, static_cast<int>(grid), st);
+  const int ncb = (a.M + 15) / 16;
   switch (ncb) {
-    case 1: return run_mfma<1>(a, static_cast<int>(grid), bg, st);
-    case 2: return run_mfma<2>(a, static_cast<int>(grid), bg, st);
-    case 3: return run_mfma<3>(a, static_cast<int>(grid), bg, st);
-    case 4: return run_mfma<4>(a, static_cast<int>(grid), bg, st);
-    case 5: return run_mfma<5>(a, static_cast<int>(grid), bg, st);
-    case 6: return run_mfma<6>(a, static_cast<int>(grid), bg, st);
+    case 1: return run_mfma16<1>(a, static_cast<int>(grid), st);
+    case 2: return run_mfma16<2>(a, static_cast<int>(grid), st);
+    case 3: return run_mfma16<3>(a, static_cast<int>(grid), st);
+    case 4: return run_mfma16<4>(a, static_cast<int>(grid), st);
+    case 5: return run_mfma16<5>(a, static_cast<int>(grid), st);
+    case 6: return run_mfma16<6>(a, static_cast<int>(grid), st);
+    case 7: return run_mfma16<7>(a, static_cast<int>(grid), st);
+    case 8: return run_mfma16<8>(a, static_cast<int>(grid), st);
+    case 9: return run_mfma16<9>(a, static_cast<int>(grid), st);
+    case 10: return run_mfma16<10>(a, static_cast<int>(grid), st);
+    case 11: return run_mfma16<11>(a, static_cast<int>(grid), st);
+    case 12: return run_mfma16<12>(a, static_cast<int>(grid), st);
     default: return hipErrorInvalidValue;
   }
 }
