@@ -20,10 +20,12 @@ it follows:
   gamma = 4).
 * "SpecTr-GBV" write-up (hypresin.com), "为什么重新设计推测解码的验证环节" and "第三步"
   (first rejection ends the block; residual next token; bonus token when all accepted).
+* Phrase-level speculation page (kongchang.com), "更换单元：从 token 到短语" (candidates in a
+  prefix tree verified in one pass, kept only where they equal the target's argmax).
 
 Parity status: every function here is pinned by a CPU test against something other than
 itself (library routines it does not call, brute force, closed forms, the pages' printed
 table, Monte Carlo against exact distributions).  No function is "parity unpinned".
 """
 
-from . import fp, philox, sampler, heads, verify  # noqa: F401
+from . import fp, philox, sampler, heads, verify, tree  # noqa: F401
