@@ -122,3 +122,74 @@ def expected_tokens_per_step(alpha, gamma):
     if alpha == 1.0:
         return float(gamma + 1)
     return (1.0 - alpha ** (gamma + 1)) / (1.0 - alpha)
+
+
+def verify_sample_sparse(target_logits, draft_idx, draft_prob, draft_tokens, u_accept, dtype,
+                         temperature=1.0, seed=0, offset=0):
+    """Speculative-sampling verification against a sparse draft distribution: q_t is given
+    on a candidate set K_t (draft_idx [B, gamma, k], ascending ids, draft_prob [B, gamma, k]:
+    the SpecVocab head's probabilities over its top-k, section 2.2.3) and is zero outside it
+    (reading: SpecVocab section 3.3 keeps the full vocabulary for verification, so the
+    residual max(0, p - q) equals p outside K).  The acceptance test, residual, bonus and
+    uniforms are those of verify_sample.  Returns (accept_len, out_tokens, diag)."""
+    tl = fp.decode(target_logits, dtype) / temperature
+    idx = np.asarray(draft_idx, dtype=np.int64)
+    qk = np.asarray(draft_prob, dtype=np.float64)
+    x = np.asarray(draft_tokens, dtype=np.int64)
+    u = np.asarray(u_accept, dtype=np.float64)
+    B, gamma = x.shape
+    V = tl.shape[2]
+    acc = np.zeros(B, np.int64)
+    out = np.full((B, gamma + 1), -1, np.int64)
+    diag = {"ratio": np.zeros((B, gamma)), "sample": []}
+
+    def q_row(b, t):
+        q = np.zeros(V)
+        q[idx[b, t]] = qk[b, t]
+        return q
+
+    for b in range(B):
+        a = gamma
+        for t in range(gamma):
+            if not (0 <= x[b, t] < V):
+                a = t
+                break
+            p, _ = _softmax(tl[b, t])
+            qx = q_row(b, t)[x[b, t]]
+            ratio = p[x[b, t]] / qx if qx > 0 else (np.inf if p[x[b, t]] > 0 else 0.0)
+            diag["ratio"][b, t] = ratio
+            if not (u[b, t] < ratio):
+                a = t
+                break
+        if a < gamma:
+            p, _ = _softmax(tl[b, a])
+            q = q_row(b, a)
+            r = p - q
+            with np.errstate(divide="ignore"):
+                ell = np.where(r > 0, np.log(np.where(r > 0, r, 1.0)), -np.inf)
+            tok, dg = two_level_sample(
+                ell,
+                lambda g: uniforms(seed, offset, PURPOSE_RESID_GROUP, b, g),
+                lambda i: uniforms(seed, offset, PURPOSE_RESID_ELEM, b, i),
+            )
+            if tok is None:
+                tok, dg = two_level_sample(
+                    tl[b, a],
+                    lambda g: uniforms(seed, offset, PURPOSE_RESID_GROUP, b, g),
+                    lambda i: uniforms(seed, offset, PURPOSE_RESID_ELEM, b, i),
+                )
+            dg["kind"] = "residual"
+            dg["p"], dg["q"] = p, q
+        else:
+            tok, dg = two_level_sample(
+                tl[b, gamma],
+                lambda g: uniforms(seed, offset, PURPOSE_BONUS_GROUP, b, g),
+                lambda i: uniforms(seed, offset, PURPOSE_BONUS_ELEM, b, i),
+            )
+            dg["kind"] = "bonus"
+        out[b, :a] = x[b, :a]
+        out[b, a] = tok
+        acc[b] = a
+        dg["a"] = a
+        diag["sample"].append(dg)
+    return acc, out, diag
