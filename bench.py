@@ -286,7 +286,7 @@ def main():
         line["hbm_roofline_frac_call"] = head["hbm_frac"]
     # roofline of the dominant kernel: the W_up streaming kernel of the headline leg
     if head and "kernels" in head:
-        kname = "stream_mfma" if "stream_mfma" in head["kernels"] else "stream_valu"
+        kname = next(k for k in ("head_tile", "stream_mfma", "stream_valu") if k in head["kernels"])
         kavg = head["kernels"][kname]["avg_us"]
         kbytes = V * r * 2 + 48 * r * 2
         achieved = kbytes / (kavg * 1e-6) / 1e9

@@ -200,7 +200,48 @@ int run_head(const void* x, int64_t M, int64_t K, const void* W, int64_t V, int 
   const bool bf16 = dtype == SH_BF16;
   const float invT = 1.0f / temperature;
   const bool want_lg = mode == SH_SAMPLE || lse != nullptr || logprob != nullptr;
-  const int64_t NG = (V + sh::kGroup - 1) / sh::kGroup;
+  if (sh::head_tile_supported(M, K, V, bf16)) {
+    // short bf16 rows, at most kTileMaxRows activation rows: one tile-streaming pass with
+    // in-kernel group draws, then the finalize
+    const int grid = sh::head_tile_grid(M, K, V);
+    sh::TileArgs a{};
+    a.W = W;
+    a.x = x;
+    a.V = V;
+    a.K = static_cast<int>(K);
+    a.M = static_cast<int>(M);
+    a.row0 = 0;
+    a.invT = invT;
+    a.want_stats = want_lg ? 1 : 0;
+    a.want_argmax = mode == SH_GREEDY ? 1 : 0;
+    a.sample = mode == SH_SAMPLE ? 1 : 0;
+    a.seed = seed;
+    a.offset = offset;
+    a.zout = logits;
+    a.zout_ld = V;
+    a.partials = partials;
+    a.partials_ld = sh::kMaxPartials;
+    SH_HIP(sh::launch_head_tile(a, grid, st), "head tile kernel");
+    sh::FinalizeArgs f{};
+    f.partials = partials;
+    f.partials_ld = sh::kMaxPartials;
+    f.P = grid;
+    f.W = W;
+    f.x = x;
+    f.V = V;
+    f.K = K;
+    f.M = static_cast<int>(M);
+    f.bf16 = true;
+    f.mode = mode == SH_SAMPLE ? 1 : 0;
+    f.invT = invT;
+    f.seed = seed;
+    f.offset = offset;
+    f.token = token;
+    f.lse = lse;
+    f.logprob = logprob;
+    SH_HIP(sh::launch_head_fin(f, st), "head finalize kernel");
+    return SH_OK;
+  }
   const bool mfma = bf16 && M > kValuMaxRows;
   const int64_t chunk = mfma ? kMfmaMaxRows : kValuMaxRows;
   int producers = 0;
@@ -380,10 +421,26 @@ int draft_head_specvocab(const void* h, int64_t M, int64_t d, const void* W_down
   SH_HIP(sh::launch_rowdot(W_down, h, dprime, d, M, bf16, hp, reinterpret_cast<float*>(ws + L.rd_off), st,
                            reinterpret_cast<uint32_t*>(ws + L.tk_off + TL.hist_off), sh::topk_counter_words(M)),
          "reduced-state kernels");
+  const bool tile = sh::head_tile_supported(M, dprime, V, bf16);
+  const int tile_grid = tile ? sh::head_tile_grid(M, dprime, V) : 0;
   const bool mfma = bf16 && M > kValuMaxRows;
-  const int64_t chunk = mfma ? kMfmaMaxRows : kValuMaxRows;
+  const int64_t chunk = tile ? M : mfma ? kMfmaMaxRows : kValuMaxRows;
   for (int64_t m0 = 0; m0 < M; m0 += chunk) {
     const int64_t mc = (M - m0) < chunk ? (M - m0) : chunk;
+    if (tile) {
+      sh::TileArgs a{};
+      a.W = W_vocab;
+      a.x = static_cast<const char*>(hp) + static_cast<size_t>(m0 * dprime) * 2;
+      a.V = V;
+      a.K = static_cast<int>(dprime);
+      a.M = static_cast<int>(mc);
+      a.row0 = static_cast<int>(m0);
+      a.invT = 1.f;
+      a.zout = scores + m0 * V;
+      a.zout_ld = V;
+      SH_HIP(sh::launch_head_tile(a, tile_grid, st), "approximate scorer kernel");
+      continue;
+    }
     sh::StreamArgs a{};
     a.W = W_vocab;
     a.x = static_cast<const char*>(hp) + static_cast<size_t>(m0 * dprime) * esize(dtype);

@@ -840,7 +840,8 @@ __global__ __launch_bounds__(256) void k_stream_mfma(StreamArgs a) {
   if (g < NG) load_batch(g, 0, 0, XA, YA);
 
   if constexpr (!BG) {
-    stage16<8>(bs, KS * NCB * kWave, [&](int it) {
+    // fragments of all nb * KB k-steps (zero past K) so every MFMA of a batch is unconditional
+    stage16<8>(bs, nb * KB * NCB * kWave, [&](int it) {
       if (it < 0) return buffer_load16(xrs, kOutOfRange);
       const int ks = it / (NCB * kWave);
       const int cb = (it / kWave) % NCB;
@@ -863,10 +864,11 @@ __global__ __launch_bounds__(256) void k_stream_mfma(StreamArgs a) {
         g2 = g + nwt;
       }
     }
-    if (g2 < NG)
-      load_batch(g2, t2, b2, FX, FY);
-    else
-      load_batch(g, t, b, FX, FY);
+    // one straight-line load sequence: past the wave's last group the current batch is
+    // re-read (cache-resident), so the wait before each MFMA below leaves exactly the
+    // prefetched batch in flight
+    const bool more = g2 < NG;
+    load_batch(more ? g2 : g, more ? t2 : t, more ? b2 : b, FX, FY);
     if (b == 0) {
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb)
@@ -875,14 +877,12 @@ __global__ __launch_bounds__(256) void k_stream_mfma(StreamArgs a) {
     }
 #pragma unroll
     for (int j = 0; j < KB; ++j) {
-      const int ks = b * KB + j;
-      if (ks < KS) {
-        const bf16x8_t af = __builtin_bit_cast(bf16x8_t, UX[j]);
+      const int ks = b * KB + j;   // k-steps past K hold zero fragments on both sides
+      const bf16x8_t af = __builtin_bit_cast(bf16x8_t, UX[j]);
 #pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) {
-          const uint4 bv = BG ? UY[j][cb] : bs[(ks * NCB + cb) * kWave + l];
-          acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, __builtin_bit_cast(bf16x8_t, bv), acc[cb], 0, 0, 0);
-        }
+      for (int cb = 0; cb < NCB; ++cb) {
+        const uint4 bv = BG ? UY[j][cb] : bs[(ks * NCB + cb) * kWave + l];
+        acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, __builtin_bit_cast(bf16x8_t, bv), acc[cb], 0, 0, 0);
       }
     }
     if (b == nb - 1) epilogue_tile(g, t);
@@ -1212,7 +1212,8 @@ static hipError_t run_mfma(const StreamArgs& a, int grid, hipStream_t st) {
   const int nw = 4;
   const int rec = nw * a.M * static_cast<int>(sizeof(Partial));
   const int KS = static_cast<int>((a.K + 15) / 16);
-  const int frag = KS * NCB * 1024;
+  constexpr int KB = 8;   // k-steps per load batch of k_stream_mfma<NCB, false>
+  const int frag = (KS + KB - 1) / KB * KB * NCB * 1024;
   const int bytes = frag > rec ? frag : rec;
   TraceScope ts("stream_mfma", st);
   hipError_t e = allow_lds(k_stream_mfma<NCB, false>, bytes);
@@ -1277,7 +1278,7 @@ hipError_t launch_stream(const StreamArgs& a, bool use_mfma, int* producers, hip
   // (32 rows x 32 bytes per load, four loads completing each 128-byte line in one batch) is
   // the faster one; otherwise the 16x16x32 kernel.
   const int KS16 = static_cast<int>((a.K + 15) / 16);
-  if (a.M > 16 && a.M <= 64 && static_cast<int64_t>(KS16) * ((a.M + 31) / 32) * 1024 <= di.max_lds)
+  if (a.M > 16 && a.M <= 64 && static_cast<int64_t>((KS16 + 7) / 8 * 8) * ((a.M + 31) / 32) * 1024 <= di.max_lds)
     return a.M <= 32 ? run_mfma<1>(a, static_cast<int>(grid), st) : run_mfma<2>(a, static_cast<int>(grid), st);
   const int ncb = (a.M + 15) / 16;
   switch (ncb) {

@@ -47,6 +47,35 @@ struct FinalizeArgs {
   float* logprob;
 };
 
+// Tile-streaming head pass (bf16, rows of 128, 256, 384 or 512 elements, at most kTileMaxRows
+// activation rows):
+// z[m, v] = W[v, :] . x[m, :]; optional raw logits; per-workgroup Partials of y = z * invT
+// (lse, best group score with the Philox group draw, argmax).
+constexpr int kTileMaxRows = 64;
+struct TileArgs {
+  const void* W;      // [V, K] bf16
+  const void* x;      // [M, K] bf16
+  int64_t V;
+  int K;
+  int M;              // rows of this pass, <= kTileMaxRows
+  int row0;           // absolute index of x's first row (Philox row of the group draws)
+  float invT;
+  int want_stats;     // row lse (and, with sample, the group draws)
+  int want_argmax;
+  int sample;
+  uint64_t seed, offset;
+  float* zout;        // nullable [M, zout_ld]
+  int64_t zout_ld;
+  Partial* partials;  // [M, partials_ld], one per workgroup; nullable when no stats are wanted
+  int64_t partials_ld;
+};
+bool head_tile_supported(int64_t M, int64_t K, int64_t V, bool bf16);
+// workgroups of a tile pass over V rows for passes of up to M activation rows
+int head_tile_grid(int64_t M, int64_t K, int64_t V);
+hipError_t launch_head_tile(const TileArgs& a, int grid, hipStream_t st);
+// per row: merge the Partials, greedy token or the two-level draw (recomputing the winning group)
+hipError_t launch_head_fin(const FinalizeArgs& f, hipStream_t st);
+
 struct DeviceInfo {
   int cus;
   int max_lds;   // bytes of dynamic LDS a workgroup may use
