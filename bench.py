@@ -288,7 +288,7 @@ def main():
     if head and "kernels" in head:
         kname = next(k for k in ("head_tile", "stream_mfma", "stream_valu") if k in head["kernels"])
         kavg = head["kernels"][kname]["avg_us"]
-        kbytes = V * r * 2 + 48 * r * 2
+        kbytes = V * r * 2 + 48 * r * 2   # the W_up pass: W_up and h_r
         achieved = kbytes / (kavg * 1e-6) / 1e9
         traffic = None
         tpath = os.path.join(ROOT, "profiles", "traffic_stream_mfma_llama_lowrank_M48.json")

@@ -1,18 +1,20 @@
-// Tile-streaming head kernel for gfx950: bf16 weights with rows of at most 1 KB (the SlimSpec
-// r -> V map at r <= 512, the SpecVocab approximate scorer at d' <= 512).
+// Tile-streaming head kernels for gfx950: bf16 weights with rows of 128, 256, 384 or 512
+// elements and at most 64 activation rows (the SlimSpec r -> V map at r = d/8, the SpecVocab
+// approximate scorer at d' = d/16).
 //
-//   k_head_tile  four waves per workgroup, one workgroup per CU; each wave owns whole 64-row
-//                vocabulary groups (g = its wave index + i * waves in the grid).  A group is
-//                four 16-row tiles; tile t + 1 is loaded while tile t is multiplied on
-//                v_mfma_f32_16x16x32_bf16 (weights as the A operand straight from HBM, one
-//                16-byte load per lane per 32-wide k-step; the activations' B fragments stay in
-//                registers for the whole pass).  After the fourth tile the group's 64 logits of
-//                every activation row are reduced once: in-lane over 16 rows, then across the
-//                four lanes holding the rest; lane (col, qd) then folds the group into the
-//                running lse, the best group score L_g + Gumbel(u_g) (sampling) and the argmax of
-//                activation row 16 qd + col.  Each workgroup writes one Partial per row.
-//   k_head_fin   per row: merges the workgroups' Partials into lse, argmax and the winning
-//                group; sampling recomputes that group's 64 logits and draws the element.
+//   k_head_tile     z = W x over all V rows with per-workgroup Partials (lse, best group
+//                   score, argmax) and/or raw scores.  Four waves per workgroup, one
+//                   workgroup per CU; each wave owns whole 64-row vocabulary groups.  A group
+//                   is four 16-row tiles; tile t + 1 is loaded while tile t is multiplied on
+//                   v_mfma_f32_16x16x32_bf16 (weights as the A operand straight from HBM, one
+//                   16-byte load per lane per 32-wide k-step; the activations' B fragments stay
+//                   in registers for the whole pass).  After the fourth tile the group's 64
+//                   logits of every activation row are reduced once: in-lane over 16 rows, then
+//                   across the four lanes holding the rest; lane (col, qd) folds the group into
+//                   the running lse, the best group score L_g + Gumbel(u_g) (sampling) and the
+//                   argmax of activation row 16 qd + col.
+//   k_head_fin      per row: merges the workgroups' Partials into lse, argmax and the winning
+//                   group; sampling recomputes that group's 64 logits and draws the element.
 //
 // The sampler is the two-level Gumbel-max over groups of 64 consecutive candidates; the group
 // draws use Philox purpose 0 (draft group), the element draw purpose 1 (draft element).
@@ -26,122 +28,120 @@ namespace {
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kTileThreads = 256;   // 4 waves: the four 16-row tiles of a group
-
-}  // namespace
-
+constexpr int kTileThreads = 256;   // four waves
+constexpr int kTileWaves = kTileThreads / kWave;
 // EPI bits: kEpiStats (row lse; with sampling, the group draws), kEpiArgmax (greedy argmax)
 constexpr int kEpiStats = 1, kEpiArgmax = 2;
 
-template <int NCB, int KS, bool ZOUT, int EPI>
-__global__ __launch_bounds__(kTileThreads, 1) void k_head_tile(TileArgs a) {
-  constexpr int NC = NCB * 16;           // activation rows (columns of the output tiles) per pass
-  constexpr int RPL = (NCB + 3) / 4;     // activation rows finished by each lane
-  constexpr bool STATS = (EPI & kEpiStats) != 0, AMAX = (EPI & kEpiArgmax) != 0;
-  constexpr int CPRP = KS * 4;           // 16-byte chunks per activation row in LDS (K padded)
-  constexpr int RS = CPRP + 4;           // LDS row stride in chunks
-  extern __shared__ uint4 smem[];        // staged activations [NC][RS], later Partial records [4][NC]
-  const int l = lane_id(), w = wave_id();
-  const int col = l & 15, qd = l >> 4;
-  const uint32_t rowbytes = static_cast<uint32_t>(a.K) * 2;
-  const int CPR = static_cast<int>(rowbytes / 16);
-  const int V32 = static_cast<int>(a.V);
-  const int NG = (V32 + kGroup - 1) / kGroup;
-  const int Mx = a.M;
-  const int NW = static_cast<int>(gridDim.x) * (kTileThreads / kWave);
-  const int gw = static_cast<int>(blockIdx.x) * (kTileThreads / kWave) + w;
-  const int iters = gw < NG ? (NG - gw + NW - 1) / NW : 0;   // this wave's groups gw, gw + NW, ...
-  const float c2 = a.invT * kLog2e;
-  const char* Wb = static_cast<const char*>(a.W);
+}  // namespace
 
-  // ---- weight tiles: tile t of group g is 16 rows; lane (col, qd) of load j holds row col,
-  // bytes 64 j + 16 qd .. +16 (the A operand of v_mfma_f32_16x16x32_bf16).  The descriptor
-  // starts at the tile's first row (or at V past the last row) and reaches to the end of the
-  // matrix: rows past V read zero.  Scalar arithmetic only (the host admits matrices of at most
-  // 0xFFFFFFF0 bytes, and rows of exactly KS 32-wide k-steps).
-  const uint32_t vbytes = static_cast<uint32_t>(V32) * rowbytes;
-  const uint32_t lane_off = static_cast<uint32_t>(col) * rowbytes + static_cast<uint32_t>(qd) * 16;
-  auto tile_load = [&](int g, int t, uint4 (&X)[KS]) {
+// ----------------------------------------------------------------------------------------
+// One tile pass of a workgroup: geometry, the activation fragments, the pipelined group loop
+// and the per-workgroup Partial of every activation row.
+// ----------------------------------------------------------------------------------------
+template <int NCB, int KS, bool ZOUT, int EPI>
+struct TilePass {
+  static constexpr int NC = NCB * 16;   // activation rows (columns of the output tiles)
+  static constexpr bool STATS = (EPI & kEpiStats) != 0, AMAX = (EPI & kEpiArgmax) != 0;
+  static constexpr int CPRP = KS * 4;   // 16-byte chunks per activation row
+  static constexpr int RS = CPRP + 4;   // LDS row stride of the staged activations, in chunks
+  static constexpr int XPER = (NC * CPRP + kTileThreads - 1) / kTileThreads;
+  // LDS bytes: staged activations [NC][RS], later the Partial records [4][NC]
+  static constexpr int kLds = (NC * RS * 16 > kTileWaves * NC * 32) ? NC * RS * 16 : kTileWaves * NC * 32;
+
+  const TileArgs& a;
+  uint4* smem;
+  int l, w, col, qd;
+  uint32_t rowbytes, vbytes, lane_off;
+  int V32, NG, Mx;
+  float c2;
+  uint4 Bf[KS][NCB];
+  f32x4_t acc[4][NCB];
+  // running state of activation row 16 qd + col (lanes with qd < NCB)
+  float rm = -INFINITY, rsum = 0.f, gbest = -INFINITY, bz = -INFINITY;
+  int32_t gid = 0x7fffffff, bi = 0x7fffffff;
+
+  __device__ __forceinline__ TilePass(const TileArgs& args, uint4* lds) : a(args), smem(lds) {
+    l = lane_id();
+    w = wave_id();
+    col = l & 15;
+    qd = l >> 4;
+    rowbytes = static_cast<uint32_t>(a.K) * 2;
+    V32 = static_cast<int>(a.V);
+    NG = (V32 + kGroup - 1) / kGroup;
+    Mx = a.M;
+    c2 = a.invT * kLog2e;
+    // (the host admits matrices of at most 0xFFFFFFF0 bytes and rows of exactly KS k-steps)
+    vbytes = static_cast<uint32_t>(V32) * rowbytes;
+    lane_off = static_cast<uint32_t>(col) * rowbytes + static_cast<uint32_t>(qd) * 16;
+  }
+
+  // Tile t of group g: lane (col, qd) of load j holds row col, bytes 64 j + 16 qd .. +16 (the A
+  // operand).  The descriptor starts at the tile's first row (or at V past the last row) and
+  // reaches to the end of the matrix, so rows past V read zero.  Scalar arithmetic only: the
+  // prefetch issues no vector instruction besides the loads.
+  __device__ __forceinline__ void tile_load(int g, int t, uint4 (&X)[KS]) const {
     const int r0 = g * kGroup + t * 16;
     const uint32_t b0 = r0 < V32 ? static_cast<uint32_t>(r0) * rowbytes : vbytes;
-    const rsrc_t rs = make_rsrc(Wb + b0, vbytes - b0);
+    const rsrc_t rs = make_rsrc(static_cast<const char*>(a.W) + b0, vbytes - b0);
 #pragma unroll
     for (int j = 0; j < KS; ++j) X[j] = buffer_load16(rs, lane_off + static_cast<uint32_t>(j) * 64);
-  };
+  }
 
-  // ---- activations: staged contiguously through LDS, then each wave keeps its B fragments in
-  // registers: Bf[j][cb] holds x[cb * 16 + col][32 j + 8 qd ..+8], zero past M and K
-  uint4 XA[KS], XB[KS];
-  uint4 Bf[KS][NCB];
-  {
+  // Activations, contiguously (flat 16-byte chunks of x [M][K]), then through LDS into the
+  // register B fragments: Bf[j][cb] = x[cb * 16 + col][32 j + 8 qd ..+8], zero past M.
+  __device__ __forceinline__ void stage_issue(uint4 (&xv)[XPER]) const {
     const rsrc_t xrs = make_rsrc(a.x, static_cast<uint32_t>(Mx) * rowbytes);
-    constexpr int XPER = (NC * CPRP + kTileThreads - 1) / kTileThreads;
-    uint4 xv[XPER];
 #pragma unroll
     for (int q = 0; q < XPER; ++q) {
       const int f = q * kTileThreads + static_cast<int>(threadIdx.x);
-      xv[q] = buffer_load16(xrs, f < Mx * CPR ? static_cast<uint32_t>(f) * 16 : kOutOfRange);
+      xv[q] = buffer_load16(xrs, f < Mx * CPRP ? static_cast<uint32_t>(f) * 16 : kOutOfRange);
     }
-    tile_load(iters > 0 ? gw : 0, 0, XA);
-    __builtin_amdgcn_sched_barrier(0);
+  }
+  __device__ __forceinline__ void stage_finish(const uint4 (&xv)[XPER]) {
 #pragma unroll
     for (int q = 0; q < XPER; ++q) {
       const int f = q * kTileThreads + static_cast<int>(threadIdx.x);
-      const int m = f / CPR, c = f - m * CPR;
-      if (f < Mx * CPR) smem[m * RS + c] = xv[q];
+      const int m = f / CPRP, c = f - m * CPRP;
+      if (f < Mx * CPRP) smem[m * RS + c] = xv[q];
     }
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < KS; ++j)
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
-        const int m = cb * 16 + col, c = 4 * j + qd;
-        Bf[j][cb] = (m < Mx && c < CPR) ? smem[m * RS + c] : zero16();
+        const int m = cb * 16 + col;
+        Bf[j][cb] = m < Mx ? smem[m * RS + 4 * j + qd] : zero16();
       }
   }
 
-  // ---- running state of the rows this lane finishes: row cb * 16 + col for cb = qd + 4 k
-  float rm[RPL], rsum[RPL], gbest[RPL], bz[RPL];
-  int32_t gid[RPL], bi[RPL];
-#pragma unroll
-  for (int k = 0; k < RPL; ++k) {
-    rm[k] = -INFINITY;
-    rsum[k] = 0.f;
-    gbest[k] = -INFINITY;
-    bz[k] = -INFINITY;
-    gid[k] = 0x7fffffff;
-    bi[k] = 0x7fffffff;
+  // Gumbel(u) of this lane's row for group g (independent of the MFMAs, so it overlaps them)
+  __device__ __forceinline__ float draw(int g) const {
+    const int m = qd * 16 + col;
+    if (STATS && a.sample != 0 && qd < NCB && m < Mx)
+      return gumbel(philox_uniform(a.seed, a.offset, kDraftGroup, static_cast<uint64_t>(a.row0 + m),
+                                   static_cast<uint64_t>(g)));
+    return 0.f;
   }
-  const bool sample = a.sample != 0;
-  // Gumbel(u) of this lane's rows for group g (independent of the MFMAs: overlaps them)
-  auto draw = [&](int g, float (&gu)[RPL]) {
-#pragma unroll
-    for (int k = 0; k < RPL; ++k) {
-      const int m = (qd + 4 * k) * 16 + col;
-      gu[k] = 0.f;
-      if (STATS && sample && qd + 4 * k < NCB && m < Mx)
-        gu[k] = gumbel(philox_uniform(a.seed, a.offset, kDraftGroup, static_cast<uint64_t>(a.row0 + m),
-                                      static_cast<uint64_t>(g)));
-    }
-  };
 
-  f32x4_t acc[4][NCB];
-  auto mma = [&](const uint4 (&X)[KS], auto tc) {
-    constexpr int t = decltype(tc)::value;
+  template <int T>
+  __device__ __forceinline__ void mma(const uint4 (&X)[KS]) {
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) acc[t][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int cb = 0; cb < NCB; ++cb) acc[T][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < KS; ++j) {
       const bf16x8_t af = __builtin_bit_cast(bf16x8_t, X[j]);
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb)
-        acc[t][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, __builtin_bit_cast(bf16x8_t, Bf[j][cb]), acc[t][cb], 0, 0, 0);
+        acc[T][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, __builtin_bit_cast(bf16x8_t, Bf[j][cb]), acc[T][cb], 0, 0, 0);
     }
-  };
-  // raw logits of tile t: lane (col, qd) holds rows 16 t + 4 qd .. +3 of activation row cb * 16 + col
-  auto store_z = [&](int g, int t) {
+  }
+
+  // raw logits of tile T: lane (col, qd) holds rows 16 T + 4 qd .. +3 of activation row cb*16+col
+  template <int T>
+  __device__ __forceinline__ void store_z(int g) const {
     if constexpr (ZOUT) {
-      const int r0 = g * kGroup + t * 16 + qd * 4;
+      const int r0 = g * kGroup + T * 16 + qd * 4;
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
         const int m = cb * 16 + col;
@@ -149,13 +149,14 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_head_tile(TileArgs a) {
           float* zo = a.zout + static_cast<int64_t>(m) * a.zout_ld;
 #pragma unroll
           for (int v = 0; v < 4; ++v)
-            if (r0 + v < V32) zo[r0 + v] = acc[t][cb][v];
+            if (r0 + v < V32) zo[r0 + v] = acc[T][cb][v];
         }
       }
     }
-  };
+  }
+
   // fold group g (the four tiles' accumulators) into the running state
-  auto group_end = [&](int g, const float (&gu)[RPL]) {
+  __device__ __forceinline__ void group_end(int g, float gu) {
     if constexpr (EPI != 0) {
       const int gb = g * kGroup;
       const bool full = gb + kGroup <= V32;
@@ -186,7 +187,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_head_tile(TileArgs a) {
 #pragma unroll
           for (int i = 15; i >= 0; --i)   // the lane's rows rise with i: keep the lowest
             if (z[i] == zm) bsel = i;
-          zi = gb + (bsel >> 2) * 16 + qd * 4 + (bsel & 3);
+          zi = zm == -INFINITY ? 0x7fffffff : gb + (bsel >> 2) * 16 + qd * 4 + (bsel & 3);
         }
         // the four lanes col, col + 16, col + 32, col + 48 hold the group's 64 rows
 #pragma unroll
@@ -204,104 +205,116 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_head_tile(TileArgs a) {
             zm = fmaxf(zm, zm2);
           }
         }
-        // lane (col, qd) finishes activation row cb * 16 + col when cb = qd + 4 k
-#pragma unroll
-        for (int k = 0; k < RPL; ++k) {
-          if (cb == qd + 4 * k && cb * 16 + col < Mx) {
-            if constexpr (STATS) {
-              const float L = zm * a.invT + log2f(ss) * kLn2;   // group log-sum-exp of y = z / T
-              const float mn = fmaxf(rm[k], L);
-              rsum[k] = rsum[k] * fast_exp2((rm[k] - mn) * kLog2e) + fast_exp2((L - mn) * kLog2e);
-              rm[k] = mn;
-              const float sc = L + gu[k];
-              if (sample && sc > gbest[k]) {   // groups rise: strict > keeps the lowest on ties
-                gbest[k] = sc;
-                gid[k] = g;
-              }
+        // lane (col, qd) finishes activation row 16 qd + col
+        if (cb == qd && cb * 16 + col < Mx) {
+          if constexpr (STATS) {
+            const float L = zm * a.invT + log2f(ss) * kLn2;   // group log-sum-exp of y = z / T
+            const float mn = fmaxf(rm, L);
+            rsum = rsum * fast_exp2((rm - mn) * kLog2e) + fast_exp2((L - mn) * kLog2e);
+            rm = mn;
+            const float sc = L + gu;
+            if (a.sample != 0 && sc > gbest) {   // groups rise: strict > keeps the lowest on ties
+              gbest = sc;
+              gid = g;
             }
-            if constexpr (AMAX) argmax_merge(bz[k], bi[k], zm, zi);
           }
+          if constexpr (AMAX) argmax_merge(bz, bi, zm, zi);
         }
       }
     }
-  };
-
-  // Pipeline: tile t + 1 (or the next group's tile 0) is loaded while tile t is multiplied.
-  // Loads are straight-line (past the last group the current tile is re-read, cache-resident)
-  // and pinned above the MFMAs by scheduling barriers, so the wait before each MFMA leaves
-  // exactly the next tile in flight.
-  for (int i = 0; i < iters; ++i) {
-    const int g = gw + i * NW;
-    const int gn = i + 1 < iters ? g + NW : g;
-    float gu[RPL];
-    tile_load(g, 1, XB);
-    __builtin_amdgcn_sched_barrier(0);
-    draw(g, gu);
-    mma(XA, std::integral_constant<int, 0>{});
-    store_z(g, 0);
-    tile_load(g, 2, XA);
-    __builtin_amdgcn_sched_barrier(0);
-    mma(XB, std::integral_constant<int, 1>{});
-    store_z(g, 1);
-    tile_load(g, 3, XB);
-    __builtin_amdgcn_sched_barrier(0);
-    mma(XA, std::integral_constant<int, 2>{});
-    store_z(g, 2);
-    tile_load(gn, i + 1 < iters ? 0 : 3, XA);
-    __builtin_amdgcn_sched_barrier(0);
-    mma(XB, std::integral_constant<int, 3>{});
-    store_z(g, 3);
-    group_end(g, gu);
   }
-  if constexpr (EPI != 0) {
-    // merge the four waves' states per activation row, one Partial per row per workgroup
+
+  // Groups gw, gw + nw, ... of this wave; XA holds tile 0 of the first (already issued).
+  // Tile t + 1 (or the next group's tile 0) is loaded while tile t is multiplied; loads are
+  // straight-line (past the last group the current tile is re-read, cache-resident) and pinned
+  // above the MFMAs by scheduling barriers, so the wait before each MFMA leaves exactly the
+  // next tile in flight.
+  __device__ __forceinline__ void run(int gw, int nw, uint4 (&XA)[KS], uint4 (&XB)[KS]) {
+    const int iters = gw < NG ? (NG - gw + nw - 1) / nw : 0;
+    for (int i = 0; i < iters; ++i) {
+      const int g = gw + i * nw;
+      const int gn = i + 1 < iters ? g + nw : g;
+      tile_load(g, 1, XB);
+      __builtin_amdgcn_sched_barrier(0);
+      const float gu = draw(g);
+      mma<0>(XA);
+      store_z<0>(g);
+      tile_load(g, 2, XA);
+      __builtin_amdgcn_sched_barrier(0);
+      mma<1>(XB);
+      store_z<1>(g);
+      tile_load(g, 3, XB);
+      __builtin_amdgcn_sched_barrier(0);
+      mma<2>(XA);
+      store_z<2>(g);
+      tile_load(gn, i + 1 < iters ? 0 : 3, XA);
+      __builtin_amdgcn_sched_barrier(0);
+      mma<3>(XB);
+      store_z<3>(g);
+      group_end(g, gu);
+    }
+  }
+
+  // merge the four waves' states per activation row: one Partial per row per workgroup
+  __device__ __forceinline__ void write_partials(int wg) {
     __syncthreads();   // the staged activations are no longer read
     Partial* rec = reinterpret_cast<Partial*>(smem);
-#pragma unroll
-    for (int k = 0; k < RPL; ++k) {
-      const int cb = qd + 4 * k, m = cb * 16 + col;
-      if (cb < NCB && m < Mx) {
-        Partial p;
-        p.m = rm[k];
-        p.s = rsum[k];
-        p.gscore = gbest[k];
-        p.g = gid[k];
-        p.zmax = bz[k];
-        p.zid = bi[k];
-        p.pad0 = p.pad1 = 0.f;
-        rec[w * NC + m] = p;
-      }
+    const int m = qd * 16 + col;
+    if (qd < NCB && m < Mx) {
+      Partial p;
+      p.m = rm;
+      p.s = rsum;
+      p.gscore = gbest;
+      p.g = gid;
+      p.zmax = bz;
+      p.zid = bi;
+      p.pad0 = p.pad1 = 0.f;
+      rec[w * NC + m] = p;
     }
     __syncthreads();
-    for (int m = threadIdx.x; m < Mx; m += kTileThreads) {
-      Partial p = rec[m];
+    for (int r = threadIdx.x; r < Mx; r += kTileThreads) {
+      Partial p = rec[r];
 #pragma unroll
-      for (int ww = 1; ww < kTileThreads / kWave; ++ww) partial_merge(p, rec[ww * NC + m]);
-      a.partials[static_cast<int64_t>(m) * a.partials_ld + blockIdx.x] = p;
+      for (int ww = 1; ww < kTileWaves; ++ww) partial_merge(p, rec[ww * NC + r]);
+      a.partials[static_cast<int64_t>(r) * a.partials_ld + wg] = p;
     }
   }
+};
+
+template <int NCB, int KS, bool ZOUT, int EPI>
+__global__ __launch_bounds__(kTileThreads, 1) void k_head_tile(TileArgs a) {
+  extern __shared__ uint4 smem[];
+  TilePass<NCB, KS, ZOUT, EPI> p(a, smem);
+  const int gw = static_cast<int>(blockIdx.x) * kTileWaves + p.w;
+  const int nw = static_cast<int>(gridDim.x) * kTileWaves;
+  uint4 XA[KS], XB[KS];
+  {
+    uint4 xv[TilePass<NCB, KS, ZOUT, EPI>::XPER];
+    p.stage_issue(xv);
+    p.tile_load(gw < p.NG ? gw : 0, 0, XA);
+    __builtin_amdgcn_sched_barrier(0);
+    p.stage_finish(xv);
+  }
+  p.run(gw, nw, XA, XB);
+  if constexpr (EPI != 0) p.write_partials(static_cast<int>(blockIdx.x));
 }
 
 // ----------------------------------------------------------------------------------------
-// k_head_fin: one workgroup (16 waves) per row.
+// Finalize of one row from its producers' Partials: lse, greedy token, or the two-level draw
+// recomputing the winning group's logits.
+// `nthreads` threads of the workgroup take part; zs holds 64 floats, rec nthreads/64 Partials.
 // ----------------------------------------------------------------------------------------
-constexpr int kHfThreads = 1024;
-constexpr int kHfWaves = kHfThreads / kWave;
-constexpr int kHfRowsPerWave = kGroup / kHfWaves;   // 4
-
 template <bool BF16>
-__global__ __launch_bounds__(kHfThreads) void k_head_fin(FinalizeArgs f) {
-  __shared__ Partial rec[kHfWaves];
-  __shared__ float zs[kGroup];
-  const int m = blockIdx.x;
+__device__ __forceinline__ void finalize_row(const FinalizeArgs& f, int m, int nthreads, float* zs, Partial* rec) {
   const int l = lane_id(), w = wave_id();
+  const int nwaves = nthreads / kWave;
   Partial acc = partial_empty();
   const Partial* pp = f.partials + static_cast<int64_t>(m) * f.partials_ld;
-  for (int p = threadIdx.x; p < f.P; p += kHfThreads) partial_merge(acc, pp[p]);
+  for (int p = threadIdx.x; p < f.P; p += nthreads) partial_merge(acc, pp[p]);
   wave_partial_merge(acc);
   if (l == 0) rec[w] = acc;
   __syncthreads();
-  acc = l < kHfWaves ? rec[l] : partial_empty();
+  acc = l < nwaves ? rec[l] : partial_empty();
   wave_partial_merge(acc);   // the same result in every wave
   const float lse = acc.m + logf(acc.s);
 
@@ -311,39 +324,41 @@ __global__ __launch_bounds__(kHfThreads) void k_head_fin(FinalizeArgs f) {
     tok = acc.zid;
     ytok = acc.zmax * f.invT;
   } else {
-    // recompute the 64 logits of the winning group, 4 rows per wave, loads issued together
+    // recompute the 64 logits of the winning group, 64 / nwaves rows per wave, loads together
+    const int rpw = kGroup / nwaves;
     const int C = static_cast<int>(f.K * (BF16 ? 2 : 4) / 16);
     const int CPL = (C + kWave - 1) / kWave;
     const uint32_t rowbytes = static_cast<uint32_t>(C) * 16;
     const int64_t gbase = static_cast<int64_t>(acc.g == 0x7fffffff ? 0 : acc.g) * kGroup;
-    const int64_t r0 = gbase + w * kHfRowsPerWave;
-    const int nrows = f.V - r0 >= kHfRowsPerWave ? kHfRowsPerWave : (f.V - r0 > 0 ? static_cast<int>(f.V - r0) : 0);
+    const int64_t r0 = gbase + w * rpw;
+    const int nrows = f.V - r0 >= rpw ? rpw : (f.V - r0 > 0 ? static_cast<int>(f.V - r0) : 0);
     const rsrc_t wrs = make_rsrc(static_cast<const char*>(f.W) + static_cast<size_t>(nrows > 0 ? r0 : 0) * rowbytes,
                                  static_cast<uint32_t>(nrows) * rowbytes);
     const rsrc_t xrs = make_rsrc(static_cast<const char*>(f.x) + static_cast<size_t>(m) * rowbytes, rowbytes);
-    float z[kHfRowsPerWave];
+    for (int j0 = 0; j0 < rpw; j0 += 4) {
+      float z[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int q0 = 0; q0 < CPL; q0 += 4) {
+        uint4 xv[4], wv[4][4];
 #pragma unroll
-    for (int j = 0; j < kHfRowsPerWave; ++j) z[j] = 0.f;
-    for (int q0 = 0; q0 < CPL; q0 += 4) {
-      uint4 xv[4], wv[4][kHfRowsPerWave];
+        for (int qq = 0; qq < 4; ++qq) {
+          const int c = (q0 + qq) * kWave + l;
+          const bool cok = q0 + qq < CPL && c < C;
+          xv[qq] = buffer_load16(xrs, cok ? static_cast<uint32_t>(c) * 16 : kOutOfRange);
 #pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-        const int c = (q0 + qq) * kWave + l;
-        const bool cok = q0 + qq < CPL && c < C;
-        xv[qq] = buffer_load16(xrs, cok ? static_cast<uint32_t>(c) * 16 : kOutOfRange);
+          for (int j = 0; j < 4; ++j)
+            wv[qq][j] = buffer_load16(wrs, cok ? static_cast<uint32_t>(j0 + j) * rowbytes + static_cast<uint32_t>(c) * 16
+                                               : kOutOfRange);
+        }
 #pragma unroll
-        for (int j = 0; j < kHfRowsPerWave; ++j)
-          wv[qq][j] = buffer_load16(wrs, cok ? static_cast<uint32_t>(j) * rowbytes + static_cast<uint32_t>(c) * 16 : kOutOfRange);
+        for (int qq = 0; qq < 4; ++qq)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) z[j] = chunk_dot<BF16>(wv[qq][j], xv[qq], z[j]);
       }
 #pragma unroll
-      for (int qq = 0; qq < 4; ++qq)
-#pragma unroll
-        for (int j = 0; j < kHfRowsPerWave; ++j) z[j] = chunk_dot<BF16>(wv[qq][j], xv[qq], z[j]);
-    }
-#pragma unroll
-    for (int j = 0; j < kHfRowsPerWave; ++j) {
-      const float s = wave_sum(z[j]);
-      if (l == 0) zs[w * kHfRowsPerWave + j] = s;
+      for (int j = 0; j < 4; ++j) {
+        const float s = wave_sum(z[j]);
+        if (l == 0) zs[w * rpw + j0 + j] = s;
+      }
     }
     __syncthreads();
     if (w != 0) return;   // the element draw is one wave's work
@@ -362,6 +377,15 @@ __global__ __launch_bounds__(kHfThreads) void k_head_fin(FinalizeArgs f) {
     if (f.lse) f.lse[m] = lse;
     if (f.logprob) f.logprob[m] = ytok - lse;
   }
+}
+
+constexpr int kHfThreads = 1024;
+
+template <bool BF16>
+__global__ __launch_bounds__(kHfThreads) void k_head_fin(FinalizeArgs f) {
+  __shared__ Partial rec[kHfThreads / kWave];
+  __shared__ float zs[kGroup];
+  finalize_row<BF16>(f, static_cast<int>(blockIdx.x), kHfThreads, zs, rec);
 }
 
 // ----------------------------------------------------------------------------------------
@@ -387,23 +411,19 @@ int tile_ks(int64_t K) {
 int tile_ncb(int64_t M) { return static_cast<int>((M + 15) / 16); }
 int tile_lds(int ncb, int ks) {
   const int stage = ncb * 16 * (ks * 4 + 4) * 16;
-  const int rec = 4 * ncb * 16 * static_cast<int>(sizeof(Partial));
+  const int rec = kTileWaves * ncb * 16 * static_cast<int>(sizeof(Partial));
   return stage > rec ? stage : rec;
 }
 
 template <int NCB, int KS, bool ZOUT, int EPI>
 hipError_t run_tile(const TileArgs& a, int grid, hipStream_t st) {
-  if constexpr (NCB * KS > kMaxBFrags) {
-    return hipErrorInvalidValue;   // excluded by head_tile_supported
-  } else {
-    const int lds = tile_lds(NCB, KS);
-    hipError_t e = allow_lds_tile(k_head_tile<NCB, KS, ZOUT, EPI>, lds);
-    if (e != hipSuccess) return e;
-    TraceScope ts("head_tile", st);
-    hipLaunchKernelGGL((k_head_tile<NCB, KS, ZOUT, EPI>), dim3(static_cast<unsigned>(grid)), dim3(kTileThreads), lds,
-                       st, a);
-    return hipGetLastError();
-  }
+  constexpr int lds = TilePass<NCB, KS, ZOUT, EPI>::kLds;
+  hipError_t e = allow_lds_tile(k_head_tile<NCB, KS, ZOUT, EPI>, lds);
+  if (e != hipSuccess) return e;
+  TraceScope ts("head_tile", st);
+  hipLaunchKernelGGL((k_head_tile<NCB, KS, ZOUT, EPI>), dim3(static_cast<unsigned>(grid)), dim3(kTileThreads), lds,
+                     st, a);
+  return hipGetLastError();
 }
 
 template <int NCB, int KS>
@@ -452,7 +472,7 @@ int head_tile_grid(int64_t M, int64_t K, int64_t V) {
   if (device_info(&di) != hipSuccess) di.cus = 256;
   // one workgroup (four waves) per CU: the activation fragments take most of the register file
   const int64_t NG = (V + kGroup - 1) / kGroup;
-  int64_t grid = (NG + 3) / 4;
+  int64_t grid = (NG + kTileWaves - 1) / kTileWaves;
   if (grid > di.cus) grid = di.cus;
   if (grid > kMaxPartials) grid = kMaxPartials;
   return static_cast<int>(grid < 1 ? 1 : grid);

@@ -70,6 +70,7 @@ struct TileArgs {
   int64_t partials_ld;
 };
 bool head_tile_supported(int64_t M, int64_t K, int64_t V, bool bf16);
+
 // workgroups of a tile pass over V rows for passes of up to M activation rows
 int head_tile_grid(int64_t M, int64_t K, int64_t V);
 hipError_t launch_head_tile(const TileArgs& a, int grid, hipStream_t st);

@@ -87,6 +87,23 @@ def test_lowrank_small(case, mode, T):
     _lowrank(*case, mode, T)
 
 
+# shapes of the tile-streaming pass (bf16, r = 128..512 in steps of 32, at most 64 rows) with
+# several groups per wave: ragged V, d not a multiple of 32, 1..64 rows
+LOWRANK_TILE = [
+    (520, 8200, 128, 1, "bf16"),
+    (520, 8200, 128, 6, "bf16"),
+    (512, 8200, 256, 17, "bf16"),
+    (520, 20000, 384, 48, "bf16"),
+    (1024, 20000, 512, 64, "bf16"),
+]
+
+
+@pytest.mark.parametrize("mode,T", [("greedy", 1.0), ("sample", 1.0), ("sample", 0.7)])
+@pytest.mark.parametrize("case", LOWRANK_TILE, ids=lambda c: "d%d-V%d-r%d-M%d-%s" % c)
+def test_lowrank_tile(case, mode, T):
+    _lowrank(*case, mode, T, want_logits=False)
+
+
 DENSE_SMALL = [
     (256, 1024, 4, "f32"),
     (520, 1000, 3, "bf16"),    # 65 chunks per row: two chunks per lane, masked
