@@ -32,13 +32,15 @@ constexpr int kMaxPartials = 2048;   // upper bound on producer workgroups per r
 //   (m, s):      online log-sum-exp of y = z / T over the rows seen: lse = m + log s
 //   (gscore, g): best group score L_g + Gumbel(u_g) and its group id (sampling)
 //   (zmax, zid): largest raw logit and its id, lowest id on ties (greedy)
+//   xz:          verification rows: the raw logit at the row's draft token when the token
+//                lies in this part of the vocabulary, else -inf
 // ---------------------------------------------------------------------------------------
 struct alignas(16) Partial {
   float m, s, gscore;
   int32_t g;
   float zmax;
   int32_t zid;
-  float pad0, pad1;
+  float xz, pad1;
 };
 
 __device__ __forceinline__ Partial partial_empty() {
@@ -49,7 +51,8 @@ __device__ __forceinline__ Partial partial_empty() {
   p.g = 0x7fffffff;
   p.zmax = -INFINITY;
   p.zid = 0x7fffffff;
-  p.pad0 = p.pad1 = 0.f;
+  p.xz = -INFINITY;
+  p.pad1 = 0.f;
   return p;
 }
 

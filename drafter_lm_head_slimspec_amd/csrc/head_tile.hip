@@ -268,7 +268,8 @@ struct TilePass {
       p.g = gid;
       p.zmax = bz;
       p.zid = bi;
-      p.pad0 = p.pad1 = 0.f;
+      p.xz = -INFINITY;
+      p.pad1 = 0.f;
       rec[w * NC + m] = p;
     }
     __syncthreads();

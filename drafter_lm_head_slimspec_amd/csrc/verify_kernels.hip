@@ -189,7 +189,17 @@ __global__ __launch_bounds__(256) void k_verify_rows(VerifyArgs a) {
     p.s = S;
   }
   Partial out = block_merge(p, red4);
-  if (threadIdx.x == 0) a.partials[(b * R + r) * a.S + s] = out;
+  if (threadIdx.x == 0) {
+    // sampling: the raw logit at this row's draft token if it lies in the segment, so that
+    // acceptance finds it among the partials instead of in the logit row
+    out.xz = -INFINITY;
+    if constexpr (!GREEDY) {
+      const int t = r < a.gamma ? r : r - static_cast<int>(a.gamma) - 1;
+      const int32_t x = a.tokens[b * a.gamma + t];
+      if (x >= e_begin && x < e_end) out.xz = load_logit<BF16>(row, x);
+    }
+    a.partials[(b * R + r) * a.S + s] = out;
+  }
 }
 
 // Element draw of a two-level Gumbel-max inside 64-element group g (wave 0): returns the
@@ -210,15 +220,32 @@ __device__ __forceinline__ int32_t draw_in_group(int32_t g, int64_t V, uint64_t 
 // Merges the row partials of sequence b into rowp (lane i of a wave loads segment partial i,
 // S <= 64, merged by a fixed butterfly: every kernel that calls this computes the same
 // values) and returns the leading-accept count (acceptance of all positions at once, lane t).
+// The draft token's logits come from the partials' xz fields, so no logit row is read here.
 template <bool BF16>
 __device__ int seq_accept(const VerifyArgs& a, int64_t b, Partial* rowp, int* sh_a) {
   const int l = lane_id(), w = wave_id();
   const int R = rows_per_seq(a.mode, a.gamma);
   const int gamma = static_cast<int>(a.gamma);
-  for (int r = w; r < R; r += blockDim.x / kWave) {
-    Partial p = l < a.S ? a.partials[(b * R + r) * a.S + l] : partial_empty();
-    wave_partial_merge(p);
-    if (l == 0) rowp[r] = p;
+  const int nw = blockDim.x / kWave;
+  // up to kAccBatch rows per wave at a time, every load of a batch issued before the merges
+  constexpr int kAccBatch = 4;
+  for (int r0 = w; r0 < R; r0 += nw * kAccBatch) {
+    Partial p[kAccBatch];
+#pragma unroll
+    for (int j = 0; j < kAccBatch; ++j) {
+      const int r = r0 + j * nw;
+      p[j] = (r < R && l < a.S) ? a.partials[(b * R + r) * a.S + l] : partial_empty();
+    }
+#pragma unroll
+    for (int j = 0; j < kAccBatch; ++j) {
+      const int r = r0 + j * nw;
+      const float xz = wave_max(p[j].xz);   // one segment at most holds a finite value
+      wave_partial_merge(p[j]);
+      if (l == 0 && r < R) {
+        p[j].xz = xz;
+        rowp[r] = p[j];
+      }
+    }
   }
   __syncthreads();
   if (w == 0) {
@@ -229,8 +256,8 @@ __device__ int seq_accept(const VerifyArgs& a, int64_t b, Partial* rowp, int* sh
       if (a.mode == 0) {
         acc = valid && x == rowp[l].zid;
       } else if (valid) {
-        const float yp = load_logit<BF16>(row_ptr<BF16>(a, b, l), x) * a.invT;
-        const float yq = load_logit<BF16>(row_ptr<BF16>(a, b, gamma + 1 + l), x) * a.invT;
+        const float yp = rowp[l].xz * a.invT;
+        const float yq = rowp[gamma + 1 + l].xz * a.invT;
         const float lp = yp - (rowp[l].m + logf(rowp[l].s));
         const float lq = yq - (rowp[gamma + 1 + l].m + logf(rowp[gamma + 1 + l].s));
         acc = a.u[b * a.gamma + l] < expf(lp - lq);
@@ -245,6 +272,7 @@ __device__ int seq_accept(const VerifyArgs& a, int64_t b, Partial* rowp, int* sh
 }
 
 constexpr int kMaxVerifyRows = 2 * 64 + 1;
+constexpr int kResidGroups = 1024;   // groups of a residual segment handled per round
 
 // Residual group scores of one vocabulary segment of the rejected position (sampling only):
 // per group log2 of sum max(0, p - q), with p = exp2(z_p c - lse_p log2 e) and q likewise.
@@ -257,6 +285,7 @@ __global__ __launch_bounds__(256) void k_verify_resid(VerifyArgs a) {
   __shared__ Partial rowp[kMaxVerifyRows];
   __shared__ Partial red4[4];
   __shared__ int sh_a;
+  __shared__ float gw[kResidGroups];   // log2 weight of each group of the current round
   const int s2 = blockIdx.x;
   const int64_t b = blockIdx.y;
   const int l = lane_id();
@@ -289,38 +318,58 @@ __global__ __launch_bounds__(256) void k_verify_resid(VerifyArgs a) {
       buf[2 * u + 1] = buffer_load16(rq, (e < n && !bonus) ? e * ES : kOutOfRange);
     }
   };
-  pipelined<2 * UNR>(n, step * UNR, load, [&](uint4 (&buf)[2 * UNR], uint32_t base) {
+  // the segment's groups in rounds of kResidGroups: first their log2 weights into LDS ...
+  const int64_t g_first = e_begin / kGroup;
+  for (uint32_t r0 = 0; r0 < n; r0 += kResidGroups * kGroup) {
+    const uint32_t rn = n - r0 < kResidGroups * kGroup ? n - r0 : kResidGroups * kGroup;
+    pipelined<2 * UNR>(rn, step * UNR, [&](uint4 (&buf)[2 * UNR], uint32_t base) { load(buf, r0 + base); },
+                       [&](uint4 (&buf)[2 * UNR], uint32_t base) {
 #pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      const uint32_t e = base + u * step + tid * EPT;
-      const bool in = e < n;
-      float vp[EPT], vq[EPT];
-      unpack<BF16>(buf[2 * u], vp);
-      unpack<BF16>(buf[2 * u + 1], vq);
-      float gr = 0.f, gm = 0.f;   // group score log2 sum, relative to gm
-      if (bonus) {
-        // log-sum-exp of the group's y values (base 2), max-shifted over its LPG lanes
-        gm = in ? chunk_max<EPT>(vp) * c : -INFINITY;
+      for (int u = 0; u < UNR; ++u) {
+        const uint32_t e = base + u * step + tid * EPT;   // relative to r0
+        const bool in = e < rn;
+        float vp[EPT], vq[EPT];
+        unpack<BF16>(buf[2 * u], vp);
+        unpack<BF16>(buf[2 * u + 1], vq);
+        float gr = 0.f, gm = 0.f;   // group weight = 2^gm * gr
+        if (bonus) {
+          // log-sum-exp of the group's y values (base 2), max-shifted over its LPG lanes
+          gm = in ? chunk_max<EPT>(vp) * c : -INFINITY;
 #pragma unroll
-        for (int o = 1; o < LPG; o <<= 1) gm = fmaxf(gm, xor_lane(gm, o));
-        if (in) {
+          for (int o = 1; o < LPG; o <<= 1) gm = fmaxf(gm, xor_lane(gm, o));
+          if (in) {
 #pragma unroll
-          for (int i = 0; i < EPT; ++i) gr += fast_exp2(fmaf(vp[i], c, -gm));
+            for (int i = 0; i < EPT; ++i) gr += fast_exp2(fmaf(vp[i], c, -gm));
+          }
+        } else if (in) {
+#pragma unroll
+          for (int i = 0; i < EPT; ++i)
+            gr += fmaxf(fast_exp2(fmaf(vp[i], c, -Lp)) - fast_exp2(fmaf(vq[i], c, -Lq)), 0.f);
         }
-      } else if (in) {
 #pragma unroll
-        for (int i = 0; i < EPT; ++i)
-          gr += fmaxf(fast_exp2(fmaf(vp[i], c, -Lp)) - fast_exp2(fmaf(vq[i], c, -Lq)), 0.f);
+        for (int o = 1; o < LPG; o <<= 1) gr += xor_lane(gr, o);
+        if (in && (l % LPG) == 0) gw[e / kGroup] = gr > 0.f ? gm + log2f(gr) : -INFINITY;
       }
+    });
+    __syncthreads();
+    // ... then one Philox block per four consecutive groups, all threads at once
+    const int64_t ga = g_first + r0 / kGroup;                 // first group of the round
+    const int64_t gb = ga + (rn + kGroup - 1) / kGroup;       // one past the last
+    for (int64_t q = ga / 4 + tid; q * 4 < gb; q += blockDim.x) {
+      uint64_t words[4];
+      philox_block(a.seed, a.offset, purpose, static_cast<uint64_t>(b), static_cast<uint64_t>(q) * 4, words);
 #pragma unroll
-      for (int o = 1; o < LPG; o <<= 1) gr += xor_lane(gr, o);
-      if (in && (l % LPG) == 0 && gr > 0.f) {
-        const int64_t gi = (e_begin + e) / kGroup;
-        const float G = gumbel(philox_uniform(a.seed, a.offset, purpose, b, gi));
-        argmax_merge(best.gscore, best.g, (gm + log2f(gr)) * kLn2 + G, static_cast<int32_t>(gi));
+      for (int j = 0; j < 4; ++j) {
+        const int64_t gi = q * 4 + j;
+        if (gi >= ga && gi < gb) {
+          const float lw = gw[gi - ga];
+          if (lw != -INFINITY)
+            argmax_merge(best.gscore, best.g, lw * kLn2 + gumbel(word_to_uniform(words[j])), static_cast<int32_t>(gi));
+        }
       }
     }
-  });
+    __syncthreads();   // gw is rewritten by the next round
+  }
   best = block_merge(best, red4);
   if (threadIdx.x == 0) a.partials2[b * a.S2 + s2] = best;
 }
