@@ -45,6 +45,10 @@ def parse():
     p.add_argument("--no-trace", action="store_true", help="skip the per-kernel event pass")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a device-to-device copy of this many MiB (counter calibration)")
+    p.add_argument("--traffic-summary", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
+                   help="only write the HBM traffic summary of the headline kernel from four rocprofv3 "
+                        "--pmc counter_collection.csv files (head leg FETCH_SIZE, WRITE_SIZE; the "
+                        "calibration copy's FETCH_SIZE, WRITE_SIZE)")
     return p.parse_args()
 
 
@@ -56,12 +60,73 @@ def sha_of(paths):
     return h.hexdigest()
 
 
-KERNEL_SOURCES = ["drafter_lm_head_slimspec_amd/csrc/head_kernels.hip",
+KERNEL_SOURCES = ["drafter_lm_head_slimspec_amd/csrc/head_tile.hip",
                   "drafter_lm_head_slimspec_amd/csrc/device_common.h"]
+HEAD_KERNEL = "k_head_tile"
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic_head_tile_llama_lowrank_M48.json")
+COPY_MIB = 1024
+COPY_LAUNCHES = 3
+
+
+def counter_kib(path, kernel, counter, launches=None):
+    """KiB per dispatch of `counter` over the dispatches whose name contains `kernel`; with
+    `launches`, the sum over all matching dispatches divided by that many launches (a copy
+    the runtime splits into several dispatches)."""
+    import csv
+    vals = {}
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            if kernel in row["Kernel_Name"] and row["Counter_Name"] == counter:
+                d = row["Dispatch_Id"]
+                vals[d] = vals.get(d, 0.0) + float(row["Counter_Value"])
+    if not vals:
+        raise SystemExit(f"no {counter} rows for {kernel} in {path}")
+    tot = sum(vals.values())
+    return tot / launches if launches else tot / len(vals), len(vals)
+
+
+def traffic_summary(paths):
+    """HBM bytes per launch of the headline kernel: its FETCH_SIZE / WRITE_SIZE readings, each
+    scaled by the ratio of a device copy's known byte count to the same counter's reading."""
+    fpath, wpath, cfpath, cwpath = paths
+    fk, nf = counter_kib(fpath, HEAD_KERNEL, "FETCH_SIZE")
+    wk, nw = counter_kib(wpath, HEAD_KERNEL, "WRITE_SIZE")
+    copy_bytes = COPY_MIB << 20
+    cf, _ = counter_kib(cfpath, "copyBuffer", "FETCH_SIZE", COPY_LAUNCHES)
+    cw, _ = counter_kib(cwpath, "copyBuffer", "WRITE_SIZE", COPY_LAUNCHES)
+    fscale, wscale = copy_bytes / (cf * 1024), copy_bytes / (cw * 1024)
+    from drafter_lm_head_slimspec_amd import configs
+    w = configs.LLAMA
+    alg = w.V * w.r * 2 + 48 * w.r * 2
+    hbm = fk * 1024 * fscale + wk * 1024 * wscale
+    out = {"kernel": HEAD_KERNEL, "workload": "llama3.1-8b-head low-rank r=512, 48 rows, sampling",
+           "source_sha256": sha_of(KERNEL_SOURCES), "source_files": KERNEL_SOURCES,
+           "dispatches": {"fetch": nf, "write": nw},
+           "fetch_kib_per_dispatch": fk, "write_kib_per_dispatch": wk, "copy_calibration_mib": COPY_MIB,
+           "fetch_scale": fscale, "write_scale": wscale, "hbm_bytes_per_launch": hbm,
+           "alg_bytes_per_launch": alg, "traffic_over_alg": hbm / alg,
+           "commands": [
+               "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o run -- "
+               "python3 bench.py --legs lowrank48 --steps 10 --warmup 2 --no-trace --no-cpu-baseline",
+               "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o run -- "
+               "python3 bench.py --legs lowrank48 --steps 10 --warmup 2 --no-trace --no-cpu-baseline",
+               "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_copyF -o run -- "
+               f"python3 bench.py --copy-calibration {COPY_MIB}",
+               "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_copyW -o run -- "
+               f"python3 bench.py --copy-calibration {COPY_MIB}",
+               "python3 bench.py --traffic-summary gpurun_out/pmc_fetch/run_counter_collection.csv "
+               "gpurun_out/pmc_write/run_counter_collection.csv gpurun_out/pmc_copyF/run_counter_collection.csv "
+               "gpurun_out/pmc_copyW/run_counter_collection.csv"]}
+    with open(TRAFFIC_JSON, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps({"hbm_bytes_per_launch": hbm, "traffic_over_alg": hbm / alg}))
 
 
 def main():
     args = parse()
+    if args.traffic_summary:
+        traffic_summary(args.traffic_summary)
+        return
     if args.gpus != 1:
         log(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for {args.gpus}).")
         sys.exit(2)
@@ -77,10 +142,10 @@ def main():
         a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
         b = torch.empty_like(a)
         torch.cuda.synchronize()
-        for _ in range(3):
+        for _ in range(COPY_LAUNCHES):
             b.copy_(a)
         torch.cuda.synchronize()
-        print(json.dumps({"copy_bytes": n, "launches": 3}))
+        print(json.dumps({"copy_bytes": n, "launches": COPY_LAUNCHES}))
         return
 
     w = configs.LLAMA
@@ -291,9 +356,8 @@ def main():
         kbytes = V * r * 2 + 48 * r * 2   # the W_up pass: W_up and h_r
         achieved = kbytes / (kavg * 1e-6) / 1e9
         traffic = None
-        tpath = os.path.join(ROOT, "profiles", "traffic_stream_mfma_llama_lowrank_M48.json")
-        if os.path.exists(tpath):
-            t = json.load(open(tpath))
+        if kname == "head_tile" and os.path.exists(TRAFFIC_JSON):
+            t = json.load(open(TRAFFIC_JSON))
             if t.get("source_sha256") == sha_of(KERNEL_SOURCES):
                 traffic = t.get("hbm_bytes_per_launch")
         line["roofline"] = {"bound": "hbm", "kernel": kname, "achieved": achieved, "peak": HBM_PEAK_GBS,
