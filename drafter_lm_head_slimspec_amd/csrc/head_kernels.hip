@@ -1,7 +1,9 @@
 // Drafter LM-head kernels for gfx950.
 //
 //   k_rowdot        h_r = round(W_down h): the SlimSpec d -> r map (SlimSpec write-up,
-//                   section 三) and the SpecVocab d -> d' map (SpecVocab write-up, 2.2.1).
+//                   section 三) and the SpecVocab d -> d' map (SpecVocab write-up, 2.2.1);
+//                   fp32 on VALU, bf16 on MFMA (k_rowdot_tile in one pass for up to 64 rows,
+//                   k_rowdot_mfma + k_rowdot_reduce split over K beyond that).
 //   k_stream_valu   skinny head product (M <= 8 rows): coalesced 16-byte weight streaming,
 //                   one 64-row vocabulary group per wave at a time.
 //   k_stream_mfma16 the same contract once the rows make the product dense (M > 8):
@@ -206,6 +208,91 @@ __global__ __launch_bounds__(256) void k_rowdot_reduce(const float* __restrict__
     const int64_t z0 = static_cast<int64_t>(blockIdx.x) * per;
     const int64_t z1 = z0 + per < zero_words ? z0 + per : zero_words;
     for (int64_t i = z0 + threadIdx.x; i < z1; i += blockDim.x) zero[i] = 0u;
+  }
+}
+
+// ----------------------------------------------------------------------------------------
+// bf16 down-projection for at most kRdTileMaxM input rows, in one kernel:
+//   k_rowdot_tile    grid (ceil(R/16), ceil(M/16)): a workgroup of 8 waves owns a 16 x 16
+//                    output tile (16 rows of Wd by 16 input rows) over the whole of K; wave w
+//                    takes a contiguous eighth of the 32-wide k-steps (v_mfma_f32_16x16x32_bf16,
+//                    fragments straight from global memory, two batches of 8 k-steps in flight),
+//                    the 8 waves' accumulators are summed in LDS in a fixed order and rounded
+//                    once to bf16.  No split over workgroups, so no second pass and no scratch;
+//                    also clears a scratch block for a later kernel.
+// ----------------------------------------------------------------------------------------
+constexpr int kRdtWaves = 8;
+constexpr int kRdtBatch = 8;                  // k-steps per batch of loads
+constexpr int64_t kRdTileMaxM = 64;
+
+typedef float rd_f32x4_t __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(kRdtWaves * kWave) void k_rowdot_tile(const void* __restrict__ Wd,
+                                                                   const void* __restrict__ x, int R, int K, int M,
+                                                                   uint16_t* __restrict__ out,
+                                                                   uint32_t* __restrict__ zero, int64_t zero_words) {
+  __shared__ float red[kRdtWaves][4][kWave];
+  if (zero != nullptr) {
+    const int64_t nwg = static_cast<int64_t>(gridDim.x) * gridDim.y;
+    const int64_t per = (zero_words + nwg - 1) / nwg;
+    const int64_t z0 = (static_cast<int64_t>(blockIdx.y) * gridDim.x + blockIdx.x) * per;
+    const int64_t z1 = z0 + per < zero_words ? z0 + per : zero_words;
+    for (int64_t i = z0 + threadIdx.x; i < z1; i += blockDim.x) zero[i] = 0u;
+  }
+  const int l = lane_id(), w = wave_id();
+  const int row = l & 15, q = l >> 4;
+  const int j0 = blockIdx.x * 16, m0 = blockIdx.y * 16;
+  const uint32_t rowbytes = static_cast<uint32_t>(K) * 2;
+  const int jrows = R - j0 < 16 ? R - j0 : 16;
+  const int mrows = M - m0 < 16 ? M - m0 : 16;
+  const rsrc_t wrs = make_rsrc(static_cast<const char*>(Wd) + static_cast<size_t>(j0) * rowbytes,
+                               static_cast<uint32_t>(jrows) * rowbytes);
+  const rsrc_t xrs = make_rsrc(static_cast<const char*>(x) + static_cast<size_t>(m0) * rowbytes,
+                               static_cast<uint32_t>(mrows) * rowbytes);
+  const int kst = (K + 31) / 32;
+  const int ksw = (kst + kRdtWaves - 1) / kRdtWaves;
+  const int s0 = w * ksw;
+  const int s1 = s0 + ksw < kst ? s0 + ksw : kst;
+  const uint32_t aoff = row < jrows ? static_cast<uint32_t>(row) * rowbytes : kOutOfRange;
+  const uint32_t boff = row < mrows ? static_cast<uint32_t>(row) * rowbytes : kOutOfRange;
+  // k-step s of this lane: elements 32 s + 8 q .. +8 (rows are whole 16-byte chunks)
+  auto load = [&](uint4 (&A)[kRdtBatch], uint4 (&B)[kRdtBatch], int sb) {
+#pragma unroll
+    for (int t = 0; t < kRdtBatch; ++t) {
+      const int s = sb + t;
+      const int k = s * 32 + q * 8;
+      const bool ok = s < s1 && k < K;
+      A[t] = buffer_load16(wrs, ok && aoff != kOutOfRange ? aoff + static_cast<uint32_t>(k) * 2 : kOutOfRange);
+      B[t] = buffer_load16(xrs, ok && boff != kOutOfRange ? boff + static_cast<uint32_t>(k) * 2 : kOutOfRange);
+    }
+  };
+  rd_f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  auto mma = [&](const uint4 (&A)[kRdtBatch], const uint4 (&B)[kRdtBatch]) {
+#pragma unroll
+    for (int t = 0; t < kRdtBatch; ++t)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, A[t]),
+                                                    __builtin_bit_cast(bf16x8_t, B[t]), acc, 0, 0, 0);
+  };
+  uint4 A0[kRdtBatch], B0[kRdtBatch], A1[kRdtBatch], B1[kRdtBatch];
+  load(A0, B0, s0);
+  for (int sb = s0; sb < s1; sb += 2 * kRdtBatch) {
+    load(A1, B1, sb + kRdtBatch);   // past s1 the loads are out of range: no memory traffic
+    mma(A0, B0);
+    if (sb + 2 * kRdtBatch < s1) load(A0, B0, sb + 2 * kRdtBatch);
+    mma(A1, B1);
+  }
+  // lane l holds rows j0 + 4 (l / 16) + v of column m0 + l % 16
+#pragma unroll
+  for (int v = 0; v < 4; ++v) red[w][v][l] = acc[v];
+  __syncthreads();
+  if (threadIdx.x < 4 * kWave) {
+    const int v = threadIdx.x / kWave, ll = threadIdx.x % kWave;
+    float sum = red[0][v][ll];
+#pragma unroll
+    for (int ww = 1; ww < kRdtWaves; ++ww) sum += red[ww][v][ll];
+    const int j = j0 + 4 * (ll >> 4) + v;
+    const int m = m0 + (ll & 15);
+    if (j < R && m < M) out[static_cast<int64_t>(m) * R + j] = f32_to_bf16_rne(sum);
   }
 }
 
@@ -1141,6 +1228,13 @@ size_t rowdot_scratch_bytes(int64_t M, int64_t R, int64_t K) {
 
 hipError_t launch_rowdot(const void* Wd, const void* x, int64_t R, int64_t K, int64_t M, bool bf16,
                          void* out, float* scratch, hipStream_t st, uint32_t* zero, int64_t zero_words) {
+  if (bf16 && M <= kRdTileMaxM) {
+    const dim3 grid(static_cast<unsigned>((R + 15) / 16), static_cast<unsigned>((M + 15) / 16));
+    TraceScope ts("rowdot_tile", st);
+    hipLaunchKernelGGL(k_rowdot_tile, grid, dim3(kRdtWaves * kWave), 0, st, Wd, x, static_cast<int>(R),
+                       static_cast<int>(K), static_cast<int>(M), static_cast<uint16_t*>(out), zero, zero_words);
+    return hipGetLastError();
+  }
   if (bf16) {
     const int ncb = static_cast<int>((M + 31) / 32) < 6 ? static_cast<int>((M + 31) / 32) : 6;
     hipError_t e;

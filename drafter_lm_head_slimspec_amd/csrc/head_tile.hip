@@ -336,6 +336,9 @@ __device__ __forceinline__ void finalize_row(const FinalizeArgs& f, int m, int n
     const rsrc_t wrs = make_rsrc(static_cast<const char*>(f.W) + static_cast<size_t>(nrows > 0 ? r0 : 0) * rowbytes,
                                  static_cast<uint32_t>(nrows) * rowbytes);
     const rsrc_t xrs = make_rsrc(static_cast<const char*>(f.x) + static_cast<size_t>(m) * rowbytes, rowbytes);
+    // wave 0: the element Gumbel of row gbase + l, computed while the first loads are in flight
+    float gel = 0.f;
+    bool gel_done = w != 0;
     for (int j0 = 0; j0 < rpw; j0 += 4) {
       float z[4] = {0.f, 0.f, 0.f, 0.f};
       for (int q0 = 0; q0 < CPL; q0 += 4) {
@@ -350,6 +353,11 @@ __device__ __forceinline__ void finalize_row(const FinalizeArgs& f, int m, int n
             wv[qq][j] = buffer_load16(wrs, cok ? static_cast<uint32_t>(j0 + j) * rowbytes + static_cast<uint32_t>(c) * 16
                                                : kOutOfRange);
         }
+        if (!gel_done) {
+          gel = gumbel(philox_uniform(f.seed, f.offset, kDraftElem, static_cast<uint64_t>(m),
+                                      static_cast<uint64_t>(gbase + l)));
+          gel_done = true;
+        }
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq)
 #pragma unroll
@@ -363,10 +371,12 @@ __device__ __forceinline__ void finalize_row(const FinalizeArgs& f, int m, int n
     }
     __syncthreads();
     if (w != 0) return;   // the element draw is one wave's work
+    if (!gel_done)
+      gel = gumbel(philox_uniform(f.seed, f.offset, kDraftElem, static_cast<uint64_t>(m), static_cast<uint64_t>(gbase + l)));
     const int64_t row = gbase + l;
     const bool valid = row < f.V;
     const float y = zs[l] * f.invT;
-    float e = valid ? y + gumbel(philox_uniform(f.seed, f.offset, kDraftElem, static_cast<uint64_t>(m), row)) : -INFINITY;
+    float e = valid ? y + gel : -INFINITY;
     int32_t ei = valid ? l : 0x7fffffff;
     wave_argmax(e, ei);
     const int el = ei == 0x7fffffff ? 0 : ei;
