@@ -39,7 +39,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--legs", default="all",
                    help="comma list of legs (lowrank48,lowrank48g,lowrank6,dense48,dense6,specvocab1,"
-                        "specvocab16,verify,verifyg) or 'all' or 'headline'")
+                        "specvocab16,verify,verifyg,verifysparse) or 'all' or 'headline'")
     p.add_argument("--rotate", type=int, default=5, help="device copies of each weight set")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-trace", action="store_true", help="skip the per-kernel event pass")
@@ -152,7 +152,7 @@ def main():
     d, V, r, dp, k = w.d, w.V, w.r, w.dprime, w.k
     seeds = w.seeds
     legs_all = ["lowrank48", "lowrank48g", "lowrank6", "dense48", "dense6", "specvocab1", "specvocab16",
-                "verify", "verifyg"]
+                "verify", "verifyg", "verifysparse"]
     if args.legs == "all":
         legs = legs_all
     elif args.legs == "headline":
@@ -329,6 +329,31 @@ def main():
             o = run_leg(name, calls, vw.B * vw.gamma, alg, "draft tokens")
             o["config"] = {"B": vw.B, "gamma": vw.gamma, "V": vw.V, "sigma": 1.0}
 
+    if "verifysparse" in legs:
+        vw = configs.VERIFY
+        ks = w.k   # the SpecVocab head's candidate count
+        inp = synth.verify_sparse_inputs(vw.B, vw.gamma, vw.V, ks, 1.0, "bf16", vw.seeds)
+        tl = [bf(inp["target"])]
+        for _ in range(2):
+            tl.append(tl[0].clone())
+        idx = torch.from_numpy(inp["idx"]).to(dev)
+        prob = torch.from_numpy(inp["prob"]).to(dev)
+        toks = torch.from_numpy(inp["tokens"]).to(dev)
+        u = torch.from_numpy(inp["u"]).to(dev)
+        need = sh.load().sh_verify_sparse_workspace_bytes(vw.B, vw.gamma, vw.V, ks)
+        calls = []
+        for i in range(3):
+            acc = torch.empty(vw.B, dtype=torch.int32, device=dev)
+            out = torch.empty(vw.B, vw.gamma + 1, dtype=torch.int32, device=dev)
+            ws = torch.zeros(need, dtype=torch.uint8, device=dev)
+            c = sh.prepared("spec_verify_sparse", vw.B, vw.gamma, vw.V, ks, sh.SH_BF16, tl[i], idx, prob, toks, u,
+                            1.0, vw.seeds["philox"], i, acc, out, ws, need, torch.cuda.current_stream().cuda_stream)
+            c.keep = (acc, out, ws)
+            calls.append(c)
+        alg = vw.B * (vw.gamma + 1) * vw.V * 2 + vw.B * vw.gamma * ks * 8 + vw.B * vw.gamma * 8 + vw.B * (vw.gamma + 2) * 4
+        o = run_leg("verifysparse", calls, vw.B * vw.gamma, alg, "draft tokens")
+        o["config"] = {"B": vw.B, "gamma": vw.gamma, "V": vw.V, "k": ks, "sigma": 1.0}
+
     head = results.get("lowrank48")
     line = {
         "metric": METRIC,
@@ -371,6 +396,8 @@ def main():
         line["nu_specvocab1_vs_dense6"] = results["specvocab1"]["ms_per_call"] / results["dense6"]["ms_per_call"]
     if "verify" in results:
         line["verify_tokens_per_s"] = results["verify"]["tokens_per_s"]
+    if "verifysparse" in results:
+        line["verify_sparse_tokens_per_s"] = results["verifysparse"]["tokens_per_s"]
     line["legs"] = {kk: {x: v for x, v in vv.items() if x != "kernels"} for kk, vv in results.items()}
     line["kernels_us"] = {kk: {kn: round(kv["avg_us"], 3) for kn, kv in vv.items()} for kk, vv in kernel_trace.items()}
 

@@ -4,6 +4,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <string>
+#include <utility>
 
 #include "../../include/spechead.h"
 #include "device_common.h"
@@ -158,9 +159,11 @@ struct VerifyLayout {
   int S, S2;
 };
 
-VerifyLayout verify_layout(int mode, int64_t B, int64_t gamma, int64_t V) {
+// kind: 0 greedy, 1 sampling against draft logits, 2 sampling against a sparse draft
+VerifyLayout verify_layout(int kind, int64_t B, int64_t gamma, int64_t V) {
   VerifyLayout L{};
-  const int64_t R = mode == SH_GREEDY ? gamma + 1 : 2 * gamma + 1;
+  const int mode = kind;
+  const int64_t R = sh::verify_rows_per_seq(kind, gamma);
   L.S = sh::verify_segments(B, gamma, V, mode);
   L.S2 = sh::verify_resid_segments(B, V, mode);
   size_t off = 0;
@@ -341,6 +344,11 @@ size_t sh_verify_workspace_bytes(int mode, int64_t B, int64_t gamma, int64_t V) 
   return verify_layout(mode, B, gamma, V).total;
 }
 
+size_t sh_verify_sparse_workspace_bytes(int64_t B, int64_t gamma, int64_t V, int64_t k) {
+  if (B < 1 || gamma < 1 || V < 1 || k < 1 || k > V) return 0;
+  return verify_layout(2, B, gamma, V).total;
+}
+
 size_t sh_topk_workspace_bytes(int64_t M, int64_t V, int64_t k) {
   if (M < 1 || V < 1 || k < 1 || k > V) return 0;
   return topk_layout(M, V).total;
@@ -507,6 +515,59 @@ int spec_verify(int mode, int64_t B, int64_t gamma, int64_t V, int dtype, const 
   a.accept_len = accept_len;
   a.out_tokens = out_tokens;
   const VerifyLayout L = verify_layout(mode, B, gamma, V);
+  char* ws = static_cast<char*>(workspace);
+  a.partials = reinterpret_cast<sh::Partial*>(ws + L.part_off);
+  a.S = L.S;
+  a.partials2 = reinterpret_cast<sh::Partial*>(ws + L.part2_off);
+  a.S2 = L.S2;
+  SH_HIP(sh::launch_verify(a, static_cast<hipStream_t>(stream)), "verify kernels");
+  return SH_OK;
+}
+
+int spec_verify_sparse(int64_t B, int64_t gamma, int64_t V, int64_t k, int dtype, const void* target_logits,
+                       const int32_t* draft_idx, const float* draft_prob, const int32_t* draft_tokens,
+                       const float* u_accept, float temperature, uint64_t seed, uint64_t offset,
+                       int32_t* accept_len, int32_t* out_tokens, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  g_last_error.clear();
+  SH_TRY(check_dtype_mode(dtype, SH_SAMPLE));
+  SH_TRY(check_temperature(temperature));
+  if (B < 1 || B > 65535) return fail(SH_ERR_SHAPE, "B must be in [1, 65535]");
+  if (gamma < 1 || gamma > kMaxGamma) return fail(SH_ERR_SHAPE, "gamma must be in [1, %lld]", static_cast<long long>(kMaxGamma));
+  SH_TRY(check_rowlen("V", V, dtype));
+  if (V > (int64_t{1} << 28)) return fail(SH_ERR_SHAPE, "V above 2^28");
+  if (k < 1 || k > V) return fail(SH_ERR_PARAM, "k must be in [1, V]");
+  if (k > kMaxK) return fail(SH_ERR_UNSUPPORTED, "k above %lld", static_cast<long long>(kMaxK));
+  SH_TRY(check_ptr(target_logits, "target_logits"));
+  const std::pair<const void*, const char*> small[] = {
+      {draft_idx, "draft_idx"}, {draft_prob, "draft_prob"}, {draft_tokens, "draft_tokens"}, {u_accept, "u_accept"}};
+  for (const auto& pn : small) {
+    if (pn.first == nullptr) return fail(SH_ERR_NULL, "%s is NULL", pn.second);
+    if (!aligned(pn.first, 4)) return fail(SH_ERR_ALIGN, "%s is not 4-byte aligned", pn.second);
+  }
+  SH_TRY(check_out(accept_len, "accept_len"));
+  SH_TRY(check_out(out_tokens, "out_tokens"));
+  const size_t need = sh_verify_sparse_workspace_bytes(B, gamma, V, k);
+  SH_TRY(check_workspace(workspace, workspace_bytes, need));
+  sh::VerifyArgs a{};
+  a.mode = 2;
+  a.B = B;
+  a.gamma = gamma;
+  a.V = V;
+  a.bf16 = dtype == SH_BF16;
+  a.target = target_logits;
+  a.draft = nullptr;
+  a.tokens = draft_tokens;
+  a.u = u_accept;
+  a.invT = 1.0f / temperature;
+  a.seed = seed;
+  a.offset = offset;
+  a.accept_len = accept_len;
+  a.out_tokens = out_tokens;
+  a.qidx = draft_idx;
+  a.qprob = draft_prob;
+  a.k = k;
+  const VerifyLayout L = verify_layout(2, B, gamma, V);
   char* ws = static_cast<char*>(workspace);
   a.partials = reinterpret_cast<sh::Partial*>(ws + L.part_off);
   a.S = L.S;

@@ -124,6 +124,8 @@ hipError_t launch_gather_finalize(const float* zbuf, const int32_t* idx, int64_t
                                   float* logprob, hipStream_t st);
 
 // verification
+// mode 0 greedy, 1 sampling against dense draft logits, 2 sampling against a sparse draft
+// distribution (q given on a candidate set per position, zero elsewhere)
 struct VerifyArgs {
   int mode;
   int64_t B, gamma, V;
@@ -140,7 +142,12 @@ struct VerifyArgs {
   int S;
   Partial* partials2;  // [B, S2] residual-segment partials (sampling)
   int S2;
+  const int32_t* qidx;  // mode 2: [B, gamma, k] candidate ids (distinct)
+  const float* qprob;   // mode 2: [B, gamma, k] their draft probabilities
+  int64_t k;
 };
+// target rows + (mode 1) draft rows per sequence
+__host__ __device__ inline int64_t verify_rows_per_seq(int mode, int64_t gamma) { return mode == 1 ? 2 * gamma + 1 : gamma + 1; }
 int verify_segments(int64_t B, int64_t gamma, int64_t V, int mode);
 int verify_resid_segments(int64_t B, int64_t V, int mode);
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t st);

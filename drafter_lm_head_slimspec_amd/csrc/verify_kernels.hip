@@ -7,6 +7,11 @@
 //                   leading-accept count a; its segment of the residual
 //                   norm(max(0, p_a - q_a)) (a < gamma) or of p_gamma (a = gamma, the bonus
 //                   draw) is folded into the group scores of the two-level draw
+//                   With a sparse draft distribution (q given on a candidate set per position,
+//                   the SpecVocab head's top-k probabilities; zero elsewhere) the row pass
+//                   skips the draft rows and looks q_t(x_t) up in the candidate list, and the
+//                   residual is max(0, p - q) with q scattered from that list (equal to p
+//                   outside it; SpecVocab write-up 3.3: verification keeps the full vocabulary).
 //   k_verify_finish one workgroup per sequence: the same acceptance, then the last token
 //                   (greedy: argmax of p_a; sampling: the element draw inside the winning
 //                   residual group, or inside the bonus group of p_gamma) and the outputs
@@ -44,7 +49,7 @@ __device__ __forceinline__ float load_logit(const void* row, int64_t i) {
 }
 
 __device__ __forceinline__ int rows_per_seq(int mode, int64_t gamma) {
-  return mode == 0 ? static_cast<int>(gamma + 1) : static_cast<int>(2 * gamma + 1);
+  return static_cast<int>(verify_rows_per_seq(mode, gamma));
 }
 
 template <bool BF16>
@@ -188,8 +193,22 @@ __global__ __launch_bounds__(256) void k_verify_rows(VerifyArgs a) {
     p.m = M == -INFINITY ? -INFINITY : M * kLn2;
     p.s = S;
   }
+  // sparse draft (segment 0 only): q_t(x_t) from the candidate list, into pad1 (-1: absent)
+  float qx = -1.f;
+  if (!GREEDY && a.mode == 2 && s == 0) {
+    __shared__ float sh_q;
+    if (threadIdx.x == 0) sh_q = 0.f;
+    __syncthreads();
+    const int32_t x = a.tokens[b * a.gamma + r];
+    const int64_t base = (b * a.gamma + r) * a.k;
+    for (int64_t j = threadIdx.x; j < a.k; j += blockDim.x)
+      if (a.qidx[base + j] == x) sh_q = a.qprob[base + j];
+    __syncthreads();
+    qx = sh_q;
+  }
   Partial out = block_merge(p, red4);
   if (threadIdx.x == 0) {
+    out.pad1 = qx;
     // sampling: the raw logit at this row's draft token if it lies in the segment, so that
     // acceptance finds it among the partials instead of in the logit row
     out.xz = -INFINITY;
@@ -240,9 +259,11 @@ __device__ int seq_accept(const VerifyArgs& a, int64_t b, Partial* rowp, int* sh
     for (int j = 0; j < kAccBatch; ++j) {
       const int r = r0 + j * nw;
       const float xz = wave_max(p[j].xz);   // one segment at most holds a finite value
+      const float qx = wave_max(l < a.S ? p[j].pad1 : -1.f);   // sparse draft: segment 0 holds it
       wave_partial_merge(p[j]);
       if (l == 0 && r < R) {
         p[j].xz = xz;
+        p[j].pad1 = qx;
         rowp[r] = p[j];
       }
     }
@@ -255,6 +276,12 @@ __device__ int seq_accept(const VerifyArgs& a, int64_t b, Partial* rowp, int* sh
       const bool valid = x >= 0 && x < a.V;
       if (a.mode == 0) {
         acc = valid && x == rowp[l].zid;
+      } else if (a.mode == 2) {
+        // q_t(x) = 0 makes p/q infinite: accepted whenever p_t(x) > 0 (in double precision:
+        // log p above the logarithm of the smallest subnormal)
+        const float lp = rowp[l].xz * a.invT - (rowp[l].m + logf(rowp[l].s));
+        const float qx = rowp[l].pad1;
+        acc = valid && (qx > 0.f ? a.u[b * a.gamma + l] < expf(lp - logf(qx)) : lp > -745.13f);
       } else if (valid) {
         const float yp = rowp[l].xz * a.invT;
         const float yq = rowp[gamma + 1 + l].xz * a.invT;
@@ -273,19 +300,24 @@ __device__ int seq_accept(const VerifyArgs& a, int64_t b, Partial* rowp, int* sh
 
 constexpr int kMaxVerifyRows = 2 * 64 + 1;
 constexpr int kResidGroups = 1024;   // groups of a residual segment handled per round
+constexpr int kSparseRoundGroups = 128;   // the same with a sparse draft (q of the span in LDS)
 
 // Residual group scores of one vocabulary segment of the rejected position (sampling only):
-// per group log2 of sum max(0, p - q), with p = exp2(z_p c - lse_p log2 e) and q likewise.
-template <bool BF16>
+// per group log2 of sum max(0, p - q), with p = exp2(z_p c - lse_p log2 e) and q likewise
+// (dense draft), or q from the candidate list, scattered into LDS one round at a time
+// (sparse draft: zero outside the candidates).
+template <bool BF16, bool SPARSE>
 __global__ __launch_bounds__(256) void k_verify_resid(VerifyArgs a) {
   constexpr int EPT = BF16 ? 8 : 4;
   constexpr int LPG = kGroup / EPT;
   constexpr uint32_t ES = BF16 ? 2 : 4;
   constexpr int UNR = 2;
+  constexpr int RG = SPARSE ? kSparseRoundGroups : kResidGroups;   // groups per round
   __shared__ Partial rowp[kMaxVerifyRows];
   __shared__ Partial red4[4];
   __shared__ int sh_a;
-  __shared__ float gw[kResidGroups];   // log2 weight of each group of the current round
+  __shared__ float gw[RG];                             // log2 weight of each group of the round
+  __shared__ float qs[SPARSE ? RG * kGroup : 1];       // sparse draft: q over the round's span
   const int s2 = blockIdx.x;
   const int64_t b = blockIdx.y;
   const int l = lane_id();
@@ -295,10 +327,11 @@ __global__ __launch_bounds__(256) void k_verify_resid(VerifyArgs a) {
   // rejected at a: residual max(0, p_a - q_a); all accepted: the bonus draw from p_gamma
   const bool bonus = acc_len == gamma;
   const char* prow = static_cast<const char*>(row_ptr<BF16>(a, b, acc_len));
-  const char* qrow = bonus ? prow : static_cast<const char*>(row_ptr<BF16>(a, b, gamma + 1 + acc_len));
+  const char* qrow = (bonus || SPARSE) ? prow : static_cast<const char*>(row_ptr<BF16>(a, b, gamma + 1 + acc_len));
+  const bool qdense = !bonus && !SPARSE;
   const float c = a.invT * kLog2e;
   const float Lp = bonus ? 0.f : (rowp[acc_len].m + logf(rowp[acc_len].s)) * kLog2e;
-  const float Lq = bonus ? 0.f : (rowp[gamma + 1 + acc_len].m + logf(rowp[gamma + 1 + acc_len].s)) * kLog2e;
+  const float Lq = qdense ? (rowp[gamma + 1 + acc_len].m + logf(rowp[gamma + 1 + acc_len].s)) * kLog2e : 0.f;
   const uint32_t purpose = bonus ? kBonusGroup : kResidGroup;
   const int64_t NG = (a.V + kGroup - 1) / kGroup;
   const int64_t GPS = (NG + a.S2 - 1) / a.S2;
@@ -315,13 +348,26 @@ __global__ __launch_bounds__(256) void k_verify_resid(VerifyArgs a) {
     for (int u = 0; u < UNR; ++u) {
       const uint32_t e = base + u * step + tid * EPT;
       buf[2 * u] = buffer_load16(rp, e < n ? e * ES : kOutOfRange);
-      buf[2 * u + 1] = buffer_load16(rq, (e < n && !bonus) ? e * ES : kOutOfRange);
+      buf[2 * u + 1] = buffer_load16(rq, (e < n && qdense) ? e * ES : kOutOfRange);
     }
   };
   // the segment's groups in rounds of kResidGroups: first their log2 weights into LDS ...
   const int64_t g_first = e_begin / kGroup;
-  for (uint32_t r0 = 0; r0 < n; r0 += kResidGroups * kGroup) {
-    const uint32_t rn = n - r0 < kResidGroups * kGroup ? n - r0 : kResidGroups * kGroup;
+  for (uint32_t r0 = 0; r0 < n; r0 += RG * kGroup) {
+    const uint32_t rn = n - r0 < RG * kGroup ? n - r0 : RG * kGroup;
+    if constexpr (SPARSE) {
+      if (!bonus) {
+        for (uint32_t i = tid; i < rn; i += blockDim.x) qs[i] = 0.f;
+        __syncthreads();
+        const int64_t lo = e_begin + r0, hi = lo + rn;
+        const int64_t base = (b * a.gamma + acc_len) * a.k;
+        for (int64_t j = tid; j < a.k; j += blockDim.x) {
+          const int32_t id = a.qidx[base + j];
+          if (id >= lo && id < hi) qs[id - lo] = a.qprob[base + j];
+        }
+        __syncthreads();
+      }
+    }
     pipelined<2 * UNR>(rn, step * UNR, [&](uint4 (&buf)[2 * UNR], uint32_t base) { load(buf, r0 + base); },
                        [&](uint4 (&buf)[2 * UNR], uint32_t base) {
 #pragma unroll
@@ -342,9 +388,16 @@ __global__ __launch_bounds__(256) void k_verify_resid(VerifyArgs a) {
             for (int i = 0; i < EPT; ++i) gr += fast_exp2(fmaf(vp[i], c, -gm));
           }
         } else if (in) {
+          if constexpr (SPARSE) {
 #pragma unroll
-          for (int i = 0; i < EPT; ++i)
-            gr += fmaxf(fast_exp2(fmaf(vp[i], c, -Lp)) - fast_exp2(fmaf(vq[i], c, -Lq)), 0.f);
+            for (int i = 0; i < EPT; ++i) vq[i] = qs[e + i];
+#pragma unroll
+            for (int i = 0; i < EPT; ++i) gr += fmaxf(fast_exp2(fmaf(vp[i], c, -Lp)) - vq[i], 0.f);
+          } else {
+#pragma unroll
+            for (int i = 0; i < EPT; ++i)
+              gr += fmaxf(fast_exp2(fmaf(vp[i], c, -Lp)) - fast_exp2(fmaf(vq[i], c, -Lq)), 0.f);
+          }
         }
 #pragma unroll
         for (int o = 1; o < LPG; o <<= 1) gr += xor_lane(gr, o);
@@ -385,17 +438,33 @@ __global__ __launch_bounds__(256) void k_verify_finish(VerifyArgs a) {
   const int64_t b = blockIdx.x;
   const int l = lane_id(), w = wave_id();
   const int gamma = static_cast<int>(a.gamma);
+  __shared__ float qg[kGroup];   // sparse draft: q over the winning residual group
   const int acc_len = seq_accept<BF16>(a, b, rowp, &sh_a);
-  const bool resid = a.mode == 1 && acc_len < gamma;
+  const bool resid = a.mode != 0 && acc_len < gamma;
+  const bool qdense = resid && a.mode == 1;
   const char* prow = static_cast<const char*>(row_ptr<BF16>(a, b, acc_len));
-  const char* qrow = resid ? static_cast<const char*>(row_ptr<BF16>(a, b, gamma + 1 + acc_len)) : nullptr;
+  const char* qrow = qdense ? static_cast<const char*>(row_ptr<BF16>(a, b, gamma + 1 + acc_len)) : nullptr;
   const float c = a.invT * kLog2e;
   const float Lp = (rowp[acc_len].m + logf(rowp[acc_len].s)) * kLog2e;
-  const float Lq = resid ? (rowp[gamma + 1 + acc_len].m + logf(rowp[gamma + 1 + acc_len].s)) * kLog2e : 0.f;
+  const float Lq = qdense ? (rowp[gamma + 1 + acc_len].m + logf(rowp[gamma + 1 + acc_len].s)) * kLog2e : 0.f;
   Partial best = partial_empty();
-  if (a.mode == 1) {   // residual or bonus group winner from the residual kernel's segments
+  if (a.mode != 0) {   // residual or bonus group winner from the residual kernel's segments
     best = l < a.S2 ? a.partials2[b * a.S2 + l] : partial_empty();
     wave_partial_merge(best);   // argmax merges: exact in any order
+  }
+  if (a.mode == 2 && resid) {
+    // the candidates that fall in the winning group (every wave merged the same winner)
+    if (threadIdx.x < kGroup) qg[threadIdx.x] = 0.f;
+    __syncthreads();
+    if (best.g != 0x7fffffff) {
+      const int64_t lo = static_cast<int64_t>(best.g) * kGroup;
+      const int64_t base = (b * a.gamma + acc_len) * a.k;
+      for (int64_t j = threadIdx.x; j < a.k; j += blockDim.x) {
+        const int32_t id = a.qidx[base + j];
+        if (id >= lo && id < lo + kGroup) qg[id - lo] = a.qprob[base + j];
+      }
+    }
+    __syncthreads();
   }
   const bool fallback = resid && best.gscore == -INFINITY;
   if (fallback) {
@@ -435,9 +504,9 @@ __global__ __launch_bounds__(256) void k_verify_finish(VerifyArgs a) {
                               [&](int64_t i) { return load_logit<BF16>(prow, i) * a.invT; });
   } else if (!fallback) {
     tok = draw_in_group<BF16>(best.g, a.V, a.seed, a.offset, kResidElem, b, [&](int64_t i) {
-      const float rr = fmaxf(fast_exp2(fmaf(load_logit<BF16>(prow, i), c, -Lp)) -
-                                 fast_exp2(fmaf(load_logit<BF16>(qrow, i), c, -Lq)),
-                             0.f);
+      const float qi = qdense ? fast_exp2(fmaf(load_logit<BF16>(qrow, i), c, -Lq))
+                              : qg[i - static_cast<int64_t>(best.g) * kGroup];
+      const float rr = fmaxf(fast_exp2(fmaf(load_logit<BF16>(prow, i), c, -Lp)) - qi, 0.f);
       return rr > 0.f ? logf(rr) : -INFINITY;
     });
   } else {
@@ -456,7 +525,7 @@ __global__ __launch_bounds__(256) void k_verify_finish(VerifyArgs a) {
 }
 
 int verify_segments(int64_t B, int64_t gamma, int64_t V, int mode) {
-  const int64_t R = mode == 0 ? gamma + 1 : 2 * gamma + 1;
+  const int64_t R = verify_rows_per_seq(mode, gamma);
   const int64_t NG = (V + kGroup - 1) / kGroup;
   int64_t S = (2048 + B * R - 1) / (B * R);
   if (S > 64) S = 64;
@@ -476,7 +545,7 @@ int verify_resid_segments(int64_t B, int64_t V, int mode) {
 }
 
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t st) {
-  const int R = a.mode == 0 ? static_cast<int>(a.gamma + 1) : static_cast<int>(2 * a.gamma + 1);
+  const int R = static_cast<int>(verify_rows_per_seq(a.mode, a.gamma));
   const dim3 grid(static_cast<unsigned>(a.S), static_cast<unsigned>(R), static_cast<unsigned>(a.B));
   {
     TraceScope ts("verify_rows", st);
@@ -494,13 +563,20 @@ hipError_t launch_verify(const VerifyArgs& a, hipStream_t st) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (a.mode == 1) {
+  if (a.mode != 0) {
     const dim3 grid2(static_cast<unsigned>(a.S2), static_cast<unsigned>(a.B));
     TraceScope ts("verify_resid", st);
-    if (a.bf16)
-      hipLaunchKernelGGL(k_verify_resid<true>, grid2, dim3(256), 0, st, a);
-    else
-      hipLaunchKernelGGL(k_verify_resid<false>, grid2, dim3(256), 0, st, a);
+    if (a.mode == 2) {
+      if (a.bf16)
+        hipLaunchKernelGGL((k_verify_resid<true, true>), grid2, dim3(256), 0, st, a);
+      else
+        hipLaunchKernelGGL((k_verify_resid<false, true>), grid2, dim3(256), 0, st, a);
+    } else {
+      if (a.bf16)
+        hipLaunchKernelGGL((k_verify_resid<true, false>), grid2, dim3(256), 0, st, a);
+      else
+        hipLaunchKernelGGL((k_verify_resid<false, false>), grid2, dim3(256), 0, st, a);
+    }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -40,6 +40,9 @@ _SIGS = {
                                   _u64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "spec_verify": (_i, [_i, _i64, _i64, _i64, _i, _vp, _vp, _vp, _vp, _f, _u64, _u64, _vp, _vp, _vp,
                          _sz, _vp]),
+    "sh_verify_sparse_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64]),
+    "spec_verify_sparse": (_i, [_i64, _i64, _i64, _i64, _i, _vp, _vp, _vp, _vp, _vp, _f, _u64, _u64, _vp,
+                                _vp, _vp, _sz, _vp]),
     "sh_topk": (_i, [_vp, _i64, _i64, _i64, _vp, _vp, _sz, _vp]),
     "sh_philox_uniform": (_i, [_u64, _u64, ctypes.c_uint32, _i64, _i64, _vp, _vp]),
     "sh_trace_enable": (_i, [_i64]),
@@ -205,6 +208,31 @@ def spec_verify(target, draft, tokens, u=None, mode="sample", temperature=1.0, s
     _check(lib.spec_verify(m, B, gamma, V, _dt(target), _p(target), _p(draft) if m == SAMPLE else None,
                            _p(tokens), _p(u) if m == SAMPLE else None, float(temperature), int(seed),
                            int(offset), _p(acc), _p(out), _p(ws), ws.numel(), _stream(dev)))
+    return acc, out
+
+
+def spec_verify_sparse(target, draft_idx, draft_prob, tokens, u, temperature=1.0, seed=0, offset=0):
+    """Sampling verification against a sparse draft distribution (draft_prob on draft_idx,
+    zero elsewhere): the SpecVocab head's (topk_idx, topk_prob) per draft position."""
+    lib = load()
+    _contig(target, draft_idx, draft_prob, tokens, u)
+    B, g1, V = target.shape
+    gamma = g1 - 1
+    k = draft_idx.shape[-1]
+    dev = target.device
+    if draft_idx.shape != (B, gamma, k) or draft_prob.shape != (B, gamma, k):
+        raise ValueError("draft_idx / draft_prob must be [B, gamma, k]")
+    if draft_idx.dtype != torch.int32 or tokens.dtype != torch.int32:
+        raise TypeError("draft_idx and draft tokens must be int32")
+    if draft_prob.dtype != torch.float32 or u.dtype != torch.float32:
+        raise TypeError("draft_prob and u must be float32")
+    acc = torch.empty(B, dtype=torch.int32, device=dev)
+    out = torch.empty(B, gamma + 1, dtype=torch.int32, device=dev)
+    need = lib.sh_verify_sparse_workspace_bytes(B, gamma, V, k)
+    ws = workspace(need, dev, "verify")
+    _check(lib.spec_verify_sparse(B, gamma, V, k, _dt(target), _p(target), _p(draft_idx), _p(draft_prob),
+                                  _p(tokens), _p(u), float(temperature), int(seed), int(offset), _p(acc), _p(out),
+                                  _p(ws), ws.numel(), _stream(dev)))
     return acc, out
 
 

@@ -11,7 +11,10 @@ Recipe (per workload; see ``configs``):
 * draft tokens: x ~ categorical(softmax(draft / T)) drawn by NumPy's own Gumbel draws
   (sampling) or x = argmax(draft) (greedy);
 * accept uniforms u = (n + 0.5) * 2^-23 with n uniform in [0, 2^23), drawn by NumPy's
-  Philox bit generator, so u is exact in float32 and strictly inside (0, 1).
+  Philox bit generator, so u is exact in float32 and strictly inside (0, 1);
+* a sparse draft distribution (input data of the sparse verification, in the layout of the
+  SpecVocab head's output): per position the k ids of largest draft logit, with weights
+  exp(draft / T) normalised over those ids, and a token drawn from them.
 bf16 values are produced by PyTorch's float32 -> bfloat16 conversion (round to nearest
 even) and kept as uint16 bit patterns on the host.
 """
@@ -112,3 +115,28 @@ def verify_inputs(B, gamma, V, sigma, dtype, seeds, mode="sample", temperature=1
             tokens[b] = np.argmax(d32 / np.float32(temperature) + g, axis=-1)
     u = uniforms_open((B, gamma), seeds["uniforms"] + int(round(sigma * 1000)))
     return {"target": target, "draft": draft, "tokens": tokens, "u": u}
+
+
+def verify_sparse_inputs(B, gamma, V, k, sigma, dtype, seeds, temperature=1.0, target_std=3.0):
+    """verify_inputs' target logits and uniforms with a sparse draft distribution in place of
+    the draft logits: per position the k ids with the largest draft logits (ascending ids) and
+    q = softmax(draft / T) over those ids alone (the shape of the SpecVocab head's topk_idx /
+    topk_prob); draft tokens are drawn from q."""
+    base = verify_inputs(B, gamma, V, sigma, dtype, seeds, mode="greedy", temperature=temperature,
+                         target_std=target_std)
+    tok_rng = np.random.default_rng([seeds["tokens"], int(round(sigma * 1000)), k])
+    idx = np.empty((B, gamma, k), dtype=np.int32)
+    prob = np.empty((B, gamma, k), dtype=np.float32)
+    tokens = np.empty((B, gamma), dtype=np.int32)
+    for b in range(B):
+        d = as_f32(base["draft"][b], dtype).astype(np.float64) / temperature
+        for t in range(gamma):
+            top = np.sort(np.argpartition(-d[t], k - 1)[:k]) if k < V else np.arange(V)
+            y = d[t, top]
+            w = np.exp(y - y.max())
+            q = (w / w.sum()).astype(np.float32)
+            idx[b, t] = top
+            prob[b, t] = q
+            qq = q.astype(np.float64)
+            tokens[b, t] = top[tok_rng.choice(k, p=qq / qq.sum())]
+    return {"target": base["target"], "idx": idx, "prob": prob, "tokens": tokens, "u": base["u"]}

@@ -75,6 +75,9 @@ size_t sh_head_workspace_bytes(int op, int64_t M, int64_t d, int64_t r, int64_t 
 /* Workspace size for spec_verify.  Pure host arithmetic, no HIP call. */
 size_t sh_verify_workspace_bytes(int mode, int64_t B, int64_t gamma, int64_t V);
 
+/* Workspace size for spec_verify_sparse (0 for invalid sizes).  Pure host arithmetic. */
+size_t sh_verify_sparse_workspace_bytes(int64_t B, int64_t gamma, int64_t V, int64_t k);
+
 /*
  * Dense head (SlimSpec write-up, section 三).
  *   h       [M, d]   hidden states, dtype
@@ -151,6 +154,33 @@ int spec_verify(int mode, int64_t B, int64_t gamma, int64_t V, int dtype,
                 const float* u_accept, float temperature, uint64_t seed, uint64_t offset,
                 int32_t* accept_len, int32_t* out_tokens, void* workspace,
                 size_t workspace_bytes, void* stream);
+
+/*
+ * Sampling verification against a sparse draft distribution: the bridge from the SpecVocab
+ * head (SpecVocab write-up, 2.2.3: the draft's probabilities live on its k candidates; 3.3:
+ * verification keeps the full vocabulary) to speculative sampling (explainer, "为什么答案
+ * 不会变").  q_t is draft_prob on draft_idx and zero elsewhere; p_t = softmax(target_t / T).
+ *   target_logits [B, gamma+1, V] dtype (device)
+ *   draft_idx     [B, gamma, k] int32 (device): candidate ids of each position, distinct,
+ *                 in [0, V) (the SpecVocab head's topk_idx)
+ *   draft_prob    [B, gamma, k] float (device): q on those ids (its topk_prob)
+ *   draft_tokens  [B, gamma] int32, u_accept [B, gamma] float in (0,1) (device)
+ *   B <= 65535, 1 <= gamma <= 64, V <= 2^28, 1 <= k <= min(V, 16384), temperature > 0
+ *   Accept t iff u_t < p_t(x_t) / q_t(x_t); a draft id with q_t(x_t) = 0 is accepted when
+ *   p_t(x_t) > 0 (the ratio is infinite); an id outside [0, V) is never accepted.  If a < gamma
+ *   the last token is drawn from norm(max(0, p_a - q_a)), which is p_a outside the candidates
+ *   (purposes 3/4, row b), else from p_gamma (purposes 5/6, row b), by the same two-level
+ *   Gumbel rule as spec_verify.
+ *   accept_len [B] int32, out_tokens [B, gamma+1] int32 (-1 after the last emitted token).
+ *   Returns SH_ERR_* before any launch on invalid arguments; the call is asynchronous on
+ *   `stream`.  Workspace: sh_verify_sparse_workspace_bytes(B, gamma, V, k), 256-byte aligned,
+ *   contents irrelevant.
+ */
+int spec_verify_sparse(int64_t B, int64_t gamma, int64_t V, int64_t k, int dtype,
+                       const void* target_logits, const int32_t* draft_idx, const float* draft_prob,
+                       const int32_t* draft_tokens, const float* u_accept, float temperature,
+                       uint64_t seed, uint64_t offset, int32_t* accept_len, int32_t* out_tokens,
+                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Top-k building block of draft_head_specvocab (SpecVocab write-up, section 2.2.2), exposed

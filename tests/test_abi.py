@@ -21,7 +21,8 @@ def lib():
 
 def test_header_declares_the_four_entry_points():
     names = libutil.header_functions()
-    for n in ("draft_head_dense", "draft_head_lowrank", "draft_head_specvocab", "spec_verify"):
+    for n in ("draft_head_dense", "draft_head_lowrank", "draft_head_specvocab", "spec_verify",
+              "spec_verify_sparse"):
         assert n in names
 
 
@@ -123,6 +124,32 @@ def test_verify_validation(lib):
     assert v(wsb=8) == sh.SH_ERR_WORKSPACE
     assert v(mode=sh.GREEDY, dl=None, u=None, wsb=8) == sh.SH_ERR_WORKSPACE   # greedy needs no draft
     assert v(mode=9) == sh.SH_ERR_DTYPE
+
+
+@no_gpu
+def test_verify_sparse_validation(lib):
+    def v(B=2, gamma=4, V=1024, k=64, tl=A, idx=B, prob=C, tok=D, u=A, T=1.0, acc=C, out=D, wsb=1 << 30,
+          dtype=sh.SH_F32):
+        return lib.spec_verify_sparse(B, gamma, V, k, dtype, tl, idx, prob, tok, u, T, 0, 0, acc, out, WS, wsb,
+                                      None)
+    assert v(gamma=0) == sh.SH_ERR_SHAPE
+    assert v(gamma=65) == sh.SH_ERR_SHAPE
+    assert v(B=0) == sh.SH_ERR_SHAPE
+    assert v(V=1023) == sh.SH_ERR_SHAPE
+    assert v(k=0) == sh.SH_ERR_PARAM
+    assert v(k=1025) == sh.SH_ERR_PARAM
+    assert v(k=20000, V=40000) == sh.SH_ERR_UNSUPPORTED
+    assert v(idx=None) == sh.SH_ERR_NULL
+    assert v(prob=None) == sh.SH_ERR_NULL
+    assert v(tok=None) == sh.SH_ERR_NULL
+    assert v(u=None) == sh.SH_ERR_NULL
+    assert v(tl=None) == sh.SH_ERR_NULL
+    assert v(idx=ctypes.c_void_p(0x7f0000100002)) == sh.SH_ERR_ALIGN
+    assert v(T=0.0) == sh.SH_ERR_PARAM
+    assert v(dtype=5) == sh.SH_ERR_DTYPE
+    assert v(wsb=8) == sh.SH_ERR_WORKSPACE
+    assert lib.sh_verify_sparse_workspace_bytes(64, 5, 151936, 2048) > 0
+    assert lib.sh_verify_sparse_workspace_bytes(64, 5, 151936, 0) == 0
 
 
 @no_gpu
