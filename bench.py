@@ -39,7 +39,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--legs", default="all",
                    help="comma list of legs (lowrank48,lowrank48g,lowrank6,dense48,dense6,specvocab1,"
-                        "specvocab16,verify,verifyg,verifysparse) or 'all' or 'headline'")
+                        "specvocab16,verify,verifyg,verifysparse,verifytree) or 'all' or 'headline'")
     p.add_argument("--rotate", type=int, default=5, help="device copies of each weight set")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-trace", action="store_true", help="skip the per-kernel event pass")
@@ -152,7 +152,7 @@ def main():
     d, V, r, dp, k = w.d, w.V, w.r, w.dprime, w.k
     seeds = w.seeds
     legs_all = ["lowrank48", "lowrank48g", "lowrank6", "dense48", "dense6", "specvocab1", "specvocab16",
-                "verify", "verifyg", "verifysparse"]
+                "verify", "verifyg", "verifysparse", "verifytree"]
     if args.legs == "all":
         legs = legs_all
     elif args.legs == "headline":
@@ -354,6 +354,30 @@ def main():
         o = run_leg("verifysparse", calls, vw.B * vw.gamma, alg, "draft tokens")
         o["config"] = {"B": vw.B, "gamma": vw.gamma, "V": vw.V, "k": ks, "sigma": 1.0}
 
+    if "verifytree" in legs:
+        vw = configs.VERIFY
+        TB, TN = vw.B, 16   # 64 candidate trees of 16 nodes over the verification vocabulary
+        inp = synth.tree_inputs(TB, TN, vw.V, 0.5, "bf16", vw.seeds)
+        tl = [bf(inp["target"])]
+        for _ in range(2):
+            tl.append(tl[0].clone())
+        ttok = torch.from_numpy(inp["tokens"]).to(dev)
+        tpar = torch.from_numpy(inp["parent"]).to(dev)
+        need = sh.load().sh_verify_tree_workspace_bytes(TB, TN, vw.V)
+        calls = []
+        for i in range(3):
+            acc = torch.empty(TB, dtype=torch.int32, device=dev)
+            node = torch.empty(TB, dtype=torch.int32, device=dev)
+            out = torch.empty(TB, TN, dtype=torch.int32, device=dev)
+            ws = torch.zeros(need, dtype=torch.uint8, device=dev)
+            c = sh.prepared("spec_verify_tree", TB, TN, vw.V, sh.SH_BF16, tl[i], ttok, tpar, acc, node, out, ws,
+                            need, torch.cuda.current_stream().cuda_stream)
+            c.keep = (acc, node, out, ws)
+            calls.append(c)
+        alg = TB * TN * vw.V * 2 + TB * TN * 8 + TB * (TN + 2) * 4
+        o = run_leg("verifytree", calls, TB * (TN - 1), alg, "candidate nodes")
+        o["config"] = {"B": TB, "N": TN, "V": vw.V, "sigma": 0.5}
+
     head = results.get("lowrank48")
     line = {
         "metric": METRIC,
@@ -398,6 +422,8 @@ def main():
         line["verify_tokens_per_s"] = results["verify"]["tokens_per_s"]
     if "verifysparse" in results:
         line["verify_sparse_tokens_per_s"] = results["verifysparse"]["tokens_per_s"]
+    if "verifytree" in results:
+        line["verify_tree_nodes_per_s"] = results["verifytree"]["tokens_per_s"]
     line["legs"] = {kk: {x: v for x, v in vv.items() if x != "kernels"} for kk, vv in results.items()}
     line["kernels_us"] = {kk: {kn: round(kv["avg_us"], 3) for kn, kv in vv.items()} for kk, vv in kernel_trace.items()}
 

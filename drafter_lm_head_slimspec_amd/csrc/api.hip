@@ -344,6 +344,11 @@ size_t sh_verify_workspace_bytes(int mode, int64_t B, int64_t gamma, int64_t V) 
   return verify_layout(mode, B, gamma, V).total;
 }
 
+size_t sh_verify_tree_workspace_bytes(int64_t B, int64_t N, int64_t V) {
+  if (B < 1 || N < 1 || N > sh::kMaxTreeNodes || V < 1) return 0;
+  return verify_layout(0, B, N - 1, V).total;
+}
+
 size_t sh_verify_sparse_workspace_bytes(int64_t B, int64_t gamma, int64_t V, int64_t k) {
   if (B < 1 || gamma < 1 || V < 1 || k < 1 || k > V) return 0;
   return verify_layout(2, B, gamma, V).total;
@@ -574,6 +579,46 @@ int spec_verify_sparse(int64_t B, int64_t gamma, int64_t V, int64_t k, int dtype
   a.partials2 = reinterpret_cast<sh::Partial*>(ws + L.part2_off);
   a.S2 = L.S2;
   SH_HIP(sh::launch_verify(a, static_cast<hipStream_t>(stream)), "verify kernels");
+  return SH_OK;
+}
+
+int spec_verify_tree(int64_t B, int64_t N, int64_t V, int dtype, const void* target_logits,
+                     const int32_t* node_token, const int32_t* parent, int32_t* accept_len,
+                     int32_t* accept_node, int32_t* out_tokens, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  g_last_error.clear();
+  SH_TRY(check_dtype_mode(dtype, SH_GREEDY));
+  if (B < 1 || B > 65535) return fail(SH_ERR_SHAPE, "B must be in [1, 65535]");
+  if (N < 1 || N > sh::kMaxTreeNodes) return fail(SH_ERR_SHAPE, "N must be in [1, %d]", sh::kMaxTreeNodes);
+  SH_TRY(check_rowlen("V", V, dtype));
+  if (V > (int64_t{1} << 28)) return fail(SH_ERR_SHAPE, "V above 2^28");
+  SH_TRY(check_ptr(target_logits, "target_logits"));
+  const std::pair<const void*, const char*> small[] = {{node_token, "node_token"}, {parent, "parent"}};
+  for (const auto& pn : small) {
+    if (pn.first == nullptr) return fail(SH_ERR_NULL, "%s is NULL", pn.second);
+    if (!aligned(pn.first, 4)) return fail(SH_ERR_ALIGN, "%s is not 4-byte aligned", pn.second);
+  }
+  SH_TRY(check_out(accept_len, "accept_len"));
+  SH_TRY(check_out(accept_node, "accept_node"));
+  SH_TRY(check_out(out_tokens, "out_tokens"));
+  const size_t need = sh_verify_tree_workspace_bytes(B, N, V);
+  SH_TRY(check_workspace(workspace, workspace_bytes, need));
+  sh::VerifyArgs a{};
+  a.mode = 0;
+  a.B = B;
+  a.gamma = N - 1;
+  a.V = V;
+  a.bf16 = dtype == SH_BF16;
+  a.target = target_logits;
+  a.tokens = node_token;
+  a.parent = parent;
+  a.accept_len = accept_len;
+  a.accept_node = accept_node;
+  a.out_tokens = out_tokens;
+  const VerifyLayout L = verify_layout(0, B, N - 1, V);
+  a.partials = reinterpret_cast<sh::Partial*>(static_cast<char*>(workspace) + L.part_off);
+  a.S = L.S;
+  SH_HIP(sh::launch_verify_tree(a, static_cast<hipStream_t>(stream)), "tree verify kernels");
   return SH_OK;
 }
 

@@ -145,12 +145,17 @@ struct VerifyArgs {
   const int32_t* qidx;  // mode 2: [B, gamma, k] candidate ids (distinct)
   const float* qprob;   // mode 2: [B, gamma, k] their draft probabilities
   int64_t k;
+  const int32_t* parent;  // tree verification: [B, gamma + 1] parent of each node
+  int32_t* accept_node;   // tree verification: [B] deepest accepted node
 };
 // target rows + (mode 1) draft rows per sequence
 __host__ __device__ inline int64_t verify_rows_per_seq(int mode, int64_t gamma) { return mode == 1 ? 2 * gamma + 1 : gamma + 1; }
 int verify_segments(int64_t B, int64_t gamma, int64_t V, int mode);
 int verify_resid_segments(int64_t B, int64_t V, int mode);
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t st);
+// greedy verification of a candidate tree of gamma + 1 nodes per sequence (mode 0 rows)
+constexpr int kMaxTreeNodes = 1024;
+hipError_t launch_verify_tree(const VerifyArgs& a, hipStream_t st);
 
 hipError_t launch_philox(uint64_t seed, uint64_t offset, uint32_t purpose, int64_t rows, int64_t n,
                          float* out, hipStream_t st);

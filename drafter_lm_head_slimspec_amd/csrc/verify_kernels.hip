@@ -524,6 +524,111 @@ __global__ __launch_bounds__(256) void k_verify_finish(VerifyArgs a) {
   if (l == 0) a.accept_len[b] = acc_len;
 }
 
+// Greedy verification of a candidate tree (phrase-level speculation page, "更换单元：从
+// token 到短语": the candidates of a round form a prefix tree scored in one target pass, and a
+// node survives only where it equals the target's own argmax).  One workgroup per tree of
+// N = gamma + 1 nodes, one thread per node: node n is accepted when its parent p (in [0, n))
+// is accepted and its token equals the argmax of p's target row; pointer jumping over the
+// parent links gives every node "all links to the root match" and its depth in log2 N rounds;
+// the deepest accepted node (lowest index on ties) ends the path, followed by its argmax.
+__global__ __launch_bounds__(kMaxTreeNodes) void k_tree_finish(VerifyArgs a) {
+  __shared__ int32_t g[kMaxTreeNodes];     // argmax of each node's target row
+  __shared__ int32_t anc[kMaxTreeNodes];   // current jump target (0 = the root)
+  __shared__ int32_t dep[kMaxTreeNodes];   // links summed so far
+  __shared__ int32_t okf[kMaxTreeNodes];   // every link summed so far matches
+  __shared__ int32_t red_k[kMaxTreeNodes / kWave], red_n[kMaxTreeNodes / kWave];
+  const int64_t b = blockIdx.x;
+  const int N = static_cast<int>(a.gamma + 1);
+  const int l = lane_id(), w = wave_id(), nw = blockDim.x / kWave;
+  const int n = threadIdx.x;
+  for (int r = w; r < N; r += nw) {
+    Partial p = l < a.S ? a.partials[(b * N + r) * a.S + l] : partial_empty();
+    wave_partial_merge(p);
+    if (l == 0) g[r] = p.zid;
+  }
+  int32_t par = 0, tok = 0;
+  if (n < N) {
+    par = a.parent[b * N + n];
+    tok = a.tokens[b * N + n];
+  }
+  __syncthreads();
+  if (n < N) {
+    const bool valid = n > 0 && par >= 0 && par < n;
+    anc[n] = valid ? par : 0;
+    dep[n] = n > 0 ? 1 : 0;
+    okf[n] = n == 0 ? 1 : (valid && tok == g[par] ? 1 : 0);
+  }
+  __syncthreads();
+  for (int span = 1; span < N; span <<= 1) {
+    int32_t a2 = 0, d2 = 0, o2 = 1;
+    if (n < N) {
+      const int32_t up = anc[n];
+      a2 = anc[up];
+      d2 = dep[n] + dep[up];
+      o2 = okf[n] & okf[up];
+    }
+    __syncthreads();
+    if (n < N) {
+      anc[n] = a2;
+      dep[n] = d2;
+      okf[n] = o2;
+    }
+    __syncthreads();
+  }
+  // deepest accepted node, lowest index on ties (the root, depth 0, is always accepted)
+  int32_t key = (n < N && okf[n]) ? dep[n] : -1, id = n;
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) {
+    const int32_t k2 = __shfl_xor(key, s), i2 = __shfl_xor(id, s);
+    if (k2 > key || (k2 == key && i2 < id)) {
+      key = k2;
+      id = i2;
+    }
+  }
+  if (l == 0) {
+    red_k[w] = key;
+    red_n[w] = id;
+  }
+  __syncthreads();
+  int32_t best = red_n[0], bdep = red_k[0];
+  for (int i = 1; i < nw; ++i)
+    if (red_k[i] > bdep || (red_k[i] == bdep && red_n[i] < best)) {
+      bdep = red_k[i];
+      best = red_n[i];
+    }
+  int32_t* out = a.out_tokens + b * N;
+  if (n < N && n > bdep) out[n] = -1;
+  if (n == 0) {
+    // the path, leaf to root: node m sits at position depth(m) - 1
+    int32_t m = best;
+    for (int t = bdep - 1; t >= 0; --t) {
+      out[t] = a.tokens[b * N + m];
+      m = a.parent[b * N + m];
+    }
+    out[bdep] = g[best];
+    a.accept_len[b] = bdep;
+    a.accept_node[b] = best;
+  }
+}
+
+hipError_t launch_verify_tree(const VerifyArgs& a, hipStream_t st) {
+  const int N = static_cast<int>(a.gamma + 1);
+  if (N < 1 || N > kMaxTreeNodes || a.mode != 0) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>(a.S), static_cast<unsigned>(N), static_cast<unsigned>(a.B));
+  {
+    TraceScope ts("verify_rows", st);
+    if (a.bf16)
+      hipLaunchKernelGGL((k_verify_rows<true, true>), grid, dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((k_verify_rows<false, true>), grid, dim3(256), 0, st, a);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  TraceScope ts("tree_finish", st);
+  hipLaunchKernelGGL(k_tree_finish, dim3(static_cast<unsigned>(a.B)), dim3(kMaxTreeNodes), 0, st, a);
+  return hipGetLastError();
+}
+
 int verify_segments(int64_t B, int64_t gamma, int64_t V, int mode) {
   const int64_t R = verify_rows_per_seq(mode, gamma);
   const int64_t NG = (V + kGroup - 1) / kGroup;

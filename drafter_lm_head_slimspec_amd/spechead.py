@@ -41,6 +41,8 @@ _SIGS = {
     "spec_verify": (_i, [_i, _i64, _i64, _i64, _i, _vp, _vp, _vp, _vp, _f, _u64, _u64, _vp, _vp, _vp,
                          _sz, _vp]),
     "sh_verify_sparse_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64]),
+    "sh_verify_tree_workspace_bytes": (_sz, [_i64, _i64, _i64]),
+    "spec_verify_tree": (_i, [_i64, _i64, _i64, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "spec_verify_sparse": (_i, [_i64, _i64, _i64, _i64, _i, _vp, _vp, _vp, _vp, _vp, _f, _u64, _u64, _vp,
                                 _vp, _vp, _sz, _vp]),
     "sh_topk": (_i, [_vp, _i64, _i64, _i64, _vp, _vp, _sz, _vp]),
@@ -234,6 +236,27 @@ def spec_verify_sparse(target, draft_idx, draft_prob, tokens, u, temperature=1.0
                                   _p(tokens), _p(u), float(temperature), int(seed), int(offset), _p(acc), _p(out),
                                   _p(ws), ws.numel(), _stream(dev)))
     return acc, out
+
+
+def spec_verify_tree(target, node_token, parent):
+    """Greedy verification of B candidate trees of N nodes: target [B, N, V], node_token and
+    parent [B, N] int32 -> (accept_len [B], accept_node [B], out_tokens [B, N])."""
+    lib = load()
+    _contig(target, node_token, parent)
+    B, N, V = target.shape
+    dev = target.device
+    if node_token.shape != (B, N) or parent.shape != (B, N):
+        raise ValueError("node_token / parent must be [B, N]")
+    if node_token.dtype != torch.int32 or parent.dtype != torch.int32:
+        raise TypeError("node_token and parent must be int32")
+    acc = torch.empty(B, dtype=torch.int32, device=dev)
+    node = torch.empty(B, dtype=torch.int32, device=dev)
+    out = torch.empty(B, N, dtype=torch.int32, device=dev)
+    need = lib.sh_verify_tree_workspace_bytes(B, N, V)
+    ws = workspace(need, dev, "verify")
+    _check(lib.spec_verify_tree(B, N, V, _dt(target), _p(target), _p(node_token), _p(parent), _p(acc), _p(node),
+                                _p(out), _p(ws), ws.numel(), _stream(dev)))
+    return acc, node, out
 
 
 def topk(scores, k):

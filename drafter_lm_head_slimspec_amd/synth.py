@@ -14,7 +14,10 @@ Recipe (per workload; see ``configs``):
   Philox bit generator, so u is exact in float32 and strictly inside (0, 1);
 * a sparse draft distribution (input data of the sparse verification, in the layout of the
   SpecVocab head's output): per position the k ids of largest draft logit, with weights
-  exp(draft / T) normalised over those ids, and a token drawn from them.
+  exp(draft / T) normalised over those ids, and a token drawn from them;
+* candidate trees: parent[n] uniform in [0, n) (a random recursive tree) or, with probability
+  `chain`, n - 1; the c-th child of a node proposes the c-th largest id of a noisy copy
+  (target + N(0, sigma^2)) of that node's target row, as a tree drafter's top-c branches.
 bf16 values are produced by PyTorch's float32 -> bfloat16 conversion (round to nearest
 even) and kept as uint16 bit patterns on the host.
 """
@@ -140,3 +143,27 @@ def verify_sparse_inputs(B, gamma, V, k, sigma, dtype, seeds, temperature=1.0, t
             qq = q.astype(np.float64)
             tokens[b, t] = top[tok_rng.choice(k, p=qq / qq.sum())]
     return {"target": base["target"], "idx": idx, "prob": prob, "tokens": tokens, "u": base["u"]}
+
+
+def tree_inputs(B, N, V, sigma, dtype, seeds, chain=0.5, target_std=3.0):
+    """Target logits [B, N, V] (row n scores the token after node n's prefix), node tokens and
+    parent links [B, N] of B candidate trees of N nodes (node 0 the root, parent -1)."""
+    rng = np.random.default_rng([seeds["logits"], int(round(sigma * 1000)), N])
+    target = normal(rng, (B, N, V), target_std, dtype, chunk_rows=4)
+    shape_rng = np.random.default_rng([seeds["tokens"], N, 11])
+    noise_rng = np.random.default_rng([seeds["logits"], int(round(sigma * 1000)), N, 13])
+    parent = np.full((B, N), -1, dtype=np.int32)
+    tokens = np.zeros((B, N), dtype=np.int32)
+    for b in range(B):
+        for n in range(1, N):
+            parent[b, n] = n - 1 if shape_rng.random() < chain else shape_rng.integers(0, n)
+        tokens[b, 0] = shape_rng.integers(0, V)
+        children = {}
+        for n in range(1, N):
+            children.setdefault(int(parent[b, n]), []).append(n)
+        for p, kids in children.items():
+            noisy = as_f32(target[b, p], dtype) + noise_rng.standard_normal(V, dtype=np.float32) * np.float32(sigma)
+            order = np.argsort(-noisy, kind="stable")[:len(kids)]
+            for c, n in enumerate(kids):
+                tokens[b, n] = order[c]
+    return {"target": target, "tokens": tokens, "parent": parent}

@@ -75,6 +75,9 @@ size_t sh_head_workspace_bytes(int op, int64_t M, int64_t d, int64_t r, int64_t 
 /* Workspace size for spec_verify.  Pure host arithmetic, no HIP call. */
 size_t sh_verify_workspace_bytes(int mode, int64_t B, int64_t gamma, int64_t V);
 
+/* Workspace size for spec_verify_tree (0 for invalid sizes).  Pure host arithmetic. */
+size_t sh_verify_tree_workspace_bytes(int64_t B, int64_t N, int64_t V);
+
 /* Workspace size for spec_verify_sparse (0 for invalid sizes).  Pure host arithmetic. */
 size_t sh_verify_sparse_workspace_bytes(int64_t B, int64_t gamma, int64_t V, int64_t k);
 
@@ -176,6 +179,31 @@ int spec_verify(int mode, int64_t B, int64_t gamma, int64_t V, int dtype,
  *   `stream`.  Workspace: sh_verify_sparse_workspace_bytes(B, gamma, V, k), 256-byte aligned,
  *   contents irrelevant.
  */
+/*
+ * Greedy verification of a tree of candidate continuations (phrase-level speculation page,
+ * section "更换单元：从 token 到短语": the candidates of a round share prefixes, form a prefix
+ * tree scored in one target pass, and a candidate survives only where it equals the target's
+ * own argmax, so the output equals greedy decoding).
+ *   target_logits [B, N, V] dtype (device): row n scores the token that follows node n's prefix
+ *   node_token    [B, N] int32 (device): the token node n proposes (node 0 is the root, the
+ *                 last accepted token; its entry is not verified)
+ *   parent        [B, N] int32 (device): parent of node n; a node whose parent is not in
+ *                 [0, n) is never accepted, nor is any node below it
+ *   B <= 65535, 1 <= N <= 1024, V <= 2^28
+ *   Node n is accepted when its parent is accepted and node_token[n] equals the argmax (ties ->
+ *   lowest id) of its parent's row.  The deepest accepted node m (lowest index on ties) ends
+ *   the accepted path; the argmax of row m follows it (correction or bonus token).
+ *   accept_len  [B] int32: depth of m (tokens accepted)
+ *   accept_node [B] int32: m
+ *   out_tokens  [B, N] int32: the path's tokens root-side first, then argmax of row m, then -1
+ *   Returns SH_ERR_* before any launch on invalid arguments; asynchronous on `stream`.
+ *   Workspace: sh_verify_tree_workspace_bytes(B, N, V), 256-byte aligned, contents irrelevant.
+ */
+int spec_verify_tree(int64_t B, int64_t N, int64_t V, int dtype, const void* target_logits,
+                     const int32_t* node_token, const int32_t* parent, int32_t* accept_len,
+                     int32_t* accept_node, int32_t* out_tokens, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
 int spec_verify_sparse(int64_t B, int64_t gamma, int64_t V, int64_t k, int dtype,
                        const void* target_logits, const int32_t* draft_idx, const float* draft_prob,
                        const int32_t* draft_tokens, const float* u_accept, float temperature,

@@ -22,7 +22,7 @@ def lib():
 def test_header_declares_the_four_entry_points():
     names = libutil.header_functions()
     for n in ("draft_head_dense", "draft_head_lowrank", "draft_head_specvocab", "spec_verify",
-              "spec_verify_sparse"):
+              "spec_verify_sparse", "spec_verify_tree"):
         assert n in names
 
 
@@ -150,6 +150,25 @@ def test_verify_sparse_validation(lib):
     assert v(wsb=8) == sh.SH_ERR_WORKSPACE
     assert lib.sh_verify_sparse_workspace_bytes(64, 5, 151936, 2048) > 0
     assert lib.sh_verify_sparse_workspace_bytes(64, 5, 151936, 0) == 0
+
+
+@no_gpu
+def test_verify_tree_validation(lib):
+    def v(B=2, N=8, V=1024, tl=A, tok=B, par=C, acc=C, node=D, out=D, wsb=1 << 30, dtype=sh.SH_F32):
+        return lib.spec_verify_tree(B, N, V, dtype, tl, tok, par, acc, node, out, WS, wsb, None)
+    assert v(N=0) == sh.SH_ERR_SHAPE
+    assert v(N=1025) == sh.SH_ERR_SHAPE
+    assert v(B=0) == sh.SH_ERR_SHAPE
+    assert v(V=1023) == sh.SH_ERR_SHAPE
+    assert v(tl=None) == sh.SH_ERR_NULL
+    assert v(tok=None) == sh.SH_ERR_NULL
+    assert v(par=None) == sh.SH_ERR_NULL
+    assert v(node=None) == sh.SH_ERR_NULL
+    assert v(par=ctypes.c_void_p(0x7f0000100002)) == sh.SH_ERR_ALIGN
+    assert v(dtype=3) == sh.SH_ERR_DTYPE
+    assert v(wsb=8) == sh.SH_ERR_WORKSPACE
+    assert lib.sh_verify_tree_workspace_bytes(64, 32, 151936) > 0
+    assert lib.sh_verify_tree_workspace_bytes(64, 1025, 151936) == 0
 
 
 @no_gpu
