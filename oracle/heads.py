@@ -4,7 +4,8 @@
   the d-dim hidden state to V scores through a V x d matrix, cost O(V d)).
 * low-rank (SlimSpec, section 三 and Q&A Q1): h_r = W_down h (d -> r), z = W_up h_r
   (r -> V); every one of the V tokens keeps a score.  Layout reading: W_down is stored as
-  [r, d] and W_up as [V, r] so both products are row dot products.
+  [r, d] and W_up as [V, r] so both products are row dot products.  Position-adaptive rank
+  (section 七): row m uses nested prefixes of rank r_m of the same pair.
 * SpecVocab (2kiu.com write-up, sections 2.2.1-2.2.3): h' = W_down h (d' = d/16),
   s = W_vocab h' (approximate scores), K = top-k(s), z' = U[K,:] h (exact logits from
   the full hidden state), q = softmax(z') over the k candidates; q is 0 outside K.
@@ -82,6 +83,30 @@ def head_lowrank(h, W_down, W_up, dtype, mode=GREEDY, temperature=1.0, seed=0, o
     out = _finish(Z, mode, temperature, seed, offset)
     out["h_r_exact"] = pre
     out["h_r"] = hr
+    return out
+
+
+def head_lowrank_adaptive(h, W_down, W_up, ranks, dtype, mode=GREEDY, temperature=1.0, seed=0,
+                          offset=0):
+    """Position-adaptive rank ("SlimSpec" write-up, section 七, the second future direction:
+    earlier draft positions get a larger rank, later ones a smaller one).  Reading: one factor
+    pair of rank r_max serves every position through nested prefixes, so row m of rank r_m uses
+    the first r_m rows of W_down and the first r_m columns of W_up:
+        z_m = W_up[:, :r_m] round(W_down[:r_m] h_m),   1 <= r_m <= r_max.
+    Selection, rounding and uniforms are those of head_lowrank (Philox row = m)."""
+    pre, hr = lowrank_down(h, W_down, dtype)          # [M, r_max]; row m keeps its first r_m
+    Wu = fp.decode(W_up, dtype)
+    ranks = [int(r) for r in np.asarray(ranks).reshape(-1)]
+    M = hr.shape[0]
+    if len(ranks) != M or min(ranks) < 1 or max(ranks) > Wu.shape[1]:
+        raise ValueError("ranks must hold one value in [1, r_max] per row")
+    Z = np.empty((M, Wu.shape[0]))
+    for m, r in enumerate(ranks):
+        Z[m] = Wu[:, :r] @ hr[m, :r]
+    out = _finish(Z, mode, temperature, seed, offset)
+    mask = np.arange(hr.shape[1])[None, :] < np.array(ranks)[:, None]
+    out["h_r_exact"] = np.where(mask, pre, 0.0)
+    out["h_r"] = np.where(mask, hr, 0.0)
     return out
 
 
