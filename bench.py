@@ -39,7 +39,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--legs", default="all",
                    help="comma list of legs (lowrank48,lowrank48g,lowrank6,dense48,dense6,specvocab1,"
-                        "specvocab16,verify,verifyg,verifysparse,verifytree) or 'all' or 'headline'")
+                        "specvocab16,verify,verifyg,verifysparse,verifytree,adaptive48,adaptive48s) or 'all' "
+                        "or 'headline'")
     p.add_argument("--rotate", type=int, default=5, help="device copies of each weight set")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-trace", action="store_true", help="skip the per-kernel event pass")
@@ -151,7 +152,8 @@ def main():
     w = configs.LLAMA
     d, V, r, dp, k = w.d, w.V, w.r, w.dprime, w.k
     seeds = w.seeds
-    legs_all = ["lowrank48", "lowrank48g", "lowrank6", "dense48", "dense6", "specvocab1", "specvocab16",
+    legs_all = ["lowrank48", "lowrank48g", "lowrank6", "adaptive48", "adaptive48s", "dense48", "dense6",
+                "specvocab1", "specvocab16",
                 "verify", "verifyg", "verifysparse", "verifytree"]
     if args.legs == "all":
         legs = legs_all
@@ -298,6 +300,29 @@ def main():
             alg = (dp * d + V * dp) * 2 + u * d * 2 + M * d * 2 + M * k * 12
             out = run_leg(name, calls, M, alg)
             out["union_rows"] = u
+
+    # position-adaptive rank: 8 sequences x 6 draft positions with ranks falling by position
+    # (nested prefixes of the r = 512 pair); "s" = every position at rank <= 256 (half the columns)
+    for name, sched in (("adaptive48", [512, 512, 384, 384, 256, 256]), ("adaptive48s", [256, 256, 192, 192, 128, 128])):
+        if name not in legs:
+            continue
+        ranks = np.array(sched * 8, dtype=np.int32)
+        cols = min(r, (int(ranks.max()) + 127) // 128 * 128)
+        calls = []
+        for i in range(R):
+            tok = torch.empty(48, dtype=torch.int32, device=dev)
+            lse = torch.empty(48, dtype=torch.float32, device=dev)
+            lp = torch.empty(48, dtype=torch.float32, device=dev)
+            need = sh.load().sh_head_workspace_bytes(sh.OP_LOWRANK, 48, d, r, V, 0)
+            ws = torch.zeros(need, dtype=torch.uint8, device=dev)
+            c = sh.prepared("draft_head_lowrank_adaptive", h48, 48, d, Wd[i], r, Wu[i], V, ranks, sh.SH_BF16,
+                            sh.SAMPLE, 1.0, seeds["philox"], i, tok, lse, lp, None, ws, need,
+                            torch.cuda.current_stream().cuda_stream)
+            c.keep = (tok, lse, lp, ws)
+            calls.append(c)
+        alg = (int(ranks.max()) * d + V * cols + 48 * d) * 2 + 48 * 12
+        o = run_leg(name, calls, 48, alg)
+        o["config"] = {"ranks_by_position": sched, "columns_read": cols}
 
     if "verify" in legs or "verifyg" in legs:
         vw = configs.VERIFY

@@ -197,13 +197,18 @@ int check_workspace(void* ws, size_t have, size_t need) {
 
 // Stream z = W x over V rows for M rows of x, then finalize selection.  Shared by the dense
 // and low-rank heads.  lg: [M][ceil(V/64)] group log-sum-exps, partials: [M][kMaxPartials].
+// ld: row stride of W and x in elements when only the first K elements of each row are used
+// (0: rows of K elements); a stride other than K needs the tile path.
 int run_head(const void* x, int64_t M, int64_t K, const void* W, int64_t V, int dtype, int mode,
              float temperature, uint64_t seed, uint64_t offset, int32_t* token, float* lse,
-             float* logprob, float* logits, sh::Partial* partials, float* lg, hipStream_t st) {
+             float* logprob, float* logits, sh::Partial* partials, float* lg, hipStream_t st,
+             int64_t ld = 0) {
   const bool bf16 = dtype == SH_BF16;
   const float invT = 1.0f / temperature;
   const bool want_lg = mode == SH_SAMPLE || lse != nullptr || logprob != nullptr;
-  if (sh::head_tile_supported(M, K, V, bf16)) {
+  if (ld != 0 && ld != K && !sh::head_tile_supported(M, K, V, bf16, ld))
+    return fail(SH_ERR_UNSUPPORTED, "row prefixes need the tile path");
+  if (sh::head_tile_supported(M, K, V, bf16, ld)) {
     // short bf16 rows, at most kTileMaxRows activation rows: one tile-streaming pass with
     // in-kernel group draws, then the finalize
     const int grid = sh::head_tile_grid(M, K, V);
@@ -212,6 +217,7 @@ int run_head(const void* x, int64_t M, int64_t K, const void* W, int64_t V, int 
     a.x = x;
     a.V = V;
     a.K = static_cast<int>(K);
+    a.ld = static_cast<int>(ld);
     a.M = static_cast<int>(M);
     a.row0 = 0;
     a.invT = invT;
@@ -233,6 +239,7 @@ int run_head(const void* x, int64_t M, int64_t K, const void* W, int64_t V, int 
     f.x = x;
     f.V = V;
     f.K = K;
+    f.ld = ld;
     f.M = static_cast<int>(M);
     f.bf16 = true;
     f.mode = mode == SH_SAMPLE ? 1 : 0;
@@ -399,6 +406,43 @@ int draft_head_lowrank(const void* h, int64_t M, int64_t d, const void* W_down, 
          "down-projection kernels");
   return run_head(hr, M, r, W_up, V, dtype, mode, temperature, seed, offset, token, lse, logprob,
                   logits, parts, lg, st);
+}
+
+int draft_head_lowrank_adaptive(const void* h, int64_t M, int64_t d, const void* W_down, int64_t r_max,
+                                const void* W_up, int64_t V, const int32_t* ranks, int dtype, int mode,
+                                float temperature, uint64_t seed, uint64_t offset, int32_t* token, float* lse,
+                                float* logprob, float* logits, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  g_last_error.clear();
+  SH_TRY(check_common_head(h, M, d, V, dtype, mode, temperature, token, lse, logprob));
+  SH_TRY(check_ptr(W_down, "W_down"));
+  SH_TRY(check_ptr(W_up, "W_up"));
+  SH_TRY(check_rowlen("r_max", r_max, dtype));
+  SH_TRY(check_opt_out(logits, "logits"));
+  if (ranks == nullptr) return fail(SH_ERR_NULL, "ranks is NULL");
+  if (dtype != SH_BF16) return fail(SH_ERR_UNSUPPORTED, "position-adaptive rank needs bf16");
+  if (M > sh::kRowdotRanksMaxM) return fail(SH_ERR_UNSUPPORTED, "M above %d", sh::kRowdotRanksMaxM);
+  int64_t rmax_used = 0;
+  for (int64_t m = 0; m < M; ++m) {
+    if (ranks[m] < 1 || ranks[m] > r_max) return fail(SH_ERR_PARAM, "ranks[%lld] not in [1, r_max]", static_cast<long long>(m));
+    rmax_used = ranks[m] > rmax_used ? ranks[m] : rmax_used;
+  }
+  // columns read: the largest rank rounded up to 128 (the tile pass's row lengths), or r_max
+  int64_t K = (rmax_used + 127) / 128 * 128;
+  if (K > r_max) K = r_max;
+  if (!sh::head_tile_supported(M, K, V, true, r_max))
+    return fail(SH_ERR_UNSUPPORTED, "shape outside the tile pass (r_max %lld, columns %lld)",
+                static_cast<long long>(r_max), static_cast<long long>(K));
+  const HeadLayout L = head_layout(SH_OP_LOWRANK, M, d, r_max, V, 0, SH_F32);
+  SH_TRY(check_workspace(workspace, workspace_bytes, L.total));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  void* hr = ws + L.hr_off;
+  auto* parts = reinterpret_cast<sh::Partial*>(ws + L.part_off);
+  auto* lg = reinterpret_cast<float*>(ws + L.lg_off);
+  SH_HIP(sh::launch_rowdot_ranked(W_down, h, r_max, d, M, ranks, hr, st), "down-projection kernel");
+  return run_head(hr, M, K, W_up, V, dtype, mode, temperature, seed, offset, token, lse, logprob, logits, parts,
+                  lg, st, r_max);
 }
 
 int draft_head_specvocab(const void* h, int64_t M, int64_t d, const void* W_down, int64_t dprime,

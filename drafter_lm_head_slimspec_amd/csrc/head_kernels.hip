@@ -224,13 +224,20 @@ __global__ __launch_bounds__(256) void k_rowdot_reduce(const float* __restrict__
 constexpr int kRdtWaves = 8;
 constexpr int kRdtBatch = 8;                  // k-steps per batch of loads
 constexpr int64_t kRdTileMaxM = 64;
+static_assert(kRdTileMaxM == kRowdotRanksMaxM, "one rank per row of a one-pass launch");
 
 typedef float rd_f32x4_t __attribute__((ext_vector_type(4)));
+
+// per-row output counts (position-adaptive rank: row m keeps its first r[m] outputs)
+struct RowRanks {
+  int32_t r[kRdTileMaxM];
+};
 
 __global__ __launch_bounds__(kRdtWaves * kWave) void k_rowdot_tile(const void* __restrict__ Wd,
                                                                    const void* __restrict__ x, int R, int K, int M,
                                                                    uint16_t* __restrict__ out,
-                                                                   uint32_t* __restrict__ zero, int64_t zero_words) {
+                                                                   uint32_t* __restrict__ zero, int64_t zero_words,
+                                                                   RowRanks rk) {
   __shared__ float red[kRdtWaves][4][kWave];
   if (zero != nullptr) {
     const int64_t nwg = static_cast<int64_t>(gridDim.x) * gridDim.y;
@@ -292,7 +299,7 @@ __global__ __launch_bounds__(kRdtWaves * kWave) void k_rowdot_tile(const void* _
     for (int ww = 1; ww < kRdtWaves; ++ww) sum += red[ww][v][ll];
     const int j = j0 + 4 * (ll >> 4) + v;
     const int m = m0 + (ll & 15);
-    if (j < R && m < M) out[static_cast<int64_t>(m) * R + j] = f32_to_bf16_rne(sum);
+    if (j < R && m < M) out[static_cast<int64_t>(m) * R + j] = j < rk.r[m] ? f32_to_bf16_rne(sum) : uint16_t{0};
   }
 }
 
@@ -1229,10 +1236,12 @@ size_t rowdot_scratch_bytes(int64_t M, int64_t R, int64_t K) {
 hipError_t launch_rowdot(const void* Wd, const void* x, int64_t R, int64_t K, int64_t M, bool bf16,
                          void* out, float* scratch, hipStream_t st, uint32_t* zero, int64_t zero_words) {
   if (bf16 && M <= kRdTileMaxM) {
+    RowRanks rk;
+    for (int m = 0; m < kRdTileMaxM; ++m) rk.r[m] = static_cast<int32_t>(R);
     const dim3 grid(static_cast<unsigned>((R + 15) / 16), static_cast<unsigned>((M + 15) / 16));
     TraceScope ts("rowdot_tile", st);
     hipLaunchKernelGGL(k_rowdot_tile, grid, dim3(kRdtWaves * kWave), 0, st, Wd, x, static_cast<int>(R),
-                       static_cast<int>(K), static_cast<int>(M), static_cast<uint16_t*>(out), zero, zero_words);
+                       static_cast<int>(K), static_cast<int>(M), static_cast<uint16_t*>(out), zero, zero_words, rk);
     return hipGetLastError();
   }
   if (bf16) {
@@ -1267,6 +1276,18 @@ hipError_t launch_rowdot(const void* Wd, const void* x, int64_t R, int64_t K, in
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_rowdot<false>, grid, dim3(256), lds, st, Wd, x, static_cast<int>(R), C,
                      static_cast<int>(M), out, zero, zero_words);
+  return hipGetLastError();
+}
+
+hipError_t launch_rowdot_ranked(const void* Wd, const void* x, int64_t R, int64_t K, int64_t M,
+                                const int32_t* ranks, void* out, hipStream_t st) {
+  if (M < 1 || M > kRdTileMaxM) return hipErrorInvalidValue;
+  RowRanks rk;
+  for (int m = 0; m < kRdTileMaxM; ++m) rk.r[m] = m < M ? ranks[m] : 0;
+  const dim3 grid(static_cast<unsigned>((R + 15) / 16), static_cast<unsigned>((M + 15) / 16));
+  TraceScope ts("rowdot_tile", st);
+  hipLaunchKernelGGL(k_rowdot_tile, grid, dim3(kRdtWaves * kWave), 0, st, Wd, x, static_cast<int>(R),
+                     static_cast<int>(K), static_cast<int>(M), static_cast<uint16_t*>(out), nullptr, int64_t{0}, rk);
   return hipGetLastError();
 }
 

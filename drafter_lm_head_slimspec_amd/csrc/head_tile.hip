@@ -66,7 +66,7 @@ struct TilePass {
     w = wave_id();
     col = l & 15;
     qd = l >> 4;
-    rowbytes = static_cast<uint32_t>(a.K) * 2;
+    rowbytes = static_cast<uint32_t>(a.ld > 0 ? a.ld : a.K) * 2;   // row stride
     V32 = static_cast<int>(a.V);
     NG = (V32 + kGroup - 1) / kGroup;
     Mx = a.M;
@@ -88,14 +88,16 @@ struct TilePass {
     for (int j = 0; j < KS; ++j) X[j] = buffer_load16(rs, lane_off + static_cast<uint32_t>(j) * 64);
   }
 
-  // Activations, contiguously (flat 16-byte chunks of x [M][K]), then through LDS into the
+  // Activations (16-byte chunks of the first K elements of each row of x), then through LDS into the
   // register B fragments: Bf[j][cb] = x[cb * 16 + col][32 j + 8 qd ..+8], zero past M.
   __device__ __forceinline__ void stage_issue(uint4 (&xv)[XPER]) const {
     const rsrc_t xrs = make_rsrc(a.x, static_cast<uint32_t>(Mx) * rowbytes);
 #pragma unroll
     for (int q = 0; q < XPER; ++q) {
       const int f = q * kTileThreads + static_cast<int>(threadIdx.x);
-      xv[q] = buffer_load16(xrs, f < Mx * CPRP ? static_cast<uint32_t>(f) * 16 : kOutOfRange);
+      const int m = f / CPRP, c = f - m * CPRP;
+      xv[q] = buffer_load16(xrs, f < Mx * CPRP ? static_cast<uint32_t>(m) * rowbytes + static_cast<uint32_t>(c) * 16
+                                               : kOutOfRange);
     }
   }
   __device__ __forceinline__ void stage_finish(const uint4 (&xv)[XPER]) {
@@ -327,15 +329,16 @@ __device__ __forceinline__ void finalize_row(const FinalizeArgs& f, int m, int n
   } else {
     // recompute the 64 logits of the winning group, 64 / nwaves rows per wave, loads together
     const int rpw = kGroup / nwaves;
-    const int C = static_cast<int>(f.K * (BF16 ? 2 : 4) / 16);
+    const int C = static_cast<int>(f.K * (BF16 ? 2 : 4) / 16);   // chunks of each row's used prefix
     const int CPL = (C + kWave - 1) / kWave;
-    const uint32_t rowbytes = static_cast<uint32_t>(C) * 16;
+    const uint32_t rowbytes = static_cast<uint32_t>((f.ld > 0 ? f.ld : f.K) * (BF16 ? 2 : 4));   // row stride
     const int64_t gbase = static_cast<int64_t>(acc.g == 0x7fffffff ? 0 : acc.g) * kGroup;
     const int64_t r0 = gbase + w * rpw;
     const int nrows = f.V - r0 >= rpw ? rpw : (f.V - r0 > 0 ? static_cast<int>(f.V - r0) : 0);
     const rsrc_t wrs = make_rsrc(static_cast<const char*>(f.W) + static_cast<size_t>(nrows > 0 ? r0 : 0) * rowbytes,
                                  static_cast<uint32_t>(nrows) * rowbytes);
-    const rsrc_t xrs = make_rsrc(static_cast<const char*>(f.x) + static_cast<size_t>(m) * rowbytes, rowbytes);
+    const rsrc_t xrs = make_rsrc(static_cast<const char*>(f.x) + static_cast<size_t>(m) * rowbytes,
+                                 static_cast<uint32_t>(C) * 16);
     // wave 0: the element Gumbel of row gbase + l, computed while the first loads are in flight
     float gel = 0.f;
     bool gel_done = w != 0;
@@ -468,10 +471,11 @@ hipError_t run_tile_ks(const TileArgs& a, int grid, hipStream_t st) {
 
 }  // namespace
 
-bool head_tile_supported(int64_t M, int64_t K, int64_t V, bool bf16) {
-  if (!bf16 || M < 1 || M > kTileMaxRows || K < 1 || K * 2 > 1024) return false;
+bool head_tile_supported(int64_t M, int64_t K, int64_t V, bool bf16, int64_t ld) {
+  if (ld <= 0) ld = K;
+  if (!bf16 || M < 1 || M > kTileMaxRows || K < 1 || K * 2 > 1024 || ld < K || ld % 8 != 0) return false;
   if (K % 32 != 0 || tile_ks(K) * 32 != K) return false;   // rows of exactly KS 32-wide k-steps
-  if (V < 1 || V * K * 2 > int64_t{0xFFFFFFF0}) return false;   // 32-bit buffer ranges
+  if (V < 1 || V * ld * 2 > int64_t{0xFFFFFFF0}) return false;   // 32-bit buffer ranges
   const int ncb = tile_ncb(M), ks = tile_ks(K);
   return ks * ncb <= kMaxBFrags && tile_lds(ncb, ks) <= kLdsPerCu;
 }
@@ -490,7 +494,7 @@ int head_tile_grid(int64_t M, int64_t K, int64_t V) {
 }
 
 hipError_t launch_head_tile(const TileArgs& a, int grid, hipStream_t st) {
-  if (!head_tile_supported(a.M, a.K, a.V, true)) return hipErrorInvalidValue;
+  if (!head_tile_supported(a.M, a.K, a.V, true, a.ld)) return hipErrorInvalidValue;
   switch (tile_ncb(a.M)) {
     case 1: return run_tile_ks<1>(a, grid, st);
     case 2: return run_tile_ks<2>(a, grid, st);

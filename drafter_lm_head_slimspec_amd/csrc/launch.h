@@ -37,6 +37,7 @@ struct FinalizeArgs {
   const void* W;            // [V, K] (sampling: recompute the winning group)
   const void* x;            // [M, K]
   int64_t V, K;
+  int64_t ld;               // row stride of W and x in elements (0: K); K <= ld uses row prefixes
   int M;
   bool bf16;
   int mode;                 // 0 greedy, 1 sample
@@ -56,7 +57,8 @@ struct TileArgs {
   const void* W;      // [V, K] bf16
   const void* x;      // [M, K] bf16
   int64_t V;
-  int K;
+  int K;              // elements of each row used (the prefix of rows of `ld` elements)
+  int ld;             // row stride of W and x in elements (0: K)
   int M;              // rows of this pass, <= kTileMaxRows
   int row0;           // absolute index of x's first row (Philox row of the group draws)
   float invT;
@@ -69,7 +71,7 @@ struct TileArgs {
   Partial* partials;  // [M, partials_ld], one per workgroup; nullable when no stats are wanted
   int64_t partials_ld;
 };
-bool head_tile_supported(int64_t M, int64_t K, int64_t V, bool bf16);
+bool head_tile_supported(int64_t M, int64_t K, int64_t V, bool bf16, int64_t ld = 0);
 
 // workgroups of a tile pass over V rows for passes of up to M activation rows
 int head_tile_grid(int64_t M, int64_t K, int64_t V);
@@ -89,6 +91,11 @@ size_t rowdot_scratch_bytes(int64_t M, int64_t R, int64_t K);
 hipError_t launch_rowdot(const void* Wd, const void* x, int64_t R, int64_t K, int64_t M, bool bf16,
                          void* out, float* scratch, hipStream_t st, uint32_t* zero = nullptr,
                          int64_t zero_words = 0);
+// bf16, M <= kRowdotRanksMaxM: as launch_rowdot, but row m keeps only its first ranks[m]
+// outputs (the rest are written as zero); ranks is a host array
+constexpr int kRowdotRanksMaxM = 64;
+hipError_t launch_rowdot_ranked(const void* Wd, const void* x, int64_t R, int64_t K, int64_t M,
+                                const int32_t* ranks, void* out, hipStream_t st);
 // Chooses the VALU (skinny) or MFMA path; returns the number of producer workgroups.
 hipError_t launch_stream(const StreamArgs& a, bool use_mfma, int* producers, hipStream_t st);
 hipError_t launch_head_finalize(const FinalizeArgs& f, hipStream_t st);

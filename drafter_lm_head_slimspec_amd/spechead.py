@@ -8,6 +8,7 @@ import ctypes
 import os
 import threading
 
+import numpy as np
 import torch
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspechead.so")
@@ -36,6 +37,8 @@ _SIGS = {
                               _vp, _sz, _vp]),
     "draft_head_lowrank": (_i, [_vp, _i64, _i64, _vp, _i64, _vp, _i64, _i, _i, _f, _u64, _u64, _vp,
                                 _vp, _vp, _vp, _vp, _sz, _vp]),
+    "draft_head_lowrank_adaptive": (_i, [_vp, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i, _i, _f, _u64, _u64,
+                                         _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "draft_head_specvocab": (_i, [_vp, _i64, _i64, _vp, _i64, _vp, _vp, _i64, _i64, _i, _i, _f, _u64,
                                   _u64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "spec_verify": (_i, [_i, _i64, _i64, _i64, _i, _vp, _vp, _vp, _vp, _f, _u64, _u64, _vp, _vp, _vp,
@@ -165,6 +168,31 @@ def draft_head_lowrank(h, W_down, W_up, mode="greedy", temperature=1.0, seed=0, 
     _check(lib.draft_head_lowrank(_p(h), M, d, _p(W_down), r, _p(W_up), V, _dt(h), _mode(mode),
                                   float(temperature), int(seed), int(offset), _p(token), _p(lse),
                                   _p(logprob), _p(logits), _p(ws), ws.numel(), _stream(dev)))
+    return {"token": token, "lse": lse, "logprob": logprob, "logits": logits}
+
+
+def draft_head_lowrank_adaptive(h, W_down, W_up, ranks, mode="greedy", temperature=1.0, seed=0, offset=0,
+                                want_logits=False):
+    """Position-adaptive rank: row m uses the first ranks[m] rows of W_down / columns of W_up
+    (ranks: host integers, one per row)."""
+    lib = load()
+    _contig(h, W_down, W_up)
+    M, d = h.shape
+    r = W_down.shape[0]
+    V = W_up.shape[0]
+    rk = np.ascontiguousarray(np.asarray(ranks, dtype=np.int32).reshape(-1))
+    if rk.size != M:
+        raise ValueError("one rank per row")
+    dev = h.device
+    token = torch.empty(M, dtype=torch.int32, device=dev)
+    lse = torch.empty(M, dtype=torch.float32, device=dev)
+    logprob = torch.empty(M, dtype=torch.float32, device=dev)
+    logits = torch.empty(M, V, dtype=torch.float32, device=dev) if want_logits else None
+    need = lib.sh_head_workspace_bytes(OP_LOWRANK, M, d, r, V, 0)
+    ws = workspace(need, dev)
+    _check(lib.draft_head_lowrank_adaptive(_p(h), M, d, _p(W_down), r, _p(W_up), V, rk.ctypes.data_as(_vp), _dt(h),
+                                           _mode(mode), float(temperature), int(seed), int(offset), _p(token),
+                                           _p(lse), _p(logprob), _p(logits), _p(ws), ws.numel(), _stream(dev)))
     return {"token": token, "lse": lse, "logprob": logprob, "logits": logits}
 
 
@@ -304,11 +332,16 @@ def prepared(fn_name, *args):
     for a in args:
         if isinstance(a, torch.Tensor):
             conv.append(ctypes.c_void_p(a.data_ptr()))
+        elif isinstance(a, np.ndarray):   # host array (kept alive by the closure below)
+            conv.append(a.ctypes.data_as(_vp))
         else:
             conv.append(a)
     conv = tuple(conv)
 
+    hold = args
+
     def call():
+        assert hold is not None
         rc = fn(*conv)
         if rc != SH_OK:
             _check(rc)

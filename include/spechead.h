@@ -114,6 +114,26 @@ int draft_head_lowrank(const void* h, int64_t M, int64_t d, const void* W_down, 
                        void* stream);
 
 /*
+ * Position-adaptive rank (SlimSpec write-up, section 七, second future direction: earlier
+ * draft positions get a larger rank, later ones a smaller one).  One factor pair of rank
+ * r_max serves every row through nested prefixes: row m uses the first ranks[m] rows of
+ * W_down and the first ranks[m] columns of W_up,
+ *   z_m = W_up[:, :r_m] round(W_down[:r_m] h_m),
+ * with the selection, outputs and Philox uniforms of draft_head_lowrank.
+ *   h [M, d], W_down [r_max, d], W_up [V, r_max]: device, bf16 only, 1 <= M <= 64
+ *   ranks [M] int32: a HOST array, each in [1, r_max] (read during the call)
+ *   Only the first max(ranks) columns of W_up are read, rounded up to 128 (or r_max): a call
+ *   whose rows all have small ranks streams fewer bytes.  Shapes outside the bf16 tile pass
+ *   (r_max a multiple of 8, columns read in {128, 256, 384, 512}) return SH_ERR_UNSUPPORTED.
+ *   Workspace: sh_head_workspace_bytes(SH_OP_LOWRANK, M, d, r_max, V, 0).
+ */
+int draft_head_lowrank_adaptive(const void* h, int64_t M, int64_t d, const void* W_down, int64_t r_max,
+                                const void* W_up, int64_t V, const int32_t* ranks, int dtype, int mode,
+                                float temperature, uint64_t seed, uint64_t offset, int32_t* token,
+                                float* lse, float* logprob, float* logits, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
+/*
  * SpecVocab dynamic-vocabulary head (SpecVocab write-up, sections 2.2.1-2.2.3 and 5.1).
  *   W_down  [d', d]  reduced-state map, dtype;  h' = W_down h rounded once to dtype
  *   W_vocab [V, d']  approximate scorer, dtype;  s = W_vocab h' (float32)

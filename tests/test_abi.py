@@ -22,7 +22,7 @@ def lib():
 def test_header_declares_the_four_entry_points():
     names = libutil.header_functions()
     for n in ("draft_head_dense", "draft_head_lowrank", "draft_head_specvocab", "spec_verify",
-              "spec_verify_sparse", "spec_verify_tree"):
+              "spec_verify_sparse", "spec_verify_tree", "draft_head_lowrank_adaptive"):
         assert n in names
 
 
@@ -169,6 +169,24 @@ def test_verify_tree_validation(lib):
     assert v(wsb=8) == sh.SH_ERR_WORKSPACE
     assert lib.sh_verify_tree_workspace_bytes(64, 32, 151936) > 0
     assert lib.sh_verify_tree_workspace_bytes(64, 1025, 151936) == 0
+
+
+@no_gpu
+def test_lowrank_adaptive_validation(lib):
+    ranks = (ctypes.c_int32 * 4)(128, 64, 32, 1)
+    bad = (ctypes.c_int32 * 4)(128, 0, 32, 1)
+    big = (ctypes.c_int32 * 4)(513, 64, 32, 1)
+
+    def v(M=4, d=512, r=512, V=8200, rk=ranks, dtype=sh.SH_BF16, wsb=1 << 30):
+        return lib.draft_head_lowrank_adaptive(A, M, d, B, r, C, V, rk, dtype, 0, 1.0, 0, 0, D, None, None, None,
+                                               WS, wsb, None)
+    assert v(rk=None) == sh.SH_ERR_NULL
+    assert v(rk=bad) == sh.SH_ERR_PARAM
+    assert v(rk=big) == sh.SH_ERR_PARAM
+    assert v(dtype=sh.SH_F32) == sh.SH_ERR_UNSUPPORTED
+    assert v(M=65) == sh.SH_ERR_UNSUPPORTED
+    assert v(r=520, rk=big) == sh.SH_ERR_UNSUPPORTED   # 520 columns read: outside the tile pass
+    assert v(wsb=16) == sh.SH_ERR_WORKSPACE
 
 
 @no_gpu
