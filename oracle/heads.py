@@ -110,6 +110,28 @@ def head_lowrank_adaptive(h, W_down, W_up, ranks, dtype, mode=GREEDY, temperatur
     return out
 
 
+def head_trimmed(h, W_S, ids, dtype, mode=GREEDY, temperature=1.0, seed=0, offset=0):
+    """Static trimmed-vocabulary head ("SlimSpec" write-up, section 二: static vocabulary
+    trimming scores only a fixed reduced vocabulary, and a trimmed-away token can never be
+    proposed).  W_S [n_S, d] holds the kept rows W[ids] (trimmed once, offline); the head is the
+    dense head over those n_S rows, and the chosen position j maps back to the id ids[j].
+    Reading: sampling groups, lse and logprob are over the n_S kept positions in the given
+    order (Philox row = m)."""
+    out = head_dense(h, W_S, dtype, mode, temperature, seed, offset)
+    ids = np.asarray(ids, dtype=np.int64)
+    out["position"] = out["token"].copy()
+    out["token"] = ids[out["token"]]
+    return out
+
+
+def trimmed_acceptance_ceiling(p, ids):
+    """Largest acceptance rate any draft supported on the kept ids can reach against the target
+    distribution p: sum_x min(p(x), q(x)) <= p(S) for every q with q = 0 outside S, with equality
+    for q = p restricted to S and renormalised (SlimSpec write-up, section 二: the ceiling)."""
+    p = np.asarray(p, dtype=np.float64)
+    return float(p[np.asarray(ids, dtype=np.int64)].sum())
+
+
 def topk_ascending(s, k):
     """Indices of the k largest entries of s (ties -> lowest index), sorted ascending."""
     s = np.asarray(s, dtype=np.float64)
