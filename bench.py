@@ -39,7 +39,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--legs", default="all",
                    help="comma list of legs (lowrank48,lowrank48g,lowrank6,dense48,dense6,specvocab1,"
-                        "specvocab16,verify,verifyg,verifysparse,verifytree,adaptive48,adaptive48s) or 'all' "
+                        "specvocab16,verify,verifyg,verifysparse,verifytree,adaptive48,adaptive48s,trimmed48,"
+                        "trimmed6) or 'all' "
                         "or 'headline'")
     p.add_argument("--rotate", type=int, default=5, help="device copies of each weight set")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -153,6 +154,7 @@ def main():
     d, V, r, dp, k = w.d, w.V, w.r, w.dprime, w.k
     seeds = w.seeds
     legs_all = ["lowrank48", "lowrank48g", "lowrank6", "adaptive48", "adaptive48s", "dense48", "dense6",
+                "trimmed48", "trimmed6",
                 "specvocab1", "specvocab16",
                 "verify", "verifyg", "verifysparse", "verifytree"]
     if args.legs == "all":
@@ -178,7 +180,7 @@ def main():
         Wu.append(Wu[0].clone())
     h48 = bf(h48_np)
     h6 = bf(h6_np)
-    need_dense = any(x.startswith("dense") or x.startswith("specvocab") for x in legs)
+    need_dense = any(x.startswith(("dense", "specvocab", "trimmed")) for x in legs)
     W = bf(synth.dense_weights(V, d, "bf16", seeds["weights"])) if need_dense else None
     log(f"  inputs ready in {time.time() - t0:.1f}s")
 
@@ -300,6 +302,32 @@ def main():
             alg = (dp * d + V * dp) * 2 + u * d * 2 + M * d * 2 + M * k * 12
             out = run_leg(name, calls, M, alg)
             out["union_rows"] = u
+
+    # static trimmed vocabulary: the dense head over 32768 kept rows (a seeded id subset; the
+    # kept rows are gathered once, as a trimmed head stores them)
+    if "trimmed48" in legs or "trimmed6" in legs:
+        n_keep = 32768
+        keep = np.sort(np.random.default_rng(seeds["weights"] + 77).choice(V, n_keep, replace=False)).astype(np.int32)
+        keep_t = torch.from_numpy(keep).to(dev)
+        WS = [W.index_select(0, keep_t.long()).contiguous()]
+        WS.append(WS[0].clone())
+        for name, hh, M in (("trimmed48", h48, 48), ("trimmed6", h6, 6)):
+            if name not in legs:
+                continue
+            calls = []
+            for i in range(2):
+                tok = torch.empty(M, dtype=torch.int32, device=dev)
+                lse = torch.empty(M, dtype=torch.float32, device=dev)
+                lp = torch.empty(M, dtype=torch.float32, device=dev)
+                need = sh.load().sh_head_workspace_bytes(sh.OP_DENSE, M, d, 0, n_keep, 0)
+                ws = torch.zeros(need, dtype=torch.uint8, device=dev)
+                c = sh.prepared("draft_head_trimmed", hh, M, d, WS[i], n_keep, keep_t, sh.SH_BF16, sh.SAMPLE, 1.0,
+                                seeds["philox"], i, tok, lse, lp, None, ws, need, torch.cuda.current_stream().cuda_stream)
+                c.keep = (tok, lse, lp, ws)
+                calls.append(c)
+            o = run_leg(name, calls, M, (n_keep * d + M * d) * 2 + n_keep * 4 + M * 12)
+            o["config"] = {"kept_rows": n_keep}
+        del WS
 
     # position-adaptive rank: 8 sequences x 6 draft positions with ranks falling by position
     # (nested prefixes of the r = 512 pair); "s" = every position at rank <= 256 (half the columns)

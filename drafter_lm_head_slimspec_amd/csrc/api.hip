@@ -202,7 +202,7 @@ int check_workspace(void* ws, size_t have, size_t need) {
 int run_head(const void* x, int64_t M, int64_t K, const void* W, int64_t V, int dtype, int mode,
              float temperature, uint64_t seed, uint64_t offset, int32_t* token, float* lse,
              float* logprob, float* logits, sh::Partial* partials, float* lg, hipStream_t st,
-             int64_t ld = 0) {
+             int64_t ld = 0, const int32_t* id_map = nullptr) {
   const bool bf16 = dtype == SH_BF16;
   const float invT = 1.0f / temperature;
   const bool want_lg = mode == SH_SAMPLE || lse != nullptr || logprob != nullptr;
@@ -249,6 +249,7 @@ int run_head(const void* x, int64_t M, int64_t K, const void* W, int64_t V, int 
     f.token = token;
     f.lse = lse;
     f.logprob = logprob;
+    f.id_map = id_map;
     SH_HIP(sh::launch_head_fin(f, st), "head finalize kernel");
     return SH_OK;
   }
@@ -295,6 +296,7 @@ int run_head(const void* x, int64_t M, int64_t K, const void* W, int64_t V, int 
   f.token = token;
   f.lse = lse;
   f.logprob = logprob;
+  f.id_map = id_map;
   SH_HIP(sh::launch_head_finalize(f, st), "head finalize kernel");
   return SH_OK;
 }
@@ -381,6 +383,25 @@ int draft_head_dense(const void* h, int64_t M, int64_t d, const void* W, int64_t
   auto* lg = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.lg_off);
   return run_head(h, M, d, W, V, dtype, mode, temperature, seed, offset, token, lse, logprob,
                   logits, parts, lg, st);
+}
+
+int draft_head_trimmed(const void* h, int64_t M, int64_t d, const void* W_S, int64_t n_S, const int32_t* ids,
+                       int dtype, int mode, float temperature, uint64_t seed, uint64_t offset, int32_t* token,
+                       float* lse, float* logprob, float* logits, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  g_last_error.clear();
+  SH_TRY(check_common_head(h, M, d, n_S, dtype, mode, temperature, token, lse, logprob));
+  SH_TRY(check_ptr(W_S, "W_S"));
+  if (ids == nullptr) return fail(SH_ERR_NULL, "ids is NULL");
+  if (!aligned(ids, 4)) return fail(SH_ERR_ALIGN, "ids is not 4-byte aligned");
+  SH_TRY(check_opt_out(logits, "logits"));
+  const HeadLayout L = head_layout(SH_OP_DENSE, M, d, 0, n_S, 0, SH_F32);
+  SH_TRY(check_workspace(workspace, workspace_bytes, L.total));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  auto* parts = reinterpret_cast<sh::Partial*>(static_cast<char*>(workspace) + L.part_off);
+  auto* lg = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.lg_off);
+  return run_head(h, M, d, W_S, n_S, dtype, mode, temperature, seed, offset, token, lse, logprob, logits, parts, lg,
+                  st, 0, ids);
 }
 
 int draft_head_lowrank(const void* h, int64_t M, int64_t d, const void* W_down, int64_t r,

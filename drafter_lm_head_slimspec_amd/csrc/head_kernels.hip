@@ -1177,7 +1177,8 @@ __global__ __launch_bounds__(kFinThreads) void k_head_finalize(FinalizeArgs f) {
     ytok = __shfl(y, el);
   }
   if (threadIdx.x == 0) {
-    f.token[m] = tok;
+    // a trimmed head reports the vocabulary id of the chosen kept row
+    f.token[m] = (f.id_map != nullptr && tok >= 0 && tok < f.V) ? f.id_map[tok] : tok;
     if (f.lse) f.lse[m] = lse;
     if (f.logprob) f.logprob[m] = ytok - lse;
   }

@@ -387,7 +387,8 @@ __device__ __forceinline__ void finalize_row(const FinalizeArgs& f, int m, int n
     ytok = __shfl(y, el);
   }
   if (threadIdx.x == 0) {
-    f.token[m] = tok;
+    // a trimmed head reports the vocabulary id of the chosen kept row
+    f.token[m] = (f.id_map != nullptr && tok >= 0 && tok < f.V) ? f.id_map[tok] : tok;
     if (f.lse) f.lse[m] = lse;
     if (f.logprob) f.logprob[m] = ytok - lse;
   }

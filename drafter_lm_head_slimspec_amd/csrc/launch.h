@@ -46,6 +46,7 @@ struct FinalizeArgs {
   int32_t* token;
   float* lse;
   float* logprob;
+  const int32_t* id_map;    // nullable [V]: the token written is id_map[row chosen]
 };
 
 // Tile-streaming head pass (bf16, rows of 128, 256, 384 or 512 elements, at most kTileMaxRows

@@ -37,6 +37,8 @@ _SIGS = {
                               _vp, _sz, _vp]),
     "draft_head_lowrank": (_i, [_vp, _i64, _i64, _vp, _i64, _vp, _i64, _i, _i, _f, _u64, _u64, _vp,
                                 _vp, _vp, _vp, _vp, _sz, _vp]),
+    "draft_head_trimmed": (_i, [_vp, _i64, _i64, _vp, _i64, _vp, _i, _i, _f, _u64, _u64, _vp, _vp, _vp, _vp, _vp,
+                                _sz, _vp]),
     "draft_head_lowrank_adaptive": (_i, [_vp, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i, _i, _f, _u64, _u64,
                                          _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "draft_head_specvocab": (_i, [_vp, _i64, _i64, _vp, _i64, _vp, _vp, _i64, _i64, _i, _i, _f, _u64,
@@ -168,6 +170,27 @@ def draft_head_lowrank(h, W_down, W_up, mode="greedy", temperature=1.0, seed=0, 
     _check(lib.draft_head_lowrank(_p(h), M, d, _p(W_down), r, _p(W_up), V, _dt(h), _mode(mode),
                                   float(temperature), int(seed), int(offset), _p(token), _p(lse),
                                   _p(logprob), _p(logits), _p(ws), ws.numel(), _stream(dev)))
+    return {"token": token, "lse": lse, "logprob": logprob, "logits": logits}
+
+
+def draft_head_trimmed(h, W_S, ids, mode="greedy", temperature=1.0, seed=0, offset=0, want_logits=False):
+    """Dense head over the kept rows W_S = W[ids]; the token is the vocabulary id ids[j]."""
+    lib = load()
+    _contig(h, W_S, ids)
+    M, d = h.shape
+    n = W_S.shape[0]
+    if ids.dtype != torch.int32 or ids.shape != (n,):
+        raise TypeError("ids must be int32 [n_S]")
+    dev = h.device
+    token = torch.empty(M, dtype=torch.int32, device=dev)
+    lse = torch.empty(M, dtype=torch.float32, device=dev)
+    logprob = torch.empty(M, dtype=torch.float32, device=dev)
+    logits = torch.empty(M, n, dtype=torch.float32, device=dev) if want_logits else None
+    need = lib.sh_head_workspace_bytes(OP_DENSE, M, d, 0, n, 0)
+    ws = workspace(need, dev)
+    _check(lib.draft_head_trimmed(_p(h), M, d, _p(W_S), n, _p(ids), _dt(h), _mode(mode), float(temperature),
+                                  int(seed), int(offset), _p(token), _p(lse), _p(logprob), _p(logits), _p(ws),
+                                  ws.numel(), _stream(dev)))
     return {"token": token, "lse": lse, "logprob": logprob, "logits": logits}
 
 

@@ -101,6 +101,23 @@ int draft_head_dense(const void* h, int64_t M, int64_t d, const void* W, int64_t
                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Static trimmed-vocabulary head (SlimSpec write-up, section 二: static trimming scores only a
+ * fixed reduced vocabulary, and a trimmed-away token can never be proposed, which caps the
+ * acceptance rate at the target's mass on the kept ids).  The dense head over n_S kept rows:
+ *   W_S [n_S, d] device: the kept rows W[ids], gathered once by the caller
+ *   ids [n_S] int32 device: their vocabulary ids
+ *   token [M]: ids[j] for the chosen kept position j; lse / logprob over the kept rows;
+ *   logits (nullable) [M, n_S] float, y = z / T in kept-row order.
+ *   Sampling groups are the 64-position groups of the kept-row order (Philox purposes 0/1,
+ *   row m).  Shapes, dtypes and errors as draft_head_dense with V = n_S.
+ *   Workspace: sh_head_workspace_bytes(SH_OP_DENSE, M, d, 0, n_S, 0).
+ */
+int draft_head_trimmed(const void* h, int64_t M, int64_t d, const void* W_S, int64_t n_S, const int32_t* ids,
+                       int dtype, int mode, float temperature, uint64_t seed, uint64_t offset, int32_t* token,
+                       float* lse, float* logprob, float* logits, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/*
  * SlimSpec low-rank head (SlimSpec write-up, section 三 and Q&A Q1).
  *   W_down  [r, d]   (the d -> r map stored row per output), dtype
  *   W_up    [V, r]   dtype

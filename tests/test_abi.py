@@ -22,7 +22,7 @@ def lib():
 def test_header_declares_the_four_entry_points():
     names = libutil.header_functions()
     for n in ("draft_head_dense", "draft_head_lowrank", "draft_head_specvocab", "spec_verify",
-              "spec_verify_sparse", "spec_verify_tree", "draft_head_lowrank_adaptive"):
+              "spec_verify_sparse", "spec_verify_tree", "draft_head_lowrank_adaptive", "draft_head_trimmed"):
         assert n in names
 
 
@@ -186,6 +186,20 @@ def test_lowrank_adaptive_validation(lib):
     assert v(dtype=sh.SH_F32) == sh.SH_ERR_UNSUPPORTED
     assert v(M=65) == sh.SH_ERR_UNSUPPORTED
     assert v(r=520, rk=big) == sh.SH_ERR_UNSUPPORTED   # 520 columns read: outside the tile pass
+    assert v(wsb=16) == sh.SH_ERR_WORKSPACE
+
+
+@no_gpu
+def test_trimmed_validation(lib):
+    def v(M=4, d=256, n=1024, ids=C, tok=D, wsb=1 << 30, mode=0):
+        return lib.draft_head_trimmed(A, M, d, B, n, ids, sh.SH_F32, mode, 1.0, 0, 0, tok, None, None, None, WS, wsb,
+                                      None)
+    assert v(ids=None) == sh.SH_ERR_NULL
+    assert v(ids=ctypes.c_void_p(0x7f0000100002)) == sh.SH_ERR_ALIGN
+    assert v(tok=None) == sh.SH_ERR_NULL
+    assert v(n=0) != sh.SH_OK
+    assert v(M=0) == sh.SH_ERR_SHAPE
+    assert v(mode=4) == sh.SH_ERR_DTYPE
     assert v(wsb=16) == sh.SH_ERR_WORKSPACE
 
 
