@@ -18,6 +18,8 @@
 //
 // The sampler is the two-level Gumbel-max over groups of 64 consecutive candidates; the group
 // draws use Philox purpose 0 (draft group), the element draw purpose 1 (draft element).
+#include <hip/hip_ext.h>
+
 #include "device_common.h"
 #include "launch.h"
 #include "trace.h"
@@ -435,9 +437,10 @@ hipError_t run_tile(const TileArgs& a, int grid, hipStream_t st) {
   constexpr int lds = TilePass<NCB, KS, ZOUT, EPI>::kLds;
   hipError_t e = allow_lds_tile(k_head_tile<NCB, KS, ZOUT, EPI>, lds);
   if (e != hipSuccess) return e;
-  TraceScope ts("head_tile", st);
-  hipLaunchKernelGGL((k_head_tile<NCB, KS, ZOUT, EPI>), dim3(static_cast<unsigned>(grid)), dim3(kTileThreads), lds,
-                     st, a);
+  // the launch stamps the trace events itself: their interval is the kernel's execution
+  TraceScope ts("head_tile", st, true);
+  hipExtLaunchKernelGGL((k_head_tile<NCB, KS, ZOUT, EPI>), dim3(static_cast<unsigned>(grid)), dim3(kTileThreads), lds,
+                        st, ts.start(), ts.stop(), 0, a);
   return hipGetLastError();
 }
 

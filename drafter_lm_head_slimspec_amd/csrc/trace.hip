@@ -27,21 +27,25 @@ bool g_on = false;
 
 }  // namespace
 
-TraceScope::TraceScope(const char* name, hipStream_t st) : name_(name), st_(st), idx_(-1) {
+TraceScope::TraceScope(const char* name, hipStream_t st, bool by_launch)
+    : name_(name), st_(st), idx_(-1), by_launch_(by_launch) {
   if (!g_on) return;
   std::lock_guard<std::mutex> lk(g_mu);
   if (!g_on || g_next + 2 > g_pool.size()) return;
   idx_ = static_cast<int>(g_next);
   g_next += 2;
-  (void)hipEventRecord(g_pool[idx_], st_);
+  if (!by_launch_) (void)hipEventRecord(g_pool[idx_], st_);
 }
 
 TraceScope::~TraceScope() {
   if (idx_ < 0) return;
   std::lock_guard<std::mutex> lk(g_mu);
-  (void)hipEventRecord(g_pool[idx_ + 1], st_);
+  if (!by_launch_) (void)hipEventRecord(g_pool[idx_ + 1], st_);
   g_recs.push_back(Rec{name_, idx_, idx_ + 1});
 }
+
+hipEvent_t TraceScope::start() const { return idx_ < 0 ? nullptr : g_pool[idx_]; }
+hipEvent_t TraceScope::stop() const { return idx_ < 0 ? nullptr : g_pool[idx_ + 1]; }
 
 }  // namespace sh
 
