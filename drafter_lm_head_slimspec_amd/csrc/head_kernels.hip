@@ -214,17 +214,26 @@ __global__ __launch_bounds__(256) void k_rowdot_reduce(const float* __restrict__
 // ----------------------------------------------------------------------------------------
 // bf16 down-projection for at most kRdTileMaxM input rows, in one kernel:
 //   k_rowdot_tile    grid (ceil(R/16), ceil(M/16)): a workgroup of 8 waves owns a 16 x 16
-//                    output tile (16 rows of Wd by 16 input rows) over the whole of K; wave w
-//                    takes a contiguous eighth of the 32-wide k-steps (v_mfma_f32_16x16x32_bf16,
-//                    fragments straight from global memory, two batches of 8 k-steps in flight),
-//                    the 8 waves' accumulators are summed in LDS in a fixed order and rounded
-//                    once to bf16.  No split over workgroups, so no second pass and no scratch;
-//                    also clears a scratch block for a later kernel.
+//                    output tile (16 rows of Wd by 16 input rows) over the whole of K.  K is
+//                    walked in chunks of 512 elements; every chunk of both matrices is read
+//                    with whole 1 KB row segments per wave instruction (full cache lines),
+//                    all chunks of a batch of 8 issued up front, and passed through a
+//                    double-buffered, XOR-swizzled LDS tile from which the 8 waves read
+//                    their v_mfma_f32_16x16x32_bf16 fragments (two 32-wide k-steps each per
+//                    chunk).  The waves' accumulators are summed in LDS in a fixed order and
+//                    rounded once to bf16.  No split over workgroups, so no second pass and
+//                    no scratch; also clears a scratch block for a later kernel.
 // ----------------------------------------------------------------------------------------
 constexpr int kRdtWaves = 8;
-constexpr int kRdtBatch = 8;                  // k-steps per batch of loads
+constexpr int kRdtThreads = kRdtWaves * kWave;
+constexpr int kRdtChunk = 512;                      // elements of K per chunk
+constexpr int kRdtCpr = kRdtChunk * 2 / 16;         // 16-byte pieces per row per chunk (64)
+constexpr int kRdtPieces = 2 * 16 * kRdtCpr;        // W and x pieces per chunk (2048)
+constexpr int kRdtPerThread = kRdtPieces / kRdtThreads;   // 4
+constexpr int kRdtBatch = 8;                        // chunks whose loads are in flight together
 constexpr int64_t kRdTileMaxM = 64;
 static_assert(kRdTileMaxM == kRowdotRanksMaxM, "one rank per row of a one-pass launch");
+static_assert(kRdtCpr / 4 == 2 * kRdtWaves, "two k-steps per wave per chunk");
 
 typedef float rd_f32x4_t __attribute__((ext_vector_type(4)));
 
@@ -233,11 +242,13 @@ struct RowRanks {
   int32_t r[kRdTileMaxM];
 };
 
-__global__ __launch_bounds__(kRdtWaves * kWave) void k_rowdot_tile(const void* __restrict__ Wd,
-                                                                   const void* __restrict__ x, int R, int K, int M,
-                                                                   uint16_t* __restrict__ out,
-                                                                   uint32_t* __restrict__ zero, int64_t zero_words,
-                                                                   RowRanks rk) {
+__global__ __launch_bounds__(kRdtThreads) void k_rowdot_tile(const void* __restrict__ Wd,
+                                                             const void* __restrict__ x, int R, int K, int M,
+                                                             uint16_t* __restrict__ out,
+                                                             uint32_t* __restrict__ zero, int64_t zero_words,
+                                                             RowRanks rk) {
+  // [buffer][matrix 0 = Wd, 1 = x][row 0..15][piece slot], slot = piece ^ (row & 7)
+  __shared__ uint4 tile[2][2][16][kRdtCpr];
   __shared__ float red[kRdtWaves][4][kWave];
   if (zero != nullptr) {
     const int64_t nwg = static_cast<int64_t>(gridDim.x) * gridDim.y;
@@ -247,46 +258,61 @@ __global__ __launch_bounds__(kRdtWaves * kWave) void k_rowdot_tile(const void* _
     for (int64_t i = z0 + threadIdx.x; i < z1; i += blockDim.x) zero[i] = 0u;
   }
   const int l = lane_id(), w = wave_id();
-  const int row = l & 15, q = l >> 4;
+  const int tid = static_cast<int>(threadIdx.x);
   const int j0 = blockIdx.x * 16, m0 = blockIdx.y * 16;
   const uint32_t rowbytes = static_cast<uint32_t>(K) * 2;
   const int jrows = R - j0 < 16 ? R - j0 : 16;
   const int mrows = M - m0 < 16 ? M - m0 : 16;
-  const rsrc_t wrs = make_rsrc(static_cast<const char*>(Wd) + static_cast<size_t>(j0) * rowbytes,
-                               static_cast<uint32_t>(jrows) * rowbytes);
-  const rsrc_t xrs = make_rsrc(static_cast<const char*>(x) + static_cast<size_t>(m0) * rowbytes,
-                               static_cast<uint32_t>(mrows) * rowbytes);
-  const int kst = (K + 31) / 32;
-  const int ksw = (kst + kRdtWaves - 1) / kRdtWaves;
-  const int s0 = w * ksw;
-  const int s1 = s0 + ksw < kst ? s0 + ksw : kst;
-  const uint32_t aoff = row < jrows ? static_cast<uint32_t>(row) * rowbytes : kOutOfRange;
-  const uint32_t boff = row < mrows ? static_cast<uint32_t>(row) * rowbytes : kOutOfRange;
-  // k-step s of this lane: elements 32 s + 8 q .. +8 (rows are whole 16-byte chunks)
-  auto load = [&](uint4 (&A)[kRdtBatch], uint4 (&B)[kRdtBatch], int sb) {
+  const rsrc_t rs[2] = {make_rsrc(static_cast<const char*>(Wd) + static_cast<size_t>(j0) * rowbytes,
+                                  static_cast<uint32_t>(jrows) * rowbytes),
+                        make_rsrc(static_cast<const char*>(x) + static_cast<size_t>(m0) * rowbytes,
+                                  static_cast<uint32_t>(mrows) * rowbytes)};
+  const int nc = (K + kRdtChunk - 1) / kRdtChunk;
+  // piece i of this thread in a chunk: matrix, row and piece index within the row's 1 KB
+  // (pieces i * 512 + tid: two per matrix, each wave one row's 64 pieces)
+  static_assert(kRdtThreads == 8 * kRdtCpr && kRdtPerThread == 4, "piece layout");
+  auto piece = [&](int i, int& mat, int& row, int& pc) {
+    mat = i >> 1;
+    row = (i & 1) * 8 + tid / kRdtCpr;
+    pc = tid % kRdtCpr;
+  };
+  auto issue = [&](int c, uint4 (&v)[kRdtPerThread]) {
 #pragma unroll
-    for (int t = 0; t < kRdtBatch; ++t) {
-      const int s = sb + t;
-      const int k = s * 32 + q * 8;
-      const bool ok = s < s1 && k < K;
-      A[t] = buffer_load16(wrs, ok && aoff != kOutOfRange ? aoff + static_cast<uint32_t>(k) * 2 : kOutOfRange);
-      B[t] = buffer_load16(xrs, ok && boff != kOutOfRange ? boff + static_cast<uint32_t>(k) * 2 : kOutOfRange);
+    for (int i = 0; i < kRdtPerThread; ++i) {
+      int mat, row, pc;
+      piece(i, mat, row, pc);
+      const int k = c * kRdtChunk + pc * 8;
+      v[i] = buffer_load16(rs[mat], (c < nc && k < K) ? static_cast<uint32_t>(row) * rowbytes + static_cast<uint32_t>(k) * 2
+                                                      : kOutOfRange);
     }
   };
   rd_f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  auto mma = [&](const uint4 (&A)[kRdtBatch], const uint4 (&B)[kRdtBatch]) {
+  const int row = l & 15, q = l >> 4;
+  for (int cb = 0; cb < nc; cb += kRdtBatch) {
+    uint4 v[kRdtBatch][kRdtPerThread];
 #pragma unroll
-    for (int t = 0; t < kRdtBatch; ++t)
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, A[t]),
-                                                    __builtin_bit_cast(bf16x8_t, B[t]), acc, 0, 0, 0);
-  };
-  uint4 A0[kRdtBatch], B0[kRdtBatch], A1[kRdtBatch], B1[kRdtBatch];
-  load(A0, B0, s0);
-  for (int sb = s0; sb < s1; sb += 2 * kRdtBatch) {
-    load(A1, B1, sb + kRdtBatch);   // past s1 the loads are out of range: no memory traffic
-    mma(A0, B0);
-    if (sb + 2 * kRdtBatch < s1) load(A0, B0, sb + 2 * kRdtBatch);
-    mma(A1, B1);
+    for (int c = 0; c < kRdtBatch; ++c) issue(cb + c, v[c]);
+#pragma unroll
+    for (int c = 0; c < kRdtBatch; ++c) {
+      if (cb + c < nc) {   // uniform over the workgroup
+        const int buf = c & 1;
+#pragma unroll
+        for (int i = 0; i < kRdtPerThread; ++i) {
+          int mat, rr, pc;
+          piece(i, mat, rr, pc);
+          tile[buf][mat][rr][pc ^ (rr & 7)] = v[c][i];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int pc = (2 * w + t) * 4 + q;   // k-step 2w + t of the chunk, lane quarter q
+          const uint4 a = tile[buf][0][row][pc ^ (row & 7)];
+          const uint4 b = tile[buf][1][row][pc ^ (row & 7)];
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                        acc, 0, 0, 0);
+        }
+      }
+    }
   }
   // lane l holds rows j0 + 4 (l / 16) + v of column m0 + l % 16
 #pragma unroll
@@ -1241,7 +1267,7 @@ hipError_t launch_rowdot(const void* Wd, const void* x, int64_t R, int64_t K, in
     for (int m = 0; m < kRdTileMaxM; ++m) rk.r[m] = static_cast<int32_t>(R);
     const dim3 grid(static_cast<unsigned>((R + 15) / 16), static_cast<unsigned>((M + 15) / 16));
     TraceScope ts("rowdot_tile", st);
-    hipLaunchKernelGGL(k_rowdot_tile, grid, dim3(kRdtWaves * kWave), 0, st, Wd, x, static_cast<int>(R),
+    hipLaunchKernelGGL(k_rowdot_tile, grid, dim3(kRdtThreads), 0, st, Wd, x, static_cast<int>(R),
                        static_cast<int>(K), static_cast<int>(M), static_cast<uint16_t*>(out), zero, zero_words, rk);
     return hipGetLastError();
   }
@@ -1287,7 +1313,7 @@ hipError_t launch_rowdot_ranked(const void* Wd, const void* x, int64_t R, int64_
   for (int m = 0; m < kRdTileMaxM; ++m) rk.r[m] = m < M ? ranks[m] : 0;
   const dim3 grid(static_cast<unsigned>((R + 15) / 16), static_cast<unsigned>((M + 15) / 16));
   TraceScope ts("rowdot_tile", st);
-  hipLaunchKernelGGL(k_rowdot_tile, grid, dim3(kRdtWaves * kWave), 0, st, Wd, x, static_cast<int>(R),
+  hipLaunchKernelGGL(k_rowdot_tile, grid, dim3(kRdtThreads), 0, st, Wd, x, static_cast<int>(R),
                      static_cast<int>(K), static_cast<int>(M), static_cast<uint16_t*>(out), nullptr, int64_t{0}, rk);
   return hipGetLastError();
 }
