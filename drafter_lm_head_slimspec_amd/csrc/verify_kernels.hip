@@ -83,6 +83,21 @@ __device__ __forceinline__ Partial block_merge(Partial p, Partial* red4) {
   return r;
 }
 
+// block-wide argmax of one (score, id) per thread, lowest id on ties; result valid in thread 0
+__device__ __forceinline__ void block_argmax(float& v, int32_t& i, Partial* red4) {
+  wave_argmax(v, i);
+  const int w = wave_id(), nw = blockDim.x / kWave;
+  if (lane_id() == 0) {
+    red4[w].gscore = v;
+    red4[w].g = i;
+  }
+  __syncthreads();
+  v = red4[0].gscore;
+  i = red4[0].g;
+  for (int k = 1; k < nw; ++k) argmax_merge(v, i, red4[k].gscore, red4[k].g);
+  __syncthreads();
+}
+
 // Software-pipelined walk over [0, n) in spans of UNR chunks: the next span's loads are in
 // flight while the current one is processed (ping-pong buffers; past n the loads are
 // out-of-range, which costs no memory traffic, and proc sees chunks with e >= n).
@@ -237,8 +252,9 @@ __device__ __forceinline__ int32_t draw_in_group(int32_t g, int64_t V, uint64_t 
 }
 
 // Merges the row partials of sequence b into rowp (lane i of a wave loads segment partial i,
-// S <= 64, merged by a fixed butterfly: every kernel that calls this computes the same
-// values) and returns the leading-accept count (acceptance of all positions at once, lane t).
+// S <= 64, merged by a fixed butterfly over the first S lanes rounded up to a power of two:
+// every kernel that calls this computes the same values) and returns the leading-accept
+// count (acceptance of all positions at once, lane t).
 // The draft token's logits come from the partials' xz fields, so no logit row is read here.
 template <bool BF16>
 __device__ int seq_accept(const VerifyArgs& a, int64_t b, Partial* rowp, int* sh_a) {
@@ -246,25 +262,64 @@ __device__ int seq_accept(const VerifyArgs& a, int64_t b, Partial* rowp, int* sh
   const int R = rows_per_seq(a.mode, a.gamma);
   const int gamma = static_cast<int>(a.gamma);
   const int nw = blockDim.x / kWave;
-  // up to kAccBatch rows per wave at a time, every load of a batch issued before the merges
+  // wave 0, lanes < gamma: the draft token and its uniform, issued first (they depend on
+  // nothing); then every partial of the sequence this wave merges, all through one buffer
+  // descriptor with out-of-range lanes, so no load waits behind a branch
+  int32_t x = -1;
+  float uu = 0.f;
+  if (w == 0 && l < gamma) {
+    x = a.tokens[b * a.gamma + l];
+    if (a.mode != 0) uu = a.u[b * a.gamma + l];
+  }
+  const rsrc_t prs = make_rsrc(a.partials + b * R * a.S, static_cast<uint32_t>(R * a.S) * sizeof(Partial));
+  int span = 1;
+  while (span < a.S) span <<= 1;
   constexpr int kAccBatch = 4;
   for (int r0 = w; r0 < R; r0 += nw * kAccBatch) {
-    Partial p[kAccBatch];
+    uint4 raw[kAccBatch][2];
 #pragma unroll
     for (int j = 0; j < kAccBatch; ++j) {
       const int r = r0 + j * nw;
-      p[j] = (r < R && l < a.S) ? a.partials[(b * R + r) * a.S + l] : partial_empty();
+      const uint32_t off = (r < R && l < a.S) ? static_cast<uint32_t>(r * a.S + l) * sizeof(Partial) : kOutOfRange;
+      raw[j][0] = buffer_load16(prs, off);
+      raw[j][1] = buffer_load16(prs, off == kOutOfRange ? kOutOfRange : off + 16);
     }
 #pragma unroll
     for (int j = 0; j < kAccBatch; ++j) {
       const int r = r0 + j * nw;
-      const float xz = wave_max(p[j].xz);   // one segment at most holds a finite value
-      const float qx = wave_max(l < a.S ? p[j].pad1 : -1.f);   // sparse draft: segment 0 holds it
-      wave_partial_merge(p[j]);
+      Partial p = partial_empty();
+      if (r < R && l < a.S) {   // selects on loaded values, not a guard of the loads
+        p.m = __uint_as_float(raw[j][0].x);
+        p.s = __uint_as_float(raw[j][0].y);
+        p.gscore = __uint_as_float(raw[j][0].z);
+        p.g = static_cast<int32_t>(raw[j][0].w);
+        p.zmax = __uint_as_float(raw[j][1].x);
+        p.zid = static_cast<int32_t>(raw[j][1].y);
+        p.xz = __uint_as_float(raw[j][1].z);
+        p.pad1 = __uint_as_float(raw[j][1].w);
+      }
+      // butterfly over the first `span` lanes only (span = S rounded up to a power of two):
+      // lanes past S hold empty records, and every kernel merges in this same order
+      float xz = p.xz;   // one segment at most holds a finite value
+      float qx = l < a.S ? p.pad1 : -1.f;   // sparse draft: segment 0 holds it
+#pragma unroll
+      for (int sh = 32; sh >= 1; sh >>= 1) {
+        if (sh >= span) continue;
+        xz = fmaxf(xz, xor_lane(xz, sh));
+        qx = fmaxf(qx, xor_lane(qx, sh));
+        Partial o;
+        o.m = xor_lane(p.m, sh);
+        o.s = xor_lane(p.s, sh);
+        o.gscore = xor_lane(p.gscore, sh);
+        o.g = xor_lane(p.g, sh);
+        o.zmax = xor_lane(p.zmax, sh);
+        o.zid = xor_lane(p.zid, sh);
+        partial_merge(p, o);
+      }
       if (l == 0 && r < R) {
-        p[j].xz = xz;
-        p[j].pad1 = qx;
-        rowp[r] = p[j];
+        p.xz = xz;
+        p.pad1 = qx;
+        rowp[r] = p;
       }
     }
   }
@@ -272,7 +327,6 @@ __device__ int seq_accept(const VerifyArgs& a, int64_t b, Partial* rowp, int* sh
   if (w == 0) {
     bool acc = false;
     if (l < gamma) {
-      const int32_t x = a.tokens[b * a.gamma + l];
       const bool valid = x >= 0 && x < a.V;
       if (a.mode == 0) {
         acc = valid && x == rowp[l].zid;
@@ -281,13 +335,13 @@ __device__ int seq_accept(const VerifyArgs& a, int64_t b, Partial* rowp, int* sh
         // log p above the logarithm of the smallest subnormal)
         const float lp = rowp[l].xz * a.invT - (rowp[l].m + logf(rowp[l].s));
         const float qx = rowp[l].pad1;
-        acc = valid && (qx > 0.f ? a.u[b * a.gamma + l] < expf(lp - logf(qx)) : lp > -745.13f);
+        acc = valid && (qx > 0.f ? uu < expf(lp - logf(qx)) : lp > -745.13f);
       } else if (valid) {
         const float yp = rowp[l].xz * a.invT;
         const float yq = rowp[gamma + 1 + l].xz * a.invT;
         const float lp = yp - (rowp[l].m + logf(rowp[l].s));
         const float lq = yq - (rowp[gamma + 1 + l].m + logf(rowp[gamma + 1 + l].s));
-        acc = a.u[b * a.gamma + l] < expf(lp - lq);
+        acc = uu < expf(lp - lq);
       }
     }
     const uint64_t rej = __ballot(!acc);   // lanes >= gamma count as rejections
@@ -423,7 +477,7 @@ __global__ __launch_bounds__(256) void k_verify_resid(VerifyArgs a) {
     }
     __syncthreads();   // gw is rewritten by the next round
   }
-  best = block_merge(best, red4);
+  block_argmax(best.gscore, best.g, red4);   // only the group draw is carried
   if (threadIdx.x == 0) a.partials2[b * a.S2 + s2] = best;
 }
 
@@ -450,7 +504,7 @@ __global__ __launch_bounds__(256) void k_verify_finish(VerifyArgs a) {
   Partial best = partial_empty();
   if (a.mode != 0) {   // residual or bonus group winner from the residual kernel's segments
     best = l < a.S2 ? a.partials2[b * a.S2 + l] : partial_empty();
-    wave_partial_merge(best);   // argmax merges: exact in any order
+    wave_argmax(best.gscore, best.g);   // argmax merges: exact in any order
   }
   if (a.mode == 2 && resid) {
     // the candidates that fall in the winning group (every wave merged the same winner)
@@ -543,7 +597,7 @@ __global__ __launch_bounds__(kMaxTreeNodes) void k_tree_finish(VerifyArgs a) {
   const int n = threadIdx.x;
   for (int r = w; r < N; r += nw) {
     Partial p = l < a.S ? a.partials[(b * N + r) * a.S + l] : partial_empty();
-    wave_partial_merge(p);
+    wave_argmax(p.zmax, p.zid);   // greedy rows: only the argmax is needed
     if (l == 0) g[r] = p.zid;
   }
   int32_t par = 0, tok = 0;
