@@ -170,7 +170,8 @@ VerifyLayout verify_layout(int kind, int64_t B, int64_t gamma, int64_t V) {
   L.part_off = off;
   off = align_up(off + static_cast<size_t>(B * R * L.S) * sizeof(sh::Partial), 256);
   L.part2_off = off;
-  off = align_up(off + static_cast<size_t>(B * L.S2) * sizeof(sh::Partial), 256);
+  // per sequence: S2 residual-segment records and one acceptance record
+  off = align_up(off + static_cast<size_t>(B * (L.S2 + 1)) * sizeof(sh::Partial), 256);
   L.total = off;
   return L;
 }

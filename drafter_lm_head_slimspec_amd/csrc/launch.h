@@ -148,7 +148,7 @@ struct VerifyArgs {
   int32_t* out_tokens;
   Partial* partials;   // [B, rows, S] row-segment partials
   int S;
-  Partial* partials2;  // [B, S2] residual-segment partials (sampling)
+  Partial* partials2;  // [B, S2 + 1]: residual-segment records, then the acceptance record (sampling)
   int S2;
   const int32_t* qidx;  // mode 2: [B, gamma, k] candidate ids (distinct)
   const float* qprob;   // mode 2: [B, gamma, k] their draft probabilities

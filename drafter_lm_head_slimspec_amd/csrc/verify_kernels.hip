@@ -405,6 +405,28 @@ __global__ __launch_bounds__(256) void k_verify_resid(VerifyArgs a) {
       buf[2 * u + 1] = buffer_load16(rq, (e < n && qdense) ? e * ES : kOutOfRange);
     }
   };
+  // sparse draft: the candidate list of position acc_len, read once into registers when it
+  // has at most kQReg entries per thread (one round trip; the rounds below only scatter)
+  constexpr int kQReg = 8;
+  int32_t qid[kQReg];
+  float qpr[kQReg];
+  const bool qreg = SPARSE && !bonus && a.k <= static_cast<int64_t>(kQReg) * blockDim.x;
+  if constexpr (SPARSE) {
+    if (qreg) {
+      const int64_t base = (b * a.gamma + acc_len) * a.k;
+      const rsrc_t ri = make_rsrc(a.qidx + base, static_cast<uint32_t>(a.k) * 4u);
+      const rsrc_t rpq = make_rsrc(a.qprob + base, static_cast<uint32_t>(a.k) * 4u);
+#pragma unroll
+      for (int j = 0; j < kQReg; ++j) {
+        const uint32_t idx = j * blockDim.x + tid;
+        const bool ok = idx < static_cast<uint64_t>(a.k);
+        const uint32_t rid = buffer_load4(ri, ok ? idx * 4u : kOutOfRange);
+        const uint32_t rpr = buffer_load4(rpq, ok ? idx * 4u : kOutOfRange);
+        qid[j] = ok ? static_cast<int32_t>(rid) : -1;
+        qpr[j] = __uint_as_float(rpr);
+      }
+    }
+  }
   // the segment's groups in rounds of kResidGroups: first their log2 weights into LDS ...
   const int64_t g_first = e_begin / kGroup;
   for (uint32_t r0 = 0; r0 < n; r0 += RG * kGroup) {
@@ -414,10 +436,16 @@ __global__ __launch_bounds__(256) void k_verify_resid(VerifyArgs a) {
         for (uint32_t i = tid; i < rn; i += blockDim.x) qs[i] = 0.f;
         __syncthreads();
         const int64_t lo = e_begin + r0, hi = lo + rn;
-        const int64_t base = (b * a.gamma + acc_len) * a.k;
-        for (int64_t j = tid; j < a.k; j += blockDim.x) {
-          const int32_t id = a.qidx[base + j];
-          if (id >= lo && id < hi) qs[id - lo] = a.qprob[base + j];
+        if (qreg) {
+#pragma unroll
+          for (int j = 0; j < kQReg; ++j)
+            if (qid[j] >= lo && qid[j] < hi) qs[qid[j] - lo] = qpr[j];
+        } else {
+          const int64_t base = (b * a.gamma + acc_len) * a.k;
+          for (int64_t j = tid; j < a.k; j += blockDim.x) {
+            const int32_t id = a.qidx[base + j];
+            if (id >= lo && id < hi) qs[id - lo] = a.qprob[base + j];
+          }
         }
         __syncthreads();
       }
@@ -478,7 +506,17 @@ __global__ __launch_bounds__(256) void k_verify_resid(VerifyArgs a) {
     __syncthreads();   // gw is rewritten by the next round
   }
   block_argmax(best.gscore, best.g, red4);   // only the group draw is carried
-  if (threadIdx.x == 0) a.partials2[b * a.S2 + s2] = best;
+  if (threadIdx.x == 0) {
+    a.partials2[b * (a.S2 + 1) + s2] = best;
+    if (s2 == 0) {
+      // the sequence's acceptance for the finish kernel: accept count and the two lse
+      Partial rec = partial_empty();
+      rec.g = acc_len;
+      rec.m = Lp;
+      rec.s = Lq;
+      a.partials2[b * (a.S2 + 1) + a.S2] = rec;
+    }
+  }
 }
 
 // One workgroup per sequence: the accepted prefix, the last token, the outputs.
@@ -493,19 +531,27 @@ __global__ __launch_bounds__(256) void k_verify_finish(VerifyArgs a) {
   const int l = lane_id(), w = wave_id();
   const int gamma = static_cast<int>(a.gamma);
   __shared__ float qg[kGroup];   // sparse draft: q over the winning residual group
-  const int acc_len = seq_accept<BF16>(a, b, rowp, &sh_a);
+  // sampling: the residual kernel recorded the acceptance (count, lse of p_a and q_a);
+  // greedy: merge the row partials here
+  int acc_len;
+  float Lp = 0.f, Lq = 0.f;
+  Partial best = partial_empty();
+  if (a.mode != 0) {
+    const Partial rec = a.partials2[b * (a.S2 + 1) + a.S2];
+    acc_len = rec.g;
+    Lp = rec.m;
+    Lq = rec.s;
+    // residual or bonus group winner from the residual kernel's segments
+    best = l < a.S2 ? a.partials2[b * (a.S2 + 1) + l] : partial_empty();
+    wave_argmax(best.gscore, best.g);   // argmax merges: exact in any order
+  } else {
+    acc_len = seq_accept<BF16>(a, b, rowp, &sh_a);
+  }
   const bool resid = a.mode != 0 && acc_len < gamma;
   const bool qdense = resid && a.mode == 1;
   const char* prow = static_cast<const char*>(row_ptr<BF16>(a, b, acc_len));
   const char* qrow = qdense ? static_cast<const char*>(row_ptr<BF16>(a, b, gamma + 1 + acc_len)) : nullptr;
   const float c = a.invT * kLog2e;
-  const float Lp = (rowp[acc_len].m + logf(rowp[acc_len].s)) * kLog2e;
-  const float Lq = qdense ? (rowp[gamma + 1 + acc_len].m + logf(rowp[gamma + 1 + acc_len].s)) * kLog2e : 0.f;
-  Partial best = partial_empty();
-  if (a.mode != 0) {   // residual or bonus group winner from the residual kernel's segments
-    best = l < a.S2 ? a.partials2[b * a.S2 + l] : partial_empty();
-    wave_argmax(best.gscore, best.g);   // argmax merges: exact in any order
-  }
   if (a.mode == 2 && resid) {
     // the candidates that fall in the winning group (every wave merged the same winner)
     if (threadIdx.x < kGroup) qg[threadIdx.x] = 0.f;
