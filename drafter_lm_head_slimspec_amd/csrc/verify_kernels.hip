@@ -732,7 +732,7 @@ hipError_t launch_verify_tree(const VerifyArgs& a, hipStream_t st) {
 int verify_segments(int64_t B, int64_t gamma, int64_t V, int mode) {
   const int64_t R = verify_rows_per_seq(mode, gamma);
   const int64_t NG = (V + kGroup - 1) / kGroup;
-  int64_t S = (2048 + B * R - 1) / (B * R);
+  int64_t S = (256 + B * R - 1) / (B * R);
   if (S > 64) S = 64;
   if (S > NG) S = NG;
   if (S < 1) S = 1;
