@@ -517,6 +517,8 @@ int draft_head_specvocab(const void* h, int64_t M, int64_t d, const void* W_down
       a.invT = 1.f;
       a.zout = scores + m0 * V;
       a.zout_ld = V;
+      // a few rows: the scorer also builds the top-k histograms (cleared by the d -> d' kernel)
+      if (M <= sh::kTileHistRows) a.hist = reinterpret_cast<uint32_t*>(ws + L.tk_off + TL.hist_off);
       SH_HIP(sh::launch_head_tile(a, tile_grid, st), "approximate scorer kernel");
       continue;
     }
@@ -538,7 +540,9 @@ int draft_head_specvocab(const void* h, int64_t M, int64_t d, const void* W_down
     int p = 0;
     SH_HIP(sh::launch_stream(a, mfma, &p, st), "approximate scorer kernel");
   }
-  SH_HIP(sh::launch_topk(topk_args(ws + L.tk_off, TL, scores, M, V, k, topk_idx), st), "top-k kernels");
+  sh::TopkArgs ta = topk_args(ws + L.tk_off, TL, scores, M, V, k, topk_idx);
+  ta.hist_ready = tile && M <= sh::kTileHistRows;
+  SH_HIP(sh::launch_topk(ta, st), "top-k kernels");
   SH_HIP(sh::launch_gather_exact(U, h, topk_idx, M, d, V, k, bf16, zbuf, st), "gather kernel");
   SH_HIP(sh::launch_gather_finalize(zbuf, topk_idx, M, k, mode == SH_SAMPLE ? 1 : 0, 1.0f / temperature,
                                     seed, offset, topk_logit, topk_prob, token, lse, logprob, st),

@@ -293,6 +293,15 @@ __device__ __forceinline__ void wave_partial_merge(Partial& p) {
   }
 }
 
+// order-preserving map float -> uint32 (larger float -> larger key); -0 is treated as +0
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u << 1) == 0u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+constexpr int kTkBins = 4096;   // top-k histogram: bins of the top 12 key bits
+constexpr int kTkShift = 20;    // key >> 20 = top 12 bits
+
 // Buffer loads: a resource descriptor (base, byte range) lets the hardware return zero for
 // offsets outside the range, so ragged tails need no branch around the load.
 typedef __amdgpu_buffer_rsrc_t rsrc_t;

@@ -32,8 +32,10 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kTileThreads = 256;   // four waves
 constexpr int kTileWaves = kTileThreads / kWave;
-// EPI bits: kEpiStats (row lse; with sampling, the group draws), kEpiArgmax (greedy argmax)
-constexpr int kEpiStats = 1, kEpiArgmax = 2;
+// EPI bits: kEpiStats (row lse; with sampling, the group draws), kEpiArgmax (greedy argmax),
+// kEpiHist (with raw scores: the top-k histogram of each row's order keys, in LDS, added to
+// the caller's [M, 4096] counts at the end)
+constexpr int kEpiStats = 1, kEpiArgmax = 2, kEpiHist = 4;
 
 }  // namespace
 
@@ -45,11 +47,15 @@ template <int NCB, int KS, bool ZOUT, int EPI>
 struct TilePass {
   static constexpr int NC = NCB * 16;   // activation rows (columns of the output tiles)
   static constexpr bool STATS = (EPI & kEpiStats) != 0, AMAX = (EPI & kEpiArgmax) != 0;
+  static constexpr bool HIST = (EPI & kEpiHist) != 0;
+  static_assert(!HIST || (ZOUT && NCB == 1), "the histogram rides on the raw scores of a few rows");
   static constexpr int CPRP = KS * 4;   // 16-byte chunks per activation row
   static constexpr int RS = CPRP + 4;   // LDS row stride of the staged activations, in chunks
   static constexpr int XPER = (NC * CPRP + kTileThreads - 1) / kTileThreads;
-  // LDS bytes: staged activations [NC][RS], later the Partial records [4][NC]
-  static constexpr int kLds = (NC * RS * 16 > kTileWaves * NC * 32) ? NC * RS * 16 : kTileWaves * NC * 32;
+  // LDS bytes: staged activations [NC][RS], later the Partial records [4][NC]; then the
+  // histograms [kTileHistRows][4096] (HIST)
+  static constexpr int kLdsMain = (NC * RS * 16 > kTileWaves * NC * 32) ? NC * RS * 16 : kTileWaves * NC * 32;
+  static constexpr int kLds = kLdsMain + (HIST ? kTileHistRows * kTkBins * 4 : 0);
 
   const TileArgs& a;
   uint4* smem;
@@ -153,15 +159,35 @@ struct TilePass {
           float* zo = a.zout + static_cast<int64_t>(m) * a.zout_ld;
 #pragma unroll
           for (int v = 0; v < 4; ++v)
-            if (r0 + v < V32) zo[r0 + v] = acc[T][cb][v];
+            if (r0 + v < V32) {
+              zo[r0 + v] = acc[T][cb][v];
+              if constexpr (HIST) atomicAdd(&hist()[m * kTkBins + (order_key(acc[T][cb][v]) >> kTkShift)], 1u);
+            }
         }
+      }
+    }
+  }
+  __device__ __forceinline__ uint32_t* hist() const {
+    return reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(smem) + kLdsMain);
+  }
+  __device__ __forceinline__ void hist_clear() const {
+    if constexpr (HIST)
+      for (int i = threadIdx.x; i < kTileHistRows * kTkBins; i += kTileThreads) hist()[i] = 0u;
+  }
+  // add this workgroup's nonzero bins to the rows' histograms
+  __device__ __forceinline__ void hist_flush() const {
+    if constexpr (HIST) {
+      __syncthreads();
+      for (int i = threadIdx.x; i < Mx * kTkBins; i += kTileThreads) {
+        const uint32_t c = hist()[i];
+        if (c != 0u) atomicAdd(&a.hist[i], c);
       }
     }
   }
 
   // fold group g (the four tiles' accumulators) into the running state
   __device__ __forceinline__ void group_end(int g, float gu) {
-    if constexpr (EPI != 0) {
+    if constexpr (STATS || AMAX) {
       const int gb = g * kGroup;
       const bool full = gb + kGroup <= V32;
 #pragma unroll
@@ -298,10 +324,13 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_head_tile(TileArgs a) {
     p.stage_issue(xv);
     p.tile_load(gw < p.NG ? gw : 0, 0, XA);
     __builtin_amdgcn_sched_barrier(0);
+    p.hist_clear();   // (made visible by the staging barrier)
     p.stage_finish(xv);
   }
   p.run(gw, nw, XA, XB);
-  if constexpr (EPI != 0) p.write_partials(static_cast<int>(blockIdx.x));
+  if constexpr (TilePass<NCB, KS, ZOUT, EPI>::STATS || TilePass<NCB, KS, ZOUT, EPI>::AMAX)
+    p.write_partials(static_cast<int>(blockIdx.x));
+  p.hist_flush();
 }
 
 // ----------------------------------------------------------------------------------------
@@ -447,6 +476,12 @@ hipError_t run_tile(const TileArgs& a, int grid, hipStream_t st) {
 template <int NCB, int KS>
 hipError_t run_tile_mode(const TileArgs& a, int grid, hipStream_t st) {
   const int epi = (a.want_stats ? kEpiStats : 0) | (a.want_argmax ? kEpiArgmax : 0);
+  if (a.hist != nullptr) {   // raw scores with their histogram (the SpecVocab scorer)
+    if constexpr (NCB == 1) {
+      if (a.zout != nullptr && epi == 0 && a.M <= kTileHistRows) return run_tile<1, KS, true, kEpiHist>(a, grid, st);
+    }
+    return hipErrorInvalidValue;
+  }
   if (a.zout != nullptr) {
     switch (epi) {
       case 0: return run_tile<NCB, KS, true, 0>(a, grid, st);

@@ -71,7 +71,10 @@ struct TileArgs {
   int64_t zout_ld;
   Partial* partials;  // [M, partials_ld], one per workgroup; nullable when no stats are wanted
   int64_t partials_ld;
+  uint32_t* hist;     // nullable (with zout, M <= kTileHistRows): [M, 4096] counts of the top 12
+                      // bits of each score's order key, added to (cleared by the caller)
 };
+constexpr int kTileHistRows = 2;
 bool head_tile_supported(int64_t M, int64_t K, int64_t V, bool bf16, int64_t ld = 0);
 
 // workgroups of a tile pass over V rows for passes of up to M activation rows
@@ -115,6 +118,7 @@ struct TopkArgs {
   uint2* cand;          // [M, V]
   uint64_t* mask;       // [M, ceil(V / 64)]
   int32_t* out;         // [M, k] ascending ids
+  bool hist_ready;      // the row histograms are already built (by the scorer)
 };
 constexpr int64_t kTopkMaxV = int64_t{1} << 19;  // finishing bitmasks live in LDS
 int topk_chunks(int64_t V);

@@ -10,12 +10,6 @@
 
 namespace sh {
 
-// order-preserving map float -> uint32 (larger float -> larger key); -0 is treated as +0
-__device__ __forceinline__ uint32_t order_key(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u << 1) == 0u) u = 0u;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
 
 // ----------------------------------------------------------------------------------------
 // Top-k as a threshold search over the order keys, spread over many workgroups per row:
@@ -33,8 +27,6 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 //   Kernel boundaries order the phases: an in-kernel hand-off between workgroups would need
 //   a device-scope release per workgroup, which writes back the issuing XCD's L2.
 // ----------------------------------------------------------------------------------------
-constexpr int kTkBins = 4096;
-constexpr int kTkShift = 20;            // key >> 20 = top 12 bits
 constexpr int kTkThreads = 256;
 constexpr int kTkPerThread = 8;
 constexpr int kTkChunk = kTkThreads * kTkPerThread;
@@ -319,12 +311,13 @@ size_t topk_finish_lds(int64_t V) {
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
   const dim3 grid(static_cast<unsigned>(a.chunks), static_cast<unsigned>(a.M));
-  {
+  hipError_t e;
+  if (!a.hist_ready) {   // else the scorer built the row histograms while writing the scores
     TraceScope ts("topk_hist", st);
     hipLaunchKernelGGL(k_topk_hist, grid, dim3(kTkThreads), 0, st, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   {
     TraceScope ts("topk_select", st);
     hipLaunchKernelGGL(k_topk_select, grid, dim3(kTkThreads), 0, st, a);
