@@ -40,7 +40,7 @@ def parse():
     p.add_argument("--legs", default="all",
                    help="comma list of legs (lowrank48,lowrank48g,lowrank6,dense48,dense6,specvocab1,"
                         "specvocab16,verify,verifyg,verifysparse,verifytree,adaptive48,adaptive48s,trimmed48,"
-                        "trimmed6) or 'all' "
+                        "trimmed6,gptoss192) or 'all' "
                         "or 'headline'")
     p.add_argument("--rotate", type=int, default=5, help="device copies of each weight set")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -153,7 +153,7 @@ def main():
     w = configs.LLAMA
     d, V, r, dp, k = w.d, w.V, w.r, w.dprime, w.k
     seeds = w.seeds
-    legs_all = ["lowrank48", "lowrank48g", "lowrank6", "adaptive48", "adaptive48s", "dense48", "dense6",
+    legs_all = ["lowrank48", "lowrank48g", "lowrank6", "gptoss192", "adaptive48", "adaptive48s", "dense48", "dense6",
                 "trimmed48", "trimmed6",
                 "specvocab1", "specvocab16",
                 "verify", "verifyg", "verifysparse", "verifytree"]
@@ -302,6 +302,34 @@ def main():
             alg = (dp * d + V * dp) * 2 + u * d * 2 + M * d * 2 + M * k * 12
             out = run_leg(name, calls, M, alg)
             out["union_rows"] = u
+
+    # GPT-OSS-20B-shaped low-rank head: d 2880, V 201088, r 360, 32 sequences x 6 = 192 rows, T 0.7
+    if "gptoss192" in legs:
+        g = configs.GPTOSS
+        Mg = g.Ms[0]
+        hg = bf(synth.hidden(Mg, g.d, "bf16", g.seeds["hidden"]))
+        gd_np, gu_np = synth.lowrank_weights(g.V, g.d, g.r, "bf16", g.seeds["weights"])
+        GWd = [bf(gd_np)]
+        GWu = [bf(gu_np)]
+        del gd_np, gu_np
+        for _ in range(R - 1):
+            GWd.append(GWd[0].clone())
+            GWu.append(GWu[0].clone())
+        calls = []
+        for i in range(R):
+            tok = torch.empty(Mg, dtype=torch.int32, device=dev)
+            lse = torch.empty(Mg, dtype=torch.float32, device=dev)
+            lp = torch.empty(Mg, dtype=torch.float32, device=dev)
+            need = sh.load().sh_head_workspace_bytes(sh.OP_LOWRANK, Mg, g.d, g.r, g.V, 0)
+            ws = torch.zeros(need, dtype=torch.uint8, device=dev)
+            c = sh.prepared("draft_head_lowrank", hg, Mg, g.d, GWd[i], g.r, GWu[i], g.V, sh.SH_BF16, sh.SAMPLE,
+                            g.temperature, g.seeds["philox"], i, tok, lse, lp, None, ws, need,
+                            torch.cuda.current_stream().cuda_stream)
+            c.keep = (tok, lse, lp, ws)
+            calls.append(c)
+        o = run_leg("gptoss192", calls, Mg, (g.r * g.d + g.V * g.r + Mg * g.d) * 2 + Mg * 12)
+        o["config"] = {"workload": g.name, "d": g.d, "V": g.V, "r": g.r, "rows": Mg, "temperature": g.temperature}
+        del GWd, GWu
 
     # static trimmed vocabulary: the dense head over 32768 kept rows (a seeded id subset; the
     # kept rows are gathered once, as a trimmed head stores them)

@@ -254,6 +254,48 @@ int run_head(const void* x, int64_t M, int64_t K, const void* W, int64_t V, int 
     SH_HIP(sh::launch_head_fin(f, st), "head finalize kernel");
     return SH_OK;
   }
+  if (logits == nullptr && sh::head_wide_supported(M, K, V, bf16, ld)) {
+    // more rows than the tile pass holds, short rows: one wide pass, then the finalize
+    const int grid = sh::head_wide_grid(V);
+    sh::TileArgs a{};
+    a.W = W;
+    a.x = x;
+    a.V = V;
+    a.K = static_cast<int>(K);
+    a.ld = static_cast<int>(ld);
+    a.M = static_cast<int>(M);
+    a.row0 = 0;
+    a.invT = invT;
+    a.want_stats = want_lg ? 1 : 0;
+    a.want_argmax = mode == SH_GREEDY ? 1 : 0;
+    a.sample = mode == SH_SAMPLE ? 1 : 0;
+    a.seed = seed;
+    a.offset = offset;
+    a.partials = partials;
+    a.partials_ld = sh::kMaxPartials;
+    SH_HIP(sh::launch_head_wide(a, grid, st), "head wide kernel");
+    sh::FinalizeArgs f{};
+    f.partials = partials;
+    f.partials_ld = sh::kMaxPartials;
+    f.P = grid;
+    f.W = W;
+    f.x = x;
+    f.V = V;
+    f.K = K;
+    f.ld = ld;
+    f.M = static_cast<int>(M);
+    f.bf16 = true;
+    f.mode = mode == SH_SAMPLE ? 1 : 0;
+    f.invT = invT;
+    f.seed = seed;
+    f.offset = offset;
+    f.token = token;
+    f.lse = lse;
+    f.logprob = logprob;
+    f.id_map = id_map;
+    SH_HIP(sh::launch_head_fin(f, st), "head finalize kernel");
+    return SH_OK;
+  }
   const bool mfma = bf16 && M > kValuMaxRows;
   const int64_t chunk = mfma ? kMfmaMaxRows : kValuMaxRows;
   int producers = 0;

@@ -1,0 +1,343 @@
+// Wide-batch head kernel for gfx950: bf16 rows of at most 512 elements and 65..256 activation
+// rows (the GPT-OSS-shaped SlimSpec head: r = 360, 32 sequences x 6 draft positions).
+//
+//   k_head_wide   z = W x over all V rows with per-workgroup Partials (lse, best group score
+//                 with the Philox group draw, argmax), as k_head_tile, for more activation
+//                 rows than fit one wave's registers.  A workgroup of four waves walks a
+//                 consecutive range of 64-row vocabulary groups in pairs; each group is read
+//                 once by the whole workgroup with whole-row loads (full cache lines) into an
+//                 LDS tile while the next pair's rows are in flight in registers.  Wave w multiplies the tile by its
+//                 own 16 * NCBW activation rows (their B fragments stay in registers for the
+//                 whole pass) on v_mfma_f32_16x16x32_bf16, reading the A fragments from LDS,
+//                 and folds each group into the running state of its rows exactly as the
+//                 tile kernel does: per group one in-lane and two cross-lane reductions give
+//                 the group log-sum-exp, the group draw L_g + Gumbel(u_g) and the argmax.
+//   The per-row merge of the workgroups' Partials is k_head_fin (head_tile.hip).
+#include <hip/hip_ext.h>
+
+#include <type_traits>
+
+#include "device_common.h"
+#include "launch.h"
+#include "trace.h"
+
+namespace sh {
+
+namespace {
+
+typedef float wf32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kWideThreads = 256;   // four waves
+constexpr int kWideWaves = kWideThreads / kWave;
+constexpr int kWideStats = 1, kWideArgmax = 2;
+
+}  // namespace
+
+template <int NCBW, int KS, int EPI>
+__global__ __launch_bounds__(kWideThreads, 1) void k_head_wide(TileArgs a) {
+  constexpr bool STATS = (EPI & kWideStats) != 0, AMAX = (EPI & kWideArgmax) != 0;
+  constexpr int CPR = KS * 4;            // 16-byte chunks per row covered by the k-steps
+  constexpr int RS = CPR + 1;            // LDS row stride in chunks (odd: conflict-free reads)
+  constexpr int PER = CPR * kGroup / kWideThreads;   // row chunks each thread loads per group
+  extern __shared__ uint4 tile[];        // [2][64][RS] the current pair of groups, then 64 spare chunks
+  const int l = lane_id(), w = wave_id();
+  const int col = l & 15, qd = l >> 4;
+  const int tid = static_cast<int>(threadIdx.x);
+  const int K = a.K;
+  const uint32_t rowbytes = static_cast<uint32_t>(a.ld > 0 ? a.ld : a.K) * 2;
+  const int kc = K / 8;                  // chunks of a row that hold elements (K % 8 == 0)
+  const int V32 = static_cast<int>(a.V);
+  const int NG = (V32 + kGroup - 1) / kGroup;
+  const uint32_t vbytes = static_cast<uint32_t>(V32) * rowbytes;
+  const int Mx = a.M;
+  const int m0 = w * NCBW * 16;          // first activation row of this wave
+  const float c2 = a.invT * kLog2e;
+
+  // this wave's activation fragments: Bf[s][cb] = x[m0 + 16 cb + col][32 s + 8 qd .. +8]
+  uint4 Bf[KS][NCBW];
+  {
+    const rsrc_t xrs = make_rsrc(a.x, static_cast<uint32_t>(Mx) * rowbytes);
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+      for (int cb = 0; cb < NCBW; ++cb) {
+        const int m = m0 + cb * 16 + col, c = 4 * s + qd;
+        Bf[s][cb] = buffer_load16(xrs, (m < Mx && c < kc) ? static_cast<uint32_t>(m) * rowbytes + c * 16u : kOutOfRange);
+      }
+  }
+  // chunks past K read zero from LDS: cleared once, never overwritten
+  for (int i = tid; i < 2 * kGroup * (CPR - kc); i += kWideThreads) {
+    const int r = i / (CPR - kc), c = kc + i % (CPR - kc);
+    tile[r * RS + c] = zero16();
+  }
+  // this thread's row chunks of a group: slot tid + 256 j = (row, chunk), fixed for every group
+  uint32_t goff[PER];
+  int lidx[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int i = tid + kWideThreads * j;
+    const int r = i / kc, c = i - r * kc;
+    const bool ok = i < kGroup * kc;
+    goff[j] = ok ? static_cast<uint32_t>(r) * rowbytes + c * 16u : kOutOfRange;
+    lidx[j] = ok ? r * RS + c : 2 * kGroup * RS + (tid & 63);   // spare chunk: stores stay unconditional
+  }
+  auto gload = [&](int g, uint4 (&R)[PER]) {
+    const int r0 = g * kGroup;
+    const uint32_t b0 = r0 < V32 ? static_cast<uint32_t>(r0) * rowbytes : vbytes;
+    const rsrc_t rs = make_rsrc(static_cast<const char*>(a.W) + b0, vbytes - b0);
+#pragma unroll
+    for (int j = 0; j < PER; ++j) R[j] = buffer_load16(rs, goff[j]);
+  };
+  auto gstore = [&](const uint4 (&R)[PER], int half) {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) tile[lidx[j] + (lidx[j] < 2 * kGroup * RS ? half * kGroup * RS : 0)] = R[j];
+  };
+
+  // running state of activation row m0 + 16 qd + col (lanes with qd < NCBW)
+  float rm = -INFINITY, rsum = 0.f, gbest = -INFINITY, bz = -INFINITY;
+  int32_t gid = 0x7fffffff, bi = 0x7fffffff;
+
+  // Gumbel(u) of this lane's row for groups 4 q .. 4 q + 3: one Philox block holds all four,
+  // and a workgroup walks consecutive groups, so one block serves four of them
+  float gc[4] = {0.f, 0.f, 0.f, 0.f};
+  int gq = -1;
+  auto draw = [&](int g) -> float {
+    float gu = 0.f;
+    if constexpr (STATS) {
+      const int m = m0 + qd * 16 + col;
+      if (a.sample != 0) {
+        if ((g >> 2) != gq) {   // uniform over the workgroup
+          gq = g >> 2;
+          if (qd < NCBW && m < Mx) {
+            uint64_t wd[4];
+            philox_block(a.seed, a.offset, kDraftGroup, static_cast<uint64_t>(a.row0 + m),
+                         static_cast<uint64_t>(gq) * 4, wd);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) gc[i] = gumbel(word_to_uniform(wd[i]));
+          }
+        }
+        const int gi = g & 3;
+        gu = gi == 0 ? gc[0] : gi == 1 ? gc[1] : gi == 2 ? gc[2] : gc[3];
+      }
+    }
+    return gu;
+  };
+  // z = tile half x this wave's activation fragments.  Per k-step the four tiles' A fragments
+  // are one batch of LDS reads, issued a k-step ahead of the 4 * NCBW MFMAs that use them
+  // (with `pin`, scheduling barriers keep the reads in front)
+  auto mma = [&](int half, wf32x4_t (&acc)[4][NCBW], auto pin) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int cb = 0; cb < NCBW; ++cb) acc[t][cb] = wf32x4_t{0.f, 0.f, 0.f, 0.f};
+    const uint4* trow = tile + (half * kGroup + col) * RS + qd;
+    auto aread = [&](uint4 (&af)[4], int s) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) af[t] = trow[t * 16 * RS + 4 * s];
+    };
+    auto amma = [&](const uint4 (&af)[4], int s) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int cb = 0; cb < NCBW; ++cb)
+          acc[t][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, af[t]),
+                                                               __builtin_bit_cast(bf16x8_t, Bf[s][cb]), acc[t][cb], 0, 0, 0);
+    };
+    static_assert(KS % 2 == 0, "k-steps in pairs");
+    uint4 afA[4], afB[4];
+    aread(afA, 0);
+#pragma unroll
+    for (int s = 0; s < KS; s += 2) {
+      aread(afB, s + 1);
+      if constexpr (decltype(pin)::value) __builtin_amdgcn_sched_barrier(0);
+      amma(afA, s);
+      if (s + 2 < KS) aread(afA, s + 2);
+      if constexpr (decltype(pin)::value) __builtin_amdgcn_sched_barrier(0);
+      amma(afB, s + 1);
+    }
+  };
+  // fold group g into the running state of this lane's row
+  auto epi = [&](int g, float gu, const wf32x4_t (&acc)[4][NCBW]) {
+    const int gb = g * kGroup;
+    const bool full = gb + kGroup <= V32;
+#pragma unroll
+    for (int cb = 0; cb < NCBW; ++cb) {
+      float z[16];
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int row = gb + t * 16 + qd * 4 + v;
+          z[t * 4 + v] = (full || row < V32) ? acc[t][cb][v] : -INFINITY;
+        }
+      float zm = z[0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) zm = fmaxf(zm, z[i]);
+      float ss = 0.f;
+      if constexpr (STATS) {
+        const float off = zm * c2;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) ss += fast_exp2(fmaf(z[i], c2, -off));
+        ss = zm == -INFINITY ? 0.f : ss;
+      }
+      int32_t zi = 0x7fffffff;
+      if constexpr (AMAX) {
+        int bsel = 15;
+#pragma unroll
+        for (int i = 15; i >= 0; --i)   // the lane's rows rise with i: keep the lowest
+          if (z[i] == zm) bsel = i;
+        zi = zm == -INFINITY ? 0x7fffffff : gb + (bsel >> 2) * 16 + qd * 4 + (bsel & 3);
+      }
+      // the four lanes col, col + 16, col + 32, col + 48 hold the group's 64 rows
+#pragma unroll
+      for (int o = 16; o <= 32; o <<= 1) {
+        const float zm2 = xor_lane(zm, o);
+        if constexpr (STATS) {
+          const float ss2 = xor_lane(ss, o);
+          const float mx = fmaxf(zm, zm2);
+          ss = mx == -INFINITY ? 0.f : ss * fast_exp2((zm - mx) * c2) + ss2 * fast_exp2((zm2 - mx) * c2);
+        }
+        if constexpr (AMAX) {
+          const int32_t zi2 = xor_lane(zi, o);
+          argmax_merge(zm, zi, zm2, zi2);
+        } else {
+          zm = fmaxf(zm, zm2);
+        }
+      }
+      // lane (col, qd) finishes activation row m0 + 16 qd + col
+      if (cb == qd && m0 + cb * 16 + col < Mx) {
+        if constexpr (STATS) {
+          const float L = zm * a.invT + log2f(ss) * kLn2;   // group log-sum-exp of y = z / T
+          const float mn = fmaxf(rm, L);
+          rsum = rsum * fast_exp2((rm - mn) * kLog2e) + fast_exp2((L - mn) * kLog2e);
+          rm = mn;
+          const float sc = L + gu;
+          if (a.sample != 0 && sc > gbest) {   // groups rise: strict > keeps the lowest on ties
+            gbest = sc;
+            gid = g;
+          }
+        }
+        if constexpr (AMAX) argmax_merge(bz, bi, zm, zi);
+      }
+    }
+  };
+  wf32x4_t accA[4][NCBW];
+
+  // the workgroup's groups are the consecutive range [gs, ge), taken in pairs (g, g + 1):
+  // while a pair is multiplied out of the LDS tile, the next pair's rows are in flight in
+  // registers; storing a pair waits for every outstanding load, which is exactly that pair
+  // (past the range a cache-resident group is re-read)
+  const int G = static_cast<int>(gridDim.x);
+  const int gs = static_cast<int>((static_cast<int64_t>(blockIdx.x) * NG) / G);
+  const int ge = static_cast<int>((static_cast<int64_t>(blockIdx.x + 1) * NG) / G);
+  auto clampg = [&](int g) { return g < ge ? g : gs; };
+  uint4 RA[PER], RB[PER];
+  gload(clampg(gs), RA);
+  gload(clampg(gs + 1), RB);
+  for (int g = gs; g < ge; g += 2) {
+    __syncthreads();   // every wave is done with the previous pair's tile
+    gstore(RA, 0);
+    gstore(RB, 1);
+    __syncthreads();
+    gload(clampg(g + 2), RA);
+    gload(clampg(g + 3), RB);
+    mma(0, accA, std::true_type{});
+    epi(g, draw(g), accA);
+    if (g + 1 < ge) {
+      mma(1, accA, std::true_type{});
+      epi(g + 1, draw(g + 1), accA);
+    }
+  }
+  // one Partial per activation row per workgroup (each row belongs to one lane)
+  const int m = m0 + qd * 16 + col;
+  if (qd < NCBW && m < Mx) {
+    Partial p;
+    p.m = rm;
+    p.s = rsum;
+    p.gscore = gbest;
+    p.g = gid;
+    p.zmax = bz;
+    p.zid = bi;
+    p.xz = -INFINITY;
+    p.pad1 = 0.f;
+    a.partials[static_cast<int64_t>(m) * a.partials_ld + blockIdx.x] = p;
+  }
+}
+
+// ----------------------------------------------------------------------------------------
+// host side
+// ----------------------------------------------------------------------------------------
+namespace {
+
+int wide_ks(int64_t K) { return static_cast<int>((K + 127) / 128) * 4; }   // 4, 8, 12 or 16
+int wide_ncbw(int64_t M) { return static_cast<int>((M + 63) / 64); }      // 1..4
+int wide_lds(int ks) { return (2 * kGroup * (ks * 4 + 1) + kWave) * 16; }
+// VGPRs per lane: activation fragments, two row buffers, accumulators, offsets and state
+int wide_regs(int ncbw, int ks) { return ks * ncbw * 4 + 2 * ks * 4 + 16 * ncbw + 2 * ks + 48; }
+
+template <int NCBW, int KS, int EPI>
+hipError_t run_wide(const TileArgs& a, int grid, hipStream_t st) {
+  const int lds = wide_lds(KS);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_head_wide<NCBW, KS, EPI>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (e != hipSuccess) return e;
+  TraceScope ts("head_wide", st, true);
+  hipExtLaunchKernelGGL((k_head_wide<NCBW, KS, EPI>), dim3(static_cast<unsigned>(grid)), dim3(kWideThreads), lds, st,
+                        ts.start(), ts.stop(), 0, a);
+  return hipGetLastError();
+}
+
+template <int NCBW, int KS>
+hipError_t run_wide_mode(const TileArgs& a, int grid, hipStream_t st) {
+  const int epi = (a.want_stats ? kWideStats : 0) | (a.want_argmax ? kWideArgmax : 0);
+  switch (epi) {
+    case kWideStats: return run_wide<NCBW, KS, kWideStats>(a, grid, st);
+    case kWideArgmax: return run_wide<NCBW, KS, kWideArgmax>(a, grid, st);
+    case kWideStats | kWideArgmax: return run_wide<NCBW, KS, kWideStats | kWideArgmax>(a, grid, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int NCBW>
+hipError_t run_wide_ks(const TileArgs& a, int grid, hipStream_t st) {
+  switch (wide_ks(a.K)) {
+    case 4: return run_wide_mode<NCBW, 4>(a, grid, st);
+    case 8: return run_wide_mode<NCBW, 8>(a, grid, st);
+    case 12: return run_wide_mode<NCBW, 12>(a, grid, st);
+    default:
+      if constexpr (NCBW <= 2) return run_wide_mode<NCBW, 16>(a, grid, st);
+      return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+bool head_wide_supported(int64_t M, int64_t K, int64_t V, bool bf16, int64_t ld) {
+  if (ld <= 0) ld = K;
+  if (!bf16 || M <= kTileMaxRows || M > kWideMaxRows || K < 8 || K % 8 != 0 || K > 512) return false;
+  if (ld < K || ld % 8 != 0 || V < 1 || V * ld * 2 > int64_t{0xFFFFFFF0}) return false;
+  const int ks = wide_ks(K), ncbw = wide_ncbw(M);
+  if (ks == 16 && ncbw > 2) return false;
+  return wide_regs(ncbw, ks) <= 400 && wide_lds(ks) <= 160 * 1024;
+}
+
+int head_wide_grid(int64_t V) {
+  DeviceInfo di;
+  if (device_info(&di) != hipSuccess) di.cus = 256;
+  const int64_t NG = (V + kGroup - 1) / kGroup;
+  int64_t grid = NG < di.cus ? NG : di.cus;   // one workgroup per CU
+  if (grid > kMaxPartials) grid = kMaxPartials;
+  return static_cast<int>(grid < 1 ? 1 : grid);
+}
+
+hipError_t launch_head_wide(const TileArgs& a, int grid, hipStream_t st) {
+  if (!head_wide_supported(a.M, a.K, a.V, true, a.ld) || a.zout != nullptr || a.hist != nullptr)
+    return hipErrorInvalidValue;
+  switch (wide_ncbw(a.M)) {
+    case 2: return run_wide_ks<2>(a, grid, st);
+    case 3: return run_wide_ks<3>(a, grid, st);
+    default: return run_wide_ks<4>(a, grid, st);
+  }
+}
+
+}  // namespace sh

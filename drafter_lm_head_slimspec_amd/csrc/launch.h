@@ -80,6 +80,13 @@ bool head_tile_supported(int64_t M, int64_t K, int64_t V, bool bf16, int64_t ld 
 // workgroups of a tile pass over V rows for passes of up to M activation rows
 int head_tile_grid(int64_t M, int64_t K, int64_t V);
 hipError_t launch_head_tile(const TileArgs& a, int grid, hipStream_t st);
+
+// Wide-batch pass (bf16 rows of at most 512 elements, kTileMaxRows < M <= kWideMaxRows): the
+// same contract as the tile pass (Partials only, no raw scores)
+constexpr int kWideMaxRows = 256;
+bool head_wide_supported(int64_t M, int64_t K, int64_t V, bool bf16, int64_t ld = 0);
+int head_wide_grid(int64_t V);
+hipError_t launch_head_wide(const TileArgs& a, int grid, hipStream_t st);
 // per row: merge the Partials, greedy token or the two-level draw (recomputing the winning group)
 hipError_t launch_head_fin(const FinalizeArgs& f, hipStream_t st);
 

@@ -104,6 +104,23 @@ def test_lowrank_tile(case, mode, T):
     _lowrank(*case, mode, T, want_logits=False)
 
 
+# shapes of the wide pass (bf16, rows of at most 512 elements, 65..256 activation rows):
+# r = 360 (rows not a multiple of 32), ragged V, every column-block count, the longest rows
+LOWRANK_WIDE = [
+    (520, 8200, 360, 192, "bf16"),
+    (512, 20000, 128, 65, "bf16"),
+    (512, 9000, 256, 130, "bf16"),
+    (256, 5000, 512, 100, "bf16"),
+    (512, 7000, 200, 256, "bf16"),
+]
+
+
+@pytest.mark.parametrize("mode,T", [("greedy", 1.0), ("sample", 1.0), ("sample", 0.7)])
+@pytest.mark.parametrize("case", LOWRANK_WIDE, ids=lambda c: "d%d-V%d-r%d-M%d-%s" % c)
+def test_lowrank_wide(case, mode, T):
+    _lowrank(*case, mode, T, want_logits=False)
+
+
 DENSE_SMALL = [
     (256, 1024, 4, "f32"),
     (520, 1000, 3, "bf16"),    # 65 chunks per row: two chunks per lane, masked
