@@ -231,8 +231,8 @@ constexpr int kRdtCpr = kRdtChunk * 2 / 16;         // 16-byte pieces per row pe
 constexpr int kRdtPieces = 2 * 16 * kRdtCpr;        // W and x pieces per chunk (2048)
 constexpr int kRdtPerThread = kRdtPieces / kRdtThreads;   // 4
 constexpr int kRdtBatch = 8;                        // chunks whose loads are in flight together
-constexpr int64_t kRdTileMaxM = 64;
-static_assert(kRdTileMaxM == kRowdotRanksMaxM, "one rank per row of a one-pass launch");
+constexpr int64_t kRdTileMaxM = 256;
+static_assert(kRdTileMaxM >= kRowdotRanksMaxM, "one rank per row of a one-pass launch");
 static_assert(kRdtCpr / 4 == 2 * kRdtWaves, "two k-steps per wave per chunk");
 
 typedef float rd_f32x4_t __attribute__((ext_vector_type(4)));
