@@ -1319,34 +1319,35 @@ hipError_t launch_rowdot_ranked(const void* Wd, const void* x, int64_t R, int64_
 }
 
 template <bool BF16, int MB, int LPR, bool ONE>
-static hipError_t run_valu(const StreamArgs& a, int grid, int lds, hipStream_t st) {
-  const int rec = 4 * MB * static_cast<int>(sizeof(Partial));
+static hipError_t run_valu(const StreamArgs& a, int grid, int nw, int lds, hipStream_t st) {
+  const int rec = nw * MB * static_cast<int>(sizeof(Partial));
   const int bytes = lds > rec ? lds : rec;
   hipError_t e = allow_lds(k_stream_valu<BF16, MB, LPR, ONE>, bytes);
   if (e != hipSuccess) return e;
   TraceScope ts("stream_valu", st);
-  hipLaunchKernelGGL((k_stream_valu<BF16, MB, LPR, ONE>), dim3(grid), dim3(256), bytes, st, a);
+  hipLaunchKernelGGL((k_stream_valu<BF16, MB, LPR, ONE>), dim3(grid), dim3(nw * kWave), bytes, st, a);
   return hipGetLastError();
 }
 
 template <bool BF16, int MB>
-static hipError_t dispatch_lpr(const StreamArgs& a, int lpr, bool one, int grid, int lds, hipStream_t st) {
+static hipError_t dispatch_lpr(const StreamArgs& a, int lpr, bool one, int grid, int nw, int lds, hipStream_t st) {
   switch (lpr) {
-    case 8: return run_valu<BF16, MB, 8, true>(a, grid, lds, st);
-    case 16: return run_valu<BF16, MB, 16, true>(a, grid, lds, st);
-    case 32: return run_valu<BF16, MB, 32, true>(a, grid, lds, st);
+    case 8: return run_valu<BF16, MB, 8, true>(a, grid, nw, lds, st);
+    case 16: return run_valu<BF16, MB, 16, true>(a, grid, nw, lds, st);
+    case 32: return run_valu<BF16, MB, 32, true>(a, grid, nw, lds, st);
     default:
-      return one ? run_valu<BF16, MB, 64, true>(a, grid, lds, st) : run_valu<BF16, MB, 64, false>(a, grid, lds, st);
+      return one ? run_valu<BF16, MB, 64, true>(a, grid, nw, lds, st)
+                 : run_valu<BF16, MB, 64, false>(a, grid, nw, lds, st);
   }
 }
 
 template <bool BF16>
-static hipError_t dispatch_mb(const StreamArgs& a, int lpr, bool one, int grid, int lds, hipStream_t st) {
-  if (a.M <= 1) return dispatch_lpr<BF16, 1>(a, lpr, one, grid, lds, st);
-  if (a.M <= 2) return dispatch_lpr<BF16, 2>(a, lpr, one, grid, lds, st);
-  if (a.M <= 4) return dispatch_lpr<BF16, 4>(a, lpr, one, grid, lds, st);
-  if (a.M <= 6) return dispatch_lpr<BF16, 6>(a, lpr, one, grid, lds, st);
-  return dispatch_lpr<BF16, 8>(a, lpr, one, grid, lds, st);
+static hipError_t dispatch_mb(const StreamArgs& a, int lpr, bool one, int grid, int nw, int lds, hipStream_t st) {
+  if (a.M <= 1) return dispatch_lpr<BF16, 1>(a, lpr, one, grid, nw, lds, st);
+  if (a.M <= 2) return dispatch_lpr<BF16, 2>(a, lpr, one, grid, nw, lds, st);
+  if (a.M <= 4) return dispatch_lpr<BF16, 4>(a, lpr, one, grid, nw, lds, st);
+  if (a.M <= 6) return dispatch_lpr<BF16, 6>(a, lpr, one, grid, nw, lds, st);
+  return dispatch_lpr<BF16, 8>(a, lpr, one, grid, nw, lds, st);
 }
 
 template <int NCB>
@@ -1370,8 +1371,7 @@ constexpr int kM16Resident = 80 * 1024;
 constexpr int kM16Chunk = 64 * 1024;
 
 template <int NCB>
-static hipError_t run_mfma16(const StreamArgs& a, int grid, hipStream_t st) {
-  const int nw = 4;
+static hipError_t run_mfma16(const StreamArgs& a, int grid, int nw, hipStream_t st) {
   const int KS = static_cast<int>((a.K + 31) / 32);
   const int rec = nw * a.M * static_cast<int>(sizeof(Partial));
   const int per_ks = NCB * kWave * 16;
@@ -1403,6 +1403,11 @@ hipError_t launch_stream(const StreamArgs& a, bool use_mfma, int* producers, hip
   if (grid > kMaxPartials) grid = kMaxPartials;
   if (grid < 1) grid = 1;
   *producers = static_cast<int>(grid);
+  // few groups (a trimmed vocabulary): fewer waves per workgroup in the VALU and 16x16x32
+  // kernels, so the workgroups still cover every CU
+  int nw16 = 4;
+  if (NG < 4 * static_cast<int64_t>(di.cus)) nw16 = NG < 2 * static_cast<int64_t>(di.cus) ? 1 : 2;
+  const int64_t grid16 = (NG + nw16 - 1) / nw16 < kMaxPartials ? (NG + nw16 - 1) / nw16 : kMaxPartials;
   if (!use_mfma) {
     const int C = static_cast<int>(a.K * (a.bf16 ? 2 : 4) / 16);
     int lpr = 64;
@@ -1413,8 +1418,9 @@ hipError_t launch_stream(const StreamArgs& a, bool use_mfma, int* producers, hip
     const bool one = C <= lpr;
     const int MB = a.M <= 1 ? 1 : a.M <= 2 ? 2 : a.M <= 4 ? 4 : a.M <= 6 ? 6 : 8;
     const int lds = MB * C * 16;
-    return a.bf16 ? dispatch_mb<true>(a, lpr, one, static_cast<int>(grid), lds, st)
-                  : dispatch_mb<false>(a, lpr, one, static_cast<int>(grid), lds, st);
+    *producers = static_cast<int>(grid16);   // the same few-groups rule as below
+    return a.bf16 ? dispatch_mb<true>(a, lpr, one, static_cast<int>(grid16), nw16, lds, st)
+                  : dispatch_mb<false>(a, lpr, one, static_cast<int>(grid16), nw16, lds, st);
   }
   // Measured on MI355X: for 17..64 rows whose 32x32 fragments fit in LDS the 32x32x16 kernel
   // (32 rows x 32 bytes per load, four loads completing each 128-byte line in one batch) is
@@ -1423,19 +1429,21 @@ hipError_t launch_stream(const StreamArgs& a, bool use_mfma, int* producers, hip
   if (a.M > 16 && a.M <= 64 && static_cast<int64_t>((KS16 + 7) / 8 * 8) * ((a.M + 31) / 32) * 1024 <= di.max_lds)
     return a.M <= 32 ? run_mfma<1>(a, static_cast<int>(grid), st) : run_mfma<2>(a, static_cast<int>(grid), st);
   const int ncb = (a.M + 15) / 16;
+  *producers = static_cast<int>(grid16);
+  const int g16 = static_cast<int>(grid16);
   switch (ncb) {
-    case 1: return run_mfma16<1>(a, static_cast<int>(grid), st);
-    case 2: return run_mfma16<2>(a, static_cast<int>(grid), st);
-    case 3: return run_mfma16<3>(a, static_cast<int>(grid), st);
-    case 4: return run_mfma16<4>(a, static_cast<int>(grid), st);
-    case 5: return run_mfma16<5>(a, static_cast<int>(grid), st);
-    case 6: return run_mfma16<6>(a, static_cast<int>(grid), st);
-    case 7: return run_mfma16<7>(a, static_cast<int>(grid), st);
-    case 8: return run_mfma16<8>(a, static_cast<int>(grid), st);
-    case 9: return run_mfma16<9>(a, static_cast<int>(grid), st);
-    case 10: return run_mfma16<10>(a, static_cast<int>(grid), st);
-    case 11: return run_mfma16<11>(a, static_cast<int>(grid), st);
-    case 12: return run_mfma16<12>(a, static_cast<int>(grid), st);
+    case 1: return run_mfma16<1>(a, g16, nw16, st);
+    case 2: return run_mfma16<2>(a, g16, nw16, st);
+    case 3: return run_mfma16<3>(a, g16, nw16, st);
+    case 4: return run_mfma16<4>(a, g16, nw16, st);
+    case 5: return run_mfma16<5>(a, g16, nw16, st);
+    case 6: return run_mfma16<6>(a, g16, nw16, st);
+    case 7: return run_mfma16<7>(a, g16, nw16, st);
+    case 8: return run_mfma16<8>(a, g16, nw16, st);
+    case 9: return run_mfma16<9>(a, g16, nw16, st);
+    case 10: return run_mfma16<10>(a, g16, nw16, st);
+    case 11: return run_mfma16<11>(a, g16, nw16, st);
+    case 12: return run_mfma16<12>(a, g16, nw16, st);
     default: return hipErrorInvalidValue;
   }
 }
