@@ -120,6 +120,7 @@ struct HeadLayout {
   size_t hr_off, hr_bytes;
   size_t part_off, part_bytes;
   size_t lg_off, lg_bytes;
+  size_t gz_off, gz_bytes;     // dense: the K-chunked pass's best-group logits
   size_t score_off, score_bytes;
   size_t z_off, z_bytes;
   size_t total;
@@ -143,6 +144,9 @@ HeadLayout head_layout(int op, int64_t M, int64_t d, int64_t r, int64_t V, int64
   L.lg_off = off;
   L.lg_bytes = (op == SH_OP_SPECVOCAB) ? 0 : align_up(static_cast<size_t>(M) * static_cast<size_t>(lg_stride(V)) * 4, 256);
   off += L.lg_bytes;
+  L.gz_off = off;
+  L.gz_bytes = (op == SH_OP_DENSE) ? align_up(sh::head_kchunk_side_bytes(M, d, V), 256) : 0;
+  off += L.gz_bytes;
   L.score_off = off;
   L.score_bytes = (op == SH_OP_SPECVOCAB) ? align_up(static_cast<size_t>(M * V) * 4, 256) : 0;
   off += L.score_bytes;
@@ -203,7 +207,7 @@ int check_workspace(void* ws, size_t have, size_t need) {
 int run_head(const void* x, int64_t M, int64_t K, const void* W, int64_t V, int dtype, int mode,
              float temperature, uint64_t seed, uint64_t offset, int32_t* token, float* lse,
              float* logprob, float* logits, sh::Partial* partials, float* lg, hipStream_t st,
-             int64_t ld = 0, const int32_t* id_map = nullptr) {
+             int64_t ld = 0, const int32_t* id_map = nullptr, float* gz = nullptr) {
   const bool bf16 = dtype == SH_BF16;
   const float invT = 1.0f / temperature;
   const bool want_lg = mode == SH_SAMPLE || lse != nullptr || logprob != nullptr;
@@ -254,9 +258,11 @@ int run_head(const void* x, int64_t M, int64_t K, const void* W, int64_t V, int 
     SH_HIP(sh::launch_head_fin(f, st), "head finalize kernel");
     return SH_OK;
   }
-  if (logits == nullptr && sh::head_wide_supported(M, K, V, bf16, ld)) {
-    // more rows than the tile pass holds, short rows: one wide pass, then the finalize
-    const int grid = sh::head_wide_grid(V);
+  const bool kchunk = logits == nullptr && (ld == 0 || ld == K) && sh::head_kchunk_supported(M, K, V, bf16);
+  if (kchunk || (logits == nullptr && sh::head_wide_supported(M, K, V, bf16, ld))) {
+    // long rows (K-chunked pass) or more rows than the tile pass holds (wide pass): one pass
+    // with in-kernel group draws, then the finalize
+    const int grid = kchunk ? sh::head_kchunk_grid(V) : sh::head_wide_grid(V);
     sh::TileArgs a{};
     a.W = W;
     a.x = x;
@@ -273,7 +279,14 @@ int run_head(const void* x, int64_t M, int64_t K, const void* W, int64_t V, int 
     a.offset = offset;
     a.partials = partials;
     a.partials_ld = sh::kMaxPartials;
-    SH_HIP(sh::launch_head_wide(a, grid, st), "head wide kernel");
+    if (kchunk) {
+      a.ld = 0;
+      a.gz = gz;
+      a.gz_ld = grid;
+      SH_HIP(sh::launch_head_kchunk(a, grid, st), "head K-chunked kernel");
+    } else {
+      SH_HIP(sh::launch_head_wide(a, grid, st), "head wide kernel");
+    }
     sh::FinalizeArgs f{};
     f.partials = partials;
     f.partials_ld = sh::kMaxPartials;
@@ -293,6 +306,10 @@ int run_head(const void* x, int64_t M, int64_t K, const void* W, int64_t V, int 
     f.lse = lse;
     f.logprob = logprob;
     f.id_map = id_map;
+    if (kchunk) {
+      f.gz = gz;
+      f.gz_ld = grid;
+    }
     SH_HIP(sh::launch_head_fin(f, st), "head finalize kernel");
     return SH_OK;
   }
@@ -424,8 +441,9 @@ int draft_head_dense(const void* h, int64_t M, int64_t d, const void* W, int64_t
   hipStream_t st = static_cast<hipStream_t>(stream);
   auto* parts = reinterpret_cast<sh::Partial*>(static_cast<char*>(workspace) + L.part_off);
   auto* lg = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.lg_off);
+  auto* gz = L.gz_bytes ? reinterpret_cast<float*>(static_cast<char*>(workspace) + L.gz_off) : nullptr;
   return run_head(h, M, d, W, V, dtype, mode, temperature, seed, offset, token, lse, logprob,
-                  logits, parts, lg, st);
+                  logits, parts, lg, st, 0, nullptr, gz);
 }
 
 int draft_head_trimmed(const void* h, int64_t M, int64_t d, const void* W_S, int64_t n_S, const int32_t* ids,
@@ -443,8 +461,9 @@ int draft_head_trimmed(const void* h, int64_t M, int64_t d, const void* W_S, int
   hipStream_t st = static_cast<hipStream_t>(stream);
   auto* parts = reinterpret_cast<sh::Partial*>(static_cast<char*>(workspace) + L.part_off);
   auto* lg = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.lg_off);
+  auto* gz = L.gz_bytes ? reinterpret_cast<float*>(static_cast<char*>(workspace) + L.gz_off) : nullptr;
   return run_head(h, M, d, W_S, n_S, dtype, mode, temperature, seed, offset, token, lse, logprob, logits, parts, lg,
-                  st, 0, ids);
+                  st, 0, ids, gz);
 }
 
 int draft_head_lowrank(const void* h, int64_t M, int64_t d, const void* W_down, int64_t r,

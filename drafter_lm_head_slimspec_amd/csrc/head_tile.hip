@@ -357,6 +357,25 @@ __device__ __forceinline__ void finalize_row(const FinalizeArgs& f, int m, int n
   if (f.mode == 0) {
     tok = acc.zid;
     ytok = acc.zmax * f.invT;
+  } else if (f.gz != nullptr) {
+    // the K-chunked pass kept each workgroup's best group: read the winning group's logits
+    // from its owner, workgroup p of the P producers owning groups [p NG / P, (p + 1) NG / P)
+    if (w != 0) return;   // the element draw is one wave's work (no barrier follows)
+    const int64_t NG = (f.V + kGroup - 1) / kGroup;
+    const int64_t g = acc.g == 0x7fffffff ? 0 : acc.g;
+    const int64_t p = ((g + 1) * f.P + NG - 1) / NG - 1;
+    const int64_t gbase = g * kGroup;
+    const float z = f.gz[(static_cast<int64_t>(m) * f.gz_ld + p) * kGroup + l];
+    const float gel = gumbel(philox_uniform(f.seed, f.offset, kDraftElem, static_cast<uint64_t>(m),
+                                            static_cast<uint64_t>(gbase + l)));
+    const bool valid = gbase + l < f.V;
+    const float y = z * f.invT;
+    float e = valid ? y + gel : -INFINITY;
+    int32_t ei = valid ? l : 0x7fffffff;
+    wave_argmax(e, ei);
+    const int el = ei == 0x7fffffff ? 0 : ei;
+    tok = static_cast<int32_t>(gbase + el);
+    ytok = __shfl(y, el);
   } else {
     // recompute the 64 logits of the winning group, 64 / nwaves rows per wave, loads together
     const int rpw = kGroup / nwaves;

@@ -47,6 +47,8 @@ struct FinalizeArgs {
   float* lse;
   float* logprob;
   const int32_t* id_map;    // nullable [V]: the token written is id_map[row chosen]
+  const float* gz;          // nullable [M, gz_ld, 64]: the winning group's logits as written by
+  int64_t gz_ld;            // the K-chunked pass (its owner among the P producers), not recomputed
 };
 
 // Tile-streaming head pass (bf16, rows of 128, 256, 384 or 512 elements, at most kTileMaxRows
@@ -73,6 +75,8 @@ struct TileArgs {
   int64_t partials_ld;
   uint32_t* hist;     // nullable (with zout, M <= kTileHistRows): [M, 4096] counts of the top 12
                       // bits of each score's order key, added to (cleared by the caller)
+  float* gz;          // nullable, K-chunked pass in sampling mode: [M, gz_ld, 64] raw logits of
+  int64_t gz_ld;      // each row's best group of each workgroup
 };
 constexpr int kTileHistRows = 2;
 bool head_tile_supported(int64_t M, int64_t K, int64_t V, bool bf16, int64_t ld = 0);
@@ -87,6 +91,16 @@ constexpr int kWideMaxRows = 256;
 bool head_wide_supported(int64_t M, int64_t K, int64_t V, bool bf16, int64_t ld = 0);
 int head_wide_grid(int64_t V);
 hipError_t launch_head_wide(const TileArgs& a, int grid, hipStream_t st);
+// K-chunked pass (bf16 rows of more than 512 elements, M <= kTileMaxRows, no row stride): the
+// same contract as the tile pass (Partials only, no raw scores).  Workgroup b owns groups
+// [b NG / grid, (b + 1) NG / grid) and, in sampling mode, writes the logits of each row's best
+// group among them to gz[m, b, :].
+constexpr int kKcMaxGroups = 8;   // groups a workgroup owns at most
+bool head_kchunk_supported(int64_t M, int64_t K, int64_t V, bool bf16);
+int head_kchunk_grid(int64_t V);
+// bytes of the side buffer gz for any grid head_kchunk_grid returns (0: the pass does not apply)
+size_t head_kchunk_side_bytes(int64_t M, int64_t K, int64_t V);
+hipError_t launch_head_kchunk(const TileArgs& a, int grid, hipStream_t st);
 // per row: merge the Partials, greedy token or the two-level draw (recomputing the winning group)
 hipError_t launch_head_fin(const FinalizeArgs& f, hipStream_t st);
 

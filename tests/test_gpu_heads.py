@@ -136,6 +136,27 @@ def test_dense_small(case, mode, T):
     _dense(*case, mode, T)
 
 
+DENSE_KCHUNK = [
+    # d, V, M, dtype        rows of more than 512 elements, at most 64 activation rows, no raw
+    #                       logits: the K-chunked pass
+    (1024, 3000, 1, "bf16"),      # one activation row: the four waves split each group's tiles
+    (520, 5000, 16, "bf16"),      # K just above one chunk (a second chunk of 8 elements)
+    (4096, 20000, 6, "bf16"),     # the dense head's K, one or two groups per workgroup
+    (776, 1000, 9, "bf16"),       # ragged chunk and ragged last group
+    (1024, 1000, 17, "bf16"),     # two waves (one with a single valid row), ragged last group
+    (1032, 3000, 33, "bf16"),     # last chunk of 8 elements, three waves
+    (2048, 40000, 64, "bf16"),    # four waves, two or three groups per workgroup
+    (1536, 100000, 20, "bf16"),   # six or seven groups per workgroup
+    (1024, 151936, 24, "bf16"),   # more groups than eight per CU: more workgroups than CUs
+]
+
+
+@pytest.mark.parametrize("mode,T", [("greedy", 1.0), ("sample", 1.0), ("sample", 0.7)])
+@pytest.mark.parametrize("case", DENSE_KCHUNK, ids=lambda c: "d%d-V%d-M%d-%s" % c)
+def test_dense_kchunk(case, mode, T):
+    _dense(*case, mode, T, want_logits=False)
+
+
 def test_lowrank_without_lse_outputs():
     d, V, r, M = 512, 1000, 64, 6
     h = synth.hidden(M, d, "bf16", 1)

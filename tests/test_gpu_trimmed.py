@@ -19,7 +19,7 @@ def _need_gpu():
     sh.load()
 
 
-def _trimmed(d, V, n, M, dtype, mode, T, seed=17, offset=4):
+def _trimmed(d, V, n, M, dtype, mode, T, seed=17, offset=4, want_logits=True):
     P.log(f"trimmed d={d} V={V} kept={n} M={M} {dtype} {mode} T={T}")
     rng = np.random.default_rng(seed)
     ids = np.sort(rng.choice(V, n, replace=False)).astype(np.int32)
@@ -27,7 +27,7 @@ def _trimmed(d, V, n, M, dtype, mode, T, seed=17, offset=4):
     W = synth.dense_weights(V, d, dtype, seed)
     W_S = np.ascontiguousarray(W[ids])
     out = sh.draft_head_trimmed(P.to_device(h, dtype), P.to_device(W_S, dtype), torch.from_numpy(ids).cuda(),
-                                mode=mode, temperature=T, seed=seed, offset=offset, want_logits=True)
+                                mode=mode, temperature=T, seed=seed, offset=offset, want_logits=want_logits)
     torch.cuda.synchronize()
     o = heads.head_trimmed(h, W_S, ids, dtype, mode, T, seed, offset)
     tok = out["token"].cpu().numpy()
@@ -54,3 +54,17 @@ CASES = [
 @pytest.mark.parametrize("case", CASES, ids=lambda c: "d%d-V%d-n%d-M%d-%s" % c)
 def test_trimmed(case, mode, T):
     _trimmed(*case, mode, T)
+
+
+KCHUNK_CASES = [
+    # d, V, kept, M, dtype       without raw logits: the K-chunked pass, tokens mapped
+    (4096, 6000, 2000, 6, "bf16"),   # one column block
+    (4096, 40000, 20001, 40, "bf16"),  # three column blocks, ragged last group, several groups
+                                       # per workgroup
+]
+
+
+@pytest.mark.parametrize("mode,T", [("greedy", 1.0), ("sample", 1.0), ("sample", 0.6)])
+@pytest.mark.parametrize("case", KCHUNK_CASES, ids=lambda c: "d%d-V%d-n%d-M%d-%s" % c)
+def test_trimmed_kchunk(case, mode, T):
+    _trimmed(*case, mode, T, want_logits=False)
