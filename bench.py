@@ -481,7 +481,7 @@ def main():
         line["hbm_roofline_frac_call"] = head["hbm_frac"]
     # roofline of the dominant kernel: the W_up streaming kernel of the headline leg
     if head and "kernels" in head:
-        kname = next(k for k in ("head_tile", "stream_mfma", "stream_valu") if k in head["kernels"])
+        kname = next(k for k in ("head_tile", "head_kchunk", "head_wide", "stream_mfma", "stream_valu") if k in head["kernels"])
         kavg = head["kernels"][kname]["avg_us"]
         kbytes = V * r * 2 + 48 * r * 2   # the W_up pass: W_up and h_r
         achieved = kbytes / (kavg * 1e-6) / 1e9
