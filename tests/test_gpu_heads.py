@@ -148,6 +148,9 @@ DENSE_KCHUNK = [
     (2048, 40000, 64, "bf16"),    # four waves, two or three groups per workgroup
     (1536, 100000, 20, "bf16"),   # six or seven groups per workgroup
     (1024, 151936, 24, "bf16"),   # more groups than eight per CU: more workgroups than CUs
+    (1024, 1, 5, "bf16"),         # a one-row vocabulary: one workgroup, one partial group
+    (2048, 65, 64, "bf16"),       # 64 activation rows, a last group of one row
+    (8184, 700, 40, "bf16"),      # sixteen chunks (the longest rows accepted), the last of 504 elements
 ]
 
 
@@ -155,6 +158,12 @@ DENSE_KCHUNK = [
 @pytest.mark.parametrize("case", DENSE_KCHUNK, ids=lambda c: "d%d-V%d-M%d-%s" % c)
 def test_dense_kchunk(case, mode, T):
     _dense(*case, mode, T, want_logits=False)
+
+
+@pytest.mark.parametrize("mode", ["greedy", "sample"])
+def test_lowrank_rank_above_one_chunk(mode):
+    # r > 512: the up-projection runs on the K-chunked pass
+    _lowrank(1024, 5000, 520, 40, "bf16", mode, 1.0, want_logits=False)
 
 
 def test_lowrank_without_lse_outputs():
