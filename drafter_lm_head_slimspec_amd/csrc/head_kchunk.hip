@@ -175,37 +175,27 @@ __global__ __launch_bounds__((NCB == 1 ? 4 : NCB) * 64, 1) void k_head_kchunk(Ti
       float zm = z[0];
 #pragma unroll
       for (int i = 1; i < TPW * 4; ++i) zm = fmaxf(zm, z[i]);
+      // the four lanes col, col + 16, col + 32, col + 48 hold the wave's rows of the group
+      // and end with the same values (the max is taken first, so the sum needs no rescaling)
+      zm = fmaxf(zm, xor_lane(zm, 16));
+      zm = fmaxf(zm, xor_lane(zm, 32));
       float ss = 0.f;
       if constexpr (STATS) {
         const float off = zm * c2;
 #pragma unroll
         for (int i = 0; i < TPW * 4; ++i) ss += fast_exp2(fmaf(z[i], c2, -off));
+        ss += xor_lane(ss, 16);
+        ss += xor_lane(ss, 32);
         ss = zm == -INFINITY ? 0.f : ss;
       }
       int32_t zi = 0x7fffffff;
       if constexpr (AMAX) {
-        int bsel = TPW * 4 - 1;
 #pragma unroll
         for (int i = TPW * 4 - 1; i >= 0; --i)   // the lane's rows rise with i: keep the lowest
-          if (z[i] == zm) bsel = i;
-        zi = zm == -INFINITY ? 0x7fffffff : gb + (t0 + (bsel >> 2)) * 16 + qd * 4 + (bsel & 3);
-      }
-      // the four lanes col, col + 16, col + 32, col + 48 hold the wave's rows of the group;
-      // the butterfly leaves the same result in all four
-#pragma unroll
-      for (int o = 16; o <= 32; o <<= 1) {
-        const float zm2 = xor_lane(zm, o);
-        if constexpr (STATS) {
-          const float ss2 = xor_lane(ss, o);
-          const float mx = fmaxf(zm, zm2);
-          ss = mx == -INFINITY ? 0.f : ss * fast_exp2((zm - mx) * c2) + ss2 * fast_exp2((zm2 - mx) * c2);
-        }
-        if constexpr (AMAX) {
-          const int32_t zi2 = xor_lane(zi, o);
-          argmax_merge(zm, zi, zm2, zi2);
-        } else {
-          zm = fmaxf(zm, zm2);
-        }
+          if (z[i] == zm) zi = gb + (t0 + (i >> 2)) * 16 + qd * 4 + (i & 3);
+        zi = zm == -INFINITY ? 0x7fffffff : zi;
+        zi = min(zi, xor_lane(zi, 16));
+        zi = min(zi, xor_lane(zi, 32));
       }
       st[gi] = KcStat{zm, ss, zi};
     }

@@ -185,72 +185,86 @@ struct TilePass {
     }
   }
 
-  // fold group g (the four tiles' accumulators) into the running state
-  __device__ __forceinline__ void group_end(int g, float gu) {
-    if constexpr (STATS || AMAX) {
-      const int gb = g * kGroup;
-      const bool full = gb + kGroup <= V32;
+  // fold group g (the four tiles' accumulators) into the running state (MASK: the
+  // vocabulary's last, partial group, whose rows past V are -inf)
+  template <bool MASK>
+  __device__ __forceinline__ void group_end_body(int g, float gu) {
+    const int gb = g * kGroup;
+    // per column block: the group's max, sum of exp and first argmax of activation row
+    // 16 cb + col; the four lanes col, col + 16, col + 32, col + 48 hold its 64 rows and end
+    // with the same values (the max is taken first, so the sum needs no rescaling)
+    float bm[NCB], bs[NCB];
+    int32_t bx[NCB];
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) {
-        float z[16];
+    for (int cb = 0; cb < NCB; ++cb) {
+      float z[16];
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+      for (int t = 0; t < 4; ++t)
 #pragma unroll
-          for (int v = 0; v < 4; ++v) {
+        for (int v = 0; v < 4; ++v) {
+          if constexpr (MASK) {
             const int row = gb + t * 16 + qd * 4 + v;
-            z[t * 4 + v] = (full || row < V32) ? acc[t][cb][v] : -INFINITY;
-          }
-        float zm = z[0];
-#pragma unroll
-        for (int i = 1; i < 16; ++i) zm = fmaxf(zm, z[i]);
-        float ss = 0.f;
-        if constexpr (STATS) {
-          // (a lane whose 16 rows all lie past V has zm = -inf and keeps ss = 0)
-          const float off = zm * c2;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) ss += fast_exp2(fmaf(z[i], c2, -off));
-          ss = zm == -INFINITY ? 0.f : ss;
-        }
-        int32_t zi = 0x7fffffff;
-        if constexpr (AMAX) {
-          int bsel = 15;
-#pragma unroll
-          for (int i = 15; i >= 0; --i)   // the lane's rows rise with i: keep the lowest
-            if (z[i] == zm) bsel = i;
-          zi = zm == -INFINITY ? 0x7fffffff : gb + (bsel >> 2) * 16 + qd * 4 + (bsel & 3);
-        }
-        // the four lanes col, col + 16, col + 32, col + 48 hold the group's 64 rows
-#pragma unroll
-        for (int o = 16; o <= 32; o <<= 1) {
-          const float zm2 = xor_lane(zm, o);
-          if constexpr (STATS) {
-            const float ss2 = xor_lane(ss, o);
-            const float mx = fmaxf(zm, zm2);
-            ss = mx == -INFINITY ? 0.f : ss * fast_exp2((zm - mx) * c2) + ss2 * fast_exp2((zm2 - mx) * c2);
-          }
-          if constexpr (AMAX) {
-            const int32_t zi2 = xor_lane(zi, o);
-            argmax_merge(zm, zi, zm2, zi2);
+            z[t * 4 + v] = row < V32 ? acc[t][cb][v] : -INFINITY;
           } else {
-            zm = fmaxf(zm, zm2);
+            z[t * 4 + v] = acc[t][cb][v];
           }
         }
-        // lane (col, qd) finishes activation row 16 qd + col
-        if (cb == qd && cb * 16 + col < Mx) {
-          if constexpr (STATS) {
-            const float L = zm * a.invT + log2f(ss) * kLn2;   // group log-sum-exp of y = z / T
-            const float mn = fmaxf(rm, L);
-            rsum = rsum * fast_exp2((rm - mn) * kLog2e) + fast_exp2((L - mn) * kLog2e);
-            rm = mn;
-            const float sc = L + gu;
-            if (a.sample != 0 && sc > gbest) {   // groups rise: strict > keeps the lowest on ties
-              gbest = sc;
-              gid = g;
-            }
-          }
-          if constexpr (AMAX) argmax_merge(bz, bi, zm, zi);
+      float zm = z[0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) zm = fmaxf(zm, z[i]);
+      zm = fmaxf(zm, xor_lane(zm, 16));
+      zm = fmaxf(zm, xor_lane(zm, 32));
+      float ss = 0.f;
+      if constexpr (STATS) {
+        const float off = zm * c2;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) ss += fast_exp2(fmaf(z[i], c2, -off));
+        ss += xor_lane(ss, 16);
+        ss += xor_lane(ss, 32);
+        ss = zm == -INFINITY ? 0.f : ss;
+      }
+      int32_t zi = 0x7fffffff;
+      if constexpr (AMAX) {
+#pragma unroll
+        for (int i = 15; i >= 0; --i)   // the lane's rows rise with i: keep the lowest
+          if (z[i] == zm) zi = gb + (i >> 2) * 16 + qd * 4 + (i & 3);
+        zi = zm == -INFINITY ? 0x7fffffff : zi;
+        zi = min(zi, xor_lane(zi, 16));
+        zi = min(zi, xor_lane(zi, 32));
+      }
+      bm[cb] = zm;
+      bs[cb] = ss;
+      bx[cb] = zi;
+    }
+    // lane (col, qd) finishes activation row 16 qd + col: one fold per lane
+    float zm = bm[0], ss = bs[0];
+    int32_t zi = bx[0];
+#pragma unroll
+    for (int cb = 1; cb < NCB; ++cb)
+      if (qd == cb) {
+        zm = bm[cb];
+        ss = bs[cb];
+        zi = bx[cb];
+      }
+    if (qd < NCB && qd * 16 + col < Mx) {
+      if constexpr (STATS) {
+        const float L = zm * a.invT + log2f(ss) * kLn2;   // group log-sum-exp of y = z / T
+        const float mn = fmaxf(rm, L);
+        rsum = rsum * fast_exp2((rm - mn) * kLog2e) + fast_exp2((L - mn) * kLog2e);
+        rm = mn;
+        const float sc = L + gu;
+        if (a.sample != 0 && sc > gbest) {   // groups rise: strict > keeps the lowest on ties
+          gbest = sc;
+          gid = g;
         }
       }
+      if constexpr (AMAX) argmax_merge(bz, bi, zm, zi);
+    }
+  }
+  __device__ __forceinline__ void group_end(int g, float gu) {
+    if constexpr (STATS || AMAX) {
+      if (g * kGroup + kGroup <= V32) group_end_body<false>(g, gu);   // uniform
+      else group_end_body<true>(g, gu);
     }
   }
 

@@ -156,10 +156,16 @@ __global__ __launch_bounds__(kWideThreads, 1) void k_head_wide(TileArgs a) {
       amma(afB, s + 1);
     }
   };
-  // fold group g into the running state of this lane's row
-  auto epi = [&](int g, float gu, const wf32x4_t (&acc)[4][NCBW]) {
+  // fold group g into the running state of this lane's row (MASK: the vocabulary's last,
+  // partial group, whose rows past V are -inf)
+  auto epi_body = [&](int g, float gu, const wf32x4_t (&acc)[4][NCBW], auto mask) {
+    constexpr bool MASK = decltype(mask)::value;
     const int gb = g * kGroup;
-    const bool full = gb + kGroup <= V32;
+    // per column block: the group's max, sum of exp and first argmax of activation row
+    // m0 + 16 cb + col; the four lanes col, col + 16, col + 32, col + 48 hold its 64 rows and
+    // end with the same values (the max is taken first, so the sum needs no rescaling)
+    float bm[NCBW], bs[NCBW];
+    int32_t bx[NCBW];
 #pragma unroll
     for (int cb = 0; cb < NCBW; ++cb) {
       float z[16];
@@ -167,59 +173,68 @@ __global__ __launch_bounds__(kWideThreads, 1) void k_head_wide(TileArgs a) {
       for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const int row = gb + t * 16 + qd * 4 + v;
-          z[t * 4 + v] = (full || row < V32) ? acc[t][cb][v] : -INFINITY;
+          if constexpr (MASK) {
+            const int row = gb + t * 16 + qd * 4 + v;
+            z[t * 4 + v] = row < V32 ? acc[t][cb][v] : -INFINITY;
+          } else {
+            z[t * 4 + v] = acc[t][cb][v];
+          }
         }
       float zm = z[0];
 #pragma unroll
       for (int i = 1; i < 16; ++i) zm = fmaxf(zm, z[i]);
+      zm = fmaxf(zm, xor_lane(zm, 16));
+      zm = fmaxf(zm, xor_lane(zm, 32));
       float ss = 0.f;
       if constexpr (STATS) {
         const float off = zm * c2;
 #pragma unroll
         for (int i = 0; i < 16; ++i) ss += fast_exp2(fmaf(z[i], c2, -off));
+        ss += xor_lane(ss, 16);
+        ss += xor_lane(ss, 32);
         ss = zm == -INFINITY ? 0.f : ss;
       }
       int32_t zi = 0x7fffffff;
       if constexpr (AMAX) {
-        int bsel = 15;
 #pragma unroll
         for (int i = 15; i >= 0; --i)   // the lane's rows rise with i: keep the lowest
-          if (z[i] == zm) bsel = i;
-        zi = zm == -INFINITY ? 0x7fffffff : gb + (bsel >> 2) * 16 + qd * 4 + (bsel & 3);
+          if (z[i] == zm) zi = gb + (i >> 2) * 16 + qd * 4 + (i & 3);
+        zi = zm == -INFINITY ? 0x7fffffff : zi;
+        zi = min(zi, xor_lane(zi, 16));
+        zi = min(zi, xor_lane(zi, 32));
       }
-      // the four lanes col, col + 16, col + 32, col + 48 hold the group's 64 rows
-#pragma unroll
-      for (int o = 16; o <= 32; o <<= 1) {
-        const float zm2 = xor_lane(zm, o);
-        if constexpr (STATS) {
-          const float ss2 = xor_lane(ss, o);
-          const float mx = fmaxf(zm, zm2);
-          ss = mx == -INFINITY ? 0.f : ss * fast_exp2((zm - mx) * c2) + ss2 * fast_exp2((zm2 - mx) * c2);
-        }
-        if constexpr (AMAX) {
-          const int32_t zi2 = xor_lane(zi, o);
-          argmax_merge(zm, zi, zm2, zi2);
-        } else {
-          zm = fmaxf(zm, zm2);
-        }
-      }
-      // lane (col, qd) finishes activation row m0 + 16 qd + col
-      if (cb == qd && m0 + cb * 16 + col < Mx) {
-        if constexpr (STATS) {
-          const float L = zm * a.invT + log2f(ss) * kLn2;   // group log-sum-exp of y = z / T
-          const float mn = fmaxf(rm, L);
-          rsum = rsum * fast_exp2((rm - mn) * kLog2e) + fast_exp2((L - mn) * kLog2e);
-          rm = mn;
-          const float sc = L + gu;
-          if (a.sample != 0 && sc > gbest) {   // groups rise: strict > keeps the lowest on ties
-            gbest = sc;
-            gid = g;
-          }
-        }
-        if constexpr (AMAX) argmax_merge(bz, bi, zm, zi);
-      }
+      bm[cb] = zm;
+      bs[cb] = ss;
+      bx[cb] = zi;
     }
+    // lane (col, qd) finishes activation row m0 + 16 qd + col: one fold per lane
+    float zm = bm[0], ss = bs[0];
+    int32_t zi = bx[0];
+#pragma unroll
+    for (int cb = 1; cb < NCBW; ++cb)
+      if (qd == cb) {
+        zm = bm[cb];
+        ss = bs[cb];
+        zi = bx[cb];
+      }
+    if (qd < NCBW && m0 + qd * 16 + col < Mx) {
+      if constexpr (STATS) {
+        const float L = zm * a.invT + log2f(ss) * kLn2;   // group log-sum-exp of y = z / T
+        const float mn = fmaxf(rm, L);
+        rsum = rsum * fast_exp2((rm - mn) * kLog2e) + fast_exp2((L - mn) * kLog2e);
+        rm = mn;
+        const float sc = L + gu;
+        if (a.sample != 0 && sc > gbest) {   // groups rise: strict > keeps the lowest on ties
+          gbest = sc;
+          gid = g;
+        }
+      }
+      if constexpr (AMAX) argmax_merge(bz, bi, zm, zi);
+    }
+  };
+  auto epi = [&](int g, float gu, const wf32x4_t (&acc)[4][NCBW]) {
+    if (g * kGroup + kGroup <= V32) epi_body(g, gu, acc, std::false_type{});   // uniform
+    else epi_body(g, gu, acc, std::true_type{});
   };
   wf32x4_t accA[4][NCBW];
 
