@@ -186,6 +186,8 @@ __global__ __launch_bounds__(kTkThreads) void k_topk_select(TopkArgs a) {
 // when more of them exist than are needed.
 constexpr int kTfThreads = 1024;
 constexpr int kTfWaves = kTfThreads / kWave;
+constexpr int kTfBatch = 8;   // words (candidates) each thread loads per round trip
+typedef uint32_t tf_u32x2_t __attribute__((ext_vector_type(2)));
 
 __global__ __launch_bounds__(kTfThreads) void k_topk_finish(TopkArgs a, int cand_cap) {
   extern __shared__ uint32_t fin[];  // sel[nw], tie[nw], hist[1024], cand[cand_cap] (uint2)
@@ -202,20 +204,56 @@ __global__ __launch_bounds__(kTfThreads) void k_topk_finish(TopkArgs a, int cand
   uint32_t* tie = fin + nw;
   uint32_t* h1 = fin + 2 * nw;
   uint2* cl = reinterpret_cast<uint2*>(fin + 2 * nw + 1024);
-  // loads that depend on nothing: the row histogram, the bitmask, the candidate count
+  // loads that depend on nothing, issued together: the row histogram, the candidate count and
+  // the bitmask (kTfBatch words per thread per round trip)
   const uint4 hq = reinterpret_cast<const uint4*>(a.hist + static_cast<size_t>(m) * kTkBins)[tid];
-  const uint32_t* mw32 = reinterpret_cast<const uint32_t*>(a.mask + static_cast<size_t>(m) * mw);
-  for (int i = tid; i < nw; i += kTfThreads) {
-    sel[i] = mw32[i];
-    tie[i] = 0u;
-  }
   uint32_t C = a.count[static_cast<size_t>(m) * kTkCounterStride];
+  {
+    const rsrc_t mr = make_rsrc(a.mask + static_cast<size_t>(m) * mw, static_cast<uint32_t>(nw) * 4u);
+    auto batch = [&](int i0) {
+      uint32_t v[kTfBatch];
+#pragma unroll
+      for (int q = 0; q < kTfBatch; ++q) {
+        const int i = i0 + q * kTfThreads + tid;
+        v[q] = buffer_load4(mr, i < nw ? static_cast<uint32_t>(i) * 4u : kOutOfRange);
+      }
+#pragma unroll
+      for (int q = 0; q < kTfBatch; ++q) {
+        const int i = i0 + q * kTfThreads + tid;
+        if (i < nw) {
+          sel[i] = v[q];
+          tie[i] = 0u;
+        }
+      }
+    };
+    batch(0);   // (the first batch outside the loop: its loads go out with the two above)
+    for (int i0 = kTfBatch * kTfThreads; i0 < nw; i0 += kTfBatch * kTfThreads) batch(i0);
+  }
   if (C > static_cast<uint64_t>(V)) C = static_cast<uint32_t>(V);
   const uint2* cg = a.cand + static_cast<size_t>(m) * V;
   const bool in_lds = C <= static_cast<uint32_t>(cand_cap);
-  if (in_lds)
-    for (uint32_t i = tid; i < C; i += kTfThreads) cl[i] = cg[i];
-  const uint2* cand = in_lds ? cl : cg;
+  if (in_lds) {
+    // the candidates, staged into LDS kTfBatch per thread per round trip
+    const rsrc_t cr = make_rsrc(cg, C * 8u);
+    auto batch = [&](uint32_t i0) {
+      tf_u32x2_t v[kTfBatch];
+#pragma unroll
+      for (int q = 0; q < kTfBatch; ++q) {
+        const uint32_t i = i0 + q * kTfThreads + tid;
+        v[q] = __builtin_amdgcn_raw_buffer_load_b64(cr, i < C ? i * 8u : kOutOfRange, 0, 0);
+      }
+#pragma unroll
+      for (int q = 0; q < kTfBatch; ++q) {
+        const uint32_t i = i0 + q * kTfThreads + tid;
+        if (i < C) cl[i] = make_uint2(v[q].x, v[q].y);
+      }
+    };
+    batch(0);
+    for (uint32_t i0 = kTfBatch * kTfThreads; i0 < C; i0 += kTfBatch * kTfThreads) batch(i0);
+  }
+  // a candidate from LDS, or from the global list when it did not fit (uniform branch: LDS
+  // reads stay LDS reads)
+  auto cand_at = [&](uint32_t i) -> uint2 { return in_lds ? cl[i] : cg[i]; };
   if (tid == 0) nties = 0u;
   {
     const uint32_t c[4] = {hq.x, hq.y, hq.z, hq.w};
@@ -230,7 +268,7 @@ __global__ __launch_bounds__(kTfThreads) void k_topk_finish(TopkArgs a, int cand
     h1[tid] = 0u;
     __syncthreads();
     for (uint32_t i = tid; i < C; i += kTfThreads) {
-      const uint32_t key = cand[i].x;
+      const uint32_t key = cand_at(i).x;
       if (pass == 0 || ((key >> 10) & 1023u) == ((thr >> 10) & 1023u)) atomicAdd(&h1[(key >> shift) & 1023u], 1u);
     }
     __syncthreads();
@@ -242,7 +280,7 @@ __global__ __launch_bounds__(kTfThreads) void k_topk_finish(TopkArgs a, int cand
   // keys above the threshold are in; keys equal to it are in if all are needed, else they
   // compete by id
   for (uint32_t i = tid; i < C; i += kTfThreads) {
-    const uint2 ce = cand[i];
+    const uint2 ce = cand_at(i);
     if (ce.y >= static_cast<uint64_t>(V)) continue;
     if (ce.x > thr) {
       atomicOr(&sel[ce.y >> 5], 1u << (ce.y & 31u));
@@ -421,6 +459,7 @@ hipError_t launch_gather_exact(const void* U, const void* h, const int32_t* idx,
 // ----------------------------------------------------------------------------------------
 constexpr int kGfThreads = 256;
 constexpr int kGfWaves = kGfThreads / kWave;
+constexpr int kGfBatch = 8;   // logits each thread loads per round trip
 
 __global__ __launch_bounds__(kGfThreads) void k_gather_finalize(const float* __restrict__ zbuf,
                                                                 const int32_t* __restrict__ idx, int k,
@@ -437,10 +476,26 @@ __global__ __launch_bounds__(kGfThreads) void k_gather_finalize(const float* __r
   const int ng = (k + kGroup - 1) / kGroup;
   float* Lg = zl + k;
   float mx = -INFINITY;
-  for (int j = threadIdx.x; j < k; j += blockDim.x) {
-    const float v = z[j];
-    zl[j] = v;
-    mx = fmaxf(mx, v);
+  {
+    // kGfBatch loads per thread issued together (one memory round trip per batch)
+    const rsrc_t zr = make_rsrc(z, static_cast<uint32_t>(k) * 4u);
+    for (int j0 = 0; j0 < k; j0 += kGfBatch * kGfThreads) {
+      uint32_t v[kGfBatch];
+#pragma unroll
+      for (int q = 0; q < kGfBatch; ++q) {
+        const int j = j0 + q * kGfThreads + static_cast<int>(threadIdx.x);
+        v[q] = buffer_load4(zr, j < k ? static_cast<uint32_t>(j) * 4u : kOutOfRange);
+      }
+#pragma unroll
+      for (int q = 0; q < kGfBatch; ++q) {
+        const int j = j0 + q * kGfThreads + static_cast<int>(threadIdx.x);
+        if (j < k) {
+          const float f = __uint_as_float(v[q]);
+          zl[j] = f;
+          mx = fmaxf(mx, f);
+        }
+      }
+    }
   }
   mx = wave_max(mx);
   if (l == 0) red_f[w] = mx;
