@@ -350,12 +350,12 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_head_tile(TileArgs a) {
 // ----------------------------------------------------------------------------------------
 // Finalize of one row from its producers' Partials: lse, greedy token, or the two-level draw
 // recomputing the winning group's logits.
-// `nthreads` threads of the workgroup take part; zs holds 64 floats, rec nthreads/64 Partials.
+// NT threads of the workgroup take part; zs holds 64 floats, rec NT/64 Partials.
 // ----------------------------------------------------------------------------------------
-template <bool BF16>
-__device__ __forceinline__ void finalize_row(const FinalizeArgs& f, int m, int nthreads, float* zs, Partial* rec) {
+template <bool BF16, int NT>
+__device__ __forceinline__ void finalize_row(const FinalizeArgs& f, int m, float* zs, Partial* rec) {
   const int l = lane_id(), w = wave_id();
-  const int nwaves = nthreads / kWave;
+  constexpr int nthreads = NT, nwaves = NT / kWave;
   Partial acc = partial_empty();
   const Partial* pp = f.partials + static_cast<int64_t>(m) * f.partials_ld;
   for (int p = threadIdx.x; p < f.P; p += nthreads) partial_merge(acc, pp[p]);
@@ -406,17 +406,22 @@ __device__ __forceinline__ void finalize_row(const FinalizeArgs& f, int m, int n
     // wave 0: the element Gumbel of row gbase + l, computed while the first loads are in flight
     float gel = 0.f;
     bool gel_done = w != 0;
-    for (int j0 = 0; j0 < rpw; j0 += 4) {
-      float z[4] = {0.f, 0.f, 0.f, 0.f};
-      for (int q0 = 0; q0 < CPL; q0 += 4) {
-        uint4 xv[4], wv[4][4];
+    // RB rows and QB chunks per lane of each row per batch: RB * QB + QB loads issued together
+    constexpr int RB = kGroup / (NT / kWave) < 16 ? kGroup / (NT / kWave) : 16;
+    constexpr int QB = 16 / RB > 1 ? 16 / RB : 1;
+    for (int j0 = 0; j0 < rpw; j0 += RB) {
+      float z[RB];
 #pragma unroll
-        for (int qq = 0; qq < 4; ++qq) {
+      for (int j = 0; j < RB; ++j) z[j] = 0.f;
+      for (int q0 = 0; q0 < CPL; q0 += QB) {
+        uint4 xv[QB], wv[QB][RB];
+#pragma unroll
+        for (int qq = 0; qq < QB; ++qq) {
           const int c = (q0 + qq) * kWave + l;
           const bool cok = q0 + qq < CPL && c < C;
           xv[qq] = buffer_load16(xrs, cok ? static_cast<uint32_t>(c) * 16 : kOutOfRange);
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
+          for (int j = 0; j < RB; ++j)
             wv[qq][j] = buffer_load16(wrs, cok ? static_cast<uint32_t>(j0 + j) * rowbytes + static_cast<uint32_t>(c) * 16
                                                : kOutOfRange);
         }
@@ -426,12 +431,12 @@ __device__ __forceinline__ void finalize_row(const FinalizeArgs& f, int m, int n
           gel_done = true;
         }
 #pragma unroll
-        for (int qq = 0; qq < 4; ++qq)
+        for (int qq = 0; qq < QB; ++qq)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) z[j] = chunk_dot<BF16>(wv[qq][j], xv[qq], z[j]);
+          for (int j = 0; j < RB; ++j) z[j] = chunk_dot<BF16>(wv[qq][j], xv[qq], z[j]);
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < RB; ++j) {
         const float s = wave_sum(z[j]);
         if (l == 0) zs[w * rpw + j0 + j] = s;
       }
@@ -458,13 +463,13 @@ __device__ __forceinline__ void finalize_row(const FinalizeArgs& f, int m, int n
   }
 }
 
-constexpr int kHfThreads = 1024;
+constexpr int kHfThreads = 256;
 
 template <bool BF16>
 __global__ __launch_bounds__(kHfThreads) void k_head_fin(FinalizeArgs f) {
   __shared__ Partial rec[kHfThreads / kWave];
   __shared__ float zs[kGroup];
-  finalize_row<BF16>(f, static_cast<int>(blockIdx.x), kHfThreads, zs, rec);
+  finalize_row<BF16, kHfThreads>(f, static_cast<int>(blockIdx.x), zs, rec);
 }
 
 // ----------------------------------------------------------------------------------------
