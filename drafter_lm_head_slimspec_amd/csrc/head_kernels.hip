@@ -53,6 +53,7 @@ __device__ __forceinline__ void stage16(uint4* lds, int items, F fetch) {
 constexpr int kRowdotRows = 8;
 constexpr int kRowdotM = 8;
 constexpr int kRowdotMaxCPL = 16;   // row bytes <= 16 KB
+constexpr int64_t kRowdotVecMaxM = 2;   // bf16 input rows that take the VALU kernel (measured: faster at 1-2, slower at 6)
 
 template <bool BF16>
 __global__ __launch_bounds__(256) void k_rowdot(const void* __restrict__ Wd,
@@ -1262,6 +1263,19 @@ size_t rowdot_scratch_bytes(int64_t M, int64_t R, int64_t K) {
 
 hipError_t launch_rowdot(const void* Wd, const void* x, int64_t R, int64_t K, int64_t M, bool bf16,
                          void* out, float* scratch, hipStream_t st, uint32_t* zero, int64_t zero_words) {
+  if (bf16 && M <= kRowdotVecMaxM && K * 2 <= kRowdotMaxCPL * kWave * 16) {
+    // one or two input rows: each wave dots two weight rows on the VALU, eight rows per
+    // workgroup (R / 8 workgroups instead of R / 16 MFMA tiles that each pull 16 rows)
+    const int C = static_cast<int>(K * 2 / 16);
+    const dim3 grid(static_cast<unsigned>((R + kRowdotRows - 1) / kRowdotRows), 1u);
+    const int lds = kRowdotM * C * 16;
+    TraceScope ts("rowdot", st);
+    hipError_t e = allow_lds(k_rowdot<true>, lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_rowdot<true>, grid, dim3(256), lds, st, Wd, x, static_cast<int>(R), C,
+                       static_cast<int>(M), out, zero, zero_words);
+    return hipGetLastError();
+  }
   if (bf16 && M <= kRdTileMaxM) {
     RowRanks rk;
     for (int m = 0; m < kRdTileMaxM; ++m) rk.r[m] = static_cast<int32_t>(R);
