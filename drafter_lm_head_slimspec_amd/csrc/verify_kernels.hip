@@ -126,6 +126,29 @@ __device__ __forceinline__ float chunk_max(const float* v) {
 // a naive version): greedy rows track only the largest chunk maximum and the chunk holding
 // it (the position inside that chunk is found once at the end); sampling rows keep only the
 // running log-sum-exp, in base-2 units.
+// Visit the k candidate ids of one draft position (sparse draft): f(j, id) for every entry,
+// the ids read kScanBatch per thread per round trip (one memory latency per batch rather than
+// one per id).
+constexpr int kScanBatch = 8;
+template <typename F>
+__device__ __forceinline__ void scan_candidates(const int32_t* ids, int64_t k, F&& f) {
+  const rsrc_t ri = make_rsrc(ids, static_cast<uint32_t>(k) * 4u);
+  const int64_t nt = blockDim.x;
+  for (int64_t j0 = 0; j0 < k; j0 += kScanBatch * nt) {
+    uint32_t v[kScanBatch];
+#pragma unroll
+    for (int q = 0; q < kScanBatch; ++q) {
+      const int64_t j = j0 + q * nt + threadIdx.x;
+      v[q] = buffer_load4(ri, j < k ? static_cast<uint32_t>(j) * 4u : kOutOfRange);
+    }
+#pragma unroll
+    for (int q = 0; q < kScanBatch; ++q) {
+      const int64_t j = j0 + q * nt + threadIdx.x;
+      if (j < k) f(j, static_cast<int32_t>(v[q]));
+    }
+  }
+}
+
 template <bool BF16, bool GREEDY>
 __global__ __launch_bounds__(256) void k_verify_rows(VerifyArgs a) {
   constexpr int EPT = BF16 ? 8 : 4;   // elements per 16-byte load
@@ -216,8 +239,9 @@ __global__ __launch_bounds__(256) void k_verify_rows(VerifyArgs a) {
     __syncthreads();
     const int32_t x = a.tokens[b * a.gamma + r];
     const int64_t base = (b * a.gamma + r) * a.k;
-    for (int64_t j = threadIdx.x; j < a.k; j += blockDim.x)
-      if (a.qidx[base + j] == x) sh_q = a.qprob[base + j];
+    scan_candidates(a.qidx + base, a.k, [&](int64_t j, int32_t id) {
+      if (id == x) sh_q = a.qprob[base + j];
+    });
     __syncthreads();
     qx = sh_q;
   }
@@ -559,10 +583,9 @@ __global__ __launch_bounds__(256) void k_verify_finish(VerifyArgs a) {
     if (best.g != 0x7fffffff) {
       const int64_t lo = static_cast<int64_t>(best.g) * kGroup;
       const int64_t base = (b * a.gamma + acc_len) * a.k;
-      for (int64_t j = threadIdx.x; j < a.k; j += blockDim.x) {
-        const int32_t id = a.qidx[base + j];
+      scan_candidates(a.qidx + base, a.k, [&](int64_t j, int32_t id) {
         if (id >= lo && id < lo + kGroup) qg[id - lo] = a.qprob[base + j];
-      }
+      });
     }
     __syncthreads();
   }
