@@ -121,6 +121,12 @@ def test_token_outside_candidates_is_accepted():
     assert acc[0] == 2 and np.all(acc[1:] == gamma)
 
 
+def test_many_candidates():
+    # k = 5000: the candidate scans take several batches, and the residual pass reads the
+    # candidate list from memory instead of holding it in registers
+    _sparse(4, 3, 8000, 5000, 1.0, "bf16", SEEDS)
+
+
 def test_sparse_full_shape():
     # the verification workload (B = 64, gamma = 5, V = 151936) with the SpecVocab k = 2048
     w = configs.VERIFY
