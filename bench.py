@@ -130,7 +130,7 @@ def main():
         traffic_summary(args.traffic_summary)
         return
     if args.gpus != 1:
-        log(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for {args.gpus}).")
+        log(f"bench.py runs on one GPU only: the library has no multi-GPU path (asked for {args.gpus}).")
         sys.exit(2)
     import torch
     from drafter_lm_head_slimspec_amd import configs, spechead as sh, synth

@@ -59,7 +59,7 @@ enum sh_status {
   SH_ERR_ALIGN = 4,       /* a pointer is not 16-byte (workspace: 256-byte) aligned    */
   SH_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required                  */
   SH_ERR_PARAM = 6,       /* temperature <= 0 or not finite, k outside [1, V], ...    */
-  SH_ERR_UNSUPPORTED = 7, /* valid request this build does not implement              */
+  SH_ERR_UNSUPPORTED = 7, /* valid request outside what the library implements        */
   SH_ERR_HIP = 8          /* a HIP call or kernel launch failed                       */
 };
 
