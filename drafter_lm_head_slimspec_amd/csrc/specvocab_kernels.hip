@@ -59,15 +59,25 @@ __global__ __launch_bounds__(kTkThreads) void k_topk_hist(TopkArgs a) {
   }
 }
 
+// Inclusive prefix sum over the lanes of a wave: shifts of 1, 2, 4 and 8 lanes within each
+// 16-lane row (DPP row_shr; a lane without a source adds 0), then the totals of the rows
+// below (lanes 15, 31, 47) from scalar reads.
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x111, 0xF, 0xF, false);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x112, 0xF, 0xF, false);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x114, 0xF, 0xF, false);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x118, 0xF, 0xF, false);   // row_shr:8
+  const uint32_t r0 = __builtin_amdgcn_readlane(x, 15);
+  const uint32_t r1 = __builtin_amdgcn_readlane(x, 31);
+  const uint32_t r2 = __builtin_amdgcn_readlane(x, 47);
+  const int row = lane_id() >> 4;
+  return x + (row >= 1 ? r0 : 0u) + (row >= 2 ? r1 : 0u) + (row >= 3 ? r2 : 0u);
+}
+
 // Exclusive prefix sum over the threads of the workgroup (thread order); also the total.
 __device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wsum, uint32_t* total) {
   const int l = lane_id(), w = wave_id(), nw = blockDim.x / kWave;
-  uint32_t x = v;
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const uint32_t y = __shfl_up(x, d);
-    if (l >= d) x += y;
-  }
+  const uint32_t x = wave_inclusive_scan(v);
   if (l == kWave - 1) wsum[w] = x;
   __syncthreads();
   uint32_t before = 0u, all = 0u;
