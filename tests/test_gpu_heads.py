@@ -228,3 +228,27 @@ def test_runs_are_bit_identical():
     torch.cuda.synchronize()
     for k in ("token", "lse", "logprob"):
         assert torch.equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("case", [
+    ("dense", 4096, 20000, 48),    # K-chunked pass with the side buffer
+    ("dense", 4096, 20000, 6),     # K-chunked pass, one column block
+    ("wide", 360, 30000, 192),     # wide pass (low-rank up-projection shape)
+], ids=lambda c: "%s-K%d-V%d-M%d" % c)
+def test_head_passes_are_bit_identical(case):
+    kind, K, V, M = case
+    if kind == "dense":
+        h = P.to_device(synth.hidden(M, K, "bf16", 5), "bf16")
+        W = P.to_device(synth.dense_weights(V, K, "bf16", 5), "bf16")
+        run = lambda: sh.draft_head_dense(h, W, mode="sample", seed=3, offset=2)
+    else:
+        d = 2880
+        h = P.to_device(synth.hidden(M, d, "bf16", 5), "bf16")
+        Wd, Wu = synth.lowrank_weights(V, d, K, "bf16", 5)
+        Wd, Wu = P.to_device(Wd, "bf16"), P.to_device(Wu, "bf16")
+        run = lambda: sh.draft_head_lowrank(h, Wd, Wu, mode="sample", temperature=0.7, seed=3, offset=2)
+    a = run()
+    b = run()
+    torch.cuda.synchronize()
+    for k in ("token", "lse", "logprob"):
+        assert torch.equal(a[k], b[k]), k
