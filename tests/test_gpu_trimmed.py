@@ -68,3 +68,30 @@ KCHUNK_CASES = [
 @pytest.mark.parametrize("case", KCHUNK_CASES, ids=lambda c: "d%d-V%d-n%d-M%d-%s" % c)
 def test_trimmed_kchunk(case, mode, T):
     _trimmed(*case, mode, T, want_logits=False)
+
+
+@pytest.mark.parametrize("mode", ["greedy", "sample"])
+def test_trimmed_kchunk_vocabulary_ends(mode):
+    # kept ids include the first and the last vocabulary entry; 1001 kept rows leave a last
+    # group of 41 rows
+    d, V, n, M, seed = 2048, 9000, 1001, 24, 23
+    rng = np.random.default_rng(seed)
+    ids = np.sort(np.concatenate([[0, V - 1], rng.choice(np.arange(1, V - 1), n - 2, replace=False)])).astype(np.int32)
+    h = synth.hidden(M, d, "bf16", seed)
+    W = synth.dense_weights(V, d, "bf16", seed)
+    # make the two end rows the best scores of every row, so that greedy picks them
+    W[[0, V - 1]] = synth.store(np.sign(synth.as_f32(h[:2], "bf16")) * np.float32(0.05), "bf16")
+    W_S = np.ascontiguousarray(W[ids])
+    out = sh.draft_head_trimmed(P.to_device(h, "bf16"), P.to_device(W_S, "bf16"), torch.from_numpy(ids).cuda(),
+                                mode=mode, seed=seed, offset=1)
+    torch.cuda.synchronize()
+    o = heads.head_trimmed(h, W_S, ids, "bf16", mode, 1.0, seed, 1)
+    tok = out["token"].cpu().numpy()
+    assert np.all(np.isin(tok, ids))
+    got = dict(out)
+    got["token"] = torch.from_numpy(np.searchsorted(ids, tok).astype(np.int32))
+    want = dict(o)
+    want["token"] = o["position"]
+    _check_outputs(got, want, "bf16", mode, 1.0, seed, 1, None, f"trimmed ends {mode}")
+    if mode == "greedy":
+        assert tok[0] == 0 and tok[1] == V - 1
