@@ -51,6 +51,9 @@ def parse():
                    help="only write the HBM traffic summary of the headline kernel from four rocprofv3 "
                         "--pmc counter_collection.csv files (head leg FETCH_SIZE, WRITE_SIZE; the "
                         "calibration copy's FETCH_SIZE, WRITE_SIZE)")
+    p.add_argument("--pmc-summary", nargs="+", metavar="CSV",
+                   help="only print, as a markdown table, the mean per dispatch of every counter in the given "
+                        "rocprofv3 --pmc counter_collection.csv files, per kernel")
     return p.parse_args()
 
 
@@ -124,10 +127,37 @@ def traffic_summary(paths):
     print(json.dumps({"hbm_bytes_per_launch": hbm, "traffic_over_alg": hbm / alg}))
 
 
+def pmc_summary(paths):
+    """Mean per dispatch of each counter, per kernel (name up to its argument list), over the
+    given rocprofv3 counter_collection.csv files; one markdown row per kernel."""
+    import csv
+    per = {}   # kernel -> counter -> {dispatch: value}
+    for path in paths:
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                kn = row["Kernel_Name"].split("(")[0][:80]
+                c = per.setdefault(kn, {}).setdefault(row["Counter_Name"], {})
+                key = (path, row["Dispatch_Id"])
+                c[key] = c.get(key, 0.0) + float(row["Counter_Value"])
+    counters = sorted({c for k in per.values() for c in k})
+    print("| kernel | dispatches | " + " | ".join(counters) + " |")
+    print("|---|---|" + "---|" * len(counters))
+    for kn in sorted(per):
+        n = max(len(v) for v in per[kn].values())
+        cells = []
+        for c in counters:
+            v = per[kn].get(c)
+            cells.append(f"{sum(v.values()) / len(v):.6g}" if v else "")
+        print(f"| `{kn}` | {n} | " + " | ".join(cells) + " |")
+
+
 def main():
     args = parse()
     if args.traffic_summary:
         traffic_summary(args.traffic_summary)
+        return
+    if args.pmc_summary:
+        pmc_summary(args.pmc_summary)
         return
     if args.gpus != 1:
         log(f"bench.py runs on one GPU only: the library has no multi-GPU path (asked for {args.gpus}).")
