@@ -1,6 +1,7 @@
 // C ABI of libspechead: argument validation (host only, before any HIP call), workspace
 // carving and the kernel sequence of each call.  Declarations and contracts: spechead.h.
 #include <cmath>
+#include <cstdint>
 #include <cstdarg>
 #include <cstdio>
 #include <string>
@@ -406,6 +407,12 @@ size_t sh_head_workspace_bytes(int op, int64_t M, int64_t d, int64_t r, int64_t 
   if (op != SH_OP_DENSE && op != SH_OP_LOWRANK && op != SH_OP_SPECVOCAB) return 0;
   // sized for f32 intermediates so one workspace serves both dtypes
   return head_layout(op, M, d, r, V, k, SH_F32).total;
+}
+
+size_t sh_head_intermediate_offset(int op, int64_t M, int64_t d, int64_t r, int64_t V, int64_t k) {
+  if (op != SH_OP_LOWRANK && op != SH_OP_SPECVOCAB) return SIZE_MAX;
+  if (sh_head_workspace_bytes(op, M, d, r, V, k) == 0) return SIZE_MAX;
+  return head_layout(op, M, d, r, V, k, SH_F32).hr_off;
 }
 
 size_t sh_verify_workspace_bytes(int mode, int64_t B, int64_t gamma, int64_t V) {

@@ -20,6 +20,8 @@
 // Loads use buffer descriptors whose byte range makes out-of-range lanes read zero, so no
 // load sits behind a branch; the streaming loops keep one batch of loads in flight while
 // the previous batch is consumed (ping-pong buffers, no register copies between them).
+#include <mutex>
+
 #include "device_common.h"
 #include "launch.h"
 #include "trace.h"
@@ -1215,14 +1217,21 @@ __global__ __launch_bounds__(kFinThreads) void k_head_finalize(FinalizeArgs f) {
 // host launchers
 // ----------------------------------------------------------------------------------------
 hipError_t device_info(DeviceInfo* out) {
+  // per-device attributes, filled once; the mutex makes concurrent first calls from several
+  // host threads safe (later calls read the filled entry under the same lock)
+  static std::mutex mu;
   static DeviceInfo cache[64];
   static bool have[64] = {false};
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  if (dev >= 0 && dev < 64 && have[dev]) {
-    *out = cache[dev];
-    return hipSuccess;
+  const bool cached = dev >= 0 && dev < 64;
+  if (cached) {
+    std::lock_guard<std::mutex> g(mu);
+    if (have[dev]) {
+      *out = cache[dev];
+      return hipSuccess;
+    }
   }
   DeviceInfo di;
   e = hipDeviceGetAttribute(&di.cus, hipDeviceAttributeMultiprocessorCount, dev);
@@ -1231,7 +1240,8 @@ hipError_t device_info(DeviceInfo* out) {
   e = hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
   if (e != hipSuccess) return e;
   di.max_lds = lds;
-  if (dev >= 0 && dev < 64) {
+  if (cached) {
+    std::lock_guard<std::mutex> g(mu);
     cache[dev] = di;
     have[dev] = true;
   }

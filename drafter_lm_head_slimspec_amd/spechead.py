@@ -31,6 +31,7 @@ _sz = ctypes.c_size_t
 
 _SIGS = {
     "sh_head_workspace_bytes": (_sz, [_i, _i64, _i64, _i64, _i64, _i64]),
+    "sh_head_intermediate_offset": (_sz, [_i, _i64, _i64, _i64, _i64, _i64]),
     "sh_verify_workspace_bytes": (_sz, [_i, _i64, _i64, _i64]),
     "sh_topk_workspace_bytes": (_sz, [_i64, _i64, _i64]),
     "draft_head_dense": (_i, [_vp, _i64, _i64, _vp, _i64, _i, _i, _f, _u64, _u64, _vp, _vp, _vp, _vp,
@@ -128,6 +129,14 @@ def workspace(nbytes, device, kind="head"):
     return buf
 
 
+def _intermediate(lib, op, ws, M, d, r, V, k, dtype):
+    """Copy of the rounded intermediate (h_r or h') a head call left in its workspace."""
+    off = lib.sh_head_intermediate_offset(op, M, d, r, V, k)
+    esz = 2 if dtype == torch.bfloat16 else 4
+    raw = ws[off:off + M * r * esz].clone()
+    return raw.view(dtype).view(M, r)
+
+
 def _contig(*ts):
     for t in ts:
         if t is not None and not t.is_contiguous():
@@ -154,7 +163,7 @@ def draft_head_dense(h, W, mode="greedy", temperature=1.0, seed=0, offset=0, wan
 
 
 def draft_head_lowrank(h, W_down, W_up, mode="greedy", temperature=1.0, seed=0, offset=0,
-                       want_logits=False, want_lse=True):
+                       want_logits=False, want_lse=True, want_intermediate=False):
     lib = load()
     _contig(h, W_down, W_up)
     M, d = h.shape
@@ -170,7 +179,10 @@ def draft_head_lowrank(h, W_down, W_up, mode="greedy", temperature=1.0, seed=0, 
     _check(lib.draft_head_lowrank(_p(h), M, d, _p(W_down), r, _p(W_up), V, _dt(h), _mode(mode),
                                   float(temperature), int(seed), int(offset), _p(token), _p(lse),
                                   _p(logprob), _p(logits), _p(ws), ws.numel(), _stream(dev)))
-    return {"token": token, "lse": lse, "logprob": logprob, "logits": logits}
+    out = {"token": token, "lse": lse, "logprob": logprob, "logits": logits}
+    if want_intermediate:
+        out["h_r"] = _intermediate(lib, OP_LOWRANK, ws, M, d, r, V, 0, h.dtype)
+    return out
 
 
 def draft_head_trimmed(h, W_S, ids, mode="greedy", temperature=1.0, seed=0, offset=0, want_logits=False):
@@ -195,7 +207,7 @@ def draft_head_trimmed(h, W_S, ids, mode="greedy", temperature=1.0, seed=0, offs
 
 
 def draft_head_lowrank_adaptive(h, W_down, W_up, ranks, mode="greedy", temperature=1.0, seed=0, offset=0,
-                                want_logits=False):
+                                want_logits=False, want_intermediate=False):
     """Position-adaptive rank: row m uses the first ranks[m] rows of W_down / columns of W_up
     (ranks: host integers, one per row)."""
     lib = load()
@@ -216,11 +228,14 @@ def draft_head_lowrank_adaptive(h, W_down, W_up, ranks, mode="greedy", temperatu
     _check(lib.draft_head_lowrank_adaptive(_p(h), M, d, _p(W_down), r, _p(W_up), V, rk.ctypes.data_as(_vp), _dt(h),
                                            _mode(mode), float(temperature), int(seed), int(offset), _p(token),
                                            _p(lse), _p(logprob), _p(logits), _p(ws), ws.numel(), _stream(dev)))
-    return {"token": token, "lse": lse, "logprob": logprob, "logits": logits}
+    out = {"token": token, "lse": lse, "logprob": logprob, "logits": logits}
+    if want_intermediate:
+        out["h_r"] = _intermediate(lib, OP_LOWRANK, ws, M, d, r, V, 0, h.dtype)
+    return out
 
 
 def draft_head_specvocab(h, W_down, W_vocab, U, k, mode="greedy", temperature=1.0, seed=0, offset=0,
-                         want_lse=True):
+                         want_lse=True, want_intermediate=False):
     lib = load()
     _contig(h, W_down, W_vocab, U)
     M, d = h.shape
@@ -239,8 +254,11 @@ def draft_head_specvocab(h, W_down, W_vocab, U, k, mode="greedy", temperature=1.
                                     _dt(h), _mode(mode), float(temperature), int(seed), int(offset),
                                     _p(idx), _p(zl), _p(q), _p(token), _p(lse), _p(logprob), _p(ws),
                                     ws.numel(), _stream(dev)))
-    return {"topk_idx": idx, "topk_logit": zl, "topk_prob": q, "token": token, "lse": lse,
-            "logprob": logprob}
+    out = {"topk_idx": idx, "topk_logit": zl, "topk_prob": q, "token": token, "lse": lse,
+           "logprob": logprob}
+    if want_intermediate:
+        out["h_prime"] = _intermediate(lib, OP_SPECVOCAB, ws, M, d, dprime, V, k, h.dtype)
+    return out
 
 
 def spec_verify(target, draft, tokens, u=None, mode="sample", temperature=1.0, seed=0, offset=0):

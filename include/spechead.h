@@ -31,6 +31,9 @@
  *   - No allocation: the caller passes a workspace of at least sh_*_workspace_bytes(...)
  *     bytes; its contents on entry do not matter (each call clears what it counts into).
  *     Calls that may overlap in time must use distinct workspaces.
+ *   - Threads: calls from several host threads are safe when their workspaces are distinct
+ *     (the per-device attribute cache is filled under a lock).  Tracing (sh_trace_*) is a
+ *     process-wide switch meant for one measuring thread.
  *   - Determinism: identical inputs, seed and offset give bit-identical outputs.
  *   - Sampling randomness: Philox4x64-10 (Salmon et al., SC'11) with key (seed, 0) and
  *     counter (index / 4, row, purpose, offset); the draw is output word index % 4 mapped to
@@ -72,6 +75,16 @@ enum sh_op { SH_OP_DENSE = 0, SH_OP_LOWRANK = 1, SH_OP_SPECVOCAB = 2 };
  * Pure host arithmetic, no HIP call.  Returns 0 for invalid arguments. */
 size_t sh_head_workspace_bytes(int op, int64_t M, int64_t d, int64_t r, int64_t V, int64_t k);
 
+/* Where a completed low-rank or SpecVocab head call leaves its rounded intermediate in the
+ * workspace: the byte offset of h_r = round(W_down h) [M, r] (SH_OP_LOWRANK; also the
+ * position-adaptive call, with r = r_max, rows zero past their rank) or h' [M, d'] (SH_OP_SPECVOCAB,
+ * r = d'), row-major in the call's dtype.  The value is the one the oracle of the SlimSpec
+ * write-up, section 三, rounds once to the storage dtype; callers may read it back after the
+ * call has completed on its stream (e.g. to check the up-projection on the exact h_r the
+ * kernels used).  Same arguments as sh_head_workspace_bytes; pure host arithmetic.  Returns
+ * SIZE_MAX for SH_OP_DENSE or invalid arguments. */
+size_t sh_head_intermediate_offset(int op, int64_t M, int64_t d, int64_t r, int64_t V, int64_t k);
+
 /* Workspace size for spec_verify.  Pure host arithmetic, no HIP call. */
 size_t sh_verify_workspace_bytes(int mode, int64_t B, int64_t gamma, int64_t V);
 
@@ -106,8 +119,10 @@ int draft_head_dense(const void* h, int64_t M, int64_t d, const void* W, int64_t
  * acceptance rate at the target's mass on the kept ids).  The dense head over n_S kept rows:
  *   W_S [n_S, d] device: the kept rows W[ids], gathered once by the caller
  *   ids [n_S] int32 device: their vocabulary ids
- *   token [M]: ids[j] for the chosen kept position j; lse / logprob over the kept rows;
- *   logits (nullable) [M, n_S] float, y = z / T in kept-row order.
+ *   token [M]: ids[j] for the chosen kept position j; lse / logprob (of y = z / T) over the
+ *   kept rows;
+ *   logits (nullable) [M, n_S] float: the raw scores z = W_S h in kept-row order (not divided
+ *   by T, as for draft_head_dense).
  *   Sampling groups are the 64-position groups of the kept-row order (Philox purposes 0/1,
  *   row m).  Shapes, dtypes and errors as draft_head_dense with V = n_S.
  *   Workspace: sh_head_workspace_bytes(SH_OP_DENSE, M, d, 0, n_S, 0).
@@ -196,27 +211,6 @@ int spec_verify(int mode, int64_t B, int64_t gamma, int64_t V, int dtype,
                 size_t workspace_bytes, void* stream);
 
 /*
- * Sampling verification against a sparse draft distribution: the bridge from the SpecVocab
- * head (SpecVocab write-up, 2.2.3: the draft's probabilities live on its k candidates; 3.3:
- * verification keeps the full vocabulary) to speculative sampling (explainer, "为什么答案
- * 不会变").  q_t is draft_prob on draft_idx and zero elsewhere; p_t = softmax(target_t / T).
- *   target_logits [B, gamma+1, V] dtype (device)
- *   draft_idx     [B, gamma, k] int32 (device): candidate ids of each position, distinct,
- *                 in [0, V) (the SpecVocab head's topk_idx)
- *   draft_prob    [B, gamma, k] float (device): q on those ids (its topk_prob)
- *   draft_tokens  [B, gamma] int32, u_accept [B, gamma] float in (0,1) (device)
- *   B <= 65535, 1 <= gamma <= 64, V <= 2^28, 1 <= k <= min(V, 16384), temperature > 0
- *   Accept t iff u_t < p_t(x_t) / q_t(x_t); a draft id with q_t(x_t) = 0 is accepted when
- *   p_t(x_t) > 0 (the ratio is infinite); an id outside [0, V) is never accepted.  If a < gamma
- *   the last token is drawn from norm(max(0, p_a - q_a)), which is p_a outside the candidates
- *   (purposes 3/4, row b), else from p_gamma (purposes 5/6, row b), by the same two-level
- *   Gumbel rule as spec_verify.
- *   accept_len [B] int32, out_tokens [B, gamma+1] int32 (-1 after the last emitted token).
- *   Returns SH_ERR_* before any launch on invalid arguments; the call is asynchronous on
- *   `stream`.  Workspace: sh_verify_sparse_workspace_bytes(B, gamma, V, k), 256-byte aligned,
- *   contents irrelevant.
- */
-/*
  * Greedy verification of a tree of candidate continuations (phrase-level speculation page,
  * section "更换单元：从 token 到短语": the candidates of a round share prefixes, form a prefix
  * tree scored in one target pass, and a candidate survives only where it equals the target's
@@ -241,6 +235,27 @@ int spec_verify_tree(int64_t B, int64_t N, int64_t V, int dtype, const void* tar
                      int32_t* accept_node, int32_t* out_tokens, void* workspace,
                      size_t workspace_bytes, void* stream);
 
+/*
+ * Sampling verification against a sparse draft distribution: the bridge from the SpecVocab
+ * head (SpecVocab write-up, 2.2.3: the draft's probabilities live on its k candidates; 3.3:
+ * verification keeps the full vocabulary) to speculative sampling (explainer, "为什么答案
+ * 不会变").  q_t is draft_prob on draft_idx and zero elsewhere; p_t = softmax(target_t / T).
+ *   target_logits [B, gamma+1, V] dtype (device)
+ *   draft_idx     [B, gamma, k] int32 (device): candidate ids of each position, distinct,
+ *                 in [0, V) (the SpecVocab head's topk_idx)
+ *   draft_prob    [B, gamma, k] float (device): q on those ids (its topk_prob)
+ *   draft_tokens  [B, gamma] int32, u_accept [B, gamma] float in (0,1) (device)
+ *   B <= 65535, 1 <= gamma <= 64, V <= 2^28, 1 <= k <= min(V, 16384), temperature > 0
+ *   Accept t iff u_t < p_t(x_t) / q_t(x_t); a draft id with q_t(x_t) = 0 is accepted when
+ *   p_t(x_t) > 0 (the ratio is infinite); an id outside [0, V) is never accepted.  If a < gamma
+ *   the last token is drawn from norm(max(0, p_a - q_a)), which is p_a outside the candidates
+ *   (purposes 3/4, row b), else from p_gamma (purposes 5/6, row b), by the same two-level
+ *   Gumbel rule as spec_verify.
+ *   accept_len [B] int32, out_tokens [B, gamma+1] int32 (-1 after the last emitted token).
+ *   Returns SH_ERR_* before any launch on invalid arguments; the call is asynchronous on
+ *   `stream`.  Workspace: sh_verify_sparse_workspace_bytes(B, gamma, V, k), 256-byte aligned,
+ *   contents irrelevant.
+ */
 int spec_verify_sparse(int64_t B, int64_t gamma, int64_t V, int64_t k, int dtype,
                        const void* target_logits, const int32_t* draft_idx, const float* draft_prob,
                        const int32_t* draft_tokens, const float* u_accept, float temperature,

@@ -16,6 +16,11 @@ from oracle import fp, philox, sampler
 RTOL = {"bf16": 1e-2, "f32": 1e-5}
 # decision tolerance for fp32 accumulation vs float64: 1e-5 * (1 + |score|)
 DEC_TOL = 1e-5
+# row log-sum-exp and log-probability against float64 on the same (exact) inputs: the GPU's
+# fp32 accumulation and fp32 exp / log / sums move them by a few 1e-6 at the head shapes, so
+# 1e-5 * (1 + |lse|) holds with margin while a dropped or doubled 64-row group (about
+# 64 / V in lse: 5e-4 at V = 128256, 1e-2 at V = 8200) does not pass
+LSE_RTOL = 1e-5
 
 
 def log(*a):
@@ -62,6 +67,60 @@ def rounding_flip_bound(pre_exact, terms_abs_sum, dtype, W_next_abs):
     if not amb.any():
         return np.zeros((pre_exact.shape[0], W_next_abs.shape[0]))
     return amb @ W_next_abs.T
+
+
+def check_lse_logprob(lse_gpu, lp_gpu, lse_o, y_tok, what):
+    """lse and logprob (y_tok - lse) of the GPU against the oracle's values on the same
+    inputs; y_tok is the oracle's y = z / T at the GPU's own token.  Returns the largest
+    error / tolerance ratios (lse, logprob)."""
+    lse_o = np.asarray(lse_o, np.float64)
+    tol = LSE_RTOL * (1 + np.abs(lse_o))
+    r1 = 0.0
+    if lse_gpu is not None:
+        e = np.abs(np.asarray(lse_gpu, np.float64) - lse_o)
+        bad = e > tol
+        assert not bad.any(), f"{what} lse: rows {np.flatnonzero(bad)[:5]} err {e[bad][:5]} tol {tol[bad][:5]}"
+        r1 = float(np.max(e / tol))
+    r2 = 0.0
+    if lp_gpu is not None:
+        want = np.asarray(y_tok, np.float64) - lse_o
+        tol2 = LSE_RTOL * (1 + np.abs(lse_o) + np.abs(y_tok))
+        e = np.abs(np.asarray(lp_gpu, np.float64) - want)
+        bad = e > tol2
+        assert not bad.any(), f"{what} logprob: rows {np.flatnonzero(bad)[:5]} err {e[bad][:5]} tol {tol2[bad][:5]}"
+        r2 = float(np.max(e / tol2))
+    log(f"  {what}: lse err/tol {r1:.3g}, logprob err/tol {r2:.3g}")
+    return r1, r2
+
+
+def check_intermediate(got, exact, terms_abs_sum, dtype, what, max_frac=0.01):
+    """The GPU's rounded intermediate (h_r or h') against the oracle's: float32 values from
+    fp32 accumulation rounded once to `dtype`.  bf16: each element is the oracle's rounding
+    of the exact product, or -- only where the exact value lies within the fp32 accumulation
+    error (2^-16 * sum |terms|) of a rounding midpoint -- a bf16 value within that error
+    band around it.  f32: within 2^-20 * sum |terms| of the exact value.  Returns the number of
+    flipped elements (bf16)."""
+    got = np.asarray(got, np.float64)
+    exact = np.asarray(exact, np.float64)
+    if dtype != "bf16":
+        e = np.abs(got - exact)
+        tol = 2.0 ** -20 * terms_abs_sum + 1e-30
+        assert np.all(e <= tol), f"{what}: max err/tol {np.max(e / tol)}"
+        return 0
+    want = fp.round_to_dtype(exact, "bf16")
+    diff = got != want
+    if not diff.any():
+        return 0
+    delta = 2.0 ** -16 * terms_abs_sum
+    lo = fp.round_to_dtype(exact - delta, "bf16")
+    hi = fp.round_to_dtype(exact + delta, "bf16")
+    ok = diff & (got >= lo) & (got <= hi) & (lo != hi)
+    bad = diff & ~ok
+    assert not bad.any(), f"{what}: {bad.sum()} elements off the oracle's rounding, first {np.argwhere(bad)[0]}"
+    n = int(diff.sum())
+    log(f"  {what}: {n} of {got.size} elements rounded the other way at a midpoint")
+    assert n <= max(2, max_frac * got.size), n
+    return n
 
 
 class Excusals:

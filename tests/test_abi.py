@@ -51,6 +51,18 @@ def test_workspace_sizes(lib):
     assert lib.sh_verify_workspace_bytes(7, 64, 5, 151936) == 0
 
 
+def test_intermediate_offset(lib):
+    SIZE_MAX = (1 << 64) - 1
+    for op, r, k in ((sh.OP_LOWRANK, 512, 0), (sh.OP_SPECVOCAB, 256, 2048)):
+        M, d, V = 48, 4096, 128256
+        off = lib.sh_head_intermediate_offset(op, M, d, r, V, k)
+        total = lib.sh_head_workspace_bytes(op, M, d, r, V, k)
+        # the intermediate (f32-sized slot, so it fits either dtype) lies inside the workspace
+        assert off % 256 == 0 and off + M * r * 4 <= total
+    assert lib.sh_head_intermediate_offset(sh.OP_DENSE, 48, 4096, 0, 128256, 0) == SIZE_MAX
+    assert lib.sh_head_intermediate_offset(sh.OP_LOWRANK, 0, 4096, 512, 128256, 0) == SIZE_MAX
+
+
 # fake, 256-byte aligned device addresses; never dereferenced
 A = ctypes.c_void_p(0x7f0000100000)
 B = ctypes.c_void_p(0x7f0000200000)

@@ -7,7 +7,7 @@ import torch
 from drafter_lm_head_slimspec_amd import spechead as sh, synth
 from oracle import fp, heads
 from tests import parity as P
-from tests.test_gpu_heads import _check_outputs
+from tests.test_gpu_heads import _check_outputs, _hr_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -26,13 +26,18 @@ def _adaptive(d, V, r, ranks, mode, T, seed=13, offset=2, want_logits=False):
     Wd, Wu = synth.lowrank_weights(V, d, r, "bf16", seed)
     out = sh.draft_head_lowrank_adaptive(P.to_device(h, "bf16"), P.to_device(Wd, "bf16"), P.to_device(Wu, "bf16"),
                                          ranks, mode=mode, temperature=T, seed=seed, offset=offset,
-                                         want_logits=want_logits)
+                                         want_logits=want_logits, want_intermediate=True)
     torch.cuda.synchronize()
-    o = heads.head_lowrank_adaptive(h, Wd, Wu, ranks, "bf16", mode, T, seed, offset)
+    # the GPU's h_r: row m holds round(W_down[:r_m] h_m) and zeros past r_m
+    o_ref = heads.head_lowrank_adaptive(h, Wd, Wu, ranks, "bf16", mode, T, seed, offset)
     mask = np.arange(r)[None, :] < np.array(ranks)[:, None]
     terms = np.where(mask, np.abs(fp.decode(h, "bf16")) @ np.abs(fp.decode(Wd, "bf16")).T, 0.0)
-    bound = P.rounding_flip_bound(o["h_r_exact"], terms, "bf16", np.abs(fp.decode(Wu, "bf16")))
-    _check_outputs(out, o, "bf16", mode, T, seed, offset, bound, f"adaptive M={M}")
+    hr = _hr_bits(out["h_r"], "bf16")
+    P.check_intermediate(fp.decode(hr, "bf16"), o_ref["h_r_exact"], terms, "bf16", f"adaptive M={M} h_r")
+    assert np.all(hr[~mask] == 0), "h_r is zero past each row's rank"
+    # up-projection and selection: the oracle's nested-prefix head on the GPU's h_r
+    o = heads.head_dense(hr, Wu, "bf16", mode, T, seed, offset)
+    _check_outputs(out, o, "bf16", mode, T, seed, offset, f"adaptive M={M}")
     return out, o
 
 

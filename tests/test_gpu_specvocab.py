@@ -4,7 +4,7 @@ import pytest
 import torch
 
 from drafter_lm_head_slimspec_amd import configs, spechead as sh, synth
-from oracle import fp, heads, philox
+from oracle import fp, heads, philox, sampler
 from tests import parity as P
 
 pytestmark = pytest.mark.gpu
@@ -33,52 +33,72 @@ def test_topk_on_given_scores_is_exact(V, k):
 
 
 def _specvocab(d, V, dprime, k, M, dtype, mode, T, seed, offset=2):
+    """Each stage against the oracle on the inputs the GPU stage actually used: h' against the
+    oracle's single rounding; the candidate set against the oracle's top-k of W_vocab h'_gpu
+    (swaps only at a near-tie with the k-th score); the exact logits, softmax, lse, logprob and
+    token against the oracle's arithmetic on the GPU's own candidate set."""
     P.log(f"specvocab d={d} V={V} d'={dprime} k={k} M={M} {dtype} {mode}")
     h = synth.hidden(M, d, dtype, seed)
     Wd, Wv, U = synth.specvocab_weights(V, d, dprime, dtype, seed)
     out = sh.draft_head_specvocab(P.to_device(h, dtype), P.to_device(Wd, dtype), P.to_device(Wv, dtype),
-                                  P.to_device(U, dtype), k, mode=mode, temperature=T, seed=seed, offset=offset)
+                                  P.to_device(U, dtype), k, mode=mode, temperature=T, seed=seed, offset=offset,
+                                  want_intermediate=True)
     torch.cuda.synchronize()
-    o = heads.head_specvocab(h, Wd, Wv, U, k, dtype, mode, T, seed, offset)
     idx = out["topk_idx"].cpu().numpy()
     zl = out["topk_logit"].cpu().numpy()
     q = out["topk_prob"].cpu().numpy()
     tok = out["token"].cpu().numpy()
-    terms = np.abs(fp.decode(h, dtype)) @ np.abs(fp.decode(Wd, dtype)).T
-    bound = P.rounding_flip_bound(o["h_prime_exact"], terms, dtype, np.abs(fp.decode(Wv, dtype)))
+    lse = out["lse"].cpu().numpy()
+    lp = out["logprob"].cpu().numpy()
+    hd = fp.decode(h, dtype)
+    pre = hd @ fp.decode(Wd, dtype).T
+    terms = np.abs(hd) @ np.abs(fp.decode(Wd, dtype)).T
+    hp = fp.decode(_bits(out["h_prime"], dtype), dtype)
+    P.check_intermediate(hp, pre, terms, dtype, f"specvocab M={M} h'")
+    scores = hp @ fp.decode(Wv, dtype).T
+    Ud = fp.decode(U, dtype)
     ex = P.Excusals(f"specvocab M={M} top-k boundary")
-    Ud = None
+    ext = P.Excusals(f"specvocab M={M} tokens")
+    lse_o, ytok = np.zeros(M), np.zeros(M)
     for m in range(M):
-        s = o["scores"][m]
+        s = scores[m]
         assert np.all(np.diff(idx[m]) > 0), "top-k ids must be strictly ascending"
-        gs, os_ = set(idx[m].tolist()), set(o["topk_idx"][m].tolist())
-        same = gs == os_
-        if not same:
+        K_o = heads.topk_ascending(s, k)
+        gs, os_ = set(idx[m].tolist()), set(K_o.tolist())
+        if gs != os_:
             kth = np.sort(s)[::-1][k - 1]
             for i in gs ^ os_:
-                tol = P.DEC_TOL * (1 + abs(kth)) + 2 * np.max(bound[m]) + 1e-6 * (1 + abs(kth))
+                tol = P.DEC_TOL * (1 + abs(kth))
                 assert abs(s[i] - kth) <= tol, f"row {m}: id {i} score {s[i]} vs k-th {kth}"
             ex.add(("boundary", m, len(gs ^ os_) // 2))
-        # exact logits of the GPU's candidates from the oracle's exact arithmetic
-        if Ud is None:
-            Ud = fp.decode(U, dtype)
-        zo = Ud[idx[m]] @ fp.decode(h, dtype)[m]
+        # exact logits of the GPU's candidates (full-precision h), then softmax and the draw
+        zo = Ud[idx[m]] @ hd[m]
         P.assert_logits_close(zl[m][None], zo[None], dtype, f"row {m} exact logits")
-        np.testing.assert_allclose(q[m].sum(), 1.0, rtol=1e-4)
-        if not same:
-            continue
-        np.testing.assert_allclose(q[m], o["topk_prob"][m], rtol=P.RTOL[dtype], atol=1e-7)
+        y = zo / T
+        lse_o[m] = sampler.logsumexp(y)
+        qo = np.exp(y - lse_o[m])
+        tolq = P.LSE_RTOL * (1 + abs(lse_o[m]) + np.abs(y)) * qo + 1e-9
+        assert np.all(np.abs(q[m] - qo) <= tolq), f"row {m}: softmax off by {np.max(np.abs(q[m] - qo) / tolq)} tol"
+        jg = int(np.searchsorted(idx[m], tok[m]))
+        assert jg < k and idx[m][jg] == tok[m], "the token is one of the candidates"
+        ytok[m] = y[jg]
         if mode == "greedy":
-            P.check_greedy_tokens(np.searchsorted(idx[m], tok[m:m + 1]), o["topk_logit"][m][None], ex)
+            P.check_greedy_tokens(np.array([jg]), zo[None], ext)
         else:
-            y = o["topk_logit"][m] / T
-            jg = int(np.searchsorted(idx[m], tok[m]))
-            assert idx[m][jg] == tok[m]
-            P.check_sampled_token(jg, int(o["diag"][m]["position"]), y,
-                                  lambda g, m=m: philox.uniforms(seed, offset, 0, m, g),
-                                  lambda i, m=m: philox.uniforms(seed, offset, 1, m, i),
-                                  o["diag"][m], lambda i, j: 0.0, ex, f"row{m}")
+            jo, dg = sampler.two_level_sample(y, lambda g, m=m: philox.uniforms(seed, offset, 0, m, g),
+                                              lambda i, m=m: philox.uniforms(seed, offset, 1, m, i))
+            P.check_sampled_token(jg, int(jo), y, lambda g, m=m: philox.uniforms(seed, offset, 0, m, g),
+                                  lambda i, m=m: philox.uniforms(seed, offset, 1, m, i), dg,
+                                  lambda i, j: 0.0, ext, f"row{m}")
     ex.report(M, max_frac=0.1)
+    ext.report(M)
+    P.check_lse_logprob(lse, lp, lse_o, ytok, f"specvocab M={M}")
+
+
+def _bits(t, dtype):
+    if dtype == "bf16":
+        return t.cpu().view(torch.int16).numpy().view(np.uint16)
+    return t.cpu().numpy()
 
 
 @pytest.mark.parametrize("mode", ["greedy", "sample"])

@@ -37,7 +37,7 @@ def _trimmed(d, V, n, M, dtype, mode, T, seed=17, offset=4, want_logits=True):
     got["token"] = torch.from_numpy(pos.astype(np.int32))
     want = dict(o)
     want["token"] = o["position"]
-    _check_outputs(got, want, dtype, mode, T, seed, offset, None, f"trimmed M={M}")
+    _check_outputs(got, want, dtype, mode, T, seed, offset, f"trimmed M={M}")
 
 
 CASES = [
@@ -50,9 +50,10 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("mode,T", [("greedy", 1.0), ("sample", 1.0)])
+@pytest.mark.parametrize("mode,T", [("greedy", 1.0), ("sample", 1.0), ("sample", 0.6), ("greedy", 0.6)])
 @pytest.mark.parametrize("case", CASES, ids=lambda c: "d%d-V%d-n%d-M%d-%s" % c)
 def test_trimmed(case, mode, T):
+    # raw logits z (not z / T) are compared at every temperature
     _trimmed(*case, mode, T)
 
 
@@ -92,6 +93,6 @@ def test_trimmed_kchunk_vocabulary_ends(mode):
     got["token"] = torch.from_numpy(np.searchsorted(ids, tok).astype(np.int32))
     want = dict(o)
     want["token"] = o["position"]
-    _check_outputs(got, want, "bf16", mode, 1.0, seed, 1, None, f"trimmed ends {mode}")
+    _check_outputs(got, want, "bf16", mode, 1.0, seed, 1, f"trimmed ends {mode}")
     if mode == "greedy":
         assert tok[0] == 0 and tok[1] == V - 1
