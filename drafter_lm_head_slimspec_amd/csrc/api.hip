@@ -4,6 +4,7 @@
 #include <cstdint>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 #include <utility>
 
@@ -11,8 +12,13 @@
 #include "device_common.h"
 #include "launch.h"
 
+// Scratch of draft_head_lowrank_noalloc: one array per GPU, held until the process ends.
+constexpr size_t kNoallocScratchBytes = size_t{8} << 20;
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
 namespace {
 
+constexpr int kMaxDevices = 64;
 thread_local std::string g_last_error;
 
 int fail(int code, const char* fmt, ...) {
@@ -378,6 +384,54 @@ int check_common_head(const void* h, int64_t M, int64_t d, int64_t V, int dtype,
   return SH_OK;
 }
 
+int check_lowrank_args(const void* h, int64_t M, int64_t d, const void* W_down, int64_t r, const void* W_up,
+                       int64_t V, int dtype, int mode, float temperature, int32_t* token, float* lse,
+                       float* logprob, float* logits) {
+  SH_TRY(check_common_head(h, M, d, V, dtype, mode, temperature, token, lse, logprob));
+  SH_TRY(check_ptr(W_down, "W_down"));
+  SH_TRY(check_ptr(W_up, "W_up"));
+  SH_TRY(check_rowlen("r", r, dtype));
+  if (r * static_cast<int64_t>(esize(dtype)) > kMaxRowBytes)
+    return fail(SH_ERR_UNSUPPORTED, "r * element size above %lld bytes", static_cast<long long>(kMaxRowBytes));
+  SH_TRY(check_opt_out(logits, "logits"));
+  return SH_OK;
+}
+
+// The low-rank call on a validated scratch area laid out as L (a caller workspace or the
+// static scratch below): h_r = round(W_down h), then the head over W_up.
+int run_lowrank(const void* h, int64_t M, int64_t d, const void* W_down, int64_t r, const void* W_up, int64_t V,
+                int dtype, int mode, float temperature, uint64_t seed, uint64_t offset, int32_t* token, float* lse,
+                float* logprob, float* logits, char* ws, const HeadLayout& L, hipStream_t st) {
+  void* hr = ws + L.hr_off;
+  auto* parts = reinterpret_cast<sh::Partial*>(ws + L.part_off);
+  auto* lg = reinterpret_cast<float*>(ws + L.lg_off);
+  SH_HIP(sh::launch_rowdot(W_down, h, r, d, M, dtype == SH_BF16, hr, reinterpret_cast<float*>(ws + L.rd_off), st),
+         "down-projection kernels");
+  return run_head(hr, M, r, W_up, V, dtype, mode, temperature, seed, offset, token, lse, logprob,
+                  logits, parts, lg, st);
+}
+
+// Device address of the static scratch on the current device, looked up once per device
+// with that device current.  In host code the array's name stands for a host-side shadow,
+// never the device memory: kernels only ever receive the looked-up address.
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[kMaxDevices] = {};
+
+int noalloc_scratch(char** out) {
+  int dev = 0;
+  SH_HIP(hipGetDevice(&dev), "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(SH_ERR_UNSUPPORTED, "device index %d above %d", dev, kMaxDevices - 1);
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    SH_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+    if (p == nullptr) return fail(SH_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = static_cast<char*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return SH_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -478,24 +532,27 @@ int draft_head_lowrank(const void* h, int64_t M, int64_t d, const void* W_down, 
                        uint64_t seed, uint64_t offset, int32_t* token, float* lse, float* logprob,
                        float* logits, void* workspace, size_t workspace_bytes, void* stream) {
   g_last_error.clear();
-  SH_TRY(check_common_head(h, M, d, V, dtype, mode, temperature, token, lse, logprob));
-  SH_TRY(check_ptr(W_down, "W_down"));
-  SH_TRY(check_ptr(W_up, "W_up"));
-  SH_TRY(check_rowlen("r", r, dtype));
-  if (r * static_cast<int64_t>(esize(dtype)) > kMaxRowBytes)
-    return fail(SH_ERR_UNSUPPORTED, "r * element size above %lld bytes", static_cast<long long>(kMaxRowBytes));
-  SH_TRY(check_opt_out(logits, "logits"));
+  SH_TRY(check_lowrank_args(h, M, d, W_down, r, W_up, V, dtype, mode, temperature, token, lse, logprob, logits));
   const HeadLayout L = head_layout(SH_OP_LOWRANK, M, d, r, V, 0, SH_F32);
   SH_TRY(check_workspace(workspace, workspace_bytes, L.total));
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  char* ws = static_cast<char*>(workspace);
-  void* hr = ws + L.hr_off;
-  auto* parts = reinterpret_cast<sh::Partial*>(ws + L.part_off);
-  auto* lg = reinterpret_cast<float*>(ws + L.lg_off);
-  SH_HIP(sh::launch_rowdot(W_down, h, r, d, M, dtype == SH_BF16, hr, reinterpret_cast<float*>(ws + L.rd_off), st),
-         "down-projection kernels");
-  return run_head(hr, M, r, W_up, V, dtype, mode, temperature, seed, offset, token, lse, logprob,
-                  logits, parts, lg, st);
+  return run_lowrank(h, M, d, W_down, r, W_up, V, dtype, mode, temperature, seed, offset, token, lse, logprob,
+                     logits, static_cast<char*>(workspace), L, static_cast<hipStream_t>(stream));
+}
+
+int draft_head_lowrank_noalloc(const void* h, int64_t M, int64_t d, const void* W_down, int64_t r,
+                               const void* W_up, int64_t V, int dtype, int mode, float temperature,
+                               uint64_t seed, uint64_t offset, int32_t* token, float* lse, float* logprob,
+                               float* logits, void* stream) {
+  g_last_error.clear();
+  SH_TRY(check_lowrank_args(h, M, d, W_down, r, W_up, V, dtype, mode, temperature, token, lse, logprob, logits));
+  const HeadLayout L = head_layout(SH_OP_LOWRANK, M, d, r, V, 0, SH_F32);
+  if (L.total > kNoallocScratchBytes)
+    return fail(SH_ERR_UNSUPPORTED, "the call needs %zu bytes of scratch, above the %zu-byte static scratch", L.total,
+                kNoallocScratchBytes);
+  char* ws = nullptr;
+  SH_TRY(noalloc_scratch(&ws));
+  return run_lowrank(h, M, d, W_down, r, W_up, V, dtype, mode, temperature, seed, offset, token, lse, logprob,
+                     logits, ws, L, static_cast<hipStream_t>(stream));
 }
 
 int draft_head_lowrank_adaptive(const void* h, int64_t M, int64_t d, const void* W_down, int64_t r_max,

@@ -38,6 +38,8 @@ _SIGS = {
                               _vp, _sz, _vp]),
     "draft_head_lowrank": (_i, [_vp, _i64, _i64, _vp, _i64, _vp, _i64, _i, _i, _f, _u64, _u64, _vp,
                                 _vp, _vp, _vp, _vp, _sz, _vp]),
+    "draft_head_lowrank_noalloc": (_i, [_vp, _i64, _i64, _vp, _i64, _vp, _i64, _i, _i, _f, _u64, _u64, _vp,
+                                        _vp, _vp, _vp, _vp]),
     "draft_head_trimmed": (_i, [_vp, _i64, _i64, _vp, _i64, _vp, _i, _i, _f, _u64, _u64, _vp, _vp, _vp, _vp, _vp,
                                 _sz, _vp]),
     "draft_head_lowrank_adaptive": (_i, [_vp, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i, _i, _f, _u64, _u64,
@@ -183,6 +185,22 @@ def draft_head_lowrank(h, W_down, W_up, mode="greedy", temperature=1.0, seed=0, 
     if want_intermediate:
         out["h_r"] = _intermediate(lib, OP_LOWRANK, ws, M, d, r, V, 0, h.dtype)
     return out
+
+
+def draft_head_lowrank_noalloc(h, W_down, W_up, token, lse=None, logprob=None, logits=None, mode="greedy",
+                               temperature=1.0, seed=0, offset=0):
+    """draft_head_lowrank on the library's static scratch: no workspace, and this wrapper
+    allocates nothing either -- the caller passes the output tensors (token [M] int32; lse,
+    logprob [M] and logits [M, V] float32 or None)."""
+    lib = load()
+    _contig(h, W_down, W_up, token, lse, logprob, logits)
+    M, d = h.shape
+    r = W_down.shape[0]
+    V = W_up.shape[0]
+    dev = h.device
+    _check(lib.draft_head_lowrank_noalloc(_p(h), M, d, _p(W_down), r, _p(W_up), V, _dt(h), _mode(mode),
+                                          float(temperature), int(seed), int(offset), _p(token), _p(lse),
+                                          _p(logprob), _p(logits), _stream(dev)))
 
 
 def draft_head_trimmed(h, W_S, ids, mode="greedy", temperature=1.0, seed=0, offset=0, want_logits=False):

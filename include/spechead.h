@@ -146,6 +146,24 @@ int draft_head_lowrank(const void* h, int64_t M, int64_t d, const void* W_down, 
                        void* stream);
 
 /*
+ * draft_head_lowrank without a workspace argument, for callers that cannot allocate device
+ * memory or do not own a workspace: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  Same arguments (minus workspace / workspace_bytes),
+ * kernels, outputs and error codes as draft_head_lowrank; the scratch is a static device
+ * array of 8 MiB (one per GPU the library runs on, held until the process ends), so calls
+ * whose sh_head_workspace_bytes(SH_OP_LOWRANK, M, d, r, V, 0) exceeds 8 MiB return
+ * SH_ERR_UNSUPPORTED before any HIP call (M <= 64 rows at r = 512 fits up to V = 2^19).  The
+ * call allocates nothing.  Every call on one GPU shares that GPU's array: calls that may
+ * overlap in time on one GPU (different streams, or different host threads) race and must
+ * be serialised by the caller.  The first call on a device looks up the array's device
+ * address (a HIP symbol query, no allocation).
+ */
+int draft_head_lowrank_noalloc(const void* h, int64_t M, int64_t d, const void* W_down, int64_t r,
+                               const void* W_up, int64_t V, int dtype, int mode, float temperature,
+                               uint64_t seed, uint64_t offset, int32_t* token, float* lse,
+                               float* logprob, float* logits, void* stream);
+
+/*
  * Position-adaptive rank (SlimSpec write-up, section 七, second future direction: earlier
  * draft positions get a larger rank, later ones a smaller one).  One factor pair of rank
  * r_max serves every row through nested prefixes: row m uses the first ranks[m] rows of
