@@ -152,7 +152,12 @@ HeadLayout head_layout(int op, int64_t M, int64_t d, int64_t r, int64_t V, int64
   L.lg_bytes = (op == SH_OP_SPECVOCAB) ? 0 : align_up(static_cast<size_t>(M) * static_cast<size_t>(lg_stride(V)) * 4, 256);
   off += L.lg_bytes;
   L.gz_off = off;
-  L.gz_bytes = (op == SH_OP_DENSE) ? align_up(sh::head_kchunk_side_bytes(M, d, V), 256) : 0;
+  // best-group logits: the dense head's K-chunked pass, or the low-rank head's tile pass with at
+  // most kTileSideMaxRows rows (one slot per workgroup of at most kTileMaxGrid)
+  L.gz_bytes = (op == SH_OP_DENSE) ? align_up(sh::head_kchunk_side_bytes(M, d, V), 256)
+               : (op == SH_OP_LOWRANK && M <= sh::kTileSideMaxRows)
+                   ? align_up(static_cast<size_t>(M) * sh::kTileMaxGrid * sh::kGroup * sizeof(float), 256)
+                   : 0;
   off += L.gz_bytes;
   L.score_off = off;
   L.score_bytes = (op == SH_OP_SPECVOCAB) ? align_up(static_cast<size_t>(M * V) * 4, 256) : 0;
@@ -242,6 +247,13 @@ int run_head(const void* x, int64_t M, int64_t K, const void* W, int64_t V, int 
     a.zout_ld = V;
     a.partials = partials;
     a.partials_ld = sh::kMaxPartials;
+    // sampling without raw logits: the pass keeps each workgroup's best-group logits per row
+    const bool side = gz != nullptr && mode == SH_SAMPLE && logits == nullptr && M <= sh::kTileSideMaxRows &&
+                      grid <= sh::kTileMaxGrid;
+    if (side) {
+      a.gz = gz;
+      a.gz_ld = sh::kTileMaxGrid;
+    }
     SH_HIP(sh::launch_head_tile(a, grid, st), "head tile kernel");
     sh::FinalizeArgs f{};
     f.partials = partials;
@@ -262,6 +274,11 @@ int run_head(const void* x, int64_t M, int64_t K, const void* W, int64_t V, int 
     f.lse = lse;
     f.logprob = logprob;
     f.id_map = id_map;
+    if (side) {
+      f.gz = gz;
+      f.gz_ld = sh::kTileMaxGrid;
+      f.gz_map = 1;
+    }
     SH_HIP(sh::launch_head_fin(f, st), "head finalize kernel");
     return SH_OK;
   }
@@ -407,8 +424,9 @@ int run_lowrank(const void* h, int64_t M, int64_t d, const void* W_down, int64_t
   auto* lg = reinterpret_cast<float*>(ws + L.lg_off);
   SH_HIP(sh::launch_rowdot(W_down, h, r, d, M, dtype == SH_BF16, hr, reinterpret_cast<float*>(ws + L.rd_off), st),
          "down-projection kernels");
+  auto* gz = L.gz_bytes ? reinterpret_cast<float*>(ws + L.gz_off) : nullptr;
   return run_head(hr, M, r, W_up, V, dtype, mode, temperature, seed, offset, token, lse, logprob,
-                  logits, parts, lg, st);
+                  logits, parts, lg, st, 0, nullptr, gz);
 }
 
 // Device address of the static scratch on the current device, looked up once per device
@@ -587,9 +605,10 @@ int draft_head_lowrank_adaptive(const void* h, int64_t M, int64_t d, const void*
   void* hr = ws + L.hr_off;
   auto* parts = reinterpret_cast<sh::Partial*>(ws + L.part_off);
   auto* lg = reinterpret_cast<float*>(ws + L.lg_off);
+  auto* gz = L.gz_bytes ? reinterpret_cast<float*>(ws + L.gz_off) : nullptr;
   SH_HIP(sh::launch_rowdot_ranked(W_down, h, r_max, d, M, ranks, hr, st), "down-projection kernel");
   return run_head(hr, M, K, W_up, V, dtype, mode, temperature, seed, offset, token, lse, logprob, logits, parts,
-                  lg, st, r_max);
+                  lg, st, r_max, nullptr, gz);
 }
 
 int draft_head_specvocab(const void* h, int64_t M, int64_t d, const void* W_down, int64_t dprime,

@@ -14,7 +14,8 @@
 //                   the running lse, the best group score L_g + Gumbel(u_g) (sampling) and the
 //                   argmax of activation row 16 qd + col.
 //   k_head_fin      per row: merges the workgroups' Partials into lse, argmax and the winning
-//                   group; sampling recomputes that group's 64 logits and draws the element.
+//                   group; sampling reads that group's 64 logits from the side buffer its owner
+//                   wrote (at most 48 rows), or recomputes them, and draws the element.
 //
 // The sampler is the two-level Gumbel-max over groups of 64 consecutive candidates; the group
 // draws use Philox purpose 0 (draft group), the element draw purpose 1 (draft element).
@@ -34,8 +35,14 @@ constexpr int kTileThreads = 256;   // four waves
 constexpr int kTileWaves = kTileThreads / kWave;
 // EPI bits: kEpiStats (row lse; with sampling, the group draws), kEpiArgmax (greedy argmax),
 // kEpiHist (with raw scores: the top-k histogram of each row's order keys, in LDS, added to
-// the caller's [M, 4096] counts at the end)
-constexpr int kEpiStats = 1, kEpiArgmax = 2, kEpiHist = 4;
+// the caller's [M, 4096] counts at the end), kEpiSide (sampling: each wave copies the 64 logits
+// of its best group so far per row into its own LDS area whenever that group changes; the
+// workgroup's best of them go to a side buffer, so the finalize reads them instead of
+// recomputing the winning group)
+constexpr int kEpiStats = 1, kEpiArgmax = 2, kEpiHist = 4, kEpiSide = 8;
+// the side copies pay for themselves at one column block (measured: at three blocks the
+// workgroup's copy-out at the end costs the tile pass more than the finalize saves)
+constexpr int kTileSideMaxNcb = 1;
 
 }  // namespace
 
@@ -48,14 +55,22 @@ struct TilePass {
   static constexpr int NC = NCB * 16;   // activation rows (columns of the output tiles)
   static constexpr bool STATS = (EPI & kEpiStats) != 0, AMAX = (EPI & kEpiArgmax) != 0;
   static constexpr bool HIST = (EPI & kEpiHist) != 0;
+  static constexpr bool SIDE = (EPI & kEpiSide) != 0;
   static_assert(!HIST || (ZOUT && NCB == 1), "the histogram rides on the raw scores of a few rows");
+  static_assert(!SIDE || (STATS && !ZOUT && NCB <= kTileSideMaxNcb), "side copy: sampling stats, few rows");
   static constexpr int CPRP = KS * 4;   // 16-byte chunks per activation row
   static constexpr int RS = CPRP + 4;   // LDS row stride of the staged activations, in chunks
   static constexpr int XPER = (NC * CPRP + kTileThreads - 1) / kTileThreads;
-  // LDS bytes: staged activations [NC][RS], later the Partial records [4][NC]; then the
+  // LDS bytes: staged activations [NC][RS], later the Partial records [4][NC] and the winning
+  // wave of each row [NC] (SIDE); then the side copies [4][NC][68] floats (SIDE: past the staged
+  // activations, which other waves may still read when a wave's first group ends) or the
   // histograms [kTileHistRows][4096] (HIST)
-  static constexpr int kLdsMain = (NC * RS * 16 > kTileWaves * NC * 32) ? NC * RS * 16 : kTileWaves * NC * 32;
-  static constexpr int kLds = kLdsMain + (HIST ? kTileHistRows * kTkBins * 4 : 0);
+  static constexpr int kLdsRec = kTileWaves * NC * 32 + NC * 4;
+  static constexpr int kLdsMain = (NC * RS * 16 > kLdsRec) ? NC * RS * 16 : kLdsRec;
+  // side copies: a row stride of 68 floats keeps the 16 rows of one write on distinct banks
+  static constexpr int kSideStride = kGroup + 4;
+  static constexpr int kLds = kLdsMain + (HIST ? kTileHistRows * kTkBins * 4 : 0) +
+                              (SIDE ? kTileWaves * NC * kSideStride * 4 : 0);
 
   const TileArgs& a;
   uint4* smem;
@@ -246,6 +261,7 @@ struct TilePass {
         ss = bs[cb];
         zi = bx[cb];
       }
+    bool better = false;
     if (qd < NCB && qd * 16 + col < Mx) {
       if constexpr (STATS) {
         const float L = zm * a.invT + log2f(ss) * kLn2;   // group log-sum-exp of y = z / T
@@ -256,10 +272,31 @@ struct TilePass {
         if (a.sample != 0 && sc > gbest) {   // groups rise: strict > keeps the lowest on ties
           gbest = sc;
           gid = g;
+          better = true;
         }
       }
       if constexpr (AMAX) argmax_merge(bz, bi, zm, zi);
     }
+    if constexpr (SIDE) {
+      // lane (col, cb) decided for activation row 16 cb + col; lanes (col, 0..3) hold its 64
+      // logits (tile t, value v: vocabulary row 16 t + 4 qd + v of the group)
+      const uint64_t won = __builtin_amdgcn_ballot_w64(better);
+      if (won != 0ull) {   // uniform; rare after the first groups
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+          if (((won >> (16 * cb)) & 0xFFFFull) == 0ull) continue;   // uniform
+          if ((won >> (col + 16 * cb)) & 1ull) {
+            float4* dst = side_copy(w, cb * 16 + col);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) dst[t * 4 + qd] = make_float4(acc[t][cb][0], acc[t][cb][1], acc[t][cb][2], acc[t][cb][3]);
+          }
+        }
+      }
+    }
+  }
+  // wave w's copy of the best group's 64 logits of activation row m
+  __device__ __forceinline__ float4* side_copy(int ww, int m) const {
+    return reinterpret_cast<float4*>(reinterpret_cast<char*>(smem) + kLdsMain) + (ww * NC + m) * (kSideStride / 4);
   }
   __device__ __forceinline__ void group_end(int g, float gu) {
     if constexpr (STATS || AMAX) {
@@ -317,11 +354,28 @@ struct TilePass {
       rec[w * NC + m] = p;
     }
     __syncthreads();
+    int32_t* winner = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(smem) + kTileWaves * NC * 32);
     for (int r = threadIdx.x; r < Mx; r += kTileThreads) {
       Partial p = rec[r];
+      int32_t wv = 0;
 #pragma unroll
-      for (int ww = 1; ww < kTileWaves; ++ww) partial_merge(p, rec[ww * NC + r]);
+      for (int ww = 1; ww < kTileWaves; ++ww) {
+        const Partial q = rec[ww * NC + r];
+        if (q.gscore > p.gscore || (q.gscore == p.gscore && q.g < p.g)) wv = ww;   // as partial_merge
+        partial_merge(p, q);
+      }
       a.partials[static_cast<int64_t>(r) * a.partials_ld + wg] = p;
+      if constexpr (SIDE) winner[r] = wv;
+    }
+    if constexpr (SIDE) {
+      if (a.gz != nullptr) {
+        // each row's best group of the workgroup: the winning wave's copy goes to the side buffer
+        __syncthreads();
+        for (int i = threadIdx.x; i < Mx * (kGroup / 4); i += kTileThreads) {
+          const int m = i / (kGroup / 4), q = i % (kGroup / 4);
+          reinterpret_cast<float4*>(a.gz + (static_cast<int64_t>(m) * a.gz_ld + wg) * kGroup)[q] = side_copy(winner[m], m)[q];
+        }
+      }
     }
   }
 };
@@ -377,7 +431,9 @@ __device__ __forceinline__ void finalize_row(const FinalizeArgs& f, int m, float
     if (w != 0) return;   // the element draw is one wave's work (no barrier follows)
     const int64_t NG = (f.V + kGroup - 1) / kGroup;
     const int64_t g = acc.g == 0x7fffffff ? 0 : acc.g;
-    const int64_t p = ((g + 1) * f.P + NG - 1) / NG - 1;
+    // owner of group g: a consecutive range per workgroup (K-chunked pass), or the wave stride
+    // of the tile pass (group g on wave g mod 4P, workgroup (g mod 4P) / 4)
+    const int64_t p = f.gz_map == 0 ? ((g + 1) * f.P + NG - 1) / NG - 1 : (g % (int64_t{kTileWaves} * f.P)) / kTileWaves;
     const int64_t gbase = g * kGroup;
     const float z = f.gz[(static_cast<int64_t>(m) * f.gz_ld + p) * kGroup + l];
     const float gel = gumbel(philox_uniform(f.seed, f.offset, kDraftElem, static_cast<uint64_t>(m),
@@ -528,6 +584,12 @@ hipError_t run_tile_mode(const TileArgs& a, int grid, hipStream_t st) {
       default: return run_tile<NCB, KS, true, kEpiStats | kEpiArgmax>(a, grid, st);
     }
   }
+  if (a.gz != nullptr) {   // sampling with the side copy of each row's best group
+    if constexpr (NCB <= kTileSideMaxNcb) {
+      if (a.sample != 0 && epi == kEpiStats) return run_tile<NCB, KS, false, kEpiStats | kEpiSide>(a, grid, st);
+    }
+    return hipErrorInvalidValue;
+  }
   switch (epi) {
     case kEpiStats: return run_tile<NCB, KS, false, kEpiStats>(a, grid, st);
     case kEpiArgmax: return run_tile<NCB, KS, false, kEpiArgmax>(a, grid, st);
@@ -566,12 +628,14 @@ int head_tile_grid(int64_t M, int64_t K, int64_t V) {
   const int64_t NG = (V + kGroup - 1) / kGroup;
   int64_t grid = (NG + kTileWaves - 1) / kTileWaves;
   if (grid > di.cus) grid = di.cus;
-  if (grid > kMaxPartials) grid = kMaxPartials;
+  if (grid > kTileMaxGrid) grid = kTileMaxGrid;
   return static_cast<int>(grid < 1 ? 1 : grid);
 }
 
 hipError_t launch_head_tile(const TileArgs& a, int grid, hipStream_t st) {
   if (!head_tile_supported(a.M, a.K, a.V, true, a.ld)) return hipErrorInvalidValue;
+  if (a.gz != nullptr && (a.M > kTileSideMaxRows || a.gz_ld < grid || grid > kTileMaxGrid || a.zout != nullptr))
+    return hipErrorInvalidValue;
   switch (tile_ncb(a.M)) {
     case 1: return run_tile_ks<1>(a, grid, st);
     case 2: return run_tile_ks<2>(a, grid, st);

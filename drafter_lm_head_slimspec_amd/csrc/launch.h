@@ -48,7 +48,8 @@ struct FinalizeArgs {
   float* logprob;
   const int32_t* id_map;    // nullable [V]: the token written is id_map[row chosen]
   const float* gz;          // nullable [M, gz_ld, 64]: the winning group's logits as written by
-  int64_t gz_ld;            // the K-chunked pass (its owner among the P producers), not recomputed
+  int64_t gz_ld;            // the pass (by its owner among the P producers), not recomputed
+  int gz_map;               // owner of group g: 0 K-chunked (consecutive ranges), 1 tile (wave stride)
 };
 
 // Tile-streaming head pass (bf16, rows of 128, 256, 384 or 512 elements, at most kTileMaxRows
@@ -75,9 +76,12 @@ struct TileArgs {
   int64_t partials_ld;
   uint32_t* hist;     // nullable (with zout, M <= kTileHistRows): [M, 4096] counts of the top 12
                       // bits of each score's order key, added to (cleared by the caller)
-  float* gz;          // nullable, K-chunked pass in sampling mode: [M, gz_ld, 64] raw logits of
-  int64_t gz_ld;      // each row's best group of each workgroup
+  float* gz;          // nullable, sampling mode of the K-chunked pass, and of the tile pass with at
+  int64_t gz_ld;      // most kTileSideMaxRows rows: [M, gz_ld, 64] raw logits of each row's best
+                      // group of each workgroup
 };
+constexpr int kTileSideMaxRows = 16;   // rows whose best-group logits the tile pass keeps
+constexpr int kTileMaxGrid = 256;      // workgroups of a tile pass at most (the side buffer's gz_ld)
 constexpr int kTileHistRows = 2;
 bool head_tile_supported(int64_t M, int64_t K, int64_t V, bool bf16, int64_t ld = 0);
 

@@ -11,7 +11,8 @@ import threading
 import numpy as np
 import torch
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspechead.so")
+# the built library next to this file; SPECHEAD_LIB names another build of the same sources
+LIB_PATH = os.environ.get("SPECHEAD_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspechead.so")
 
 SH_OK, SH_ERR_NULL, SH_ERR_SHAPE, SH_ERR_DTYPE, SH_ERR_ALIGN = 0, 1, 2, 3, 4
 SH_ERR_WORKSPACE, SH_ERR_PARAM, SH_ERR_UNSUPPORTED, SH_ERR_HIP = 5, 6, 7, 8
