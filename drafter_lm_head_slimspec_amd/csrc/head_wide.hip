@@ -3,15 +3,19 @@
 //
 //   k_head_wide   z = W x over all V rows with per-workgroup Partials (lse, best group score
 //                 with the Philox group draw, argmax), as k_head_tile, for more activation
-//                 rows than fit one wave's registers.  A workgroup of four waves walks a
-//                 consecutive range of 64-row vocabulary groups in pairs; each group is read
-//                 once by the whole workgroup with whole-row loads (full cache lines) into an
-//                 LDS tile while the next pair's rows are in flight in registers.  Wave w multiplies the tile by its
-//                 own 16 * NCBW activation rows (their B fragments stay in registers for the
-//                 whole pass) on v_mfma_f32_16x16x32_bf16, reading the A fragments from LDS,
-//                 and folds each group into the running state of its rows exactly as the
-//                 tile kernel does: per group one in-lane and two cross-lane reductions give
-//                 the group log-sum-exp, the group draw L_g + Gumbel(u_g) and the argmax.
+//                 rows than fit one wave's registers.  A workgroup of eight waves (two per
+//                 SIMD) walks a consecutive range of 64-row vocabulary groups in pairs; each
+//                 group is read once by the whole workgroup with whole-row loads (full cache
+//                 lines) into an LDS tile while the next pair's rows are in flight in
+//                 registers.  The activation rows form 16-row column blocks dealt round-robin
+//                 to the waves (block b to wave b mod 8, at most two per wave), so the two
+//                 waves of a SIMD together hold a quarter of the blocks and one wave's VALU
+//                 epilogue can issue while the other's MFMAs run.  Each wave multiplies the
+//                 tile by its blocks (B fragments in registers for the whole pass) on
+//                 v_mfma_f32_16x16x32_bf16, reading the A fragments from LDS, and folds each
+//                 group into the running state of its rows exactly as the tile kernel does:
+//                 per group one in-lane and two cross-lane reductions give the group
+//                 log-sum-exp, the group draw L_g + Gumbel(u_g) and the argmax.
 //   The per-row merge of the workgroups' Partials is k_head_fin (head_tile.hip).
 #include <hip/hip_ext.h>
 
@@ -27,19 +31,22 @@ namespace {
 
 typedef float wf32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kWideThreads = 256;   // four waves
+constexpr int kWideThreads = 512;   // eight waves, two per SIMD
 constexpr int kWideWaves = kWideThreads / kWave;
 constexpr int kWideStats = 1, kWideArgmax = 2;
 
 }  // namespace
 
+// The pass of one wave holding NCBW column blocks (0, 1 or 2): blocks w and w + 8 of the
+// ceil(M / 16) blocks.  Every wave runs the same loads, stores and barriers.
 template <int NCBW, int KS, int EPI>
-__global__ __launch_bounds__(kWideThreads, 1) void k_head_wide(TileArgs a) {
+__device__ __forceinline__ void wide_wave(const TileArgs& a, uint4* tile) {
   constexpr bool STATS = (EPI & kWideStats) != 0, AMAX = (EPI & kWideArgmax) != 0;
   constexpr int CPR = KS * 4;            // 16-byte chunks per row covered by the k-steps
-  constexpr int RS = CPR + 1;            // LDS row stride in chunks (odd: conflict-free reads)
+  // LDS row stride in chunks: 2 mod 4 (measured on gfx950: the 16-row fragment reads run at
+  // ~170 B/clk per CU with such strides, ~110 with odd ones, far less with multiples of 8)
+  constexpr int RS = CPR + 2;
   constexpr int PER = CPR * kGroup / kWideThreads;   // row chunks each thread loads per group
-  extern __shared__ uint4 tile[];        // [2][64][RS] the current pair of groups, then 64 spare chunks
   const int l = lane_id(), w = wave_id();
   const int col = l & 15, qd = l >> 4;
   const int tid = static_cast<int>(threadIdx.x);
@@ -50,18 +57,19 @@ __global__ __launch_bounds__(kWideThreads, 1) void k_head_wide(TileArgs a) {
   const int NG = (V32 + kGroup - 1) / kGroup;
   const uint32_t vbytes = static_cast<uint32_t>(V32) * rowbytes;
   const int Mx = a.M;
-  const int m0 = w * NCBW * 16;          // first activation row of this wave
+  // activation row of block cb of this wave, lane column col
+  auto row_of = [&](int cb) { return (w + cb * kWideWaves) * 16 + col; };
   const float c2 = a.invT * kLog2e;
 
-  // this wave's activation fragments: Bf[s][cb] = x[m0 + 16 cb + col][32 s + 8 qd .. +8]
-  uint4 Bf[KS][NCBW];
-  {
+  // this wave's activation fragments: Bf[s][cb] = x[row_of(cb)][32 s + 8 qd .. +8]
+  uint4 Bf[KS][NCBW > 0 ? NCBW : 1];
+  if constexpr (NCBW > 0) {
     const rsrc_t xrs = make_rsrc(a.x, static_cast<uint32_t>(Mx) * rowbytes);
 #pragma unroll
     for (int s = 0; s < KS; ++s)
 #pragma unroll
       for (int cb = 0; cb < NCBW; ++cb) {
-        const int m = m0 + cb * 16 + col, c = 4 * s + qd;
+        const int m = row_of(cb), c = 4 * s + qd;
         Bf[s][cb] = buffer_load16(xrs, (m < Mx && c < kc) ? static_cast<uint32_t>(m) * rowbytes + c * 16u : kOutOfRange);
       }
   }
@@ -93,7 +101,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void k_head_wide(TileArgs a) {
     for (int j = 0; j < PER; ++j) tile[lidx[j] + (lidx[j] < 2 * kGroup * RS ? half * kGroup * RS : 0)] = R[j];
   };
 
-  // running state of activation row m0 + 16 qd + col (lanes with qd < NCBW)
+  // running state of activation row row_of(qd) (lanes with qd < NCBW)
   float rm = -INFINITY, rsum = 0.f, gbest = -INFINITY, bz = -INFINITY;
   int32_t gid = 0x7fffffff, bi = 0x7fffffff;
 
@@ -104,7 +112,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void k_head_wide(TileArgs a) {
   auto draw = [&](int g) -> float {
     float gu = 0.f;
     if constexpr (STATS) {
-      const int m = m0 + qd * 16 + col;
+      const int m = row_of(qd);
       if (a.sample != 0) {
         if ((g >> 2) != gq) {   // uniform over the workgroup
           gq = g >> 2;
@@ -125,7 +133,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void k_head_wide(TileArgs a) {
   // z = tile half x this wave's activation fragments.  Per k-step the four tiles' A fragments
   // are one batch of LDS reads, issued a k-step ahead of the 4 * NCBW MFMAs that use them
   // (with `pin`, scheduling barriers keep the reads in front)
-  auto mma = [&](int half, wf32x4_t (&acc)[4][NCBW], auto pin) {
+  auto mma = [&](int half, wf32x4_t (&acc)[4][NCBW > 0 ? NCBW : 1], auto pin) {
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -158,14 +166,14 @@ __global__ __launch_bounds__(kWideThreads, 1) void k_head_wide(TileArgs a) {
   };
   // fold group g into the running state of this lane's row (MASK: the vocabulary's last,
   // partial group, whose rows past V are -inf)
-  auto epi_body = [&](int g, float gu, const wf32x4_t (&acc)[4][NCBW], auto mask) {
+  auto epi_body = [&](int g, float gu, const wf32x4_t (&acc)[4][NCBW > 0 ? NCBW : 1], auto mask) {
     constexpr bool MASK = decltype(mask)::value;
     const int gb = g * kGroup;
     // per column block: the group's max, sum of exp and first argmax of activation row
-    // m0 + 16 cb + col; the four lanes col, col + 16, col + 32, col + 48 hold its 64 rows and
+    // row_of(cb); the four lanes col, col + 16, col + 32, col + 48 hold its 64 rows and
     // end with the same values (the max is taken first, so the sum needs no rescaling)
-    float bm[NCBW], bs[NCBW];
-    int32_t bx[NCBW];
+    float bm[NCBW > 0 ? NCBW : 1], bs[NCBW > 0 ? NCBW : 1];
+    int32_t bx[NCBW > 0 ? NCBW : 1];
 #pragma unroll
     for (int cb = 0; cb < NCBW; ++cb) {
       float z[16];
@@ -207,7 +215,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void k_head_wide(TileArgs a) {
       bs[cb] = ss;
       bx[cb] = zi;
     }
-    // lane (col, qd) finishes activation row m0 + 16 qd + col: one fold per lane
+    // lane (col, qd) finishes activation row row_of(qd): one fold per lane
     float zm = bm[0], ss = bs[0];
     int32_t zi = bx[0];
 #pragma unroll
@@ -217,7 +225,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void k_head_wide(TileArgs a) {
         ss = bs[cb];
         zi = bx[cb];
       }
-    if (qd < NCBW && m0 + qd * 16 + col < Mx) {
+    if (qd < NCBW && row_of(qd) < Mx) {
       if constexpr (STATS) {
         const float L = zm * a.invT + log2f(ss) * kLn2;   // group log-sum-exp of y = z / T
         const float mn = fmaxf(rm, L);
@@ -232,11 +240,11 @@ __global__ __launch_bounds__(kWideThreads, 1) void k_head_wide(TileArgs a) {
       if constexpr (AMAX) argmax_merge(bz, bi, zm, zi);
     }
   };
-  auto epi = [&](int g, float gu, const wf32x4_t (&acc)[4][NCBW]) {
+  auto epi = [&](int g, float gu, const wf32x4_t (&acc)[4][NCBW > 0 ? NCBW : 1]) {
     if (g * kGroup + kGroup <= V32) epi_body(g, gu, acc, std::false_type{});   // uniform
     else epi_body(g, gu, acc, std::true_type{});
   };
-  wf32x4_t accA[4][NCBW];
+  wf32x4_t accA[4][NCBW > 0 ? NCBW : 1];
 
   // the workgroup's groups are the consecutive range [gs, ge), taken in pairs (g, g + 1):
   // while a pair is multiplied out of the LDS tile, the next pair's rows are in flight in
@@ -256,15 +264,17 @@ __global__ __launch_bounds__(kWideThreads, 1) void k_head_wide(TileArgs a) {
     __syncthreads();
     gload(clampg(g + 2), RA);
     gload(clampg(g + 3), RB);
-    mma(0, accA, std::true_type{});
-    epi(g, draw(g), accA);
-    if (g + 1 < ge) {
-      mma(1, accA, std::true_type{});
-      epi(g + 1, draw(g + 1), accA);
+    if constexpr (NCBW > 0) {
+      mma(0, accA, std::true_type{});
+      epi(g, draw(g), accA);
+      if (g + 1 < ge) {
+        mma(1, accA, std::true_type{});
+        epi(g + 1, draw(g + 1), accA);
+      }
     }
   }
   // one Partial per activation row per workgroup (each row belongs to one lane)
-  const int m = m0 + qd * 16 + col;
+  const int m = row_of(qd);
   if (qd < NCBW && m < Mx) {
     Partial p;
     p.m = rm;
@@ -279,49 +289,52 @@ __global__ __launch_bounds__(kWideThreads, 1) void k_head_wide(TileArgs a) {
   }
 }
 
+template <int KS, int EPI>
+__global__ __launch_bounds__(kWideThreads, 1) void k_head_wide(TileArgs a) {
+  extern __shared__ uint4 tile[];   // [2][64][RS] the current pair of groups, then 64 spare chunks
+  const int w = wave_id();
+  const int nb = (a.M + 15) / 16;   // column blocks, at most 2 * kWideWaves
+  if constexpr (KS < 16) {   // rows of 512 elements: at most 128 activation rows, one block per wave
+    if (w + kWideWaves < nb) {
+      wide_wave<2, KS, EPI>(a, tile);
+      return;
+    }
+  }
+  if (w < nb) wide_wave<1, KS, EPI>(a, tile);
+  else wide_wave<0, KS, EPI>(a, tile);
+}
+
 // ----------------------------------------------------------------------------------------
 // host side
 // ----------------------------------------------------------------------------------------
 namespace {
 
 int wide_ks(int64_t K) { return static_cast<int>((K + 127) / 128) * 4; }   // 4, 8, 12 or 16
-int wide_ncbw(int64_t M) { return static_cast<int>((M + 63) / 64); }      // 1..4
-int wide_lds(int ks) { return (2 * kGroup * (ks * 4 + 1) + kWave) * 16; }
-// VGPRs per lane: activation fragments, two row buffers, accumulators, offsets and state
-int wide_regs(int ncbw, int ks) { return ks * ncbw * 4 + 2 * ks * 4 + 16 * ncbw + 2 * ks + 48; }
+int wide_lds(int ks) { return (2 * kGroup * (ks * 4 + 2) + kWave) * 16; }
+// VGPRs per lane of a two-block wave: activation fragments, two row buffers (eight waves share
+// each group's loads), accumulators, offsets and state
+int wide_regs(int ncbw, int ks) { return ks * ncbw * 4 + 2 * (ks / 2) * 4 + 16 * ncbw + ks + 64; }
 
-template <int NCBW, int KS, int EPI>
+template <int KS, int EPI>
 hipError_t run_wide(const TileArgs& a, int grid, hipStream_t st) {
   const int lds = wide_lds(KS);
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_head_wide<NCBW, KS, EPI>),
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_head_wide<KS, EPI>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
   TraceScope ts("head_wide", st, true);
-  hipExtLaunchKernelGGL((k_head_wide<NCBW, KS, EPI>), dim3(static_cast<unsigned>(grid)), dim3(kWideThreads), lds, st,
+  hipExtLaunchKernelGGL((k_head_wide<KS, EPI>), dim3(static_cast<unsigned>(grid)), dim3(kWideThreads), lds, st,
                         ts.start(), ts.stop(), 0, a);
   return hipGetLastError();
 }
 
-template <int NCBW, int KS>
+template <int KS>
 hipError_t run_wide_mode(const TileArgs& a, int grid, hipStream_t st) {
   const int epi = (a.want_stats ? kWideStats : 0) | (a.want_argmax ? kWideArgmax : 0);
   switch (epi) {
-    case kWideStats: return run_wide<NCBW, KS, kWideStats>(a, grid, st);
-    case kWideArgmax: return run_wide<NCBW, KS, kWideArgmax>(a, grid, st);
-    case kWideStats | kWideArgmax: return run_wide<NCBW, KS, kWideStats | kWideArgmax>(a, grid, st);
+    case kWideStats: return run_wide<KS, kWideStats>(a, grid, st);
+    case kWideArgmax: return run_wide<KS, kWideArgmax>(a, grid, st);
+    case kWideStats | kWideArgmax: return run_wide<KS, kWideStats | kWideArgmax>(a, grid, st);
     default: return hipErrorInvalidValue;
-  }
-}
-
-template <int NCBW>
-hipError_t run_wide_ks(const TileArgs& a, int grid, hipStream_t st) {
-  switch (wide_ks(a.K)) {
-    case 4: return run_wide_mode<NCBW, 4>(a, grid, st);
-    case 8: return run_wide_mode<NCBW, 8>(a, grid, st);
-    case 12: return run_wide_mode<NCBW, 12>(a, grid, st);
-    default:
-      if constexpr (NCBW <= 2) return run_wide_mode<NCBW, 16>(a, grid, st);
-      return hipErrorInvalidValue;
   }
 }
 
@@ -331,9 +344,10 @@ bool head_wide_supported(int64_t M, int64_t K, int64_t V, bool bf16, int64_t ld)
   if (ld <= 0) ld = K;
   if (!bf16 || M <= kTileMaxRows || M > kWideMaxRows || K < 8 || K % 8 != 0 || K > 512) return false;
   if (ld < K || ld % 8 != 0 || V < 1 || V * ld * 2 > int64_t{0xFFFFFFF0}) return false;
-  const int ks = wide_ks(K), ncbw = wide_ncbw(M);
-  if (ks == 16 && ncbw > 2) return false;
-  return wide_regs(ncbw, ks) <= 400 && wide_lds(ks) <= 160 * 1024;
+  const int ks = wide_ks(K);
+  const int ncbw = static_cast<int>((M + 16 * kWideWaves - 1) / (16 * kWideWaves));   // blocks per wave at most
+  // two waves per SIMD: at most 256 registers per lane
+  return wide_regs(ncbw, ks) <= 256 && wide_lds(ks) <= 160 * 1024;
 }
 
 int head_wide_grid(int64_t V) {
@@ -348,10 +362,11 @@ int head_wide_grid(int64_t V) {
 hipError_t launch_head_wide(const TileArgs& a, int grid, hipStream_t st) {
   if (!head_wide_supported(a.M, a.K, a.V, true, a.ld) || a.zout != nullptr || a.hist != nullptr)
     return hipErrorInvalidValue;
-  switch (wide_ncbw(a.M)) {
-    case 2: return run_wide_ks<2>(a, grid, st);
-    case 3: return run_wide_ks<3>(a, grid, st);
-    default: return run_wide_ks<4>(a, grid, st);
+  switch (wide_ks(a.K)) {
+    case 4: return run_wide_mode<4>(a, grid, st);
+    case 8: return run_wide_mode<8>(a, grid, st);
+    case 12: return run_wide_mode<12>(a, grid, st);
+    default: return run_wide_mode<16>(a, grid, st);
   }
 }
 
