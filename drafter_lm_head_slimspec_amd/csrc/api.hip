@@ -687,10 +687,9 @@ int draft_head_specvocab(const void* h, int64_t M, int64_t d, const void* W_down
   sh::TopkArgs ta = topk_args(ws + L.tk_off, TL, scores, M, V, k, topk_idx);
   ta.hist_ready = tile && M <= sh::kTileHistRows;
   SH_HIP(sh::launch_topk(ta, st), "top-k kernels");
-  SH_HIP(sh::launch_gather_exact(U, h, topk_idx, M, d, V, k, bf16, zbuf, st), "gather kernel");
-  SH_HIP(sh::launch_gather_finalize(zbuf, topk_idx, M, k, mode == SH_SAMPLE ? 1 : 0, 1.0f / temperature,
-                                    seed, offset, topk_logit, topk_prob, token, lse, logprob, st),
-         "candidate softmax kernel");
+  SH_HIP(sh::launch_gather_select(U, h, topk_idx, M, d, V, k, bf16, zbuf, mode == SH_SAMPLE ? 1 : 0, 1.0f / temperature,
+                                  seed, offset, topk_logit, topk_prob, token, lse, logprob, ta.count, st),
+         "gather and candidate softmax kernel");
   return SH_OK;
 }
 

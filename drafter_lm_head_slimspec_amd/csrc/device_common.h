@@ -332,6 +332,42 @@ __device__ __forceinline__ uint4 load16_or_zero(const char* base_valid, const ch
   return ok ? v : make_uint4(0u, 0u, 0u, 0u);
 }
 
+// ---------------------------------------------------------------------------------------
+// Last-arriver hand-off between the workgroups of one kernel.  Each workgroup writes what
+// the last one needs with device-coherent stores (sc1: written through the issuing XCD's L2),
+// waits until they are complete, then adds one to a counter with a device-scope atomic; the
+// workgroup whose addition completes the count reads everything back with device-coherent
+// loads (sc1) and finishes the job.  Nobody waits for anybody, so no spin and no grid-wide
+// barrier; the XCD caches never need a whole-cache write-back.  The counter must be zero when
+// the kernel starts (an earlier kernel of the call clears it); the last arriver puts it back.
+// ---------------------------------------------------------------------------------------
+constexpr int kCoherent = 16;   // buffer-instruction cache policy: sc1 (device scope)
+__device__ __forceinline__ void coherent_store(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void coherent_store(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void coherent_store(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t coherent_load(const uint32_t* p) {
+  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// true in every thread of the workgroup that arrives last of n; *flag is a shared word
+__device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t n, uint32_t* flag) {
+  __builtin_amdgcn_s_waitcnt(0);   // this thread's coherent stores have completed
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t old = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t last = old == n - 1u ? 1u : 0u;
+    if (last) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *flag = last;
+  }
+  __syncthreads();
+  return *flag != 0u;
+}
+
 __device__ __forceinline__ uint4 load16(const void* p) {
   return *reinterpret_cast<const uint4*>(p);
 }

@@ -124,6 +124,64 @@ __global__ __launch_bounds__(256) void k_rowdot(const void* __restrict__ Wd,
 }
 
 // ----------------------------------------------------------------------------------------
+// k_rowdot_few: bf16 with XM (1 or 2) input rows.  One weight row per wave, four per
+// workgroup, so R / 4 workgroups share the read; the input rows are loaded straight into
+// registers (no LDS staging), every load of a lane issued before the first dot.
+// ----------------------------------------------------------------------------------------
+template <int XM, int CPL>
+__global__ __launch_bounds__(256) void k_rowdot_few(const void* __restrict__ Wd, const void* __restrict__ x, int R,
+                                                   int C, uint16_t* __restrict__ out, uint32_t* __restrict__ zero,
+                                                   int64_t zero_words) {
+  if (zero != nullptr) {
+    // side job: clear a scratch block a later kernel of the same call accumulates into
+    const int64_t nwg = gridDim.x;
+    const int64_t per = (zero_words + nwg - 1) / nwg;
+    const int64_t z0 = static_cast<int64_t>(blockIdx.x) * per;
+    const int64_t z1 = z0 + per < zero_words ? z0 + per : zero_words;
+    for (int64_t i = z0 + threadIdx.x; i < z1; i += blockDim.x) zero[i] = 0u;
+  }
+  const int l = lane_id(), w = wave_id();
+  const int j = blockIdx.x * 4 + w;
+  const uint32_t rowbytes = static_cast<uint32_t>(C) * 16;
+  const rsrc_t wrs = make_rsrc(static_cast<const char*>(Wd) + static_cast<size_t>(j < R ? j : 0) * rowbytes,
+                               j < R ? rowbytes : 0u);
+  const rsrc_t xrs = make_rsrc(x, static_cast<uint32_t>(XM) * rowbytes);
+  uint4 wv[CPL], xv[XM][CPL];
+#pragma unroll
+  for (int q = 0; q < CPL; ++q) {
+    const int c = q * kWave + l;
+    const uint32_t off = c < C ? static_cast<uint32_t>(c) * 16 : kOutOfRange;
+    wv[q] = buffer_load16(wrs, off);
+#pragma unroll
+    for (int mm = 0; mm < XM; ++mm) xv[mm][q] = buffer_load16(xrs, c < C ? mm * rowbytes + off : kOutOfRange);
+  }
+#pragma unroll
+  for (int mm = 0; mm < XM; ++mm) {
+    float a = 0.f;
+#pragma unroll
+    for (int q = 0; q < CPL; ++q) a = chunk_dot_bf16(wv[q], xv[mm][q], a);
+    a = wave_sum(a);
+    if (l == 0 && j < R) out[static_cast<size_t>(mm) * R + j] = f32_to_bf16_rne(a);
+  }
+}
+
+template <int XM>
+hipError_t run_rowdot_few(const void* Wd, const void* x, int64_t R, int C, uint16_t* out, uint32_t* zero,
+                          int64_t zero_words, hipStream_t st) {
+  const dim3 grid(static_cast<unsigned>((R + 3) / 4));
+  const int cpl = (C + kWave - 1) / kWave;
+#define SH_FEW(N)                                                                                                \
+  hipLaunchKernelGGL((k_rowdot_few<XM, N>), grid, dim3(256), 0, st, Wd, x, static_cast<int>(R), C, out, zero, \
+                     zero_words)
+  if (cpl <= 2) SH_FEW(2);
+  else if (cpl <= 4) SH_FEW(4);
+  else if (cpl <= 8) SH_FEW(8);
+  else SH_FEW(16);
+#undef SH_FEW
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------------------
 // bf16 down-projection on MFMA, split over K:
 //   k_rowdot_mfma    grid (ceil(R/32), ksplit, row chunks): workgroup = 4 waves; each wave
 //                    multiplies a 32-row tile of Wd by up to 32*NCB input rows over
@@ -1274,17 +1332,12 @@ size_t rowdot_scratch_bytes(int64_t M, int64_t R, int64_t K) {
 hipError_t launch_rowdot(const void* Wd, const void* x, int64_t R, int64_t K, int64_t M, bool bf16,
                          void* out, float* scratch, hipStream_t st, uint32_t* zero, int64_t zero_words) {
   if (bf16 && M <= kRowdotVecMaxM && K * 2 <= kRowdotMaxCPL * kWave * 16) {
-    // one or two input rows: each wave dots two weight rows on the VALU, eight rows per
-    // workgroup (R / 8 workgroups instead of R / 16 MFMA tiles that each pull 16 rows)
+    // one or two input rows: one weight row per wave on the VALU, four per workgroup (R / 4
+    // workgroups instead of R / 16 MFMA tiles that each pull 16 rows), inputs in registers
     const int C = static_cast<int>(K * 2 / 16);
-    const dim3 grid(static_cast<unsigned>((R + kRowdotRows - 1) / kRowdotRows), 1u);
-    const int lds = kRowdotM * C * 16;
     TraceScope ts("rowdot", st);
-    hipError_t e = allow_lds(k_rowdot<true>, lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_rowdot<true>, grid, dim3(256), lds, st, Wd, x, static_cast<int>(R), C,
-                       static_cast<int>(M), out, zero, zero_words);
-    return hipGetLastError();
+    return M == 1 ? run_rowdot_few<1>(Wd, x, R, C, static_cast<uint16_t*>(out), zero, zero_words, st)
+                  : run_rowdot_few<2>(Wd, x, R, C, static_cast<uint16_t*>(out), zero, zero_words, st);
   }
   if (bf16 && M <= kRdTileMaxM) {
     RowRanks rk;

@@ -152,13 +152,12 @@ inline int64_t topk_counter_words(int64_t M) { return M * 4096 + M * kTkCounterS
 hipError_t launch_zero(uint32_t* p, int64_t words, hipStream_t st);
 size_t topk_finish_lds(int64_t V);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
-hipError_t launch_gather_exact(const void* U, const void* h, const int32_t* idx, int64_t M,
-                               int64_t d, int64_t V, int64_t k, bool bf16, float* zbuf,
-                               hipStream_t st);
-hipError_t launch_gather_finalize(const float* zbuf, const int32_t* idx, int64_t M, int64_t k,
-                                  int mode, float invT, uint64_t seed, uint64_t offset,
-                                  float* topk_logit, float* topk_prob, int32_t* token, float* lse,
-                                  float* logprob, hipStream_t st);
+// exact logits of the gathered candidates, then (by the workgroup finishing each row) the
+// softmax over the k candidates and the token; counters [M, kTkCounterStride] zero on entry
+hipError_t launch_gather_select(const void* U, const void* h, const int32_t* idx, int64_t M, int64_t d, int64_t V,
+                                int64_t k, bool bf16, float* zbuf, int mode, float invT, uint64_t seed,
+                                uint64_t offset, float* topk_logit, float* topk_prob, int32_t* token, float* lse,
+                                float* logprob, uint32_t* counters, hipStream_t st);
 
 // verification
 // mode 0 greedy, 1 sampling against dense draft logits, 2 sampling against a sparse draft

@@ -2,8 +2,9 @@
 //   k_topk_*          exact top-k of the approximate scores (ties -> lowest id), as a
 //                     threshold search over order-preserving keys, ascending ids out
 //   k_gather_exact    z'_j = U[K_j, :] . h read straight from the gathered rows (no slice copy),
-//                     the hidden state held in registers
-//   k_gather_finalize softmax over the k candidates, argmax or two-level Gumbel draw
+//                     the hidden state held in registers; the workgroup that completes a row
+//                     then runs its softmax over the k candidates and the argmax or two-level
+//                     Gumbel draw (a last-arriver hand-off, no second launch)
 #include "device_common.h"
 #include "launch.h"
 #include "trace.h"
@@ -199,12 +200,15 @@ constexpr int kTfWaves = kTfThreads / kWave;
 constexpr int kTfBatch = 8;   // words (candidates) each thread loads per round trip
 typedef uint32_t tf_u32x2_t __attribute__((ext_vector_type(2)));
 
-__global__ __launch_bounds__(kTfThreads) void k_topk_finish(TopkArgs a, int cand_cap) {
-  extern __shared__ uint32_t fin[];  // sel[nw], tie[nw], hist[1024], cand[cand_cap] (uint2)
-  __shared__ uint32_t wsum[kTfWaves];
-  __shared__ uint32_t res[2];
-  __shared__ uint32_t nties;
-  const int m = blockIdx.x;
+// Finish of row m by the NT threads of a workgroup.  LDS: fin = sel[nw], tie[nw],
+// hist[1024], cand[cand_cap] (uint2); wsum[NT / 64], res[2], nties.
+template <int NT>
+__device__ void topk_finish_row(const TopkArgs& a, int m, int cand_cap, uint32_t* fin, uint32_t* wsum, uint32_t* res,
+                                uint32_t* nties_p) {
+  constexpr int HB = kTkBins / NT;    // row-histogram bins per thread
+  constexpr int PB = 1024 / NT;       // pass-histogram bins per thread
+  constexpr int aux = 0;
+  uint32_t& nties = *nties_p;
   const int tid = threadIdx.x;
   const int64_t V = a.V;
   const uint32_t k = static_cast<uint32_t>(a.k);
@@ -216,7 +220,18 @@ __global__ __launch_bounds__(kTfThreads) void k_topk_finish(TopkArgs a, int cand
   uint2* cl = reinterpret_cast<uint2*>(fin + 2 * nw + 1024);
   // loads that depend on nothing, issued together: the row histogram, the candidate count and
   // the bitmask (kTfBatch words per thread per round trip)
-  const uint4 hq = reinterpret_cast<const uint4*>(a.hist + static_cast<size_t>(m) * kTkBins)[tid];
+  uint32_t hb[HB];
+  {
+    const uint4* hq = reinterpret_cast<const uint4*>(a.hist + static_cast<size_t>(m) * kTkBins) + tid * (HB / 4);
+#pragma unroll
+    for (int q = 0; q < HB / 4; ++q) {
+      const uint4 t = hq[q];
+      hb[4 * q] = t.x;
+      hb[4 * q + 1] = t.y;
+      hb[4 * q + 2] = t.z;
+      hb[4 * q + 3] = t.w;
+    }
+  }
   uint32_t C = a.count[static_cast<size_t>(m) * kTkCounterStride];
   {
     const rsrc_t mr = make_rsrc(a.mask + static_cast<size_t>(m) * mw, static_cast<uint32_t>(nw) * 4u);
@@ -224,12 +239,12 @@ __global__ __launch_bounds__(kTfThreads) void k_topk_finish(TopkArgs a, int cand
       uint32_t v[kTfBatch];
 #pragma unroll
       for (int q = 0; q < kTfBatch; ++q) {
-        const int i = i0 + q * kTfThreads + tid;
-        v[q] = buffer_load4(mr, i < nw ? static_cast<uint32_t>(i) * 4u : kOutOfRange);
+        const int i = i0 + q * NT + tid;
+        v[q] = __builtin_amdgcn_raw_buffer_load_b32(mr, i < nw ? static_cast<uint32_t>(i) * 4u : kOutOfRange, 0, aux);
       }
 #pragma unroll
       for (int q = 0; q < kTfBatch; ++q) {
-        const int i = i0 + q * kTfThreads + tid;
+        const int i = i0 + q * NT + tid;
         if (i < nw) {
           sel[i] = v[q];
           tie[i] = 0u;
@@ -237,59 +252,63 @@ __global__ __launch_bounds__(kTfThreads) void k_topk_finish(TopkArgs a, int cand
       }
     };
     batch(0);   // (the first batch outside the loop: its loads go out with the two above)
-    for (int i0 = kTfBatch * kTfThreads; i0 < nw; i0 += kTfBatch * kTfThreads) batch(i0);
+    for (int i0 = kTfBatch * NT; i0 < nw; i0 += kTfBatch * NT) batch(i0);
   }
   if (C > static_cast<uint64_t>(V)) C = static_cast<uint32_t>(V);
   const uint2* cg = a.cand + static_cast<size_t>(m) * V;
+  const rsrc_t cr = make_rsrc(cg, C * 8u);
   const bool in_lds = C <= static_cast<uint32_t>(cand_cap);
   if (in_lds) {
     // the candidates, staged into LDS kTfBatch per thread per round trip
-    const rsrc_t cr = make_rsrc(cg, C * 8u);
     auto batch = [&](uint32_t i0) {
       tf_u32x2_t v[kTfBatch];
 #pragma unroll
       for (int q = 0; q < kTfBatch; ++q) {
-        const uint32_t i = i0 + q * kTfThreads + tid;
-        v[q] = __builtin_amdgcn_raw_buffer_load_b64(cr, i < C ? i * 8u : kOutOfRange, 0, 0);
+        const uint32_t i = i0 + q * NT + tid;
+        v[q] = __builtin_amdgcn_raw_buffer_load_b64(cr, i < C ? i * 8u : kOutOfRange, 0, aux);
       }
 #pragma unroll
       for (int q = 0; q < kTfBatch; ++q) {
-        const uint32_t i = i0 + q * kTfThreads + tid;
+        const uint32_t i = i0 + q * NT + tid;
         if (i < C) cl[i] = make_uint2(v[q].x, v[q].y);
       }
     };
     batch(0);
-    for (uint32_t i0 = kTfBatch * kTfThreads; i0 < C; i0 += kTfBatch * kTfThreads) batch(i0);
+    for (uint32_t i0 = kTfBatch * NT; i0 < C; i0 += kTfBatch * NT) batch(i0);
   }
   // a candidate from LDS, or from the global list when it did not fit (uniform branch: LDS
   // reads stay LDS reads)
-  auto cand_at = [&](uint32_t i) -> uint2 { return in_lds ? cl[i] : cg[i]; };
+  auto cand_at = [&](uint32_t i) -> uint2 {
+    if (in_lds) return cl[i];
+    const tf_u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(cr, i * 8u, 0, aux);
+    return make_uint2(v.x, v.y);
+  };
   if (tid == 0) nties = 0u;
-  {
-    const uint32_t c[4] = {hq.x, hq.y, hq.z, hq.w};
-    find_crossing<4>(c, k, wsum, res);   // includes a barrier: LDS stores above are visible
-  }
+  find_crossing<HB>(hb, k, wsum, res);   // includes a barrier: LDS stores above are visible
   const uint32_t bstar = res[0];
   uint32_t need = k - res[1];
   uint32_t thr = bstar << kTkShift;
   // two 10-bit passes over the candidates: key bits 19..10, then 9..0
   for (int pass = 0; pass < 2; ++pass) {
     const int shift = pass == 0 ? 10 : 0;
-    h1[tid] = 0u;
+#pragma unroll
+    for (int i = 0; i < PB; ++i) h1[PB * tid + i] = 0u;
     __syncthreads();
-    for (uint32_t i = tid; i < C; i += kTfThreads) {
+    for (uint32_t i = tid; i < C; i += NT) {
       const uint32_t key = cand_at(i).x;
       if (pass == 0 || ((key >> 10) & 1023u) == ((thr >> 10) & 1023u)) atomicAdd(&h1[(key >> shift) & 1023u], 1u);
     }
     __syncthreads();
-    const uint32_t c[1] = {h1[tid]};
-    find_crossing<1>(c, need, wsum, res);
+    uint32_t c[PB];
+#pragma unroll
+    for (int i = 0; i < PB; ++i) c[i] = h1[PB * tid + i];
+    find_crossing<PB>(c, need, wsum, res);
     thr |= res[0] << shift;
     need -= res[1];
   }
   // keys above the threshold are in; keys equal to it are in if all are needed, else they
   // compete by id
-  for (uint32_t i = tid; i < C; i += kTfThreads) {
+  for (uint32_t i = tid; i < C; i += NT) {
     const uint2 ce = cand_at(i);
     if (ce.y >= static_cast<uint64_t>(V)) continue;
     if (ce.x > thr) {
@@ -300,7 +319,7 @@ __global__ __launch_bounds__(kTfThreads) void k_topk_finish(TopkArgs a, int cand
     }
   }
   __syncthreads();
-  const int per = (nw + kTfThreads - 1) / kTfThreads;
+  const int per = (nw + NT - 1) / NT;
   const int w0 = tid * per < nw ? tid * per : nw;
   const int w1 = w0 + per < nw ? w0 + per : nw;
   if (nties <= need) {
@@ -335,6 +354,14 @@ __global__ __launch_bounds__(kTfThreads) void k_topk_finish(TopkArgs a, int cand
   }
 }
 
+__global__ __launch_bounds__(kTfThreads) void k_topk_finish(TopkArgs a, int cand_cap) {
+  extern __shared__ uint32_t fin[];  // sel[nw], tie[nw], hist[1024], cand[cand_cap] (uint2)
+  __shared__ uint32_t wsum[kTfWaves];
+  __shared__ uint32_t res[2];
+  __shared__ uint32_t nties;
+  topk_finish_row<kTfThreads>(a, static_cast<int>(blockIdx.x), cand_cap, fin, wsum, res, &nties);
+}
+
 __global__ void k_zero(uint32_t* p, int64_t words) {
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < words;
        i += static_cast<int64_t>(gridDim.x) * blockDim.x)
@@ -366,14 +393,15 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  // LDS of a finishing workgroup: the two bitmasks and the 1024-bin histogram, then as many
+  // candidates as fit
+  const size_t base = topk_finish_lds(a.V);
   {
     TraceScope ts("topk_select", st);
     hipLaunchKernelGGL(k_topk_select, grid, dim3(kTkThreads), 0, st, a);
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // LDS: the two bitmasks and the 1024-bin histogram, then as many candidates as fit
-  const size_t base = topk_finish_lds(a.V);
   const size_t limit = 160 * 1024 - 1024;   // leave room for the static arrays
   int cap = base < limit ? static_cast<int>((limit - base) / 8) : 0;
   if (cap > 8192) cap = 8192;
@@ -387,18 +415,144 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
 }
 
 // ----------------------------------------------------------------------------------------
-// gather + exact logits: grid (ceil(k / 16), M); each wave computes 4 candidates of row m.
+// softmax over the k candidates + selection of one row, by the 4 waves of one workgroup (the
+// gather workgroup that completes the row).  The row's logits are staged in LDS once; the
+// group draw computes all group uniforms in one pass.
+// ----------------------------------------------------------------------------------------
+constexpr int kGfThreads = 256;
+constexpr int kGfWaves = kGfThreads / kWave;
+constexpr int kGfBatch = 8;   // logits each thread loads per round trip
+
+struct GatherOut {
+  int k;
+  int mode;
+  float invT;
+  uint64_t seed, offset;
+  float* topk_logit;
+  float* topk_prob;
+  int32_t* token;
+  float* lse;
+  float* logprob;
+  uint32_t* counters;   // [M, kTkCounterStride]: word 2 counts the row's finished workgroups
+};
+
+// zl: LDS [k] logits then [ceil(k / 64)] group sums; the logits are read with device-coherent
+// loads (other workgroups of this kernel wrote them)
+__device__ void gather_finalize_row(const float* __restrict__ zbuf, const int32_t* __restrict__ idx,
+                                    const GatherOut& o, int m, float* zl, float* red_f) {
+  const int k = o.k;
+  const int l = lane_id(), w = wave_id();
+  const float* z = zbuf + static_cast<size_t>(m) * k;
+  const int ng = (k + kGroup - 1) / kGroup;
+  float* Lg = zl + k;
+  float mx = -INFINITY;
+  {
+    // kGfBatch loads per thread issued together (one memory round trip per batch)
+    const rsrc_t zr = make_rsrc(z, static_cast<uint32_t>(k) * 4u);
+    for (int j0 = 0; j0 < k; j0 += kGfBatch * kGfThreads) {
+      uint32_t v[kGfBatch];
+#pragma unroll
+      for (int q = 0; q < kGfBatch; ++q) {
+        const int j = j0 + q * kGfThreads + static_cast<int>(threadIdx.x);
+        v[q] = __builtin_amdgcn_raw_buffer_load_b32(zr, j < k ? static_cast<uint32_t>(j) * 4u : kOutOfRange, 0,
+                                                    kCoherent);
+      }
+#pragma unroll
+      for (int q = 0; q < kGfBatch; ++q) {
+        const int j = j0 + q * kGfThreads + static_cast<int>(threadIdx.x);
+        if (j < k) {
+          const float f = __uint_as_float(v[q]);
+          zl[j] = f;
+          mx = fmaxf(mx, f);
+        }
+      }
+    }
+  }
+  mx = wave_max(mx);
+  if (l == 0) red_f[w] = mx;
+  __syncthreads();
+  mx = red_f[0];
+  for (int i = 1; i < kGfWaves; ++i) mx = fmaxf(mx, red_f[i]);
+  const float c = o.invT * kLog2e;
+  const float mxc = mx * c;
+  // group sums (base 2, shifted by the row max) and the row sum from them
+  for (int g = w; g < ng; g += kGfWaves) {
+    const int j = g * kGroup + l;
+    const float t = j < k ? fast_exp2(fmaf(zl[j], c, -mxc)) : 0.f;
+    const float gs = wave_sum(t);
+    if (l == 0) Lg[g] = gs;
+  }
+  __syncthreads();
+  float sm = 0.f;
+  for (int g = threadIdx.x; g < ng; g += blockDim.x) sm += Lg[g];
+  sm = wave_sum(sm);
+  __syncthreads();
+  if (l == 0) red_f[w] = sm;
+  __syncthreads();
+  sm = red_f[0];
+  for (int i = 1; i < kGfWaves; ++i) sm += red_f[i];
+  const float lse = mx * o.invT + logf(sm);          // natural-log units of y = z / T
+  const float lse2 = mxc + log2f(sm);                // base-2 units of z * c
+  for (int j = threadIdx.x; j < k; j += blockDim.x) {
+    const float zj = zl[j];
+    if (o.topk_prob) o.topk_prob[static_cast<size_t>(m) * k + j] = fast_exp2(fmaf(zj, c, -lse2));
+    if (o.topk_logit) o.topk_logit[static_cast<size_t>(m) * k + j] = zj;
+  }
+  int32_t jstar = 0;
+  if (w == 0) {
+    if (o.mode == 0) {
+      float v = -INFINITY;
+      int32_t vi = 0x7fffffff;
+      for (int j = l; j < k; j += kWave) argmax_merge(v, vi, zl[j], j);
+      wave_argmax(v, vi);
+      jstar = vi;
+    } else {
+      // group scores: log of the group sum (natural units) + Gumbel(u_g), all groups at once
+      float best = -INFINITY;
+      int32_t bg = 0x7fffffff;
+      for (int g = l; g < ng; g += kWave) {
+        const float gs = Lg[g];
+        if (gs > 0.f) {
+          const float L = (mxc + log2f(gs)) * kLn2;
+          argmax_merge(best, bg, L + gumbel(philox_uniform(o.seed, o.offset, kDraftGroup, m, g)), g);
+        }
+      }
+      wave_argmax(best, bg);
+      const int j = bg * kGroup + l;
+      const bool valid = bg != 0x7fffffff && j < k;
+      float e = valid ? zl[j] * o.invT + gumbel(philox_uniform(o.seed, o.offset, kDraftElem, m, j)) : -INFINITY;
+      int32_t ei = valid ? j : 0x7fffffff;
+      wave_argmax(e, ei);
+      jstar = ei;
+    }
+    if (jstar < 0 || jstar >= k) jstar = 0;   // only if every candidate score were -inf
+    if (l == 0) {
+      o.token[m] = idx[static_cast<size_t>(m) * k + jstar];
+      if (o.lse) o.lse[m] = lse;
+      if (o.logprob) o.logprob[m] = zl[jstar] * o.invT - lse;
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------------------
+// gather + exact logits, then the row's softmax: grid (ceil(k / 8), M); each wave computes
+// kGatherRows candidates of row m; the workgroup that finishes row m last runs its softmax and
+// selection (gather_finalize_row), so the call needs no separate finalize launch.
 // ----------------------------------------------------------------------------------------
 constexpr int kGatherRows = 2;   // candidate rows per wave, all loads in flight together
 
 // z'[m, j] = U[K[m, j], :] . h[m, :].  Each wave takes kGatherRows candidates; a candidate's
 // row is one buffer descriptor (an invalid id gets an empty range, so its loads read zero).
 template <bool BF16, int CPL>
-__global__ __launch_bounds__(256) void k_gather_exact(const void* __restrict__ U,
-                                                      const void* __restrict__ h,
-                                                      const int32_t* __restrict__ idx, int C,
-                                                      int k, int V, float* __restrict__ zbuf) {
+__global__ __launch_bounds__(kGfThreads) void k_gather_exact(const void* __restrict__ U,
+                                                             const void* __restrict__ h,
+                                                             const int32_t* __restrict__ idx, int C,
+                                                             int V, float* __restrict__ zbuf, GatherOut o) {
+  extern __shared__ float zl[];   // the finishing workgroup's logits and group sums
+  __shared__ float red_f[kGfWaves];
+  __shared__ uint32_t last;
   const int m = blockIdx.y;
+  const int k = o.k;
   const int l = lane_id(), w = wave_id();
   const uint32_t rowbytes = static_cast<uint32_t>(C) * 16;
   const int j0 = (blockIdx.x * (blockDim.x / kWave) + w) * kGatherRows;
@@ -429,163 +583,57 @@ __global__ __launch_bounds__(256) void k_gather_exact(const void* __restrict__ U
 #pragma unroll
     for (int q = 0; q < CPL; ++q) z = chunk_dot<BF16>(wv[jj][q], hr[q], z);
     z = wave_sum(z);
-    if (l == 0 && j0 + jj < k) zbuf[static_cast<size_t>(m) * k + j0 + jj] = z;
+    if (l == 0 && j0 + jj < k) coherent_store(&zbuf[static_cast<size_t>(m) * k + j0 + jj], z);
   }
+  if (arrive_last(&o.counters[static_cast<size_t>(m) * kTkCounterStride + 2], gridDim.x, &last))
+    gather_finalize_row(zbuf, idx, o, m, zl, red_f);
 }
 
 template <bool BF16, int CPL>
 static hipError_t run_gather(const void* U, const void* h, const int32_t* idx, int C, int64_t M,
-                             int64_t V, int64_t k, float* zbuf, hipStream_t st) {
-  const int per_wg = 4 * kGatherRows;
-  const dim3 grid(static_cast<unsigned>((k + per_wg - 1) / per_wg), static_cast<unsigned>(M));
-  hipLaunchKernelGGL((k_gather_exact<BF16, CPL>), grid, dim3(256), 0, st, U, h, idx, C,
-                     static_cast<int>(k), static_cast<int>(V), zbuf);
+                             int64_t V, float* zbuf, const GatherOut& o, hipStream_t st) {
+  const int per_wg = kGfWaves * kGatherRows;
+  const dim3 grid(static_cast<unsigned>((o.k + per_wg - 1) / per_wg), static_cast<unsigned>(M));
+  const int lds = static_cast<int>((o.k + (o.k + kGroup - 1) / kGroup) * 4);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_gather_exact<BF16, CPL>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((k_gather_exact<BF16, CPL>), grid, dim3(kGfThreads), lds, st, U, h, idx, C,
+                     static_cast<int>(V), zbuf, o);
   return hipGetLastError();
 }
 
 template <bool BF16>
 static hipError_t gather_dispatch(const void* U, const void* h, const int32_t* idx, int C, int64_t M,
-                                  int64_t V, int64_t k, float* zbuf, hipStream_t st) {
+                                  int64_t V, float* zbuf, const GatherOut& o, hipStream_t st) {
   const int cpl = (C + kWave - 1) / kWave;
-  if (cpl <= 1) return run_gather<BF16, 1>(U, h, idx, C, M, V, k, zbuf, st);
-  if (cpl <= 2) return run_gather<BF16, 2>(U, h, idx, C, M, V, k, zbuf, st);
-  if (cpl <= 4) return run_gather<BF16, 4>(U, h, idx, C, M, V, k, zbuf, st);
-  if (cpl <= 8) return run_gather<BF16, 8>(U, h, idx, C, M, V, k, zbuf, st);
-  return run_gather<BF16, 16>(U, h, idx, C, M, V, k, zbuf, st);
+  if (cpl <= 1) return run_gather<BF16, 1>(U, h, idx, C, M, V, zbuf, o, st);
+  if (cpl <= 2) return run_gather<BF16, 2>(U, h, idx, C, M, V, zbuf, o, st);
+  if (cpl <= 4) return run_gather<BF16, 4>(U, h, idx, C, M, V, zbuf, o, st);
+  if (cpl <= 8) return run_gather<BF16, 8>(U, h, idx, C, M, V, zbuf, o, st);
+  return run_gather<BF16, 16>(U, h, idx, C, M, V, zbuf, o, st);
 }
 
-hipError_t launch_gather_exact(const void* U, const void* h, const int32_t* idx, int64_t M,
-                               int64_t d, int64_t V, int64_t k, bool bf16, float* zbuf,
-                               hipStream_t st) {
+hipError_t launch_gather_select(const void* U, const void* h, const int32_t* idx, int64_t M, int64_t d, int64_t V,
+                                int64_t k, bool bf16, float* zbuf, int mode, float invT, uint64_t seed,
+                                uint64_t offset, float* topk_logit, float* topk_prob, int32_t* token, float* lse,
+                                float* logprob, uint32_t* counters, hipStream_t st) {
   const int C = static_cast<int>(d * (bf16 ? 2 : 4) / 16);
-  TraceScope ts("gather_exact", st);
-  return bf16 ? gather_dispatch<true>(U, h, idx, C, M, V, k, zbuf, st)
-              : gather_dispatch<false>(U, h, idx, C, M, V, k, zbuf, st);
-}
-
-// ----------------------------------------------------------------------------------------
-// softmax over the k candidates + selection; one workgroup (4 waves) per row.  The row's
-// logits are staged in LDS once; the group draw computes all group uniforms in one pass.
-// ----------------------------------------------------------------------------------------
-constexpr int kGfThreads = 256;
-constexpr int kGfWaves = kGfThreads / kWave;
-constexpr int kGfBatch = 8;   // logits each thread loads per round trip
-
-__global__ __launch_bounds__(kGfThreads) void k_gather_finalize(const float* __restrict__ zbuf,
-                                                                const int32_t* __restrict__ idx, int k,
-                                                                int mode, float invT, uint64_t seed,
-                                                                uint64_t offset, float* topk_logit,
-                                                                float* topk_prob, int32_t* token,
-                                                                float* lse_out, float* logprob) {
-  extern __shared__ float zl[];   // [k] logits, then [ceil(k/64)] group log-sum-exps
-  __shared__ float red_f[kGfWaves];
-  __shared__ int32_t red_i[kGfWaves];
-  const int m = blockIdx.x;
-  const int l = lane_id(), w = wave_id();
-  const float* z = zbuf + static_cast<size_t>(m) * k;
-  const int ng = (k + kGroup - 1) / kGroup;
-  float* Lg = zl + k;
-  float mx = -INFINITY;
-  {
-    // kGfBatch loads per thread issued together (one memory round trip per batch)
-    const rsrc_t zr = make_rsrc(z, static_cast<uint32_t>(k) * 4u);
-    for (int j0 = 0; j0 < k; j0 += kGfBatch * kGfThreads) {
-      uint32_t v[kGfBatch];
-#pragma unroll
-      for (int q = 0; q < kGfBatch; ++q) {
-        const int j = j0 + q * kGfThreads + static_cast<int>(threadIdx.x);
-        v[q] = buffer_load4(zr, j < k ? static_cast<uint32_t>(j) * 4u : kOutOfRange);
-      }
-#pragma unroll
-      for (int q = 0; q < kGfBatch; ++q) {
-        const int j = j0 + q * kGfThreads + static_cast<int>(threadIdx.x);
-        if (j < k) {
-          const float f = __uint_as_float(v[q]);
-          zl[j] = f;
-          mx = fmaxf(mx, f);
-        }
-      }
-    }
-  }
-  mx = wave_max(mx);
-  if (l == 0) red_f[w] = mx;
-  __syncthreads();
-  mx = red_f[0];
-  for (int i = 1; i < kGfWaves; ++i) mx = fmaxf(mx, red_f[i]);
-  const float c = invT * kLog2e;
-  const float mxc = mx * c;
-  // group log-sum-exps (base 2, shifted by the row max) and the row sum from them
-  for (int g = w; g < ng; g += kGfWaves) {
-    const int j = g * kGroup + l;
-    const float t = j < k ? fast_exp2(fmaf(zl[j], c, -mxc)) : 0.f;
-    const float gs = wave_sum(t);
-    if (l == 0) Lg[g] = gs;
-  }
-  __syncthreads();
-  float sm = 0.f;
-  for (int g = threadIdx.x; g < ng; g += blockDim.x) sm += Lg[g];
-  sm = wave_sum(sm);
-  __syncthreads();
-  if (l == 0) red_f[w] = sm;
-  __syncthreads();
-  sm = red_f[0];
-  for (int i = 1; i < kGfWaves; ++i) sm += red_f[i];
-  const float lse = mx * invT + logf(sm);            // natural-log units of y = z / T
-  const float lse2 = mxc + log2f(sm);                // base-2 units of z * c
-  for (int j = threadIdx.x; j < k; j += blockDim.x) {
-    const float zj = zl[j];
-    if (topk_prob) topk_prob[static_cast<size_t>(m) * k + j] = fast_exp2(fmaf(zj, c, -lse2));
-    if (topk_logit) topk_logit[static_cast<size_t>(m) * k + j] = zj;
-  }
-  int32_t jstar = 0;
-  if (w == 0) {
-    if (mode == 0) {
-      float v = -INFINITY;
-      int32_t vi = 0x7fffffff;
-      for (int j = l; j < k; j += kWave) argmax_merge(v, vi, zl[j], j);
-      wave_argmax(v, vi);
-      jstar = vi;
-    } else {
-      // group scores: log of the group sum (natural units) + Gumbel(u_g), all groups at once
-      float best = -INFINITY;
-      int32_t bg = 0x7fffffff;
-      for (int g = l; g < ng; g += kWave) {
-        const float gs = Lg[g];
-        if (gs > 0.f) {
-          const float L = (mxc + log2f(gs)) * kLn2;
-          argmax_merge(best, bg, L + gumbel(philox_uniform(seed, offset, kDraftGroup, m, g)), g);
-        }
-      }
-      wave_argmax(best, bg);
-      const int j = bg * kGroup + l;
-      const bool valid = bg != 0x7fffffff && j < k;
-      float e = valid ? zl[j] * invT + gumbel(philox_uniform(seed, offset, kDraftElem, m, j)) : -INFINITY;
-      int32_t ei = valid ? j : 0x7fffffff;
-      wave_argmax(e, ei);
-      jstar = ei;
-    }
-    if (jstar < 0 || jstar >= k) jstar = 0;   // only if every candidate score were -inf
-    if (l == 0) {
-      token[m] = idx[static_cast<size_t>(m) * k + jstar];
-      if (lse_out) lse_out[m] = lse;
-      if (logprob) logprob[m] = zl[jstar] * invT - lse;
-    }
-  }
-}
-
-hipError_t launch_gather_finalize(const float* zbuf, const int32_t* idx, int64_t M, int64_t k,
-                                  int mode, float invT, uint64_t seed, uint64_t offset,
-                                  float* topk_logit, float* topk_prob, int32_t* token, float* lse,
-                                  float* logprob, hipStream_t st) {
-  const int lds = static_cast<int>((k + (k + kGroup - 1) / kGroup) * 4);
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_gather_finalize),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-  if (e != hipSuccess) return e;
-  TraceScope ts("gather_finalize", st);
-  hipLaunchKernelGGL(k_gather_finalize, dim3(static_cast<unsigned>(M)), dim3(kGfThreads), lds, st, zbuf,
-                     idx, static_cast<int>(k), mode, invT, seed, offset, topk_logit, topk_prob, token,
-                     lse, logprob);
-  return hipGetLastError();
+  GatherOut o{};
+  o.k = static_cast<int>(k);
+  o.mode = mode;
+  o.invT = invT;
+  o.seed = seed;
+  o.offset = offset;
+  o.topk_logit = topk_logit;
+  o.topk_prob = topk_prob;
+  o.token = token;
+  o.lse = lse;
+  o.logprob = logprob;
+  o.counters = counters;
+  TraceScope ts("gather_select", st);
+  return bf16 ? gather_dispatch<true>(U, h, idx, C, M, V, zbuf, o, st)
+              : gather_dispatch<false>(U, h, idx, C, M, V, zbuf, o, st);
 }
 
 // ----------------------------------------------------------------------------------------
