@@ -38,9 +38,9 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--legs", default="all",
-                   help="comma list of legs (lowrank48,lowrank48g,lowrank6,dense48,dense6,specvocab1,"
-                        "specvocab16,verify,verifyg,verifysparse,verifytree,adaptive48,adaptive48s,trimmed48,"
-                        "trimmed6,gptoss192) or 'all' "
+                   help="comma list of legs (lowrank48,lowrank48g,lowrank6,lowrank48logits,lowrank8x6,dense48,"
+                        "dense6,specvocab1,specvocab16,verify,verifys0.5,verifys2,verifyg,verifysparse,verifytree,"
+                        "adaptive48,adaptive48s,trimmed48,trimmed6,trimmedceiling,gptoss192) or 'all' "
                         "or 'headline'")
     p.add_argument("--rotate", type=int, default=5, help="device copies of each weight set")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -183,10 +183,10 @@ def main():
     w = configs.LLAMA
     d, V, r, dp, k = w.d, w.V, w.r, w.dprime, w.k
     seeds = w.seeds
-    legs_all = ["lowrank48", "lowrank48g", "lowrank6", "gptoss192", "adaptive48", "adaptive48s", "dense48", "dense6",
-                "trimmed48", "trimmed6",
+    legs_all = ["lowrank48", "lowrank48g", "lowrank6", "lowrank48logits", "lowrank8x6", "gptoss192", "adaptive48",
+                "adaptive48s", "dense48", "dense6", "trimmed48", "trimmed6", "trimmedceiling",
                 "specvocab1", "specvocab16",
-                "verify", "verifyg", "verifysparse", "verifytree"]
+                "verify", "verifys0.5", "verifys2", "verifyg", "verifysparse", "verifytree"]
     if args.legs == "all":
         legs = legs_all
     elif args.legs == "headline":
@@ -216,6 +216,7 @@ def main():
 
     results = {}
     kernel_trace = {}
+    line_extra = {}
 
     def timed(calls, steps, warmup):
         n = len(calls)
@@ -260,18 +261,19 @@ def main():
             f"{100 * out['hbm_frac']:5.1f}% of HBM roofline")
         return out
 
-    def lowrank_calls(h, M, mode):
+    def lowrank_calls(h, M, mode, logits=False):
         calls = []
         for i in range(R):
             tok = torch.empty(M, dtype=torch.int32, device=dev)
             lse = torch.empty(M, dtype=torch.float32, device=dev)
             lp = torch.empty(M, dtype=torch.float32, device=dev)
+            zl = torch.empty(M, V, dtype=torch.float32, device=dev) if logits else None
             need = sh.load().sh_head_workspace_bytes(sh.OP_LOWRANK, M, d, r, V, 0)
             ws = torch.zeros(need, dtype=torch.uint8, device=dev)
             calls.append(sh.prepared("draft_head_lowrank", h, M, d, Wd[i], r, Wu[i], V, sh.SH_BF16,
-                                     mode, 1.0, seeds["philox"], i, tok, lse, lp, None, ws, need,
+                                     mode, 1.0, seeds["philox"], i, tok, lse, lp, zl, ws, need,
                                      torch.cuda.current_stream().cuda_stream))
-            calls[-1].keep = (tok, lse, lp, ws)
+            calls[-1].keep = (tok, lse, lp, zl, ws)
         return calls
 
     def dense_calls(h, M, mode):
@@ -292,6 +294,27 @@ def main():
         run_leg("lowrank48g", lowrank_calls(h48, 48, sh.GREEDY), 48, lowrank_bytes(48))
     if "lowrank6" in legs:
         run_leg("lowrank6", lowrank_calls(h6, 6, sh.SAMPLE), 6, lowrank_bytes(6))
+    if "lowrank48logits" in legs:
+        # the same call also writing the raw logits [48, V] float32 (their bytes counted)
+        o = run_leg("lowrank48logits", lowrank_calls(h48, 48, sh.SAMPLE, logits=True), 48,
+                    lowrank_bytes(48) + 48 * V * 4)
+        o["config"] = {"logits": "float32 [48, V] written"}
+    if "lowrank8x6" in legs:
+        # an autoregressive drafter: gamma = 6 calls of B = 8 rows, each on its own hidden
+        # states, one step = the 6 calls (every call streams W_up again)
+        hs = [bf(synth.hidden(8, d, "bf16", seeds["hidden"] + 300 + t)) for t in range(6)]
+        per_t = [lowrank_calls(hs[t], 8, sh.SAMPLE) for t in range(6)]
+        steps = []
+        for i in range(R):
+            seq = [per_t[t][i] for t in range(6)]
+
+            def step(seq=seq):
+                for c in seq:
+                    c()
+            step.keep = seq
+            steps.append(step)
+        o = run_leg("lowrank8x6", steps, 48, 6 * lowrank_bytes(8))
+        o["config"] = {"calls_per_step": 6, "rows_per_call": 8, "note": "gamma calls of B rows"}
     dense_bytes = lambda M: (V * d + M * d) * 2 + M * 12
     if "dense48" in legs:
         run_leg("dense48", dense_calls(h48, 48, sh.SAMPLE), 48, dense_bytes(48))
@@ -387,6 +410,9 @@ def main():
             o["config"] = {"kept_rows": n_keep}
         del WS
 
+    if "trimmedceiling" in legs:
+        line_extra["trimmed_ceiling"] = trimmed_ceiling(sh, synth, W, V, d, seeds, dev, bf)
+
     # position-adaptive rank: 8 sequences x 6 draft positions with ranks falling by position
     # (nested prefixes of the r = 512 pair); "s" = every position at rank <= 256 (half the columns)
     for name, sched in (("adaptive48", [512, 512, 384, 384, 256, 256]), ("adaptive48s", [256, 256, 192, 192, 128, 128])):
@@ -410,9 +436,12 @@ def main():
         o = run_leg(name, calls, 48, alg)
         o["config"] = {"ranks_by_position": sched, "columns_read": cols}
 
-    if "verify" in legs or "verifyg" in legs:
+    vsweep = [(sg, nm) for sg, nm in ((1.0, "verify"), (0.5, "verifys0.5"), (2.0, "verifys2")) if nm in legs]
+    if "verifyg" in legs and not any(sg == 1.0 for sg, _ in vsweep):
+        vsweep.insert(0, (1.0, None))
+    for sigma, vname in vsweep:
         vw = configs.VERIFY
-        inp = synth.verify_inputs(vw.B, vw.gamma, vw.V, 1.0, "bf16", vw.seeds)
+        inp = synth.verify_inputs(vw.B, vw.gamma, vw.V, sigma, "bf16", vw.seeds)
         tl = [bf(inp["target"])]
         dl = [bf(inp["draft"])]
         for _ in range(2):
@@ -420,8 +449,9 @@ def main():
             dl.append(dl[0].clone())
         toks = torch.from_numpy(inp["tokens"]).to(dev)
         u = torch.from_numpy(inp["u"]).to(dev)
-        for name, mode in (("verify", sh.SAMPLE), ("verifyg", sh.GREEDY)):
-            if name not in legs:
+        del inp
+        for name, mode in ((vname, sh.SAMPLE), ("verifyg" if sigma == 1.0 else None, sh.GREEDY)):
+            if name is None or name not in legs:
                 continue
             calls = []
             for i in range(3):
@@ -438,7 +468,8 @@ def main():
             rows_bytes = vw.B * (vw.gamma + 1) * vw.V * 2 + (vw.B * vw.gamma * vw.V * 2 if mode == sh.SAMPLE else 0)
             alg = rows_bytes + vw.B * vw.gamma * 8 + vw.B * (vw.gamma + 2) * 4
             o = run_leg(name, calls, vw.B * vw.gamma, alg, "draft tokens")
-            o["config"] = {"B": vw.B, "gamma": vw.gamma, "V": vw.V, "sigma": 1.0}
+            o["config"] = {"B": vw.B, "gamma": vw.gamma, "V": vw.V, "sigma": sigma}
+            o["acceptance"] = acceptance_stats(calls[0].keep[0], vw.gamma)
 
     if "verifysparse" in legs:
         vw = configs.VERIFY
@@ -535,12 +566,94 @@ def main():
         line["verify_sparse_tokens_per_s"] = results["verifysparse"]["tokens_per_s"]
     if "verifytree" in results:
         line["verify_tree_nodes_per_s"] = results["verifytree"]["tokens_per_s"]
+    line.update(line_extra)
+    if any(k.startswith("verify") and "acceptance" in v for k, v in results.items()):
+        line["verify_sigma_sweep"] = {str(v["config"]["sigma"]): {"us_per_call": v["us_per_call"],
+                                                                  "tokens_per_s": v["tokens_per_s"], **v["acceptance"]}
+                                      for k, v in results.items() if "acceptance" in v and k != "verifyg"}
     line["legs"] = {kk: {x: v for x, v in vv.items() if x != "kernels"} for kk, vv in results.items()}
     line["kernels_us"] = {kk: {kn: round(kv["avg_us"], 3) for kn, kv in vv.items()} for kk, vv in kernel_trace.items()}
 
     if head and not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(h48_np, Wd_np, Wu_np, seeds["philox"])
     print(json.dumps(line), flush=True)
+
+
+def acceptance_stats(acc_t, gamma):
+    """Accepted-draft statistics of one sampling verification call: mean accepted length a,
+    mean emitted tokens a + 1, the acceptance rate over attempted positions (a accepts out of
+    min(a + 1, gamma) tries per sequence), and the explainer's closed form for E[a + 1] at that
+    rate, (1 - alpha^(gamma + 1)) / (1 - alpha)."""
+    a = acc_t.detach().cpu().numpy().astype(np.float64)
+    tries = np.minimum(a + 1, gamma).sum()
+    alpha = float(a.sum() / tries) if tries else 0.0
+    closed = (1 - alpha ** (gamma + 1)) / (1 - alpha) if alpha < 1 else gamma + 1.0
+    return {"mean_accept_len": float(a.mean()), "mean_emitted": float(a.mean() + 1), "alpha_hat": alpha,
+            "closed_form_emitted_at_alpha_hat": closed}
+
+
+def trimmed_ceiling(sh, synth, W, V, d, seeds, dev, bf):
+    """The acceptance ceiling of a static trimmed vocabulary (SlimSpec write-up, section 二):
+    a draft supported on the kept ids S can be accepted at most with probability p(S).  Target
+    scores come from the dense head (the library's kernel, raw logits) for B sequences x
+    (gamma + 1) positions; the drafter is the trimmed head over the same 32768 kept ids as the
+    trimmed legs (its sampled tokens), with draft scores equal to the target's on S (the best a
+    trimmed drafter can do: q = p restricted to S, renormalised) or with N(0, 1) noise added on S;
+    both are verified by spec_verify.  Reports the mean p(S) over the attempted positions and
+    the acceptance rates measured through verification."""
+    import torch
+    B, gamma, n_keep = 512, 5, 32768
+    keep = np.sort(np.random.default_rng(seeds["weights"] + 77).choice(V, n_keep, replace=False)).astype(np.int32)
+    keep_t = torch.from_numpy(keep).to(dev)
+    rows = B * (gamma + 1)
+    h = bf(synth.hidden(rows, d, "bf16", seeds["hidden"] + 500))
+    z = torch.empty(rows, V, dtype=torch.float32, device=dev)
+    for r0 in range(0, rows, 192):
+        out = sh.draft_head_dense(h[r0:r0 + 192], W, want_logits=True, want_lse=False)
+        z[r0:r0 + 192] = out["logits"]
+    target = z.to(torch.bfloat16).view(B, gamma + 1, V).contiguous()
+    del z
+    lp = torch.log_softmax(target.float(), dim=-1)
+    pS = torch.logsumexp(lp[:, :, keep_t.long()], dim=-1).exp()          # [B, gamma + 1]
+    W_S = W.index_select(0, keep_t.long()).contiguous()
+    hd = h.view(B, gamma + 1, d)[:, :gamma].reshape(B * gamma, d).contiguous()
+    res = {"B": B, "gamma": gamma, "kept": n_keep, "V": V}
+    gnoise = torch.Generator(device="cpu").manual_seed(seeds["weights"] + 91)
+    for kind, noise in (("exact_on_S", 0.0), ("noisy_on_S", 1.0)):
+        draft = torch.full((B, gamma, V), float("-inf"), dtype=torch.bfloat16, device=dev)
+        ds = target[:, :gamma][:, :, keep_t.long()].float()
+        if noise:
+            ds = ds + noise * torch.randn(ds.shape, generator=gnoise).to(dev)
+        draft[:, :, keep_t.long()] = ds.to(torch.bfloat16)
+        # the drafter's tokens: sampled by the trimmed head (ids in S)
+        if noise:
+            # a noisy drafter samples from its own (noisy) scores: Gumbel-max over S
+            g = -torch.log(-torch.log(torch.rand(ds.shape, generator=gnoise).to(dev).clamp_min(1e-12)))
+            toks = keep_t[(ds + g).argmax(dim=-1)].to(torch.int32)
+        else:
+            toks = sh.draft_head_trimmed(hd, W_S, keep_t, mode="sample", seed=seeds["philox"], offset=7)["token"]
+            toks = toks.view(B, gamma).contiguous()
+        u = torch.from_numpy(synth.uniforms_open((B, gamma), seeds["philox"] + 13)).to(dev)
+        acc, _ = sh.spec_verify(target, draft.contiguous(), toks.view(B, gamma).contiguous(), u, mode="sample",
+                                seed=seeds["philox"], offset=3)
+        a = acc.cpu().numpy().astype(np.int64)
+        tried = np.minimum(a + 1, gamma)
+        ps = pS[:, :gamma].cpu().numpy()
+        mask = np.arange(gamma)[None, :] < tried[:, None]
+        res[kind] = {"alpha_hat": float(a.sum() / tried.sum()), "p_S_mean_over_tries": float(ps[mask].mean()),
+                     "tries": int(tried.sum())}
+    return res
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_baseline(h, Wd, Wu, seed):
@@ -558,7 +671,7 @@ def cpu_baseline(h, Wd, Wu, seed):
         heads.head_lowrank(h, Wd, Wu, "bf16", "sample", 1.0, seed, n)
         n += 1
     dt = time.time() - t0
-    return {"value": 48 * n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    return {"value": 48 * n / dt, "unit": "tokens/s", "cores": threads, "cpu_model": cpu_model(), "kind": "oracle",
             "sample": f"{n} full oracle calls of the headline workload (48 rows x V=128256, r=512, "
                       f"sampling), {dt:.1f} s on the host"}
 

@@ -218,11 +218,15 @@ __global__ __launch_bounds__(256) void k_verify_rows(VerifyArgs a) {
         float v[EPT];
         unpack<BF16>(buf[u], v);
         if (e < n) {
+          // logits of -inf (tokens a distribution excludes, e.g. outside a trimmed
+          // vocabulary) weigh zero: while every value so far is -inf the running sum stays 0
+          // (no -inf - -inf = NaN in the shift or the rescale)
           const float Mn = fmaxf(M, chunk_max<EPT>(v) * c);
+          const float off = Mn == -INFINITY ? 0.f : Mn;
           float cs = 0.f;
 #pragma unroll
-          for (int i = 0; i < EPT; ++i) cs += fast_exp2(fmaf(v[i], c, -Mn));
-          S = S * fast_exp2(M - Mn) + cs;
+          for (int i = 0; i < EPT; ++i) cs += fast_exp2(fmaf(v[i], c, -off));
+          S = (M == Mn ? S : S * fast_exp2(M - Mn)) + cs;
           M = Mn;
         }
       }

@@ -209,6 +209,9 @@ int draft_head_specvocab(const void* h, int64_t M, int64_t d, const void* W_down
  * SpecTr-GBV write-up: the first rejection ends the block, residual next token, bonus token).
  *   target_logits [B, gamma+1, V] dtype: target scores at the gamma+1 positions
  *   draft_logits  [B, gamma,   V] dtype: draft scores (SH_SAMPLE only; NULL for greedy)
+ *                 Scores may be -inf (a token of zero probability, e.g. outside a drafter's
+ *                 trimmed vocabulary); every row needs one finite score; NaN and +inf are
+ *                 not allowed.
  *   B <= 65535, 1 <= gamma <= 64, V <= 2^28
  *   draft_tokens  [B, gamma] int32: proposed ids; an id outside [0, V) is never accepted
  *   u_accept      [B, gamma] float in (0,1): accept uniforms (SH_SAMPLE only; else NULL)

@@ -96,3 +96,42 @@ def test_trimmed_kchunk_vocabulary_ends(mode):
     _check_outputs(got, want, "bf16", mode, 1.0, seed, 1, f"trimmed ends {mode}")
     if mode == "greedy":
         assert tok[0] == 0 and tok[1] == V - 1
+
+
+def test_acceptance_ceiling_through_verification():
+    """SlimSpec write-up, section 二: a drafter that can only propose the kept ids S is accepted
+    at most with probability p(S) -- with equality for the best such drafter, q = p restricted
+    to S and renormalised.  Target scores are the dense head's logits (the library's kernel),
+    the draft scores equal them on S (minus infinity elsewhere), the draft tokens are sampled by
+    the trimmed head over S, and spec_verify decides.  The acceptance frequency over B
+    sequences must match the mean p(S) (exact, from the oracle's float64 softmax of the same
+    target scores) within four binomial standard deviations."""
+    d, V, n, B, seed = 256, 4096, 1024, 4096, 29
+    rng = np.random.default_rng(seed)
+    ids = np.sort(rng.choice(V, n, replace=False)).astype(np.int32)
+    h = synth.hidden(2 * B, d, "bf16", seed)                    # positions 0 and 1 of B sequences
+    W = synth.dense_weights(V, d, "bf16", seed)
+    Wt = P.to_device(W, "bf16")
+    z = sh.draft_head_dense(P.to_device(h, "bf16"), Wt, want_logits=True, want_lse=False)["logits"]
+    target = z.to(torch.bfloat16).view(B, 2, V).contiguous()
+    ids_t = torch.from_numpy(ids).cuda()
+    draft = torch.full((B, 1, V), float("-inf"), dtype=torch.bfloat16, device="cuda")
+    draft[:, :, ids_t.long()] = target[:, :1, ids_t.long()]
+    h0 = P.to_device(np.ascontiguousarray(h.reshape(B, 2, d)[:, 0]), "bf16")
+    W_S = P.to_device(np.ascontiguousarray(W[ids]), "bf16")
+    toks = sh.draft_head_trimmed(h0, W_S, ids_t, mode="sample", seed=seed, offset=1)["token"]
+    assert np.all(np.isin(toks.cpu().numpy(), ids))
+    u = torch.from_numpy(synth.uniforms_open((B, 1), seed + 1)).cuda()
+    acc, _ = sh.spec_verify(target, draft.contiguous(), toks.view(B, 1).contiguous(), u, mode="sample", seed=seed)
+    torch.cuda.synchronize()
+    a = acc.cpu().numpy()
+    t0 = target[:, 0].float().cpu().numpy().astype(np.float64)
+    p = np.exp(t0 - t0.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    pS = p[:, ids].sum(axis=1)
+    ceiling = [heads.trimmed_acceptance_ceiling(p[b], ids) for b in range(4)]
+    np.testing.assert_allclose(ceiling, pS[:4], rtol=1e-12)
+    alpha = a.mean()
+    sd = np.sqrt(np.mean(pS * (1 - pS)) / B)
+    P.log(f"trimmed ceiling: accept frequency {alpha:.4f}, mean p(S) {pS.mean():.4f} (sd {sd:.4f})")
+    assert abs(alpha - pS.mean()) < 4 * sd + 2e-3

@@ -162,3 +162,28 @@ def test_verify_bit_identical_runs():
     a2, o2 = sh.spec_verify(d["target"], d["draft"], d["tokens"], d["u"], seed=5, offset=1)
     torch.cuda.synchronize()
     assert torch.equal(a1, a2) and torch.equal(o1, o2)
+
+
+@pytest.mark.parametrize("dtype,V", [("bf16", 4096), ("f32", 1000)])
+def test_draft_excluding_tokens(dtype, V):
+    """A draft that gives some tokens zero probability (-inf scores, as a drafter over a trimmed
+    vocabulary does for every token outside it; SlimSpec write-up, section 二): three quarters
+    of the vocabulary masked in every draft row, whole 8-element chunks of it included, and a
+    few masked target scores.  Draft tokens come from the masked draft distribution."""
+    B, gamma = 48, 4
+    seeds = {"logits": 61, "tokens": 62, "uniforms": 63}
+    rng = np.random.default_rng(64)
+    keep = np.sort(rng.choice(V, V // 4, replace=False))
+    masked = np.setdiff1d(np.arange(V), keep)
+    ninf = synth.store(np.array([-np.inf], np.float32), dtype)[0]
+
+    def mask(inp):
+        inp["draft"][:, :, masked] = ninf
+        inp["target"][:, :, masked[:5]] = ninf
+        d = fp.decode(inp["draft"], dtype)
+        g = np.random.default_rng(65).gumbel(size=d.shape)
+        inp["tokens"] = np.argmax(d + g, axis=-1).astype(np.int32)
+        assert np.all(np.isin(inp["tokens"], keep))
+
+    acc = _sample(B, gamma, V, 0.5, dtype, seeds, mutate=mask)
+    assert np.all(acc >= 0)
