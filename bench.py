@@ -70,6 +70,7 @@ KERNEL_SOURCES = ["drafter_lm_head_slimspec_amd/csrc/head_tile.hip",
 HEAD_KERNEL = "k_head_tile"
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic_head_tile_llama_lowrank_M48.json")
 COPY_MIB = 1024
+LEG_PMC_ARGS = "--steps 5 --warmup 1 --no-trace --no-cpu-baseline --legs lowrank48"
 COPY_LAUNCHES = 3
 
 
@@ -111,17 +112,12 @@ def traffic_summary(paths):
            "fetch_scale": fscale, "write_scale": wscale, "hbm_bytes_per_launch": hbm,
            "alg_bytes_per_launch": alg, "traffic_over_alg": hbm / alg,
            "commands": [
-               "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o run -- "
-               "python3 bench.py --legs lowrank48 --steps 10 --warmup 2 --no-trace --no-cpu-baseline",
-               "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o run -- "
-               "python3 bench.py --legs lowrank48 --steps 10 --warmup 2 --no-trace --no-cpu-baseline",
-               "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_copyF -o run -- "
-               f"python3 bench.py --copy-calibration {COPY_MIB}",
-               "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_copyW -o run -- "
-               f"python3 bench.py --copy-calibration {COPY_MIB}",
-               "python3 bench.py --traffic-summary gpurun_out/pmc_fetch/run_counter_collection.csv "
-               "gpurun_out/pmc_write/run_counter_collection.csv gpurun_out/pmc_copyF/run_counter_collection.csv "
-               "gpurun_out/pmc_copyW/run_counter_collection.csv"]}
+               f"rocprofv3 --pmc {c} --output-format csv -d {os.path.dirname(p)} -o run -- "
+               f"python3 bench.py {args}"
+               for c, p, args in (("FETCH_SIZE", fpath, LEG_PMC_ARGS), ("WRITE_SIZE", wpath, LEG_PMC_ARGS),
+                                  ("FETCH_SIZE", cfpath, f"--copy-calibration {COPY_MIB}"),
+                                  ("WRITE_SIZE", cwpath, f"--copy-calibration {COPY_MIB}"))]
+           + ["python3 bench.py --traffic-summary " + " ".join(paths)]}
     with open(TRAFFIC_JSON, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps({"hbm_bytes_per_launch": hbm, "traffic_over_alg": hbm / alg}))

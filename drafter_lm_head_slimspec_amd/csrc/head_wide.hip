@@ -248,12 +248,14 @@ __device__ __forceinline__ void wide_wave(const TileArgs& a, uint4* tile) {
 
   // the workgroup's groups are the consecutive range [gs, ge), taken in pairs (g, g + 1):
   // while a pair is multiplied out of the LDS tile, the next pair's rows are in flight in
-  // registers; storing a pair waits for every outstanding load, which is exactly that pair
-  // (past the range a cache-resident group is re-read)
+  // registers; storing a pair waits for every outstanding load, which is exactly that pair.
+  // Past the range the loads go to group NG, an empty buffer range: they return zeros and
+  // touch no memory (re-reading a group of the range would miss the cache by then: a range
+  // is ~0.5 MB and 32 workgroups share one XCD's L2)
   const int G = static_cast<int>(gridDim.x);
   const int gs = static_cast<int>((static_cast<int64_t>(blockIdx.x) * NG) / G);
   const int ge = static_cast<int>((static_cast<int64_t>(blockIdx.x + 1) * NG) / G);
-  auto clampg = [&](int g) { return g < ge ? g : gs; };
+  auto clampg = [&](int g) { return g < ge ? g : NG; };
   uint4 RA[PER], RB[PER];
   gload(clampg(gs), RA);
   gload(clampg(gs + 1), RB);
