@@ -18,6 +18,7 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 
 constexpr int kWave = 64;
+constexpr int kXcds = 8;   // accelerator complex dies: workgroup b of a launch runs on die b mod 8
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 

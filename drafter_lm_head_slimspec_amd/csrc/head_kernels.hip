@@ -274,8 +274,13 @@ __global__ __launch_bounds__(256) void k_rowdot_reduce(const float* __restrict__
 
 // ----------------------------------------------------------------------------------------
 // bf16 down-projection for at most kRdTileMaxM input rows, in one kernel:
-//   k_rowdot_tile    grid (ceil(R/16), ceil(M/16)): a workgroup of 8 waves owns a 16 x 16
-//                    output tile (16 rows of Wd by 16 input rows) over the whole of K.  K is
+//   k_rowdot_tile    one workgroup per 16 x 16 output tile (16 rows of Wd by 16 input rows),
+//                    ceil(R/16) * ceil(M/16) of them: a workgroup of 8 waves owns its tile
+//                    over the whole of K.  Workgroups are dealt to the 8 XCDs round-robin by
+//                    index, so the tiles are numbered Wd-tile-major and each XCD takes one
+//                    contiguous run of that order: it reads its eighth of Wd and all input
+//                    rows once (dealt in row-major order, every XCD read all of Wd and all
+//                    input rows whenever the tile columns were not a multiple of 8).  K is
 //                    walked in chunks of 512 elements; every chunk of both matrices is read
 //                    with whole 1 KB row segments per wave instruction (full cache lines),
 //                    all chunks of a batch of 8 issued up front, and passed through a
@@ -311,16 +316,25 @@ __global__ __launch_bounds__(kRdtThreads) void k_rowdot_tile(const void* __restr
   // [buffer][matrix 0 = Wd, 1 = x][row 0..15][piece slot], slot = piece ^ (row & 7)
   __shared__ uint4 tile[2][2][16][kRdtCpr];
   __shared__ float red[kRdtWaves][4][kWave];
+  const int nwg = static_cast<int>(gridDim.x);
   if (zero != nullptr) {
-    const int64_t nwg = static_cast<int64_t>(gridDim.x) * gridDim.y;
     const int64_t per = (zero_words + nwg - 1) / nwg;
-    const int64_t z0 = (static_cast<int64_t>(blockIdx.y) * gridDim.x + blockIdx.x) * per;
+    const int64_t z0 = static_cast<int64_t>(blockIdx.x) * per;
     const int64_t z1 = z0 + per < zero_words ? z0 + per : zero_words;
     for (int64_t i = z0 + threadIdx.x; i < z1; i += blockDim.x) zero[i] = 0u;
   }
   const int l = lane_id(), w = wave_id();
   const int tid = static_cast<int>(threadIdx.x);
-  const int j0 = blockIdx.x * 16, m0 = blockIdx.y * 16;
+  // workgroup b runs on XCD b mod 8 as its (b / 8)-th: XCD x owns tiles [start(x), start(x + 1))
+  // of the Wd-tile-major order, the first nwg mod 8 XCDs one tile more than the others
+  int ot;   // this workgroup's output tile
+  {
+    const int xcd = static_cast<int>(blockIdx.x) % kXcds, local = static_cast<int>(blockIdx.x) / kXcds;
+    const int base = nwg / kXcds, extra = nwg % kXcds;
+    ot = (xcd < extra ? xcd * (base + 1) : extra * (base + 1) + (xcd - extra) * base) + local;
+  }
+  const int mt = (M + 15) / 16;
+  const int j0 = (ot / mt) * 16, m0 = (ot % mt) * 16;
   const uint32_t rowbytes = static_cast<uint32_t>(K) * 2;
   const int jrows = R - j0 < 16 ? R - j0 : 16;
   const int mrows = M - m0 < 16 ? M - m0 : 16;
@@ -1342,7 +1356,7 @@ hipError_t launch_rowdot(const void* Wd, const void* x, int64_t R, int64_t K, in
   if (bf16 && M <= kRdTileMaxM) {
     RowRanks rk;
     for (int m = 0; m < kRdTileMaxM; ++m) rk.r[m] = static_cast<int32_t>(R);
-    const dim3 grid(static_cast<unsigned>((R + 15) / 16), static_cast<unsigned>((M + 15) / 16));
+    const dim3 grid(static_cast<unsigned>(((R + 15) / 16) * ((M + 15) / 16)));
     TraceScope ts("rowdot_tile", st);
     hipLaunchKernelGGL(k_rowdot_tile, grid, dim3(kRdtThreads), 0, st, Wd, x, static_cast<int>(R),
                        static_cast<int>(K), static_cast<int>(M), static_cast<uint16_t*>(out), zero, zero_words, rk);
@@ -1388,7 +1402,7 @@ hipError_t launch_rowdot_ranked(const void* Wd, const void* x, int64_t R, int64_
   if (M < 1 || M > kRdTileMaxM) return hipErrorInvalidValue;
   RowRanks rk;
   for (int m = 0; m < kRdTileMaxM; ++m) rk.r[m] = m < M ? ranks[m] : 0;
-  const dim3 grid(static_cast<unsigned>((R + 15) / 16), static_cast<unsigned>((M + 15) / 16));
+  const dim3 grid(static_cast<unsigned>(((R + 15) / 16) * ((M + 15) / 16)));
   TraceScope ts("rowdot_tile", st);
   hipLaunchKernelGGL(k_rowdot_tile, grid, dim3(kRdtThreads), 0, st, Wd, x, static_cast<int>(R),
                      static_cast<int>(K), static_cast<int>(M), static_cast<uint16_t*>(out), nullptr, int64_t{0}, rk);
