@@ -218,16 +218,26 @@ __global__ __launch_bounds__(256) void k_verify_rows(VerifyArgs a) {
         float v[EPT];
         unpack<BF16>(buf[u], v);
         if (e < n) {
-          // logits of -inf (tokens a distribution excludes, e.g. outside a trimmed
-          // vocabulary) weigh zero: while every value so far is -inf the running sum stays 0
-          // (no -inf - -inf = NaN in the shift or the rescale)
-          const float Mn = fmaxf(M, chunk_max<EPT>(v) * c);
-          const float off = Mn == -INFINITY ? 0.f : Mn;
-          float cs = 0.f;
+          // The chunk's exponentials against the running reference M, kept unless their
+          // sum is not below 2^64: a value more than 64 (log2 units) above M, M still -inf
+          // (before the first finite value, or -inf - -inf = NaN).  Only then is the chunk
+          // redone against a raised reference (its maximum) and the sum rescaled, so most
+          // chunks pay no maximum and no rescaling exponential; S stays below 2^64 per term
+          // and far from overflow.  Logits of -inf (tokens a distribution excludes, e.g.
+          // outside a trimmed vocabulary) weigh zero, and an all -inf prefix leaves S at 0.
+          float cs = fast_exp2(fmaf(v[0], c, -M));
 #pragma unroll
-          for (int i = 0; i < EPT; ++i) cs += fast_exp2(fmaf(v[i], c, -off));
-          S = (M == Mn ? S : S * fast_exp2(M - Mn)) + cs;
-          M = Mn;
+          for (int i = 1; i < EPT; ++i) cs += fast_exp2(fmaf(v[i], c, -M));
+          if (!(cs < 0x1p64f)) {
+            const float Mn = fmaxf(M, chunk_max<EPT>(v) * c);
+            const float off = Mn == -INFINITY ? 0.f : Mn;
+            cs = 0.f;
+#pragma unroll
+            for (int i = 0; i < EPT; ++i) cs += fast_exp2(fmaf(v[i], c, -off));
+            S = M == Mn ? S : S * fast_exp2(M - Mn);
+            M = Mn;
+          }
+          S += cs;
         }
       }
     });
