@@ -147,6 +147,28 @@ def pmc_summary(paths):
         print(f"| `{kn}` | {n} | " + " | ".join(cells) + " |")
 
 
+def read_bandwidth(sh, torch, dev, reps=10):
+    """Attainable HBM read rate: the library's flat read kernel over 1 GiB (four times the
+    Infinity Cache, so every read comes from HBM), timed with events around each launch."""
+    nbytes = 1 << 30
+    buf = torch.arange(nbytes // 4, dtype=torch.int32, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    for _ in range(2):
+        sh.read_probe(buf, sink)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        sh.read_probe(buf, sink)
+    e.record()
+    torch.cuda.synchronize()
+    us = 1000.0 * s.elapsed_time(e) / reps
+    del buf
+    return {"GBps": nbytes / (us * 1e-6) / 1e9, "bytes": nbytes, "us_per_read": us,
+            "kernel": "k_read_probe: 1024 x 256 threads, flat grid-stride 16-byte loads, 4 in flight per thread",
+            "reads": reps}
+
+
 def main():
     args = parse()
     if args.traffic_summary:
@@ -537,6 +559,11 @@ def main():
     if head:
         line["hbm_roofline_frac_call"] = head["hbm_frac"]
     # roofline of the dominant kernel: the W_up streaming kernel of the headline leg
+    rbw = read_bandwidth(sh, torch, dev)
+    log(f"  read bandwidth (1 GiB flat read) {rbw['GBps']:.0f} GB/s")
+    line["read_bandwidth"] = rbw
+    for v in results.values():   # each leg's algorithmic bytes per second against the measured read rate
+        v["frac_of_measured_read"] = v["alg_bytes"] / (v["ms_per_call"] / 1000.0) / (rbw["GBps"] * 1e9)
     if head and "kernels" in head:
         kname = next(k for k in ("head_tile", "head_kchunk", "head_wide", "stream_mfma", "stream_valu") if k in head["kernels"])
         kavg = head["kernels"][kname]["avg_us"]
@@ -549,7 +576,8 @@ def main():
                 traffic = t.get("hbm_bytes_per_launch")
         line["roofline"] = {"bound": "hbm", "kernel": kname, "achieved": achieved, "peak": HBM_PEAK_GBS,
                             "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                            "alg_bytes_per_launch": kbytes, "avg_launch_us": kavg}
+                            "alg_bytes_per_launch": kbytes, "avg_launch_us": kavg,
+                            "frac_of_measured_read": achieved / rbw["GBps"]}
     if "dense48" in results and head:
         line["nu_lowrank_vs_dense_M48"] = head["ms_per_call"] / results["dense48"]["ms_per_call"]
     if "dense6" in results and "lowrank6" in results:

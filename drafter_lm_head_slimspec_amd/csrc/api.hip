@@ -865,4 +865,16 @@ int sh_philox_uniform(uint64_t seed, uint64_t offset, uint32_t purpose, int64_t 
   return SH_OK;
 }
 
+int sh_read_probe(const void* buf, uint64_t bytes, uint32_t* sink, void* stream) {
+  g_last_error.clear();
+  SH_TRY(check_ptr(buf, "buf"));
+  if (sink == nullptr) return fail(SH_ERR_NULL, "sink is NULL");
+  if (!aligned(buf, 16)) return fail(SH_ERR_ALIGN, "buf is not 16-byte aligned");
+  if (!aligned(sink, 4)) return fail(SH_ERR_ALIGN, "sink is not 4-byte aligned");
+  if (bytes == 0 || bytes % 16 != 0 || bytes > 0xFFFFFFF0ull)
+    return fail(SH_ERR_SHAPE, "bytes must be a nonzero multiple of 16, at most 0xFFFFFFF0");
+  SH_HIP(sh::launch_read_probe(buf, bytes, sink, static_cast<hipStream_t>(stream)), "read probe kernel");
+  return SH_OK;
+}
+
 }  // extern "C"

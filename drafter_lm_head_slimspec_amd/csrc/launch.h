@@ -193,6 +193,9 @@ hipError_t launch_verify(const VerifyArgs& a, hipStream_t st);
 constexpr int kMaxTreeNodes = 1024;
 hipError_t launch_verify_tree(const VerifyArgs& a, hipStream_t st);
 
+// measurement helper: XOR of every 32-bit word of buf[0, bytes) into *sink (bytes a multiple of 16,
+// at most 0xFFFFFFF0), read in the flat grid-stride order
+hipError_t launch_read_probe(const void* buf, uint64_t bytes, uint32_t* sink, hipStream_t st);
 hipError_t launch_philox(uint64_t seed, uint64_t offset, uint32_t purpose, int64_t rows, int64_t n,
                          float* out, hipStream_t st);
 

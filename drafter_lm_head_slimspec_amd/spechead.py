@@ -56,6 +56,7 @@ _SIGS = {
                                 _vp, _vp, _sz, _vp]),
     "sh_topk": (_i, [_vp, _i64, _i64, _i64, _vp, _vp, _sz, _vp]),
     "sh_philox_uniform": (_i, [_u64, _u64, ctypes.c_uint32, _i64, _i64, _vp, _vp]),
+    "sh_read_probe": (_i, [_vp, _u64, _vp, _vp]),
     "sh_trace_enable": (_i, [_i64]),
     "sh_trace_read": (_i, [ctypes.c_char_p, _sz]),
     "sh_status_str": (ctypes.c_char_p, [_i]),
@@ -367,6 +368,14 @@ def philox_uniform(seed, offset, purpose, rows, n, device):
     _check(lib.sh_philox_uniform(int(seed), int(offset), int(purpose), rows, n, _p(out),
                                  _stream(device)))
     return out
+
+
+def read_probe(buf, sink):
+    """XOR of every 32-bit word of the device tensor `buf` into the int32 device word `sink`
+    (a measurement helper: the flat read whose rate is the attainable HBM read bandwidth)."""
+    lib = load()
+    nbytes = buf.numel() * buf.element_size()
+    _check(lib.sh_read_probe(_p(buf), nbytes, _p(sink), _stream(buf.device)))
 
 
 def trace_enable(max_records=65536):

@@ -301,6 +301,18 @@ int sh_philox_uniform(uint64_t seed, uint64_t offset, uint32_t purpose, int64_t 
                       float* out, void* stream);
 
 /*
+ * Measurement helper, not a step of the method: reads the `bytes` bytes at device address buf
+ * with 16-byte loads in the flat order (1024 workgroups of 256 threads striding over the
+ * buffer, four loads in flight per thread) and XORs every 32-bit word into *sink (a device
+ * word the caller zeroes first), so that no load can be skipped and the result does not depend
+ * on order.  Timed on a buffer larger than the 256 MB Infinity Cache it gives the attainable
+ * HBM read rate, the bench's second denominator beside the 8 TB/s peak.  bytes: a nonzero
+ * multiple of 16, at most 0xFFFFFFF0; buf 16-byte aligned, sink 4-byte aligned.  Returns SH_ERR_*
+ * before any launch on invalid arguments; asynchronous on `stream`.
+ */
+int sh_read_probe(const void* buf, uint64_t bytes, uint32_t* sink, void* stream);
+
+/*
  * Opt-in kernel timing (tracing).  sh_trace_enable(n) creates 2n host-side event objects and,
  * from then on, brackets every kernel this library launches with two events recorded on the
  * launch stream (at most n launches until the next read); n = 0 disables and frees them.

@@ -225,6 +225,16 @@ def test_topk_and_philox_validation(lib):
     assert lib.sh_philox_uniform(0, 0, 0, 1, 10, None, None) == sh.SH_ERR_NULL
 
 
+@no_gpu
+def test_read_probe_validation(lib):
+    assert lib.sh_read_probe(None, 1024, C, None) == sh.SH_ERR_NULL
+    assert lib.sh_read_probe(A, 1024, None, None) == sh.SH_ERR_NULL
+    assert lib.sh_read_probe(ctypes.c_void_p(A.value + 4), 1024, C, None) == sh.SH_ERR_ALIGN
+    assert lib.sh_read_probe(A, 1024, ctypes.c_void_p(C.value + 2), None) == sh.SH_ERR_ALIGN
+    for nbytes in (0, 1000, 0xFFFFFFF0 + 16):
+        assert lib.sh_read_probe(A, nbytes, C, None) == sh.SH_ERR_SHAPE
+
+
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(FileNotFoundError):
         sh.load(str(tmp_path / "missing.so"))
