@@ -101,16 +101,21 @@ __device__ __forceinline__ void block_argmax(float& v, int32_t& i, Partial* red4
 // Software-pipelined walk over [0, n) in spans of UNR chunks: the next span's loads are in
 // flight while the current one is processed (ping-pong buffers; past n the loads are
 // out-of-range, which costs no memory traffic, and proc sees chunks with e >= n).
-template <int UNR, typename Load, typename Proc>
-__device__ __forceinline__ void pipelined(uint32_t n, uint32_t span, Load load, Proc proc) {
+template <int UNR, typename Load, typename Proc, typename Pre>
+__device__ __forceinline__ void pipelined(uint32_t n, uint32_t span, Load load, Proc proc, Pre pre) {
   uint4 A[UNR], B[UNR];
   load(A, 0u);
+  pre();   // work that needs none of the data, done while the first loads are in flight
   for (uint32_t base = 0; base < n; base += 2 * span) {
     load(B, base + span);
     proc(A, base);
     load(A, base + 2 * span);
     proc(B, base + span);
   }
+}
+template <int UNR, typename Load, typename Proc>
+__device__ __forceinline__ void pipelined(uint32_t n, uint32_t span, Load load, Proc proc) {
+  pipelined<UNR>(n, span, load, proc, [] {});
 }
 
 // Max of the EPT values of one 16-byte chunk.
@@ -409,6 +414,7 @@ __global__ __launch_bounds__(256) void k_verify_resid(VerifyArgs a) {
   __shared__ Partial red4[4];
   __shared__ int sh_a;
   __shared__ float gw[RG];                             // log2 weight of each group of the round
+  __shared__ float gg[RG];                             // Gumbel of each group of the round
   __shared__ float qs[SPARSE ? RG * kGroup : 1];       // sparse draft: q over the round's span
   const int s2 = blockIdx.x;
   const int64_t b = blockIdx.y;
@@ -488,6 +494,21 @@ __global__ __launch_bounds__(256) void k_verify_resid(VerifyArgs a) {
         __syncthreads();
       }
     }
+    const int64_t ga = g_first + r0 / kGroup;                 // first group of the round
+    const int64_t gb = ga + (rn + kGroup - 1) / kGroup;       // one past the last
+    // the round's group Gumbels depend only on (seed, offset, purpose, b, group): one Philox
+    // block per four consecutive groups, computed while the round's first loads are in flight
+    auto gumbels = [&] {
+      for (int64_t q = ga / 4 + tid; q * 4 < gb; q += blockDim.x) {
+        uint64_t words[4];
+        philox_block(a.seed, a.offset, purpose, static_cast<uint64_t>(b), static_cast<uint64_t>(q) * 4, words);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int64_t gi = q * 4 + j;
+          if (gi >= ga && gi < gb) gg[gi - ga] = gumbel(word_to_uniform(words[j]));
+        }
+      }
+    };
     pipelined<2 * UNR>(rn, step * UNR, [&](uint4 (&buf)[2 * UNR], uint32_t base) { load(buf, r0 + base); },
                        [&](uint4 (&buf)[2 * UNR], uint32_t base) {
 #pragma unroll
@@ -523,25 +544,14 @@ __global__ __launch_bounds__(256) void k_verify_resid(VerifyArgs a) {
         for (int o = 1; o < LPG; o <<= 1) gr += xor_lane(gr, o);
         if (in && (l % LPG) == 0) gw[e / kGroup] = gr > 0.f ? gm + log2f(gr) : -INFINITY;
       }
-    });
+    }, gumbels);
     __syncthreads();
-    // ... then one Philox block per four consecutive groups, all threads at once
-    const int64_t ga = g_first + r0 / kGroup;                 // first group of the round
-    const int64_t gb = ga + (rn + kGroup - 1) / kGroup;       // one past the last
-    for (int64_t q = ga / 4 + tid; q * 4 < gb; q += blockDim.x) {
-      uint64_t words[4];
-      philox_block(a.seed, a.offset, purpose, static_cast<uint64_t>(b), static_cast<uint64_t>(q) * 4, words);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int64_t gi = q * 4 + j;
-        if (gi >= ga && gi < gb) {
-          const float lw = gw[gi - ga];
-          if (lw != -INFINITY)
-            argmax_merge(best.gscore, best.g, lw * kLn2 + gumbel(word_to_uniform(words[j])), static_cast<int32_t>(gi));
-        }
-      }
+    // ... then the group scores L_g + Gumbel(u_g), all threads at once
+    for (int64_t gi = ga + tid; gi < gb; gi += blockDim.x) {
+      const float lw = gw[gi - ga];
+      if (lw != -INFINITY) argmax_merge(best.gscore, best.g, lw * kLn2 + gg[gi - ga], static_cast<int32_t>(gi));
     }
-    __syncthreads();   // gw is rewritten by the next round
+    __syncthreads();   // gw and gg are rewritten by the next round
   }
   block_argmax(best.gscore, best.g, red4);   // only the group draw is carried
   if (threadIdx.x == 0) {
