@@ -39,7 +39,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--legs", default="all",
                    help="comma list of legs (lowrank48,lowrank48g,lowrank6,lowrank48logits,lowrank8x6,dense48,"
-                        "dense6,specvocab1,specvocab16,verify,verifys0.5,verifys2,verifyg,verifysparse,verifytree,"
+                        "dense6,specvocab1,specvocab16,specvocabq1,specvocabq16,verify,verifys0.5,verifys2,verifyg,verifysparse,verifytree,"
                         "adaptive48,adaptive48s,trimmed48,trimmed6,trimmedceiling,gptoss192) or 'all' "
                         "or 'headline'")
     p.add_argument("--rotate", type=int, default=5, help="device copies of each weight set")
@@ -203,7 +203,7 @@ def main():
     seeds = w.seeds
     legs_all = ["lowrank48", "lowrank48g", "lowrank6", "lowrank48logits", "lowrank8x6", "gptoss192", "adaptive48",
                 "adaptive48s", "dense48", "dense6", "trimmed48", "trimmed6", "trimmedceiling",
-                "specvocab1", "specvocab16",
+                "specvocab1", "specvocab16", "specvocabq1", "specvocabq16",
                 "verify", "verifys0.5", "verifys2", "verifyg", "verifysparse", "verifytree"]
     if args.legs == "all":
         legs = legs_all
@@ -228,7 +228,7 @@ def main():
         Wu.append(Wu[0].clone())
     h48 = bf(h48_np)
     h6 = bf(h6_np)
-    need_dense = any(x.startswith(("dense", "specvocab", "trimmed")) for x in legs)
+    need_dense = any(x.startswith(("dense", "trimmed")) or x in ("specvocab1", "specvocab16") for x in legs)
     W = bf(synth.dense_weights(V, d, "bf16", seeds["weights"])) if need_dense else None
     log(f"  inputs ready in {time.time() - t0:.1f}s")
 
@@ -339,40 +339,53 @@ def main():
     if "dense6" in legs:
         run_leg("dense6", dense_calls(h6, 6, sh.SAMPLE), 6, dense_bytes(6))
 
-    if any(x.startswith("specvocab") for x in legs):
-        Wdp_np, Wv_np, _ = synth.specvocab_weights(V, d, dp, "bf16", seeds["weights"], with_U=False)
+    def specvocab_legs(prefix, wl, Vs, Uw):
+        """SpecVocab at vocabulary size Vs (d, d', k of workload wl), exact rows from Uw [Vs, d]."""
+        Wdp_np, Wv_np, _ = synth.specvocab_weights(Vs, wl.d, wl.dprime, "bf16", wl.seeds["weights"], with_U=False)
         Wdp = [bf(Wdp_np)]
         Wv = [bf(Wv_np)]
         for _ in range(R):
             Wdp.append(Wdp[0].clone())
             Wv.append(Wv[0].clone())
         for M in (1, 16):
-            name = f"specvocab{M}"
+            name = f"{prefix}{M}"
             if name not in legs:
                 continue
             calls, union_rows = [], []
             for i in range(R + 1):
-                hi = bf(synth.hidden(M, d, "bf16", seeds["hidden"] + 100 + i))
-                idx = torch.empty(M, k, dtype=torch.int32, device=dev)
-                zl = torch.empty(M, k, dtype=torch.float32, device=dev)
-                q = torch.empty(M, k, dtype=torch.float32, device=dev)
+                hi = bf(synth.hidden(M, wl.d, "bf16", wl.seeds["hidden"] + 100 + i))
+                idx = torch.empty(M, wl.k, dtype=torch.int32, device=dev)
+                zl = torch.empty(M, wl.k, dtype=torch.float32, device=dev)
+                q = torch.empty(M, wl.k, dtype=torch.float32, device=dev)
                 tok = torch.empty(M, dtype=torch.int32, device=dev)
                 lse = torch.empty(M, dtype=torch.float32, device=dev)
                 lp = torch.empty(M, dtype=torch.float32, device=dev)
-                need = sh.load().sh_head_workspace_bytes(sh.OP_SPECVOCAB, M, d, dp, V, k)
+                need = sh.load().sh_head_workspace_bytes(sh.OP_SPECVOCAB, M, wl.d, wl.dprime, Vs, wl.k)
                 ws = torch.zeros(need, dtype=torch.uint8, device=dev)
-                c = sh.prepared("draft_head_specvocab", hi, M, d, Wdp[i], dp, Wv[i], W, V, k, sh.SH_BF16,
-                                sh.SAMPLE, 1.0, seeds["philox"], i, idx, zl, q, tok, lse, lp, ws, need,
-                                torch.cuda.current_stream().cuda_stream)
+                c = sh.prepared("draft_head_specvocab", hi, M, wl.d, Wdp[i], wl.dprime, Wv[i], Uw, Vs, wl.k,
+                                sh.SH_BF16, sh.SAMPLE, 1.0, wl.seeds["philox"], i, idx, zl, q, tok, lse, lp, ws,
+                                need, torch.cuda.current_stream().cuda_stream)
                 c.keep = (hi, idx, zl, q, tok, lse, lp, ws)
                 c()
                 torch.cuda.synchronize()
                 union_rows.append(len(np.unique(idx.cpu().numpy())))
                 calls.append(c)
             u = float(np.mean(union_rows))
-            alg = (dp * d + V * dp) * 2 + u * d * 2 + M * d * 2 + M * k * 12
+            alg = (wl.dprime * wl.d + Vs * wl.dprime) * 2 + u * wl.d * 2 + M * wl.d * 2 + M * wl.k * 12
             out = run_leg(name, calls, M, alg)
             out["union_rows"] = u
+            out["config"] = {"workload": wl.name if Vs == wl.V else f"specvocab at V={Vs}", "d": wl.d, "V": Vs,
+                             "dprime": wl.dprime, "k": wl.k, "rows": M}
+
+    # SpecVocab at the Llama vocabulary (the headline's V = 128256) ...
+    if any(x in legs for x in ("specvocab1", "specvocab16")):
+        specvocab_legs("specvocab", w, V, W)
+    # ... and at the Qwen3-8B shape (V = 151936), its exact rows from a V x d matrix of that size
+    if any(x in legs for x in ("specvocabq1", "specvocabq16")):
+        qw = configs.QWEN
+        WQ = bf(synth.dense_weights(qw.V, qw.d, "bf16", qw.seeds["weights"]))
+        specvocab_legs("specvocabq", qw, qw.V, WQ)
+        del WQ
 
     # GPT-OSS-20B-shaped low-rank head: d 2880, V 201088, r 360, 32 sequences x 6 = 192 rows, T 0.7
     if "gptoss192" in legs:
