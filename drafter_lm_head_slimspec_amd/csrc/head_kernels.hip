@@ -274,9 +274,11 @@ __global__ __launch_bounds__(256) void k_rowdot_reduce(const float* __restrict__
 
 // ----------------------------------------------------------------------------------------
 // bf16 down-projection for at most kRdTileMaxM input rows, in one kernel:
-//   k_rowdot_tile    one workgroup per 16 x 16 output tile (16 rows of Wd by 16 input rows),
-//                    ceil(R/16) * ceil(M/16) of them: a workgroup of 8 waves owns its tile
-//                    over the whole of K.  Workgroups are dealt to the 8 XCDs round-robin by
+//   k_rowdot_tile    one workgroup per JR x MR output tile (JR rows of Wd by MR input rows,
+//                    8 or 16 each, chosen per shape so the pass fills the CUs with the least
+//                    per-workgroup reading), ceil(R/JR) * ceil(M/MR) of them: a workgroup of 8
+//                    waves owns its tile over the whole of K (a tile narrower than the
+//                    16 x 16 MFMA leaves the rest of the product unused).  Workgroups are dealt to the 8 XCDs round-robin by
 //                    index, so the tiles are numbered Wd-tile-major and each XCD takes one
 //                    contiguous run of that order: it reads its eighth of Wd and all input
 //                    rows once (dealt in row-major order, every XCD read all of Wd and all
@@ -294,8 +296,6 @@ constexpr int kRdtWaves = 8;
 constexpr int kRdtThreads = kRdtWaves * kWave;
 constexpr int kRdtChunk = 512;                      // elements of K per chunk
 constexpr int kRdtCpr = kRdtChunk * 2 / 16;         // 16-byte pieces per row per chunk (64)
-constexpr int kRdtPieces = 2 * 16 * kRdtCpr;        // W and x pieces per chunk (2048)
-constexpr int kRdtPerThread = kRdtPieces / kRdtThreads;   // 4
 constexpr int kRdtBatch = 8;                        // chunks whose loads are in flight together
 constexpr int64_t kRdTileMaxM = 256;
 static_assert(kRdTileMaxM >= kRowdotRanksMaxM, "one rank per row of a one-pass launch");
@@ -308,12 +308,16 @@ struct RowRanks {
   int32_t r[kRdTileMaxM];
 };
 
+template <int JR, int MR>
 __global__ __launch_bounds__(kRdtThreads) void k_rowdot_tile(const void* __restrict__ Wd,
                                                              const void* __restrict__ x, int R, int K, int M,
                                                              uint16_t* __restrict__ out,
                                                              uint32_t* __restrict__ zero, int64_t zero_words,
                                                              RowRanks rk) {
-  // [buffer][matrix 0 = Wd, 1 = x][row 0..15][piece slot], slot = piece ^ (row & 7)
+  static_assert((JR == 8 || JR == 16) && (MR == 8 || MR == 16), "tile rows");
+  constexpr int PER = (JR + MR) / 8;   // 16-byte pieces per thread per chunk
+  // [buffer][matrix 0 = Wd, 1 = x][row 0..15][piece slot], slot = piece ^ (row & 7); rows past
+  // JR (Wd) or MR (x) are never written: they only feed outputs that are not stored
   __shared__ uint4 tile[2][2][16][kRdtCpr];
   __shared__ float red[kRdtWaves][4][kWave];
   const int nwg = static_cast<int>(gridDim.x);
@@ -333,27 +337,28 @@ __global__ __launch_bounds__(kRdtThreads) void k_rowdot_tile(const void* __restr
     const int base = nwg / kXcds, extra = nwg % kXcds;
     ot = (xcd < extra ? xcd * (base + 1) : extra * (base + 1) + (xcd - extra) * base) + local;
   }
-  const int mt = (M + 15) / 16;
-  const int j0 = (ot / mt) * 16, m0 = (ot % mt) * 16;
+  const int mt = (M + MR - 1) / MR;
+  const int j0 = (ot / mt) * JR, m0 = (ot % mt) * MR;
   const uint32_t rowbytes = static_cast<uint32_t>(K) * 2;
-  const int jrows = R - j0 < 16 ? R - j0 : 16;
-  const int mrows = M - m0 < 16 ? M - m0 : 16;
+  const int jrows = R - j0 < JR ? R - j0 : JR;
+  const int mrows = M - m0 < MR ? M - m0 : MR;
   const rsrc_t rs[2] = {make_rsrc(static_cast<const char*>(Wd) + static_cast<size_t>(j0) * rowbytes,
                                   static_cast<uint32_t>(jrows) * rowbytes),
                         make_rsrc(static_cast<const char*>(x) + static_cast<size_t>(m0) * rowbytes,
                                   static_cast<uint32_t>(mrows) * rowbytes)};
   const int nc = (K + kRdtChunk - 1) / kRdtChunk;
-  // piece i of this thread in a chunk: matrix, row and piece index within the row's 1 KB
-  // (pieces i * 512 + tid: two per matrix, each wave one row's 64 pieces)
-  static_assert(kRdtThreads == 8 * kRdtCpr && kRdtPerThread == 4, "piece layout");
+  // piece i of this thread in a chunk: the chunk's rows are the JR rows of Wd then the MR rows of
+  // x, 64 pieces (1 KB) each; piece i * 512 + tid is row 8 i + tid / 64 (one row per wave)
+  static_assert(kRdtThreads == 8 * kRdtCpr, "piece layout");
   auto piece = [&](int i, int& mat, int& row, int& pc) {
-    mat = i >> 1;
-    row = (i & 1) * 8 + tid / kRdtCpr;
+    const int gr = 8 * i + tid / kRdtCpr;
+    mat = gr < JR ? 0 : 1;
+    row = gr < JR ? gr : gr - JR;
     pc = tid % kRdtCpr;
   };
-  auto issue = [&](int c, uint4 (&v)[kRdtPerThread]) {
+  auto issue = [&](int c, uint4 (&v)[PER]) {
 #pragma unroll
-    for (int i = 0; i < kRdtPerThread; ++i) {
+    for (int i = 0; i < PER; ++i) {
       int mat, row, pc;
       piece(i, mat, row, pc);
       const int k = c * kRdtChunk + pc * 8;
@@ -364,7 +369,7 @@ __global__ __launch_bounds__(kRdtThreads) void k_rowdot_tile(const void* __restr
   rd_f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
   const int row = l & 15, q = l >> 4;
   for (int cb = 0; cb < nc; cb += kRdtBatch) {
-    uint4 v[kRdtBatch][kRdtPerThread];
+    uint4 v[kRdtBatch][PER];
 #pragma unroll
     for (int c = 0; c < kRdtBatch; ++c) issue(cb + c, v[c]);
 #pragma unroll
@@ -372,7 +377,7 @@ __global__ __launch_bounds__(kRdtThreads) void k_rowdot_tile(const void* __restr
       if (cb + c < nc) {   // uniform over the workgroup
         const int buf = c & 1;
 #pragma unroll
-        for (int i = 0; i < kRdtPerThread; ++i) {
+        for (int i = 0; i < PER; ++i) {
           int mat, rr, pc;
           piece(i, mat, rr, pc);
           tile[buf][mat][rr][pc ^ (rr & 7)] = v[c][i];
@@ -398,9 +403,10 @@ __global__ __launch_bounds__(kRdtThreads) void k_rowdot_tile(const void* __restr
     float sum = red[0][v][ll];
 #pragma unroll
     for (int ww = 1; ww < kRdtWaves; ++ww) sum += red[ww][v][ll];
-    const int j = j0 + 4 * (ll >> 4) + v;
-    const int m = m0 + (ll & 15);
-    if (j < R && m < M) out[static_cast<int64_t>(m) * R + j] = j < rk.r[m] ? f32_to_bf16_rne(sum) : uint16_t{0};
+    const int jj = 4 * (ll >> 4) + v, mm = ll & 15;
+    const int j = j0 + jj, m = m0 + mm;
+    if (jj < JR && mm < MR && j < R && m < M)
+      out[static_cast<int64_t>(m) * R + j] = j < rk.r[m] ? f32_to_bf16_rne(sum) : uint16_t{0};
   }
 }
 
@@ -1339,6 +1345,47 @@ static hipError_t run_rowdot_mfma(const void* Wd, const void* x, int R, int K, i
   return hipGetLastError();
 }
 
+// Tile shape of the one-pass down-projection: JR rows of Wd by MR input rows per workgroup.
+// Smaller tiles cut what each workgroup reads (the pass is bound by per-CU ingest and latency,
+// not by its MFMAs) at the price of more workgroups and re-reads that the L2 serves.
+template <int JR, int MR>
+hipError_t run_rowdot_tile_shape(const void* Wd, const void* x, int64_t R, int64_t K, int64_t M, uint16_t* out,
+                                 uint32_t* zero, int64_t zero_words, const RowRanks& rk, hipStream_t st) {
+  const dim3 grid(static_cast<unsigned>(((R + JR - 1) / JR) * ((M + MR - 1) / MR)));
+  TraceScope ts("rowdot_tile", st);
+  hipLaunchKernelGGL((k_rowdot_tile<JR, MR>), grid, dim3(kRdtThreads), 0, st, Wd, x, static_cast<int>(R),
+                     static_cast<int>(K), static_cast<int>(M), out, zero, zero_words, rk);
+  return hipGetLastError();
+}
+
+// The shape with the most workgroups that still fit one per CU (fewer bytes per workgroup on
+// ties); when every shape has more, the one with the fewest.  Measured (event-timed pass):
+// 48 x 512 rows 10.7 -> 9.5 us with 16 x 8 tiles, 6 x 512 9.9 -> 8.1 and 16 x 256 11.7 -> 8.8
+// with 8 x 8; at 192 x 360 the 16 x 16 tiles stay best (13.8 against 15.9 with 8 x 8).
+hipError_t run_rowdot_tile(const void* Wd, const void* x, int64_t R, int64_t K, int64_t M, uint16_t* out,
+                           uint32_t* zero, int64_t zero_words, const RowRanks& rk, hipStream_t st) {
+  DeviceInfo di;
+  if (device_info(&di) != hipSuccess) di.cus = 256;
+  static constexpr int kShapes[4][2] = {{8, 8}, {16, 8}, {8, 16}, {16, 16}};
+  int best = -1;
+  int64_t best_n = 0;
+  for (int i = 0; i < 4; ++i) {
+    const int64_t n = ((R + kShapes[i][0] - 1) / kShapes[i][0]) * ((M + kShapes[i][1] - 1) / kShapes[i][1]);
+    const bool fits = n <= di.cus;
+    const bool better = best < 0 || (fits && (best_n > di.cus || n > best_n)) || (!fits && best_n > di.cus && n < best_n);
+    if (better) {
+      best = i;
+      best_n = n;
+    }
+  }
+  switch (best) {
+    case 0: return run_rowdot_tile_shape<8, 8>(Wd, x, R, K, M, out, zero, zero_words, rk, st);
+    case 1: return run_rowdot_tile_shape<16, 8>(Wd, x, R, K, M, out, zero, zero_words, rk, st);
+    case 2: return run_rowdot_tile_shape<8, 16>(Wd, x, R, K, M, out, zero, zero_words, rk, st);
+    default: return run_rowdot_tile_shape<16, 16>(Wd, x, R, K, M, out, zero, zero_words, rk, st);
+  }
+}
+
 size_t rowdot_scratch_bytes(int64_t M, int64_t R, int64_t K) {
   return static_cast<size_t>(rowdot_ksplit(K)) * static_cast<size_t>(M * R) * 4;
 }
@@ -1356,11 +1403,7 @@ hipError_t launch_rowdot(const void* Wd, const void* x, int64_t R, int64_t K, in
   if (bf16 && M <= kRdTileMaxM) {
     RowRanks rk;
     for (int m = 0; m < kRdTileMaxM; ++m) rk.r[m] = static_cast<int32_t>(R);
-    const dim3 grid(static_cast<unsigned>(((R + 15) / 16) * ((M + 15) / 16)));
-    TraceScope ts("rowdot_tile", st);
-    hipLaunchKernelGGL(k_rowdot_tile, grid, dim3(kRdtThreads), 0, st, Wd, x, static_cast<int>(R),
-                       static_cast<int>(K), static_cast<int>(M), static_cast<uint16_t*>(out), zero, zero_words, rk);
-    return hipGetLastError();
+    return run_rowdot_tile(Wd, x, R, K, M, static_cast<uint16_t*>(out), zero, zero_words, rk, st);
   }
   if (bf16) {
     const int ncb = static_cast<int>((M + 31) / 32) < 6 ? static_cast<int>((M + 31) / 32) : 6;
@@ -1402,11 +1445,7 @@ hipError_t launch_rowdot_ranked(const void* Wd, const void* x, int64_t R, int64_
   if (M < 1 || M > kRdTileMaxM) return hipErrorInvalidValue;
   RowRanks rk;
   for (int m = 0; m < kRdTileMaxM; ++m) rk.r[m] = m < M ? ranks[m] : 0;
-  const dim3 grid(static_cast<unsigned>(((R + 15) / 16) * ((M + 15) / 16)));
-  TraceScope ts("rowdot_tile", st);
-  hipLaunchKernelGGL(k_rowdot_tile, grid, dim3(kRdtThreads), 0, st, Wd, x, static_cast<int>(R),
-                     static_cast<int>(K), static_cast<int>(M), static_cast<uint16_t*>(out), nullptr, int64_t{0}, rk);
-  return hipGetLastError();
+  return run_rowdot_tile(Wd, x, R, K, M, static_cast<uint16_t*>(out), nullptr, int64_t{0}, rk, st);
 }
 
 template <bool BF16, int MB, int LPR, bool ONE>
