@@ -278,11 +278,12 @@ __global__ __launch_bounds__(256) void k_rowdot_reduce(const float* __restrict__
 //                    8 or 16 each, chosen per shape so the pass fills the CUs with the least
 //                    per-workgroup reading), ceil(R/JR) * ceil(M/MR) of them: a workgroup of 8
 //                    waves owns its tile over the whole of K (a tile narrower than the
-//                    16 x 16 MFMA leaves the rest of the product unused).  Workgroups are dealt to the 8 XCDs round-robin by
-//                    index, so the tiles are numbered Wd-tile-major and each XCD takes one
-//                    contiguous run of that order: it reads its eighth of Wd and all input
-//                    rows once (dealt in row-major order, every XCD read all of Wd and all
-//                    input rows whenever the tile columns were not a multiple of 8).  K is
+//                    16 x 16 MFMA leaves the rest of the product unused).  Workgroups are
+//                    dealt to the 8 XCDs round-robin by index, so the tiles are numbered
+//                    Wd-tile-major and each XCD takes one contiguous run of that order: it
+//                    reads its eighth of Wd and all input rows once (dealt in row-major
+//                    order, every XCD read all of Wd and all input rows whenever the tile
+//                    columns were not a multiple of 8).  K is
 //                    walked in chunks of 512 elements; every chunk of both matrices is read
 //                    with whole 1 KB row segments per wave instruction (full cache lines),
 //                    all chunks of a batch of 8 issued up front, and passed through a
