@@ -105,30 +105,36 @@ __device__ __forceinline__ void wide_wave(const TileArgs& a, uint4* tile) {
   float rm = -INFINITY, rsum = 0.f, gbest = -INFINITY, bz = -INFINITY;
   int32_t gid = 0x7fffffff, bi = 0x7fffffff;
 
-  // Gumbel(u) of this lane's row for groups 4 q .. 4 q + 3: one Philox block holds all four,
-  // and a workgroup walks consecutive groups, so one block serves four of them
-  float gc[4] = {0.f, 0.f, 0.f, 0.f};
-  int gq = -1;
+  // Gumbel(u) of activation row m for group g: one Philox block holds groups 4 q .. 4 q + 3,
+  // and a workgroup walks consecutive groups, so thread m of the workgroup computes each block
+  // once (gumbel_blocks) into gtab[q mod 2][m][0..3], read here by the wave owning row m
+  float* gtab = reinterpret_cast<float*>(tile + 2 * kGroup * RS + kWave);   // [2][kWideMaxRows][4]
   auto draw = [&](int g) -> float {
     float gu = 0.f;
     if constexpr (STATS) {
       const int m = row_of(qd);
-      if (a.sample != 0) {
-        if ((g >> 2) != gq) {   // uniform over the workgroup
-          gq = g >> 2;
-          if (qd < NCBW && m < Mx) {
-            uint64_t wd[4];
-            philox_block(a.seed, a.offset, kDraftGroup, static_cast<uint64_t>(a.row0 + m),
-                         static_cast<uint64_t>(gq) * 4, wd);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) gc[i] = gumbel(word_to_uniform(wd[i]));
-          }
-        }
-        const int gi = g & 3;
-        gu = gi == 0 ? gc[0] : gi == 1 ? gc[1] : gi == 2 ? gc[2] : gc[3];
-      }
+      if (a.sample != 0 && qd < NCBW && m < Mx) gu = gtab[((g >> 2) & 1) * kWideMaxRows * 4 + m * 4 + (g & 3)];
     }
     return gu;
+  };
+  // the blocks of groups g and g + 1 not computed yet (q_done: the last block computed)
+  int q_done = -1;
+  auto gumbel_blocks = [&](int g) {
+    if constexpr (STATS) {
+      if (a.sample != 0) {
+        for (int q = g >> 2; q <= ((g + 1) >> 2); ++q) {   // uniform over the workgroup
+          if (q <= q_done) continue;
+          q_done = q;
+          if (tid < Mx) {
+            uint64_t wd[4];
+            philox_block(a.seed, a.offset, kDraftGroup, static_cast<uint64_t>(a.row0 + tid),
+                         static_cast<uint64_t>(q) * 4, wd);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) gtab[(q & 1) * kWideMaxRows * 4 + tid * 4 + i] = gumbel(word_to_uniform(wd[i]));
+          }
+        }
+      }
+    }
   };
   // z = tile half x this wave's activation fragments.  Per k-step the four tiles' A fragments
   // are one batch of LDS reads, issued a k-step ahead of the 4 * NCBW MFMAs that use them
@@ -260,9 +266,10 @@ __device__ __forceinline__ void wide_wave(const TileArgs& a, uint4* tile) {
   gload(clampg(gs), RA);
   gload(clampg(gs + 1), RB);
   for (int g = gs; g < ge; g += 2) {
-    __syncthreads();   // every wave is done with the previous pair's tile
+    __syncthreads();   // every wave is done with the previous pair's tile (and Gumbels)
     gstore(RA, 0);
     gstore(RB, 1);
+    gumbel_blocks(g);   // a block is overwritten only two blocks later, after its last group
     __syncthreads();
     gload(clampg(g + 2), RA);
     gload(clampg(g + 3), RB);
@@ -293,7 +300,9 @@ __device__ __forceinline__ void wide_wave(const TileArgs& a, uint4* tile) {
 
 template <int KS, int EPI>
 __global__ __launch_bounds__(kWideThreads, 1) void k_head_wide(TileArgs a) {
-  extern __shared__ uint4 tile[];   // [2][64][RS] the current pair of groups, then 64 spare chunks
+  // [2][64][RS] the current pair of groups, 64 spare chunks, then the Gumbel table
+  // [2][kWideMaxRows][4] floats
+  extern __shared__ uint4 tile[];
   const int w = wave_id();
   const int nb = (a.M + 15) / 16;   // column blocks, at most 2 * kWideWaves
   if constexpr (KS < 16) {   // rows of 512 elements: at most 128 activation rows, one block per wave
@@ -312,7 +321,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void k_head_wide(TileArgs a) {
 namespace {
 
 int wide_ks(int64_t K) { return static_cast<int>((K + 127) / 128) * 4; }   // 4, 8, 12 or 16
-int wide_lds(int ks) { return (2 * kGroup * (ks * 4 + 2) + kWave) * 16; }
+int wide_lds(int ks) { return (2 * kGroup * (ks * 4 + 2) + kWave) * 16 + 2 * kWideMaxRows * 4 * 4; }
 // VGPRs per lane of a two-block wave: activation fragments, two row buffers (eight waves share
 // each group's loads), accumulators, offsets and state
 int wide_regs(int ncbw, int ks) { return ks * ncbw * 4 + 2 * (ks / 2) * 4 + 16 * ncbw + ks + 64; }
