@@ -275,10 +275,11 @@ __global__ __launch_bounds__(256) void k_rowdot_reduce(const float* __restrict__
 // ----------------------------------------------------------------------------------------
 // bf16 down-projection for at most kRdTileMaxM input rows, in one kernel:
 //   k_rowdot_tile    one workgroup per JR x MR output tile (JR rows of Wd by MR input rows,
-//                    8 or 16 each, chosen per shape so the pass fills the CUs with the least
-//                    per-workgroup reading), ceil(R/JR) * ceil(M/MR) of them: a workgroup of 8
-//                    waves owns its tile over the whole of K (a tile narrower than the
-//                    16 x 16 MFMA leaves the rest of the product unused).  Workgroups are
+//                    8 or 16 of Wd by 8, 16 or 32 of x, chosen per shape so the pass fills the
+//                    CUs with the least per-workgroup reading), ceil(R/JR) * ceil(M/MR) of
+//                    them: a workgroup of 8 waves owns its tile over the whole of K (a tile
+//                    narrower than the 16 x 16 MFMA leaves the rest of the product unused; 32
+//                    input rows are two MFMA column blocks sharing each Wd fragment).  Workgroups are
 //                    dealt to the 8 XCDs round-robin by index, so the tiles are numbered
 //                    Wd-tile-major and each XCD takes one contiguous run of that order: it
 //                    reads its eighth of Wd and all input rows once (dealt in row-major
@@ -315,12 +316,14 @@ __global__ __launch_bounds__(kRdtThreads) void k_rowdot_tile(const void* __restr
                                                              uint16_t* __restrict__ out,
                                                              uint32_t* __restrict__ zero, int64_t zero_words,
                                                              RowRanks rk) {
-  static_assert((JR == 8 || JR == 16) && (MR == 8 || MR == 16), "tile rows");
+  static_assert((JR == 8 || JR == 16) && (MR == 8 || MR == 16 || MR == 32), "tile rows");
   constexpr int PER = (JR + MR) / 8;   // 16-byte pieces per thread per chunk
-  // [buffer][matrix 0 = Wd, 1 = x][row 0..15][piece slot], slot = piece ^ (row & 7); rows past
-  // JR (Wd) or MR (x) are never written: they only feed outputs that are not stored
-  __shared__ uint4 tile[2][2][16][kRdtCpr];
-  __shared__ float red[kRdtWaves][4][kWave];
+  constexpr int MB = MR > 16 ? 2 : 1;  // 16-column MFMA blocks of the input rows
+  // [buffer][tile row][piece slot], slot = piece ^ (row & 7): rows 0..15 hold Wd, rows 16 + 16 b
+  // .. hold block b of x; rows past JR (Wd) or MR (x) are never written: they only feed outputs
+  // that are not stored
+  __shared__ uint4 tile[2][16 + 16 * MB][kRdtCpr];
+  __shared__ float red[kRdtWaves][MB][4][kWave];
   const int nwg = static_cast<int>(gridDim.x);
   if (zero != nullptr) {
     const int64_t per = (zero_words + nwg - 1) / nwg;
@@ -357,6 +360,7 @@ __global__ __launch_bounds__(kRdtThreads) void k_rowdot_tile(const void* __restr
     row = gr < JR ? gr : gr - JR;
     pc = tid % kRdtCpr;
   };
+  auto slot_row = [&](int mat, int row) { return mat == 0 ? row : 16 + row; };
   auto issue = [&](int c, uint4 (&v)[PER]) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
@@ -367,7 +371,9 @@ __global__ __launch_bounds__(kRdtThreads) void k_rowdot_tile(const void* __restr
                                                       : kOutOfRange);
     }
   };
-  rd_f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  rd_f32x4_t acc[MB];
+#pragma unroll
+  for (int b = 0; b < MB; ++b) acc[b] = rd_f32x4_t{0.f, 0.f, 0.f, 0.f};
   const int row = l & 15, q = l >> 4;
   for (int cb = 0; cb < nc; cb += kRdtBatch) {
     uint4 v[kRdtBatch][PER];
@@ -381,30 +387,35 @@ __global__ __launch_bounds__(kRdtThreads) void k_rowdot_tile(const void* __restr
         for (int i = 0; i < PER; ++i) {
           int mat, rr, pc;
           piece(i, mat, rr, pc);
-          tile[buf][mat][rr][pc ^ (rr & 7)] = v[c][i];
+          tile[buf][slot_row(mat, rr)][pc ^ (rr & 7)] = v[c][i];
         }
         __syncthreads();
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           const int pc = (2 * w + t) * 4 + q;   // k-step 2w + t of the chunk, lane quarter q
-          const uint4 a = tile[buf][0][row][pc ^ (row & 7)];
-          const uint4 b = tile[buf][1][row][pc ^ (row & 7)];
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
-                                                        acc, 0, 0, 0);
+          const uint4 a = tile[buf][row][pc ^ (row & 7)];
+#pragma unroll
+          for (int b = 0; b < MB; ++b) {
+            const uint4 bx = tile[buf][16 + 16 * b + row][pc ^ (row & 7)];
+            acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                             __builtin_bit_cast(bf16x8_t, bx), acc[b], 0, 0, 0);
+          }
         }
       }
     }
   }
-  // lane l holds rows j0 + 4 (l / 16) + v of column m0 + l % 16
+  // lane l holds rows j0 + 4 (l / 16) + v of column m0 + 16 b + l % 16 (block b)
 #pragma unroll
-  for (int v = 0; v < 4; ++v) red[w][v][l] = acc[v];
+  for (int b = 0; b < MB; ++b)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) red[w][b][v][l] = acc[b][v];
   __syncthreads();
-  if (threadIdx.x < 4 * kWave) {
-    const int v = threadIdx.x / kWave, ll = threadIdx.x % kWave;
-    float sum = red[0][v][ll];
+  if (threadIdx.x < MB * 4 * kWave) {
+    const int b = threadIdx.x / (4 * kWave), v = (threadIdx.x / kWave) % 4, ll = threadIdx.x % kWave;
+    float sum = red[0][b][v][ll];
 #pragma unroll
-    for (int ww = 1; ww < kRdtWaves; ++ww) sum += red[ww][v][ll];
-    const int jj = 4 * (ll >> 4) + v, mm = ll & 15;
+    for (int ww = 1; ww < kRdtWaves; ++ww) sum += red[ww][b][v][ll];
+    const int jj = 4 * (ll >> 4) + v, mm = 16 * b + (ll & 15);
     const int j = j0 + jj, m = m0 + mm;
     if (jj < JR && mm < MR && j < R && m < M)
       out[static_cast<int64_t>(m) * R + j] = j < rk.r[m] ? f32_to_bf16_rne(sum) : uint16_t{0};
@@ -1362,15 +1373,16 @@ hipError_t run_rowdot_tile_shape(const void* Wd, const void* x, int64_t R, int64
 // The shape with the most workgroups that still fit one per CU (fewer bytes per workgroup on
 // ties); when every shape has more, the one with the fewest.  Measured (event-timed pass):
 // 48 x 512 rows 10.7 -> 9.5 us with 16 x 8 tiles, 6 x 512 9.9 -> 8.1 and 16 x 256 11.7 -> 8.8
-// with 8 x 8; at 192 x 360 the 16 x 16 tiles stay best (13.8 against 15.9 with 8 x 8).
+// with 8 x 8; at 192 x 360 the 16 x 32 tiles (138 workgroups) take 12.1 us where the 276
+// 16 x 16 tiles, some CUs running two in turn, took 13.6 (and 8 x 8 tiles 15.9).
 hipError_t run_rowdot_tile(const void* Wd, const void* x, int64_t R, int64_t K, int64_t M, uint16_t* out,
                            uint32_t* zero, int64_t zero_words, const RowRanks& rk, hipStream_t st) {
   DeviceInfo di;
   if (device_info(&di) != hipSuccess) di.cus = 256;
-  static constexpr int kShapes[4][2] = {{8, 8}, {16, 8}, {8, 16}, {16, 16}};
+  static constexpr int kShapes[5][2] = {{8, 8}, {16, 8}, {8, 16}, {16, 16}, {16, 32}};
   int best = -1;
   int64_t best_n = 0;
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < 5; ++i) {
     const int64_t n = ((R + kShapes[i][0] - 1) / kShapes[i][0]) * ((M + kShapes[i][1] - 1) / kShapes[i][1]);
     const bool fits = n <= di.cus;
     const bool better = best < 0 || (fits && (best_n > di.cus || n > best_n)) || (!fits && best_n > di.cus && n < best_n);
@@ -1383,7 +1395,8 @@ hipError_t run_rowdot_tile(const void* Wd, const void* x, int64_t R, int64_t K, 
     case 0: return run_rowdot_tile_shape<8, 8>(Wd, x, R, K, M, out, zero, zero_words, rk, st);
     case 1: return run_rowdot_tile_shape<16, 8>(Wd, x, R, K, M, out, zero, zero_words, rk, st);
     case 2: return run_rowdot_tile_shape<8, 16>(Wd, x, R, K, M, out, zero, zero_words, rk, st);
-    default: return run_rowdot_tile_shape<16, 16>(Wd, x, R, K, M, out, zero, zero_words, rk, st);
+    case 3: return run_rowdot_tile_shape<16, 16>(Wd, x, R, K, M, out, zero, zero_words, rk, st);
+    default: return run_rowdot_tile_shape<16, 32>(Wd, x, R, K, M, out, zero, zero_words, rk, st);
   }
 }
 

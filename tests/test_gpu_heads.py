@@ -132,6 +132,7 @@ LOWRANK_WIDE = [
     (512, 9000, 256, 130, "bf16"),
     (256, 5000, 512, 100, "bf16"),
     (512, 7000, 200, 256, "bf16"),
+    (384, 6000, 384, 180, "bf16"),
 ]
 
 
