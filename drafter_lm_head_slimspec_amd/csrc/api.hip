@@ -83,7 +83,7 @@ int check_opt_out(const void* p, const char* name) {
 // Top-k scratch: the counter block (cleared at the start of each call) first, then the
 // candidates and the bitmask.
 struct TopkLayout {
-  size_t hist_off, count_off, cand_off, mask_off, total;
+  size_t hist_off, count_off, hist2_off, cand_off, mask_off, total;
 };
 
 TopkLayout topk_layout(int64_t M, int64_t V) {
@@ -92,7 +92,9 @@ TopkLayout topk_layout(int64_t M, int64_t V) {
   L.hist_off = off;
   off += static_cast<size_t>(M) * 4096 * 4;
   L.count_off = off;
-  off = align_up(off + static_cast<size_t>(M) * sh::kTkCounterStride * 4, 256);
+  off += static_cast<size_t>(M) * sh::kTkCounterStride * 4;
+  L.hist2_off = off;   // (hist, count and hist2 are one block the call clears)
+  off = align_up(off + static_cast<size_t>(M) * 4096 * 4, 256);
   L.cand_off = off;
   off = align_up(off + static_cast<size_t>(M * V) * 8, 256);
   L.mask_off = off;
@@ -112,6 +114,7 @@ sh::TopkArgs topk_args(void* ws, const TopkLayout& L, const float* scores, int64
   a.chunks = sh::topk_chunks(V);
   a.hist = reinterpret_cast<uint32_t*>(b + L.hist_off);
   a.count = reinterpret_cast<uint32_t*>(b + L.count_off);
+  a.hist2 = reinterpret_cast<uint32_t*>(b + L.hist2_off);
   a.cand = reinterpret_cast<uint2*>(b + L.cand_off);
   a.mask = reinterpret_cast<uint64_t*>(b + L.mask_off);
   a.out = out;

@@ -130,16 +130,17 @@ hipError_t launch_stream(const StreamArgs& a, bool use_mfma, int* producers, hip
 hipError_t launch_head_finalize(const FinalizeArgs& f, hipStream_t st);
 
 // SpecVocab pieces
-// Top-k of [M, V] float scores.  hist and count (contiguous, topk_counter_words(M) words
-// from hist) must be zero when the top-k kernels start; cand and mask are scratch.
+// Top-k of [M, V] float scores.  hist, count and hist2 (contiguous, topk_counter_words(M)
+// words from hist) must be zero when the top-k kernels start; cand and mask are scratch.
 struct TopkArgs {
   const float* scores;  // [M, V]
   int64_t V;
   int k;
   int M;
   int chunks;           // topk_chunks(V) workgroups per row
-  uint32_t* hist;       // [M, 4096]
+  uint32_t* hist;       // [M, 4096] key bits 31..20 of every score
   uint32_t* count;      // [M, kTkCounterStride] (one 128-byte line per row)
+  uint32_t* hist2;      // [M, 4096] key bits 19..8 of the scores in the threshold bin
   uint2* cand;          // [M, V]
   uint64_t* mask;       // [M, ceil(V / 64)]
   int32_t* out;         // [M, k] ascending ids
@@ -148,7 +149,7 @@ struct TopkArgs {
 constexpr int64_t kTopkMaxV = int64_t{1} << 19;  // finishing bitmasks live in LDS
 int topk_chunks(int64_t V);
 constexpr int kTkCounterStride = 32;
-inline int64_t topk_counter_words(int64_t M) { return M * 4096 + M * kTkCounterStride; }
+inline int64_t topk_counter_words(int64_t M) { return M * 4096 * 2 + M * kTkCounterStride; }
 hipError_t launch_zero(uint32_t* p, int64_t words, hipStream_t st);
 size_t topk_finish_lds(int64_t V);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st);

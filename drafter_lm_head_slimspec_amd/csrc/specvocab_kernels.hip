@@ -19,12 +19,14 @@ namespace sh {
 //   k_topk_select  grid (chunks, M): every workgroup finds the threshold bin b* (the bin
 //                  where the count of larger keys reaches k) from the row histogram, marks
 //                  its chunk's keys above b* in the row's selection bitmask (one 64-bit word
-//                  per 64 scores) and appends the keys inside b* to the row's candidate list
-//                  (one counter update per workgroup).
-//   k_topk_finish  one workgroup per row: resolves the candidates on the remaining 20 key
-//                  bits (two 10-bit histogram passes), takes the lowest ids among keys equal
-//                  to the final threshold and compacts the bitmask into ascending ids.
-//   The histogram and the candidate counter are cleared by an earlier kernel of the call.
+//                  per 64 scores), appends the keys inside b* to the row's candidate list
+//                  (one counter update per workgroup) and adds them to the row's histogram of
+//                  key bits 19..8; the row's first workgroup records b* and the count above.
+//   k_topk_finish  one workgroup per row: finds the bin of key bits 19..8 from the second
+//                  histogram, resolves the remaining 8 bits over the candidates in one
+//                  histogram pass, takes the lowest ids among keys equal to the final
+//                  threshold and compacts the bitmask into ascending ids.
+//   The histograms and the candidate counter are cleared by an earlier kernel of the call.
 //   Kernel boundaries order the phases: an in-kernel hand-off between workgroups would need
 //   a device-scope release per workgroup, which writes back the issuing XCD's L2.
 // ----------------------------------------------------------------------------------------
@@ -32,6 +34,8 @@ constexpr int kTkThreads = 256;
 constexpr int kTkPerThread = 8;
 constexpr int kTkChunk = kTkThreads * kTkPerThread;
 constexpr int kTkWaves = kTkThreads / kWave;
+constexpr int kTkShift2 = 8;         // second level: key bits 19..8
+constexpr uint32_t kTkDirect = 512;  // in-bin keys of a workgroup added to the second histogram one by one
 
 __global__ __launch_bounds__(kTkThreads) void k_topk_hist(TopkArgs a) {
   __shared__ uint32_t h[kTkBins];
@@ -119,6 +123,7 @@ __global__ __launch_bounds__(kTkThreads) void k_topk_select(TopkArgs a) {
   __shared__ uint32_t wcnt[kTkWaves];
   __shared__ uint32_t res[2];
   __shared__ uint32_t wbase;
+  __shared__ uint32_t h2l[kTkBins];   // second-level counts when a chunk holds many in-bin keys
   const int m = blockIdx.y;
   const int tid = threadIdx.x, l = lane_id(), w = wave_id();
   const int64_t V = a.V;
@@ -152,6 +157,10 @@ __global__ __launch_bounds__(kTkThreads) void k_topk_select(TopkArgs a) {
   uint64_t* mask = a.mask + static_cast<size_t>(m) * mw;
   uint2* cand = a.cand + static_cast<size_t>(m) * V;
   uint32_t* count = a.count + static_cast<size_t>(m) * kTkCounterStride;
+  if (blockIdx.x == 0 && tid == 0) {   // for the finish: b* and the count above it
+    count[4] = bstar;
+    count[5] = above;
+  }
   uint64_t bcs[kTkPerThread];
   uint32_t keys[kTkPerThread];
   uint32_t mine = 0u;
@@ -169,10 +178,25 @@ __global__ __launch_bounds__(kTkThreads) void k_topk_select(TopkArgs a) {
   }
   if (l == 0) wcnt[w] = mine;
   __syncthreads();
-  if (tid == 0) {
-    uint32_t tot = 0u;
-    for (int i = 0; i < kTkWaves; ++i) tot += wcnt[i];
-    wbase = tot != 0u ? atomicAdd(count, tot) : 0u;
+  uint32_t tot = 0u;
+  for (int i = 0; i < kTkWaves; ++i) tot += wcnt[i];
+  if (tid == 0) wbase = tot != 0u ? atomicAdd(count, tot) : 0u;
+  // the in-bin keys' bits 19..8 into the row's second histogram: one device atomic per key,
+  // or through LDS counts when the chunk holds many (a row of equal scores)
+  uint32_t* h2 = a.hist2 + static_cast<size_t>(m) * kTkBins;
+  if (tot <= kTkDirect) {
+#pragma unroll
+    for (int j = 0; j < kTkPerThread; ++j)
+      if ((bcs[j] >> l) & 1ull) atomicAdd(&h2[(keys[j] >> kTkShift2) & (kTkBins - 1)], 1u);
+  } else {   // uniform over the workgroup
+    for (int i = tid; i < kTkBins; i += kTkThreads) h2l[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kTkPerThread; ++j)
+      if ((bcs[j] >> l) & 1ull) atomicAdd(&h2l[(keys[j] >> kTkShift2) & (kTkBins - 1)], 1u);
+    __syncthreads();
+    for (int i = tid; i < kTkBins; i += kTkThreads)
+      if (h2l[i] != 0u) atomicAdd(&h2[i], h2l[i]);
   }
   __syncthreads();
   uint32_t base = wbase;
@@ -198,6 +222,7 @@ __global__ __launch_bounds__(kTkThreads) void k_topk_select(TopkArgs a) {
 constexpr int kTfThreads = 1024;
 constexpr int kTfWaves = kTfThreads / kWave;
 constexpr int kTfBatch = 8;   // words (candidates) each thread loads per round trip
+constexpr int kTfSpec = 2;    // candidates per thread loaded before their count is known
 typedef uint32_t tf_u32x2_t __attribute__((ext_vector_type(2)));
 
 // Finish of row m by the NT threads of a workgroup.  LDS: fin = sel[nw], tie[nw],
@@ -205,8 +230,8 @@ typedef uint32_t tf_u32x2_t __attribute__((ext_vector_type(2)));
 template <int NT>
 __device__ void topk_finish_row(const TopkArgs& a, int m, int cand_cap, uint32_t* fin, uint32_t* wsum, uint32_t* res,
                                 uint32_t* nties_p) {
-  constexpr int HB = kTkBins / NT;    // row-histogram bins per thread
-  constexpr int PB = 1024 / NT;       // pass-histogram bins per thread
+  constexpr int HB = kTkBins / NT;    // second-histogram bins per thread
+  static_assert(HB >= 4 && HB % 4 == 0, "second-histogram bins per thread");
   constexpr int aux = 0;
   uint32_t& nties = *nties_p;
   const int tid = threadIdx.x;
@@ -218,11 +243,21 @@ __device__ void topk_finish_row(const TopkArgs& a, int m, int cand_cap, uint32_t
   uint32_t* tie = fin + nw;
   uint32_t* h1 = fin + 2 * nw;
   uint2* cl = reinterpret_cast<uint2*>(fin + 2 * nw + 1024);
-  // loads that depend on nothing, issued together: the row histogram, the candidate count and
-  // the bitmask (kTfBatch words per thread per round trip)
+  // loads that depend on nothing, issued together: the first candidates (before their count is
+  // known; the row's list has room for V), the second histogram, the count line (candidate
+  // count, threshold bin b*, count above b*) and the bitmask (kTfBatch words per thread per
+  // round trip)
+  const uint2* cg = a.cand + static_cast<size_t>(m) * V;
+  const rsrc_t crow = make_rsrc(cg, static_cast<uint32_t>(V) * 8u);
+  tf_u32x2_t sv[kTfSpec];
+#pragma unroll
+  for (int q = 0; q < kTfSpec; ++q) {
+    const int64_t i = static_cast<int64_t>(q) * NT + tid;
+    sv[q] = __builtin_amdgcn_raw_buffer_load_b64(crow, i < V ? static_cast<uint32_t>(i) * 8u : kOutOfRange, 0, aux);
+  }
   uint32_t hb[HB];
   {
-    const uint4* hq = reinterpret_cast<const uint4*>(a.hist + static_cast<size_t>(m) * kTkBins) + tid * (HB / 4);
+    const uint4* hq = reinterpret_cast<const uint4*>(a.hist2 + static_cast<size_t>(m) * kTkBins) + tid * (HB / 4);
 #pragma unroll
     for (int q = 0; q < HB / 4; ++q) {
       const uint4 t = hq[q];
@@ -232,7 +267,9 @@ __device__ void topk_finish_row(const TopkArgs& a, int m, int cand_cap, uint32_t
       hb[4 * q + 3] = t.w;
     }
   }
-  uint32_t C = a.count[static_cast<size_t>(m) * kTkCounterStride];
+  const uint32_t* line = a.count + static_cast<size_t>(m) * kTkCounterStride;
+  uint32_t C = line[0];
+  const uint32_t bstar = line[4], above = line[5];
   {
     const rsrc_t mr = make_rsrc(a.mask + static_cast<size_t>(m) * mw, static_cast<uint32_t>(nw) * 4u);
     auto batch = [&](int i0) {
@@ -251,15 +288,20 @@ __device__ void topk_finish_row(const TopkArgs& a, int m, int cand_cap, uint32_t
         }
       }
     };
-    batch(0);   // (the first batch outside the loop: its loads go out with the two above)
+    batch(0);   // (the first batch outside the loop: its loads go out with the ones above)
     for (int i0 = kTfBatch * NT; i0 < nw; i0 += kTfBatch * NT) batch(i0);
   }
   if (C > static_cast<uint64_t>(V)) C = static_cast<uint32_t>(V);
-  const uint2* cg = a.cand + static_cast<size_t>(m) * V;
   const rsrc_t cr = make_rsrc(cg, C * 8u);
   const bool in_lds = C <= static_cast<uint32_t>(cand_cap);
   if (in_lds) {
-    // the candidates, staged into LDS kTfBatch per thread per round trip
+    // the candidates into LDS: the first ones are in registers already, the rest kTfBatch per
+    // thread per round trip
+#pragma unroll
+    for (int q = 0; q < kTfSpec; ++q) {
+      const uint32_t i = static_cast<uint32_t>(q * NT + tid);
+      if (i < C) cl[i] = make_uint2(sv[q].x, sv[q].y);
+    }
     auto batch = [&](uint32_t i0) {
       tf_u32x2_t v[kTfBatch];
 #pragma unroll
@@ -273,8 +315,7 @@ __device__ void topk_finish_row(const TopkArgs& a, int m, int cand_cap, uint32_t
         if (i < C) cl[i] = make_uint2(v[q].x, v[q].y);
       }
     };
-    batch(0);
-    for (uint32_t i0 = kTfBatch * NT; i0 < C; i0 += kTfBatch * NT) batch(i0);
+    for (uint32_t i0 = kTfSpec * NT; i0 < C; i0 += kTfBatch * NT) batch(i0);
   }
   // a candidate from LDS, or from the global list when it did not fit (uniform branch: LDS
   // reads stay LDS reads)
@@ -284,26 +325,24 @@ __device__ void topk_finish_row(const TopkArgs& a, int m, int cand_cap, uint32_t
     return make_uint2(v.x, v.y);
   };
   if (tid == 0) nties = 0u;
-  find_crossing<HB>(hb, k, wsum, res);   // includes a barrier: LDS stores above are visible
-  const uint32_t bstar = res[0];
-  uint32_t need = k - res[1];
+  // key bits 19..8 from the second histogram (the select kernel's counts of the b* keys)
+  uint32_t need = k - above;
   uint32_t thr = bstar << kTkShift;
-  // two 10-bit passes over the candidates: key bits 19..10, then 9..0
-  for (int pass = 0; pass < 2; ++pass) {
-    const int shift = pass == 0 ? 10 : 0;
-#pragma unroll
-    for (int i = 0; i < PB; ++i) h1[PB * tid + i] = 0u;
-    __syncthreads();
-    for (uint32_t i = tid; i < C; i += NT) {
-      const uint32_t key = cand_at(i).x;
-      if (pass == 0 || ((key >> 10) & 1023u) == ((thr >> 10) & 1023u)) atomicAdd(&h1[(key >> shift) & 1023u], 1u);
-    }
-    __syncthreads();
-    uint32_t c[PB];
-#pragma unroll
-    for (int i = 0; i < PB; ++i) c[i] = h1[PB * tid + i];
-    find_crossing<PB>(c, need, wsum, res);
-    thr |= res[0] << shift;
+  find_crossing<HB>(hb, need, wsum, res);   // includes a barrier: LDS stores above are visible
+  thr |= res[0] << kTkShift2;
+  need -= res[1];
+  // key bits 7..0: one histogram pass over the candidates in that bin
+  if (tid < 256) h1[tid] = 0u;
+  __syncthreads();
+  for (uint32_t i = tid; i < C; i += NT) {
+    const uint32_t key = cand_at(i).x;
+    if ((key >> kTkShift2) == (thr >> kTkShift2)) atomicAdd(&h1[key & 255u], 1u);
+  }
+  __syncthreads();
+  {
+    const uint32_t c1[1] = {tid < 256 ? h1[tid] : 0u};
+    find_crossing<1>(c1, need, wsum, res);
+    thr |= res[0];
     need -= res[1];
   }
   // keys above the threshold are in; keys equal to it are in if all are needed, else they

@@ -121,13 +121,16 @@ def test_qwen_specvocab_full(M, mode):
 
 @pytest.mark.parametrize("V,k", [(5, 3), (64, 64), (2049, 100), (4097, 2048), (30000, 1)])
 def test_topk_edge_shapes(V, k):
-    """Shapes at the chunk and 64-score segment boundaries, a single score, k = V."""
-    M = 4
+    """Shapes at the chunk and 64-score segment boundaries, a single score, k = V; a row whose
+    scores share their top 12 key bits and differ in every lower bit (each level of the threshold
+    search decides)."""
+    M = 5
     rng = np.random.default_rng(7 * V + k)
     s = rng.standard_normal((M, V)).astype(np.float32)
     s[1] = -np.abs(s[1]) * 1e30                    # negative only, large magnitudes
     s[2] = 1.5                                     # every score equal: the lowest k ids
     s[3, ::3] = s[3, 0]                            # a third of the row tied with one value
+    s[4] = rng.permutation(np.float32(1.0) + np.arange(V, dtype=np.float32) * np.float32(2.0 ** -23))
     P.log(f"topk edge M={M} V={V} k={k}")
     got = sh.topk(torch.from_numpy(s).cuda(), k).cpu().numpy()
     for m in range(M):
