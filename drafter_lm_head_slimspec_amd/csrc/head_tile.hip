@@ -66,7 +66,17 @@ struct TilePass {
   // activations, which other waves may still read when a wave's first group ends) or the
   // histograms [kTileHistRows][4096] (HIST)
   static constexpr int kLdsRec = kTileWaves * NC * 32 + NC * 4;
-  static constexpr int kLdsMain = (NC * RS * 16 > kLdsRec) ? NC * RS * 16 : kLdsRec;
+  // each wave's current weight tile, 16 rows of CPRP chunks at a row stride of CPRP + 1 chunks
+  // (the 16 rows of one fragment read then fall on distinct banks); it shares its space with
+  // the staged activations (a barrier separates them)
+  static constexpr int kSW = CPRP + 1;
+  // two tiles in flight (XA and XB) when the activation fragments and the epilogue leave the
+  // registers for it, else one (XA)
+  static constexpr bool DUAL =
+      NCB * KS < 48 || (NCB * KS == 48 && !ZOUT && (EPI == kEpiStats || EPI == kEpiArgmax));
+  static constexpr int kLdsSlots = kTileWaves * 16 * kSW * 16;
+  static constexpr int kLdsMain0 = (NC * RS * 16 > kLdsRec) ? NC * RS * 16 : kLdsRec;
+  static constexpr int kLdsMain = kLdsMain0 > kLdsSlots ? kLdsMain0 : kLdsSlots;
   // side copies: a row stride of 68 floats keeps the 16 rows of one write on distinct banks
   static constexpr int kSideStride = kGroup + 4;
   static constexpr int kLds = kLdsMain + (HIST ? kTileHistRows * kTkBins * 4 : 0) +
@@ -74,8 +84,16 @@ struct TilePass {
 
   const TileArgs& a;
   uint4* smem;
+  uint4* slot;   // this wave's weight tile
   int l, w, col, qd;
-  uint32_t rowbytes, vbytes, lane_off;
+  uint32_t rowbytes, vbytes;
+  // a tile's loads repeat their row pattern every LP loads (64 LP chunks = LROWS whole rows):
+  // this lane's offsets in the first LP loads, from the tile's first row
+  static constexpr int LP = CPRP == 48 ? 3 : 1;
+  static constexpr int LROWS = LP * kWave / CPRP;
+  uint32_t loff[LP];
+  int soff[LP];   // slot index of this lane's chunk of the first LP loads
+  int foff;       // slot index of this lane's A fragment at k-step 0: row col, chunk qd
   int V32, NG, Mx;
   float c2;
   uint4 Bf[KS][NCB];
@@ -96,19 +114,33 @@ struct TilePass {
     c2 = a.invT * kLog2e;
     // (the host admits matrices of at most 0xFFFFFFF0 bytes and rows of exactly KS k-steps)
     vbytes = static_cast<uint32_t>(V32) * rowbytes;
-    lane_off = static_cast<uint32_t>(col) * rowbytes + static_cast<uint32_t>(qd) * 16;
+    slot = lds + w * 16 * kSW;
+#pragma unroll
+    for (int j = 0; j < LP; ++j) {
+      const int f = j * kWave + l, row = f / CPRP, ch = f - row * CPRP;
+      loff[j] = static_cast<uint32_t>(row) * rowbytes + static_cast<uint32_t>(ch) * 16;
+      soff[j] = row * kSW + ch;
+    }
+    foff = col * kSW + qd;
   }
 
-  // Tile t of group g: lane (col, qd) of load j holds row col, bytes 64 j + 16 qd .. +16 (the A
-  // operand).  The descriptor starts at the tile's first row (or at V past the last row) and
-  // reaches to the end of the matrix, so rows past V read zero.  Scalar arithmetic only: the
-  // prefetch issues no vector instruction besides the loads.
+  // Tile t of group g in row layout: load j brings the tile's chunks 64 j .. 64 j + 63 in row
+  // order (whole rows, full cache lines per instruction), lane l chunk 64 j + l.  The descriptor
+  // starts at the tile's first row (or at V past the last row: group NG is an empty range that
+  // reads zeros without touching memory) and reaches to the end of the matrix, so rows past V
+  // read zero.  Scalar arithmetic only besides the loads.
   __device__ __forceinline__ void tile_load(int g, int t, uint4 (&X)[KS]) const {
     const int r0 = g * kGroup + t * 16;
     const uint32_t b0 = r0 < V32 ? static_cast<uint32_t>(r0) * rowbytes : vbytes;
     const rsrc_t rs = make_rsrc(static_cast<const char*>(a.W) + b0, vbytes - b0);
 #pragma unroll
-    for (int j = 0; j < KS; ++j) X[j] = buffer_load16(rs, lane_off + static_cast<uint32_t>(j) * 64);
+    for (int j = 0; j < KS; ++j)
+      X[j] = buffer_load16(rs, loff[j % LP] + static_cast<uint32_t>(j / LP * LROWS) * rowbytes);
+  }
+  // the tile into this wave's LDS slot: chunk ch of row r at r * kSW + ch
+  __device__ __forceinline__ void stage_tile(const uint4 (&X)[KS]) const {
+#pragma unroll
+    for (int j = 0; j < KS; ++j) slot[soff[j % LP] + (j / LP) * LROWS * kSW] = X[j];
   }
 
   // Activations (16-byte chunks of the first K elements of each row of x), then through LDS into the
@@ -149,17 +181,26 @@ struct TilePass {
     return 0.f;
   }
 
+  // tile T of the group from the LDS slot: the A fragment of k-step j is row col, chunk 4 j + qd
   template <int T>
-  __device__ __forceinline__ void mma(const uint4 (&X)[KS]) {
+  __device__ __forceinline__ void mma() {
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) acc[T][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < KS; ++j) {
-      const bf16x8_t af = __builtin_bit_cast(bf16x8_t, X[j]);
+      const bf16x8_t af = __builtin_bit_cast(bf16x8_t, slot[foff + 4 * j]);
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb)
         acc[T][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, __builtin_bit_cast(bf16x8_t, Bf[j][cb]), acc[T][cb], 0, 0, 0);
     }
+    // one fragment read ahead of its MFMAs at a time (the registers hold the tiles in flight)
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+    for (int j = 1; j < KS; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x008, NCB, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, NCB, 0);
   }
 
   // raw logits of tile T: lane (col, qd) holds rows 16 T + 4 qd .. +3 of activation row cb*16+col
@@ -305,34 +346,67 @@ struct TilePass {
     }
   }
 
-  // Groups gw, gw + nw, ... of this wave; XA holds tile 0 of the first (already issued).
-  // Tile t + 1 (or the next group's tile 0) is loaded while tile t is multiplied; loads are
-  // straight-line (past the last group the current tile is re-read, cache-resident) and pinned
-  // above the MFMAs by scheduling barriers, so the wait before each MFMA leaves exactly the
-  // next tile in flight.
+  // Groups gw, gw + nw, ... of this wave; XA and XB hold tiles 0 and 1 of the first (already
+  // issued).  Each tile goes from its registers to the LDS slot, the registers take the load
+  // of the tile two ahead (past the last group: the empty range), and the MFMAs read their
+  // fragments from the slot, so two tiles are in flight while one is multiplied (one during
+  // the group's epilogue).
   __device__ __forceinline__ void run(int gw, int nw, uint4 (&XA)[KS], uint4 (&XB)[KS]) {
     const int iters = gw < NG ? (NG - gw + nw - 1) / nw : 0;
+    if constexpr (!DUAL) {
+      for (int i = 0; i < iters; ++i) {
+        const int g = gw + i * nw;
+        const int gn = i + 1 < iters ? g + nw : NG;
+        stage_tile(XA);
+        tile_load(g, 1, XA);
+        __builtin_amdgcn_sched_barrier(0);
+        const float gu = draw(g);   // (after the load is out: Philox overlaps it)
+        mma<0>();
+        store_z<0>(g);
+        stage_tile(XA);
+        tile_load(g, 2, XA);
+        __builtin_amdgcn_sched_barrier(0);
+        mma<1>();
+        store_z<1>(g);
+        stage_tile(XA);
+        tile_load(g, 3, XA);
+        __builtin_amdgcn_sched_barrier(0);
+        mma<2>();
+        store_z<2>(g);
+        stage_tile(XA);
+        tile_load(gn, 0, XA);
+        __builtin_amdgcn_sched_barrier(0);
+        mma<3>();
+        store_z<3>(g);
+        group_end(g, gu);
+      }
+      return;
+    }
     for (int i = 0; i < iters; ++i) {
       const int g = gw + i * nw;
-      const int gn = i + 1 < iters ? g + nw : g;
-      tile_load(g, 1, XB);
-      __builtin_amdgcn_sched_barrier(0);
-      const float gu = draw(g);
-      mma<0>(XA);
-      store_z<0>(g);
+      const int gn = i + 1 < iters ? g + nw : NG;
+      stage_tile(XA);
       tile_load(g, 2, XA);
       __builtin_amdgcn_sched_barrier(0);
-      mma<1>(XB);
-      store_z<1>(g);
+      const float gu = draw(g);   // (after the load is out: Philox overlaps it)
+      mma<0>();
+      store_z<0>(g);
+      stage_tile(XB);
       tile_load(g, 3, XB);
       __builtin_amdgcn_sched_barrier(0);
-      mma<2>(XA);
-      store_z<2>(g);
-      tile_load(gn, i + 1 < iters ? 0 : 3, XA);
+      mma<1>();
+      store_z<1>(g);
+      stage_tile(XA);
+      tile_load(gn, 0, XA);
       __builtin_amdgcn_sched_barrier(0);
-      mma<3>(XB);
+      mma<2>();
+      store_z<2>(g);
+      stage_tile(XB);
+      mma<3>();
       store_z<3>(g);
       group_end(g, gu);
+      tile_load(gn, 1, XB);   // after the epilogue, whose registers it would otherwise hold
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
@@ -390,10 +464,12 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_head_tile(TileArgs a) {
   {
     uint4 xv[TilePass<NCB, KS, ZOUT, EPI>::XPER];
     p.stage_issue(xv);
-    p.tile_load(gw < p.NG ? gw : 0, 0, XA);
+    p.tile_load(gw < p.NG ? gw : p.NG, 0, XA);
+    if constexpr (TilePass<NCB, KS, ZOUT, EPI>::DUAL) p.tile_load(gw < p.NG ? gw : p.NG, 1, XB);
     __builtin_amdgcn_sched_barrier(0);
     p.hist_clear();   // (made visible by the staging barrier)
     p.stage_finish(xv);
+    __syncthreads();   // the weight slots reuse the staged activations' space
   }
   p.run(gw, nw, XA, XB);
   if constexpr (TilePass<NCB, KS, ZOUT, EPI>::STATS || TilePass<NCB, KS, ZOUT, EPI>::AMAX)
@@ -552,7 +628,9 @@ int tile_ncb(int64_t M) { return static_cast<int>((M + 15) / 16); }
 int tile_lds(int ncb, int ks) {
   const int stage = ncb * 16 * (ks * 4 + 4) * 16;
   const int rec = kTileWaves * ncb * 16 * static_cast<int>(sizeof(Partial));
-  return stage > rec ? stage : rec;
+  const int slots = kTileWaves * 16 * (ks * 4 + 1) * 16;
+  const int m = stage > rec ? stage : rec;
+  return m > slots ? m : slots;
 }
 
 template <int NCB, int KS, bool ZOUT, int EPI>
