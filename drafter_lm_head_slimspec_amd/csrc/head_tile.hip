@@ -70,10 +70,10 @@ struct TilePass {
   // (the 16 rows of one fragment read then fall on distinct banks); it shares its space with
   // the staged activations (a barrier separates them)
   static constexpr int kSW = CPRP + 1;
-  // two tiles in flight (XA and XB) when the activation fragments and the epilogue leave the
-  // registers for it, else one (XA)
-  static constexpr bool DUAL =
-      NCB * KS < 48 || (NCB * KS == 48 && !ZOUT && (EPI == kEpiStats || EPI == kEpiArgmax));
+  // two tiles in flight (XA and XB) for rows of at most 256 elements, else one (XA).  Measured
+  // on one machine: the SpecVocab scorer (256-element rows) 18.6 us with one tile in flight,
+  // 17.9 with two; the Llama-shaped W_up pass (512) 27.5 with one, 28.4 with two
+  static constexpr bool DUAL = KS <= 8;
   static constexpr int kLdsSlots = kTileWaves * 16 * kSW * 16;
   static constexpr int kLdsMain0 = (NC * RS * 16 > kLdsRec) ? NC * RS * 16 : kLdsRec;
   static constexpr int kLdsMain = kLdsMain0 > kLdsSlots ? kLdsMain0 : kLdsSlots;
