@@ -484,6 +484,62 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_head_tile(TileArgs a) {
 // recomputing the winning group's logits.
 // NT threads of the workgroup take part; zs holds 64 floats, rec NT/64 Partials.
 // ----------------------------------------------------------------------------------------
+// The Partials of the NT threads merged by the workgroup, the result in every thread.  Each wave
+// reduces the fields separately: the largest m by a max butterfly, each lane's s rescaled to it
+// once and summed by an add butterfly, the group score and the argmax by compare butterflies (no
+// exponential inside a butterfly); the waves' records then merge through LDS.
+template <int NT>
+__device__ __forceinline__ Partial block_partial_merge(const Partial& a, Partial* rec) {
+  const int l = lane_id(), w = wave_id();
+  constexpr int nwaves = NT / kWave;
+  float mw = a.m;
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) mw = fmaxf(mw, xor_lane(mw, s));
+  float sw = a.m == -INFINITY ? 0.f : a.s * __expf(a.m - mw);
+  float gs = a.gscore, zm = a.zmax;
+  int32_t gi = a.g, zi = a.zid;
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) {
+    sw += xor_lane(sw, s);
+    argmax_merge(gs, gi, xor_lane(gs, s), xor_lane(gi, s));
+    argmax_merge(zm, zi, xor_lane(zm, s), xor_lane(zi, s));
+  }
+  if (l == 0) {
+    Partial p = partial_empty();
+    p.m = mw;
+    p.s = sw;
+    p.gscore = gs;
+    p.g = gi;
+    p.zmax = zm;
+    p.zid = zi;
+    rec[w] = p;
+  }
+  __syncthreads();
+  Partial r = rec[0];
+#pragma unroll
+  for (int i = 1; i < nwaves; ++i) partial_merge(r, rec[i]);
+  return r;
+}
+
+// Sums over the wave of 16 values per lane, transposed: four exchanges that each halve the
+// values a lane holds, then two full ones, leave lane L with the total of value (L >> 2) mod 16
+// (17 exchanges instead of 16 x 6).
+__device__ __forceinline__ float wave_sum16(const float (&v)[16]) {
+  const int l = lane_id();
+  float a[8], b[4], c[2];
+  const bool h5 = (l & 32) != 0, h4 = (l & 16) != 0, h3 = (l & 8) != 0, h2 = (l & 4) != 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a[i] = (h5 ? v[i + 8] : v[i]) + xor_lane(h5 ? v[i] : v[i + 8], 32);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) b[i] = (h4 ? a[i + 4] : a[i]) + xor_lane(h4 ? a[i] : a[i + 4], 16);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) c[i] = (h3 ? b[i + 2] : b[i]) + xor_lane(h3 ? b[i] : b[i + 2], 8);
+  float d = (h2 ? c[1] : c[0]) + xor_lane(h2 ? c[0] : c[1], 4);
+  d += xor_lane(d, 2);
+  d += xor_lane(d, 1);
+  return d;
+}
+
 template <bool BF16, int NT>
 __device__ __forceinline__ void finalize_row(const FinalizeArgs& f, int m, float* zs, Partial* rec) {
   const int l = lane_id(), w = wave_id();
@@ -491,11 +547,7 @@ __device__ __forceinline__ void finalize_row(const FinalizeArgs& f, int m, float
   Partial acc = partial_empty();
   const Partial* pp = f.partials + static_cast<int64_t>(m) * f.partials_ld;
   for (int p = threadIdx.x; p < f.P; p += nthreads) partial_merge(acc, pp[p]);
-  wave_partial_merge(acc);
-  if (l == 0) rec[w] = acc;
-  __syncthreads();
-  acc = l < nwaves ? rec[l] : partial_empty();
-  wave_partial_merge(acc);   // the same result in every wave
+  acc = block_partial_merge<NT>(acc, rec);
   const float lse = acc.m + logf(acc.s);
 
   int32_t tok;
@@ -569,10 +621,15 @@ __device__ __forceinline__ void finalize_row(const FinalizeArgs& f, int m, float
 #pragma unroll
           for (int j = 0; j < RB; ++j) z[j] = chunk_dot<BF16>(wv[qq][j], xv[qq], z[j]);
       }
+      if constexpr (RB == 16) {
+        const float s = wave_sum16(z);
+        if ((l & 3) == 0) zs[w * rpw + j0 + (l >> 2)] = s;
+      } else {
 #pragma unroll
-      for (int j = 0; j < RB; ++j) {
-        const float s = wave_sum(z[j]);
-        if (l == 0) zs[w * rpw + j0 + j] = s;
+        for (int j = 0; j < RB; ++j) {
+          const float s = wave_sum(z[j]);
+          if (l == 0) zs[w * rpw + j0 + j] = s;
+        }
       }
     }
     __syncthreads();
