@@ -61,19 +61,23 @@ __device__ __forceinline__ const void* row_ptr(const VerifyArgs& a, int64_t b, i
   return static_cast<const char*>(a.draft) + static_cast<size_t>((b * a.gamma + t) * a.V) * es;
 }
 
-// block-wide fixed-order merge of one Partial per thread; result valid in thread 0
+// block-wide fixed-order merge of one Partial per thread; result valid in thread 0.  Each wave
+// reduces the fields separately (the largest m by a max butterfly, each lane's s rescaled to it
+// once and summed, the group score and the argmax by compare butterflies: no exponential inside
+// a butterfly), then the waves' records merge through LDS
 __device__ __forceinline__ Partial block_merge(Partial p, Partial* red4) {
+  float mw = p.m;
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) mw = fmaxf(mw, xor_lane(mw, s));
+  float sw = p.m == -INFINITY ? 0.f : p.s * __expf(p.m - mw);
 #pragma unroll
   for (int s = 32; s >= 1; s >>= 1) {
-    Partial q;
-    q.m = xor_lane(p.m, s);
-    q.s = xor_lane(p.s, s);
-    q.gscore = xor_lane(p.gscore, s);
-    q.g = xor_lane(p.g, s);
-    q.zmax = xor_lane(p.zmax, s);
-    q.zid = xor_lane(p.zid, s);
-    partial_merge(p, q);
+    sw += xor_lane(sw, s);
+    argmax_merge(p.gscore, p.g, xor_lane(p.gscore, s), xor_lane(p.g, s));
+    argmax_merge(p.zmax, p.zid, xor_lane(p.zmax, s), xor_lane(p.zid, s));
   }
+  p.m = mw;
+  p.s = sw;
   const int w = wave_id(), nw = blockDim.x / kWave;
   if (lane_id() == 0) red4[w] = p;
   __syncthreads();
