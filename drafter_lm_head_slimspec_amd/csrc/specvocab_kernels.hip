@@ -475,6 +475,24 @@ struct GatherOut {
   uint32_t* counters;   // [M, kTkCounterStride]: word 2 counts the row's finished workgroups
 };
 
+// Sums over the wave of 8 values per lane, transposed: three exchanges that each halve the
+// values a lane holds, then three full ones, leave lane L with the total of value (L >> 3) mod 8
+// (10 exchanges instead of 8 x 6).
+__device__ __forceinline__ float wave_sum8(const float (&v)[8]) {
+  const int l = lane_id();
+  float b[4], c[2];
+  const bool h5 = (l & 32) != 0, h4 = (l & 16) != 0, h3 = (l & 8) != 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) b[i] = (h5 ? v[i + 4] : v[i]) + xor_lane(h5 ? v[i] : v[i + 4], 32);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) c[i] = (h4 ? b[i + 2] : b[i]) + xor_lane(h4 ? b[i] : b[i + 2], 16);
+  float d = (h3 ? c[1] : c[0]) + xor_lane(h3 ? c[0] : c[1], 8);
+  d += xor_lane(d, 4);
+  d += xor_lane(d, 2);
+  d += xor_lane(d, 1);
+  return d;
+}
+
 // zl: LDS [k] logits then [ceil(k / 64)] group sums; the logits are read with device-coherent
 // loads (other workgroups of this kernel wrote them)
 __device__ void gather_finalize_row(const float* __restrict__ zbuf, const int32_t* __restrict__ idx,
@@ -485,6 +503,10 @@ __device__ void gather_finalize_row(const float* __restrict__ zbuf, const int32_
   const int ng = (k + kGroup - 1) / kGroup;
   float* Lg = zl + k;
   float mx = -INFINITY;
+  // sampling with at most 64 groups: the group Gumbels depend on nothing loaded, so wave 0
+  // computes them (lane g, group g) while the logits are in flight
+  const bool early = o.mode != 0 && ng <= kWave && w == 0;
+  float gu_early = 0.f;
   {
     // kGfBatch loads per thread issued together (one memory round trip per batch)
     const rsrc_t zr = make_rsrc(z, static_cast<uint32_t>(k) * 4u);
@@ -496,6 +518,7 @@ __device__ void gather_finalize_row(const float* __restrict__ zbuf, const int32_
         v[q] = __builtin_amdgcn_raw_buffer_load_b32(zr, j < k ? static_cast<uint32_t>(j) * 4u : kOutOfRange, 0,
                                                     kCoherent);
       }
+      if (j0 == 0 && early && l < ng) gu_early = gumbel(philox_uniform(o.seed, o.offset, kDraftGroup, m, l));
 #pragma unroll
       for (int q = 0; q < kGfBatch; ++q) {
         const int j = j0 + q * kGfThreads + static_cast<int>(threadIdx.x);
@@ -515,11 +538,15 @@ __device__ void gather_finalize_row(const float* __restrict__ zbuf, const int32_
   const float c = o.invT * kLog2e;
   const float mxc = mx * c;
   // group sums (base 2, shifted by the row max) and the row sum from them
-  for (int g = w; g < ng; g += kGfWaves) {
-    const int j = g * kGroup + l;
-    const float t = j < k ? fast_exp2(fmaf(zl[j], c, -mxc)) : 0.f;
-    const float gs = wave_sum(t);
-    if (l == 0) Lg[g] = gs;
+  for (int g0 = w * 8; g0 < ng; g0 += kGfWaves * 8) {   // eight consecutive groups per wave
+    float t[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int j = (g0 + q) * kGroup + l;
+      t[q] = (g0 + q < ng && j < k) ? fast_exp2(fmaf(zl[j], c, -mxc)) : 0.f;
+    }
+    const float gs = wave_sum8(t);   // lane L: group g0 + (L >> 3) mod 8
+    if ((l & 7) == 0 && g0 + (l >> 3) < ng) Lg[g0 + (l >> 3)] = gs;
   }
   __syncthreads();
   float sm = 0.f;
@@ -553,7 +580,8 @@ __device__ void gather_finalize_row(const float* __restrict__ zbuf, const int32_
         const float gs = Lg[g];
         if (gs > 0.f) {
           const float L = (mxc + log2f(gs)) * kLn2;
-          argmax_merge(best, bg, L + gumbel(philox_uniform(o.seed, o.offset, kDraftGroup, m, g)), g);
+          const float gu = early ? gu_early : gumbel(philox_uniform(o.seed, o.offset, kDraftGroup, m, g));
+          argmax_merge(best, bg, L + gu, g);
         }
       }
       wave_argmax(best, bg);
