@@ -602,15 +602,17 @@ __device__ void gather_finalize_row(const float* __restrict__ zbuf, const int32_
 }
 
 // ----------------------------------------------------------------------------------------
-// gather + exact logits, then the row's softmax: grid (ceil(k / 8), M); each wave computes
-// kGatherRows candidates of row m; the workgroup that finishes row m last runs its softmax and
-// selection (gather_finalize_row), so the call needs no separate finalize launch.
+// gather + exact logits, then the row's softmax: grid (ceil(k / (4 RPW)), M); each wave
+// computes RPW candidates of row m; the workgroup that finishes row m last runs its softmax and
+// selection (gather_finalize_row), so the call needs no separate finalize launch.  RPW = 4 for
+// one or two rows (fewer workgroups to count in: measured at M = 1, 15.8 -> 15.0 us), else 2
+// (at M = 16, 4 measured 52.7 against 53.0 us, 1 slower everywhere).
 // ----------------------------------------------------------------------------------------
-constexpr int kGatherRows = 2;   // candidate rows per wave, all loads in flight together
 
-// z'[m, j] = U[K[m, j], :] . h[m, :].  Each wave takes kGatherRows candidates; a candidate's
-// row is one buffer descriptor (an invalid id gets an empty range, so its loads read zero).
-template <bool BF16, int CPL>
+// z'[m, j] = U[K[m, j], :] . h[m, :].  Each wave takes RPW candidates, all loads in flight
+// together; a candidate's row is one buffer descriptor (an invalid id gets an empty range, so
+// its loads read zero).
+template <bool BF16, int CPL, int RPW>
 __global__ __launch_bounds__(kGfThreads) void k_gather_exact(const void* __restrict__ U,
                                                              const void* __restrict__ h,
                                                              const int32_t* __restrict__ idx, int C,
@@ -622,10 +624,10 @@ __global__ __launch_bounds__(kGfThreads) void k_gather_exact(const void* __restr
   const int k = o.k;
   const int l = lane_id(), w = wave_id();
   const uint32_t rowbytes = static_cast<uint32_t>(C) * 16;
-  const int j0 = (blockIdx.x * (blockDim.x / kWave) + w) * kGatherRows;
-  uint4 wv[kGatherRows][CPL];
+  const int j0 = (blockIdx.x * (blockDim.x / kWave) + w) * RPW;
+  uint4 wv[RPW][CPL];
 #pragma unroll
-  for (int jj = 0; jj < kGatherRows; ++jj) {
+  for (int jj = 0; jj < RPW; ++jj) {
     const int j = j0 + jj;
     const int id = j < k ? idx[static_cast<size_t>(m) * k + j] : -1;
     const bool ok = id >= 0 && id < V;   // ids come from the top-k; guarded anyway
@@ -645,7 +647,7 @@ __global__ __launch_bounds__(kGfThreads) void k_gather_exact(const void* __restr
     hr[q] = buffer_load16(hrs, c < C ? static_cast<uint32_t>(c) * 16 : kOutOfRange);
   }
 #pragma unroll
-  for (int jj = 0; jj < kGatherRows; ++jj) {
+  for (int jj = 0; jj < RPW; ++jj) {
     float z = 0.f;
 #pragma unroll
     for (int q = 0; q < CPL; ++q) z = chunk_dot<BF16>(wv[jj][q], hr[q], z);
@@ -656,18 +658,26 @@ __global__ __launch_bounds__(kGfThreads) void k_gather_exact(const void* __restr
     gather_finalize_row(zbuf, idx, o, m, zl, red_f);
 }
 
+template <bool BF16, int CPL, int RPW>
+static hipError_t run_gather_rpw(const void* U, const void* h, const int32_t* idx, int C, int64_t M,
+                                 int64_t V, float* zbuf, const GatherOut& o, hipStream_t st) {
+  const int per_wg = kGfWaves * RPW;
+  const dim3 grid(static_cast<unsigned>((o.k + per_wg - 1) / per_wg), static_cast<unsigned>(M));
+  const int lds = static_cast<int>((o.k + (o.k + kGroup - 1) / kGroup) * 4);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_gather_exact<BF16, CPL, RPW>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((k_gather_exact<BF16, CPL, RPW>), grid, dim3(kGfThreads), lds, st, U, h, idx, C,
+                     static_cast<int>(V), zbuf, o);
+  return hipGetLastError();
+}
+
 template <bool BF16, int CPL>
 static hipError_t run_gather(const void* U, const void* h, const int32_t* idx, int C, int64_t M,
                              int64_t V, float* zbuf, const GatherOut& o, hipStream_t st) {
-  const int per_wg = kGfWaves * kGatherRows;
-  const dim3 grid(static_cast<unsigned>((o.k + per_wg - 1) / per_wg), static_cast<unsigned>(M));
-  const int lds = static_cast<int>((o.k + (o.k + kGroup - 1) / kGroup) * 4);
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_gather_exact<BF16, CPL>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_gather_exact<BF16, CPL>), grid, dim3(kGfThreads), lds, st, U, h, idx, C,
-                     static_cast<int>(V), zbuf, o);
-  return hipGetLastError();
+  if constexpr (CPL <= 8)
+    if (M <= 2) return run_gather_rpw<BF16, CPL, 4>(U, h, idx, C, M, V, zbuf, o, st);
+  return run_gather_rpw<BF16, CPL, 2>(U, h, idx, C, M, V, zbuf, o, st);
 }
 
 template <bool BF16>
