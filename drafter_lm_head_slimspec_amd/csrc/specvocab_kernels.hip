@@ -14,7 +14,7 @@ namespace sh {
 
 // ----------------------------------------------------------------------------------------
 // Top-k as a threshold search over the order keys, spread over many workgroups per row:
-//   k_topk_hist    grid (chunks, M): histogram of the top 12 key bits of each 2048-score
+//   k_topk_hist    grid (V / 4096, M): histogram of the top 12 key bits of each 4096-score
 //                  chunk in LDS, added into the row histogram [M, 4096] in the workspace.
 //   k_topk_select  grid (chunks, M): every workgroup finds the threshold bin b* (the bin
 //                  where the count of larger keys reaches k) from the row histogram, marks
@@ -36,23 +36,28 @@ constexpr int kTkChunk = kTkThreads * kTkPerThread;
 constexpr int kTkWaves = kTkThreads / kWave;
 constexpr int kTkShift2 = 8;         // second level: key bits 19..8
 constexpr uint32_t kTkDirect = 512;  // in-bin keys of a workgroup added to the second histogram one by one
+// the histogram pass takes twice the select's chunk: half the workgroups, each adding its bins
+// to the row's histogram once (measured at 16 rows: 7.6 -> 6.8 us; the select at 16 scores per
+// thread slowed more than that at one row, so it keeps 8)
+constexpr int kTkHistPerThread = 2 * kTkPerThread;
+constexpr int kTkHistChunk = kTkThreads * kTkHistPerThread;
 
 __global__ __launch_bounds__(kTkThreads) void k_topk_hist(TopkArgs a) {
   __shared__ uint32_t h[kTkBins];
   const int m = blockIdx.y;
-  const int64_t c0 = static_cast<int64_t>(blockIdx.x) * kTkChunk;
+  const int64_t c0 = static_cast<int64_t>(blockIdx.x) * kTkHistChunk;
   const int tid = threadIdx.x;
   const rsrc_t rs = make_rsrc(a.scores + static_cast<size_t>(m) * a.V, static_cast<uint32_t>(a.V) * 4u);
-  uint32_t raw[kTkPerThread];
+  uint32_t raw[kTkHistPerThread];
 #pragma unroll
-  for (int j = 0; j < kTkPerThread; ++j) {
+  for (int j = 0; j < kTkHistPerThread; ++j) {
     const int64_t e = c0 + j * kTkThreads + tid;
     raw[j] = buffer_load4(rs, e < a.V ? static_cast<uint32_t>(e) * 4u : kOutOfRange);
   }
   for (int i = tid; i < kTkBins; i += kTkThreads) h[i] = 0u;
   __syncthreads();
 #pragma unroll
-  for (int j = 0; j < kTkPerThread; ++j) {
+  for (int j = 0; j < kTkHistPerThread; ++j) {
     const int64_t e = c0 + j * kTkThreads + tid;
     if (e < a.V) atomicAdd(&h[order_key(__uint_as_float(raw[j])) >> kTkShift], 1u);
   }
@@ -427,8 +432,9 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
   const dim3 grid(static_cast<unsigned>(a.chunks), static_cast<unsigned>(a.M));
   hipError_t e;
   if (!a.hist_ready) {   // else the scorer built the row histograms while writing the scores
+    const dim3 hgrid(static_cast<unsigned>((a.V + kTkHistChunk - 1) / kTkHistChunk), static_cast<unsigned>(a.M));
     TraceScope ts("topk_hist", st);
-    hipLaunchKernelGGL(k_topk_hist, grid, dim3(kTkThreads), 0, st, a);
+    hipLaunchKernelGGL(k_topk_hist, hgrid, dim3(kTkThreads), 0, st, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
