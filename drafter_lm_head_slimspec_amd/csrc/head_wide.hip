@@ -9,8 +9,10 @@
 //                 lines) into an LDS tile while the next pair's rows are in flight in
 //                 registers.  The activation rows form 16-row column blocks dealt round-robin
 //                 to the waves (block b to wave b mod 8, at most two per wave), so the two
-//                 waves of a SIMD together hold a quarter of the blocks and one wave's VALU
-//                 epilogue can issue while the other's MFMAs run.  Each wave multiplies the
+//                 waves of a SIMD (waves w and w + 4: the SIMD field of HW_ID, read on this
+//                 GPU) together hold a quarter of the blocks and one wave's VALU epilogue can
+//                 issue while the other's MFMAs run.  The group Gumbels of the workgroup's
+//                 whole range are drawn into LDS while its first loads are in flight.  Each wave multiplies the
 //                 tile by its blocks (B fragments in registers for the whole pass) on
 //                 v_mfma_f32_16x16x32_bf16, reading the A fragments from LDS, and folds each
 //                 group into the running state of its rows exactly as the tile kernel does:
@@ -34,6 +36,14 @@ typedef float wf32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kWideThreads = 512;   // eight waves, two per SIMD
 constexpr int kWideWaves = kWideThreads / kWave;
 constexpr int kWideStats = 1, kWideArgmax = 2;
+// LDS bytes of the pair's tile and its spare chunks, and the blocks [TB][kWideMaxRows][4] floats
+// of the Gumbel table behind them: as many as fit in 160 KB, at most 8 (a workgroup's range at
+// the GPT-OSS shape spans at most 5; a longer range falls back to a rolling table of 2)
+constexpr int wide_lds_base(int ks) { return (2 * kGroup * (ks * 4 + 2) + kWave) * 16; }
+constexpr int wide_gtab_blocks(int ks) {
+  return (160 * 1024 - wide_lds_base(ks)) / (kWideMaxRows * 16) < 8 ? (160 * 1024 - wide_lds_base(ks)) / (kWideMaxRows * 16)
+                                                                   : 8;
+}
 
 }  // namespace
 
@@ -105,15 +115,44 @@ __device__ __forceinline__ void wide_wave(const TileArgs& a, uint4* tile) {
   float rm = -INFINITY, rsum = 0.f, gbest = -INFINITY, bz = -INFINITY;
   int32_t gid = 0x7fffffff, bi = 0x7fffffff;
 
-  // Gumbel(u) of activation row m for group g: one Philox block holds groups 4 q .. 4 q + 3,
-  // and a workgroup walks consecutive groups, so thread m of the workgroup computes each block
-  // once (gumbel_blocks) into gtab[q mod 2][m][0..3], read here by the wave owning row m
-  float* gtab = reinterpret_cast<float*>(tile + 2 * kGroup * RS + kWave);   // [2][kWideMaxRows][4]
+  // the workgroup's groups are the consecutive range [gs, ge), taken in pairs (g, g + 1):
+  // while a pair is multiplied out of the LDS tile, the next pair's rows are in flight in
+  // registers; storing a pair waits for every outstanding load, which is exactly that pair.
+  // Past the range the loads go to group NG, an empty buffer range: they return zeros and
+  // touch no memory (re-reading a group of the range would miss the cache by then: a range
+  // is ~0.5 MB and 32 workgroups share one XCD's L2)
+  const int G = static_cast<int>(gridDim.x);
+  const int gs = static_cast<int>((static_cast<int64_t>(blockIdx.x) * NG) / G);
+  const int ge = static_cast<int>((static_cast<int64_t>(blockIdx.x + 1) * NG) / G);
+  auto clampg = [&](int g) { return g < ge ? g : NG; };
+  uint4 RA[PER], RB[PER];
+  gload(clampg(gs), RA);
+  gload(clampg(gs + 1), RB);
+
+  // Gumbel(u) of activation row m for group g: one Philox block holds groups 4 q .. 4 q + 3.
+  // Every block of the range [q0, q0 + nq) is computed once per workgroup into gtab[q - q0][m]
+  // while the first pair's loads are in flight (`whole`); a range with more blocks than the
+  // table holds computes them as the walk reaches them (gumbel_blocks) into gtab[q mod 2][m].
+  // Read by the wave owning row m.  (Measured at the GPT-OSS shape against computing every
+  // block between the barriers: the pass 46.0 -> 43.9 us; with the split load issue below, 41.5.)
+  float* gtab = reinterpret_cast<float*>(tile + 2 * kGroup * RS + kWave);   // [TB][kWideMaxRows][4]
+  const int q0 = gs >> 2, nq = ge > gs ? ((ge - 1) >> 2) - q0 + 1 : 0;
+  const bool whole = STATS && a.sample != 0 && nq <= wide_gtab_blocks(KS);
+  if (whole) {
+    for (int i = tid; i < nq * Mx; i += kWideThreads) {
+      const int qq = i / Mx, m = i - qq * Mx;
+      uint64_t wd[4];
+      philox_block(a.seed, a.offset, kDraftGroup, static_cast<uint64_t>(a.row0 + m), static_cast<uint64_t>(q0 + qq) * 4, wd);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) gtab[qq * kWideMaxRows * 4 + m * 4 + j] = gumbel(word_to_uniform(wd[j]));
+    }
+  }
   auto draw = [&](int g) -> float {
     float gu = 0.f;
     if constexpr (STATS) {
       const int m = row_of(qd);
-      if (a.sample != 0 && qd < NCBW && m < Mx) gu = gtab[((g >> 2) & 1) * kWideMaxRows * 4 + m * 4 + (g & 3)];
+      if (a.sample != 0 && qd < NCBW && m < Mx)
+        gu = gtab[(whole ? (g >> 2) - q0 : ((g >> 2) & 1)) * kWideMaxRows * 4 + m * 4 + (g & 3)];
     }
     return gu;
   };
@@ -121,7 +160,7 @@ __device__ __forceinline__ void wide_wave(const TileArgs& a, uint4* tile) {
   int q_done = -1;
   auto gumbel_blocks = [&](int g) {
     if constexpr (STATS) {
-      if (a.sample != 0) {
+      if (a.sample != 0 && !whole) {
         for (int q = g >> 2; q <= ((g + 1) >> 2); ++q) {   // uniform over the workgroup
           if (q <= q_done) continue;
           q_done = q;
@@ -252,19 +291,12 @@ __device__ __forceinline__ void wide_wave(const TileArgs& a, uint4* tile) {
   };
   wf32x4_t accA[4][NCBW > 0 ? NCBW : 1];
 
-  // the workgroup's groups are the consecutive range [gs, ge), taken in pairs (g, g + 1):
-  // while a pair is multiplied out of the LDS tile, the next pair's rows are in flight in
-  // registers; storing a pair waits for every outstanding load, which is exactly that pair.
-  // Past the range the loads go to group NG, an empty buffer range: they return zeros and
-  // touch no memory (re-reading a group of the range would miss the cache by then: a range
-  // is ~0.5 MB and 32 workgroups share one XCD's L2)
-  const int G = static_cast<int>(gridDim.x);
-  const int gs = static_cast<int>((static_cast<int64_t>(blockIdx.x) * NG) / G);
-  const int ge = static_cast<int>((static_cast<int64_t>(blockIdx.x + 1) * NG) / G);
-  auto clampg = [&](int g) { return g < ge ? g : NG; };
-  uint4 RA[PER], RB[PER];
-  gload(clampg(gs), RA);
-  gload(clampg(gs + 1), RB);
+  // The next pair's loads go out in two halves: the first group's before the multiplications,
+  // the second's after the first group's epilogue.  Issued together, the waves issuing last
+  // stalled on them (back-pressure of the whole chip's burst) before their own MFMAs; measured
+  // at the GPT-OSS shape (same machine, Gumbel table as above): 43.9 -> 41.5 us, and 38.0-39.0
+  // against 39.2-39.8 with the second half after the second group's MFMAs or both halves
+  // after the first group's.
   for (int g = gs; g < ge; g += 2) {
     __syncthreads();   // every wave is done with the previous pair's tile (and Gumbels)
     gstore(RA, 0);
@@ -272,14 +304,16 @@ __device__ __forceinline__ void wide_wave(const TileArgs& a, uint4* tile) {
     gumbel_blocks(g);   // a block is overwritten only two blocks later, after its last group
     __syncthreads();
     gload(clampg(g + 2), RA);
-    gload(clampg(g + 3), RB);
     if constexpr (NCBW > 0) {
       mma(0, accA, std::true_type{});
       epi(g, draw(g), accA);
+      gload(clampg(g + 3), RB);
       if (g + 1 < ge) {
         mma(1, accA, std::true_type{});
         epi(g + 1, draw(g + 1), accA);
       }
+    } else {
+      gload(clampg(g + 3), RB);
     }
   }
   // one Partial per activation row per workgroup (each row belongs to one lane)
@@ -301,7 +335,7 @@ __device__ __forceinline__ void wide_wave(const TileArgs& a, uint4* tile) {
 template <int KS, int EPI>
 __global__ __launch_bounds__(kWideThreads, 1) void k_head_wide(TileArgs a) {
   // [2][64][RS] the current pair of groups, 64 spare chunks, then the Gumbel table
-  // [2][kWideMaxRows][4] floats
+  // [TB][kWideMaxRows][4] floats
   extern __shared__ uint4 tile[];
   const int w = wave_id();
   const int nb = (a.M + 15) / 16;   // column blocks, at most 2 * kWideWaves
@@ -321,7 +355,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void k_head_wide(TileArgs a) {
 namespace {
 
 int wide_ks(int64_t K) { return static_cast<int>((K + 127) / 128) * 4; }   // 4, 8, 12 or 16
-int wide_lds(int ks) { return (2 * kGroup * (ks * 4 + 2) + kWave) * 16 + 2 * kWideMaxRows * 4 * 4; }
+int wide_lds(int ks) { return wide_lds_base(ks) + wide_gtab_blocks(ks) * kWideMaxRows * 4 * 4; }
 // VGPRs per lane of a two-block wave: activation fragments, two row buffers (eight waves share
 // each group's loads), accumulators, offsets and state
 int wide_regs(int ncbw, int ks) { return ks * ncbw * 4 + 2 * (ks / 2) * 4 + 16 * ncbw + ks + 64; }
