@@ -142,6 +142,13 @@ def test_lowrank_wide(case, mode, T):
     _lowrank(*case, mode, T, want_logits=False)
 
 
+# rows of 512 elements leave room for six Philox blocks of group draws in the wide pass's LDS
+# table; with 400000 rows (24-25 groups per workgroup) some workgroups' ranges span seven
+# blocks and draw them as the walk reaches them, the others from the table
+def test_lowrank_wide_long_range():
+    _lowrank(256, 400000, 512, 65, "bf16", "sample", 1.0, want_logits=False)
+
+
 DENSE_SMALL = [
     (256, 1024, 4, "f32"),
     (520, 1000, 3, "bf16"),    # 65 chunks per row: two chunks per lane, masked
