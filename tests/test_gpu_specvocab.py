@@ -137,6 +137,34 @@ def test_topk_edge_shapes(V, k):
         np.testing.assert_array_equal(got[m], heads.topk_ascending(s[m].astype(np.float64), k))
 
 
+@pytest.mark.parametrize("V,k", [(5, 3), (64, 64), (2049, 100), (4097, 2048), (30000, 1), (20000, 9000),
+                                 (151936, 2048)])
+def test_topk_one_and_two_rows(V, k):
+    """One or two rows take the one-workgroup selection (threshold bin, the row streamed into
+    LDS, the finish): each kind of row alone and in pairs, among them every score equal (all V
+    keys inside the threshold bin, so the candidate list spills past LDS to the global list),
+    rounded scores with many exact ties, a tied block of zeros including -0.0, and scores that
+    share their top 12 key bits and differ below."""
+    rng = np.random.default_rng(11 * V + k)
+    s = rng.standard_normal((8, V)).astype(np.float32)
+    s[1] = np.round(s[1] * 4) / 4
+    s[2, : V // 2] = 0.0
+    s[2, 1::7] = -0.0
+    s[3] = -np.abs(s[3]) * 1e30
+    s[4] = 1.5
+    s[5, ::3] = s[5, 0]
+    s[6] = rng.permutation(np.float32(1.0) + np.arange(V, dtype=np.float32) * np.float32(2.0 ** -23))
+    want = [heads.topk_ascending(s[m].astype(np.float64), k) for m in range(8)]
+    P.log(f"topk one/two rows V={V} k={k}")
+    for m in range(8):
+        got = sh.topk(torch.from_numpy(s[m:m + 1].copy()).cuda(), k).cpu().numpy()
+        np.testing.assert_array_equal(got[0], want[m])
+    for m in range(0, 8, 2):
+        got = sh.topk(torch.from_numpy(s[m:m + 2].copy()).cuda(), k).cpu().numpy()
+        np.testing.assert_array_equal(got[0], want[m])
+        np.testing.assert_array_equal(got[1], want[m + 1])
+
+
 def test_topk_on_a_dirty_workspace_repeats():
     """The workspace's contents on entry do not matter: calls on a workspace filled with
     junk, and repeated calls on one workspace, give the same ids."""
